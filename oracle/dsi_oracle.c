@@ -56,24 +56,27 @@ float orc_e4m3_decode(uint8_t b) {
 }
 
 /* Nearest e4m3 code to a finite x, ties to the code with the even mantissa,
- * saturating to +-448.  Written as a search over all 127 non-negative finite
- * codes, which is slow but obviously correct.  The sign of x is kept, so a
- * negative value that rounds to zero gives -0 (0x80). */
+ * saturating to +-448.  The non-negative finite codes 0x00..0x7E decode to
+ * strictly increasing values, so the nearest code is one of the two codes
+ * that bracket |x|: a binary search finds the largest code not above |x|,
+ * then the nearer of it and its successor is taken.  The sign of x is kept,
+ * so a negative value that rounds to zero gives -0 (0x80). */
 uint8_t orc_e4m3_encode(float x) {
   uint8_t sign = signbit(x) ? 0x80 : 0x00;
-  double a = fabs((double)x);
-  int best = 0, c;
-  double bestd;
+  double a = fabs((double)x), dlo, dhi;
+  int lo = 0, hi = 0x7E;
   if (a >= 448.0) return sign | 0x7E;
-  bestd = fabs(a - (double)orc_e4m3_decode(0));
-  for (c = 1; c <= 0x7E; c++) {
-    double d = fabs(a - (double)orc_e4m3_decode((uint8_t)c));
-    if (d < bestd || (d == bestd && (c & 1) == 0)) {
-      best = c;
-      bestd = d;
-    }
+  while (lo < hi) { /* largest code c with decode(c) <= a */
+    int mid = (lo + hi + 1) / 2;
+    if ((double)orc_e4m3_decode((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid - 1;
   }
-  return sign | (uint8_t)best;
+  dlo = a - (double)orc_e4m3_decode((uint8_t)lo);
+  dhi = (double)orc_e4m3_decode((uint8_t)(lo + 1)) - a;
+  if (dhi < dlo || (dhi == dlo && ((lo + 1) & 1) == 0)) lo = lo + 1;
+  return sign | (uint8_t)lo;
 }
 
 static uint32_t f32_bits(float x) {
