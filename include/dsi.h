@@ -1,0 +1,257 @@
+/*
+ * dsi.h — C ABI of the MI355X (gfx950) DeepSeek Sparse Attention "lightning
+ * indexer" hot path.
+ *
+ * What the path computes is defined on three web pages:
+ *   P1 = "V4.1 索引器接入稀疏 MQA logits" (summary of vLLM PR 56254): the
+ *        hierarchical (candidate-block) indexer — motivation, implementation
+ *        breakdown, key source snippets (candidate expansion kernel, row
+ *        metadata), review highlights.
+ *   P2 = "修复 DSV4 FlashInfer 稀疏 MLA 在打包 KV 布局下的地址错误" (summary of
+ *        vLLM PR 47493): packed-pool block span and the slot remap.
+ *   P3 = "DeepSeek V3.2 稀疏注意力 DSA 推理流程图解": cost table, per-layer data
+ *        flow, the six indexer steps ①–⑥, the prefill/decode table, pitfalls.
+ *
+ * Conventions shared by every call
+ *   - Fixed shapes: H = 64 indexer heads, D = 128 dims, one 132-byte K cache
+ *     row per token = 128 FP8 codes followed by the fp32 scale (P3 cost
+ *     table and data flow 1).  Token i of a cache block sits at byte i*132 of
+ *     the block.
+ *   - FP8 is OCP E4M3FN (max 448) stored as uint8; bf16 is stored as its
+ *     uint16 bit pattern.  Leading dimensions ("ld") and strides are in
+ *     elements of the array they describe, byte strides say "_bytes".
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *   - Each call only enqueues work on `stream` (0 = the default stream) and
+ *     returns; it never reads device memory from the host and never
+ *     synchronises, so every call may be captured into a HIP graph.
+ *   - Arguments known on the host are validated before any HIP call; a
+ *     failed check returns a negative status and enqueues nothing (checked
+ *     up front, never a slower fallback: P1 review highlights).  Values that
+ *     live on the device (row ranges, lengths, candidate ids, block-table
+ *     entries) are preconditions; where one is out of range the call still
+ *     touches no memory outside the buffers described by its arguments, and
+ *     the affected outputs are as documented per call.
+ *   - Calls that overlap on one stream are ordered; the library holds no
+ *     global state, so calls on different streams are independent.
+ */
+#ifndef DSI_H
+#define DSI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported entry points (the library builds with hidden default visibility). */
+#define DSI_API __attribute__((visibility("default")))
+
+#define DSI_HEADS 64
+#define DSI_HEAD_DIM 128
+#define DSI_ROW_BYTES 132
+#define DSI_MAX_TOPK 2048
+
+/* Status codes. */
+#define DSI_OK 0
+#define DSI_EINVAL (-1)       /* null pointer, negative size, ld/stride smaller than the row */
+#define DSI_EUNSUPPORTED (-2) /* a parameter outside what the kernels support (listed per call) */
+#define DSI_EALIGN (-3)       /* a pointer or byte stride without the required alignment */
+#define DSI_ELAUNCH (-4)      /* the HIP launch itself failed */
+#define DSI_EWORKSPACE (-5)   /* workspace missing or smaller than dsi_topk_workspace_bytes() */
+
+/* Element type of the logits given to dsi_topk_select. */
+#define DSI_F32 0
+#define DSI_BF16 1
+
+/* Human-readable text for a status code (static storage, never NULL). */
+DSI_API const char* dsi_status_string(int status);
+
+/* ABI version, bumped on any signature or semantic change. */
+DSI_API int dsi_abi_version(void);
+
+/*
+ * k quantization fused with cache insertion (P3 step ⑤: k is quantized as it
+ * is written into the indexer cache; row layout per P3 data flow 1).
+ *   k            bf16 [n][k_ld], first 128 values of each row used.
+ *   slot_mapping int64 [n]: destination slot of row i; slot = block*block_size
+ *                + offset.  A negative slot, or one at or beyond
+ *                num_blocks*block_size, is skipped (padding token).
+ *   pool         uint8, num_blocks blocks of block_stride_bytes; token
+ *                `offset` of block `block` is the 132 bytes at
+ *                block*block_stride_bytes + offset*132.
+ * Per token: amax = max|k|, scale = max(amax, 1e-4) / 448 (IEEE fp32
+ * division), code[d] = E4M3FN(k[d] / scale) rounded to nearest even and
+ * saturated to +-448; the row holds the 128 codes then the fp32 scale.
+ * Errors: EINVAL (null with n > 0, n < 0, k_ld < 128, block_size < 1,
+ * num_blocks < 0, block_stride_bytes < block_size*132); EALIGN (k not 4-byte
+ * aligned or k_ld odd, pool or block_stride_bytes not a multiple of 4).
+ */
+DSI_API int dsi_k_quant_and_cache(const uint16_t* k, int64_t n, int64_t k_ld, const int64_t* slot_mapping, uint8_t* pool,
+                          int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes, hipStream_t stream);
+
+/*
+ * Dense prefill indexer logits over gathered K (P3 step ⑥ and the
+ * prefill/decode table: prefill gathers the history K, then scores):
+ *   logits[t][s] = kscale[s] * sum_h w[t][h] * sum_d q[t][h][d] * k[s][d]
+ * for s in [max(row_ks[t],0), min(row_ke[t],S)), with q and k the decoded FP8
+ * values (the q scale is folded into w, P3 step ④).  No other entry of
+ * `logits` is written.
+ *   q      e4m3 [T][64][128] contiguous, 16-byte aligned.
+ *   w      bf16 [T][64] contiguous, 8-byte aligned.
+ *   k_rows [S][132] contiguous cache rows, 16-byte aligned.
+ *   row_ks, row_ke int32 [T].
+ *   logits fp32 [T][ld], ld >= S.
+ * FP8 x FP8 products on the matrix cores with fp32 accumulation; the head
+ * reduction is fp32.  Errors: EINVAL (null with T,S > 0, T < 0, S < 0,
+ * ld < S); EALIGN.
+ */
+DSI_API int dsi_mqa_logits_prefill(const uint8_t* q, const uint16_t* w, int32_t T, const uint8_t* k_rows, int32_t S,
+                           const int32_t* row_ks, const int32_t* row_ke, float* logits, int64_t ld,
+                           hipStream_t stream);
+
+/*
+ * Paged decode indexer logits straight from the cache, no gather (P3
+ * prefill/decode table).  Request b has context length context_lens[b] = L
+ * and next_n query rows (the multi-token draft of P3 "MTP"); row b*next_n+i
+ * scores tokens s in [0, min(L - next_n + i + 1, max_context_len)) with the
+ * formula of dsi_mqa_logits_prefill, reading token s at
+ *   pool + block_table[b*bt_ld + s/block_size]*block_stride_bytes
+ *        + (s % block_size)*132.
+ * No other entry of `logits` is written.  A token whose page id is outside
+ * [0, num_blocks), or whose block index s/block_size >= bt_width, scores
+ * -inf.
+ *   q [B*next_n][64][128] (16-byte aligned), w bf16 [B*next_n][64] (8-byte
+ *   aligned), context_lens int32 [B], pool (16-byte aligned),
+ *   block_table int32 [B][bt_ld], logits fp32 [B*next_n][ld],
+ *   ld >= max_context_len.
+ * Errors: EINVAL (nulls, B < 0, ld < max_context_len, bt_ld < bt_width,
+ * block_stride_bytes < block_size*132); EUNSUPPORTED (next_n not in 1..4,
+ * block_size not a positive multiple of 16); EALIGN (q, pool,
+ * block_stride_bytes not multiples of 16, w not 8-byte aligned).
+ */
+DSI_API int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                int32_t block_size, int64_t block_stride_bytes, const int32_t* block_table,
+                                int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits, int64_t ld,
+                                hipStream_t stream);
+
+/*
+ * Workspace bytes dsi_topk_select needs for these sizes (0 = none; pass any
+ * pointer or NULL then).
+ */
+DSI_API size_t dsi_topk_workspace_bytes(int32_t rows, int32_t max_width, int32_t k);
+
+/*
+ * Per-row top-k selection into the index table consumed by main attention
+ * (P3 data flow 2: the k best positions per query row, int32, -1 = empty
+ * slot; P3 pitfalls: positions are request-relative; P1: the compressed-space
+ * top-k runs on bf16 logits directly).
+ * For row r, let V be the FINITE values in columns [max(start,0),
+ * min(row_ends[r], max_width)), start = row_starts ? row_starts[r] : 0.
+ * out[r][0 .. m) holds the columns (minus start) of m = min(k, |V|) largest
+ * members of V, in no particular order; out[r][m .. k) = -1.  Among values
+ * that tie at the selection boundary any subset may be chosen.
+ *   logits  fp32 or bf16 (dtype = DSI_F32 / DSI_BF16) [rows][ld], 4-byte
+ *           aligned rows for fp32.
+ *   out     int32 [rows][out_ld], out_ld >= k.
+ * Errors: EINVAL (nulls, rows < 0, max_width < 0, ld < max_width,
+ * out_ld < k); EUNSUPPORTED (k not in 1..2048, unknown dtype);
+ * EWORKSPACE.
+ */
+DSI_API int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, int32_t rows, const int32_t* row_starts,
+                    const int32_t* row_ends, int32_t max_width, int32_t k, int32_t* out, int64_t out_ld,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Candidate expansion of the hierarchical indexer (P1 key source snippets:
+ * the per-row expansion kernel and its wrapper).  With ratio =
+ * candidate_block_size / sparse_block_kv, per row:
+ *   flatten: candidate c -> sparse blocks c*ratio .. c*ratio+ratio-1;
+ *   keep ids in [0, ceil(max(ke-ks,0)/sbk)); sort ascending, duplicates kept;
+ *   add the anchor floor(ks/sbk); pad the tail with the last kept id (or the
+ *   anchor when none is kept);
+ *   end = (n-1)*sbk + min(max(ke - (last*sbk + ks), 1), sbk), 0 when n = 0.
+ *   cand int32 [rows][cand_ld] (column slices allowed), row_ks/row_ke int32
+ *   with element strides ks_stride/ke_stride, sparse_indices int32
+ *   [rows][si_ld] (first num_candidates*ratio columns written), end int32
+ *   with element stride end_stride.
+ * Preconditions: 0 <= ks, ke < 2^31 - sparse_block_kv (int32 arithmetic).
+ * Errors: EINVAL (nulls, rows < 0, num_candidates < 1, cand_ld <
+ * num_candidates, si_ld < num_candidates*ratio, strides < 1);
+ * EUNSUPPORTED (ratio not 1 or 2 or not exact, sparse_block_kv not a power
+ * of two in 8..128, num_candidates*ratio > 1024).
+ */
+DSI_API int dsi_expand_candidates(const int32_t* cand, int64_t cand_ld, int32_t rows, int32_t num_candidates,
+                          const int32_t* row_ks, int64_t ks_stride, const int32_t* row_ke, int64_t ke_stride,
+                          int32_t candidate_block_size, int32_t sparse_block_kv, int32_t* sparse_indices,
+                          int64_t si_ld, int32_t* end, int64_t end_stride, hipStream_t stream);
+
+/*
+ * Sparse MQA logits on the candidate columns only (P1 motivation and
+ * implementation: consumer layers score only the candidate blocks into bf16
+ * logits [rows, num_sparse_blocks*sparse_block_kv]).  Column c of row r is
+ * token tok = sparse_indices[r][c/sbk]*sbk + c%sbk; when c < end[r] and
+ * row_ks[r] <= tok < row_ke[r] it holds the logit of that token (formula of
+ * dsi_mqa_logits_prefill) rounded once to bf16 (nearest even), otherwise
+ * bf16 -inf (0xFF80).  Every column of every row is written.
+ *   K source: block_table == NULL -> k_src is gathered rows [num_k][132]
+ *     (a token >= num_k scores -inf); otherwise k_src is a paged pool of
+ *     num_k blocks and row r reads block_table[row_to_req[r]*bt_ld +
+ *     tok/block_size] (row_to_req NULL = identity; a block index >= bt_width
+ *     or a page id outside [0,num_k) scores -inf).
+ *   q, w as dsi_mqa_logits_prefill with `rows` rows; sparse_indices int32
+ *   [rows][si_ld]; end, row_ks, row_ke int32 [rows]; out bf16 [rows][ld],
+ *   ld >= num_sparse_blocks*sparse_block_kv.
+ * Errors: EINVAL (nulls, rows < 0, num_sparse_blocks < 1, si_ld <
+ * num_sparse_blocks, ld too small, bt_ld < bt_width); EUNSUPPORTED
+ * (sparse_block_kv not a power of two in 8..128, block_size not a positive
+ * multiple of sparse_block_kv and of 8); EALIGN (q, k_src, block stride not
+ * multiples of 16, w not 8-byte aligned).
+ */
+DSI_API int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_t rows, const int32_t* row_ks,
+                          const int32_t* row_ke, const int32_t* sparse_indices, int64_t si_ld,
+                          int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
+                          const uint8_t* k_src, int64_t num_k, const int32_t* block_table, int64_t bt_ld,
+                          int32_t bt_width, const int32_t* row_to_req, int32_t block_size,
+                          int64_t block_stride_bytes, uint16_t* logits_bf16, int64_t ld, hipStream_t stream);
+
+/*
+ * Sparse column -> request-local position (P1 implementation breakdown: the
+ * compressed-space top-k is mapped back to context positions):
+ *   out[r][j] = (sparse_indices[r][c/sbk] - floor(row_ks[r]/sbk))*sbk + c%sbk
+ * for c = col[r][j] >= 0; -1 stays -1, as does c >= num_sparse_blocks*sbk.
+ * out may alias col (same pointer and ld).
+ * Errors: EINVAL (nulls, rows < 0, k < 0, lds smaller than k or
+ * num_sparse_blocks); EUNSUPPORTED (sparse_block_kv < 1).
+ */
+DSI_API int dsi_topk_remap(const int32_t* col, int64_t col_ld, int32_t rows, int32_t k, const int32_t* sparse_indices,
+                   int64_t si_ld, int32_t num_sparse_blocks, const int32_t* row_ks, int32_t sparse_block_kv,
+                   int32_t* out, int64_t out_ld, hipStream_t stream);
+
+/*
+ * Request-local position -> physical cache slot (P3 pitfalls: decode converts
+ * the indexer's request-relative positions into paged-cache slots; P2 key
+ * source snippets: in a packed pool a slot is block*block_span + offset, -1
+ * stays -1):
+ *   out[r][j] = block_table[req*bt_ld + p/block_size]*block_span
+ *               + p%block_size
+ * for p = idx[r][j] >= 0 and req = row_to_req ? row_to_req[r] : r; -1 for
+ * p < 0 or p/block_size >= bt_width.  block_span = block stride / 132 (equal
+ * to block_size for an unpacked pool).  out may alias idx.
+ * Errors: EINVAL (nulls, rows < 0, k < 0, lds < k, bt_ld < bt_width);
+ * EUNSUPPORTED (block_size < 1, block_span < block_size).
+ */
+DSI_API int dsi_req_index_to_global_slot(const int32_t* idx, int64_t idx_ld, int32_t rows, int32_t k,
+                                 const int32_t* row_to_req, const int32_t* block_table, int64_t bt_ld,
+                                 int32_t bt_width, int32_t block_size, int32_t block_span, int32_t* out,
+                                 int64_t out_ld, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSI_H */

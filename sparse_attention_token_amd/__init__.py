@@ -1,0 +1,319 @@
+"""Python binding of libdsi.so, the gfx950 DeepSeek Sparse Attention lightning-indexer library.
+
+Argument marshalling only: every step runs in the library's HIP kernels, on the
+caller's current torch stream.  PyTorch supplies device memory and streams.
+There is no fallback: if the library is missing or a call is rejected, an
+exception is raised.
+
+Names mirror the C ABI in include/dsi.h (without the ``dsi_`` prefix).  bf16
+arrays may be torch.bfloat16 or their 16-bit patterns (int16/uint16); FP8
+codes are uint8.  Outputs can be passed with ``out=`` (no allocation on the
+hot path) or are allocated here when omitted.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsi.so")
+
+HEADS, HEAD_DIM, ROW_BYTES, MAX_TOPK = 64, 128, 132, 2048
+F32, BF16 = 0, 1
+
+
+class DsiError(RuntimeError):
+    """A dsi_* call returned a negative status."""
+
+
+_lib = None
+_p, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+_SIGNATURES = {
+    "dsi_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dsi_abi_version": (ctypes.c_int, []),
+    "dsi_k_quant_and_cache": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _i32, _i64, _p]),
+    "dsi_mqa_logits_prefill": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _p, _p, _p, _i64, _p]),
+    "dsi_paged_mqa_logits_decode": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i64, _i32, _i64, _p, _i64, _i32,
+                                                   _i32, _p, _i64, _p]),
+    "dsi_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "dsi_topk_select": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _i32, _p, _i64, _p, _sz, _p]),
+    "dsi_expand_candidates": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _p, _i64, _i32, _i32, _p, _i64, _p,
+                                             _i64, _p]),
+    "dsi_sparse_mqa_logits": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p, _i64,
+                                             _i32, _p, _i32, _i64, _p, _i64, _p]),
+    "dsi_topk_remap": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _i32, _p, _i32, _p, _i64, _p]),
+    "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _p, _i64,
+                                                    _p]),
+}
+
+ENTRY_POINTS = tuple(_SIGNATURES)
+
+
+def lib():
+    """The loaded library (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python sparse_attention_token_amd/build.py")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().dsi_status_string(code).decode()
+
+
+def _check(code: int, name: str):
+    if code != 0:
+        raise DsiError(f"dsi_{name}: {status_string(code)} (status {code})")
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+    return dev
+
+
+def _need(t, dtypes, name, ndim=None):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+
+
+def _rows(t, name):
+    """Leading dimension of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: need a 2-D tensor with contiguous rows")
+    return t.stride(0)
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+
+
+def k_quant_and_cache(k, slot_mapping, pool, block_size, block_stride_bytes=None, num_blocks=None):
+    """Quantize bf16 k [n, >=128] into the 132-byte rows of `pool` at `slot_mapping` (int64)."""
+    dev = _dev(k, slot_mapping, pool)
+    _need(k, _BF16, "k")
+    _need(slot_mapping, (torch.int64,), "slot_mapping")
+    _need(pool, (torch.uint8,), "pool")
+    _contig(pool, "pool")
+    k_ld = _rows(k, "k")
+    if block_stride_bytes is None:
+        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * ROW_BYTES
+    if num_blocks is None:
+        num_blocks = pool.numel() // block_stride_bytes
+    n = k.shape[0]
+    with torch.cuda.device(dev):
+        _check(lib().dsi_k_quant_and_cache(_ptr(k), n, k_ld, _ptr(slot_mapping), _ptr(pool), num_blocks,
+                                           block_size, block_stride_bytes, _stream(k)), "k_quant_and_cache")
+    return pool
+
+
+def mqa_logits_prefill(q, w, k_rows, row_ks, row_ke, out=None):
+    """Dense logits over gathered K rows [S,132]; fp32 out [T, >=S] (entries outside [ks,ke) untouched)."""
+    dev = _dev(q, w, k_rows, row_ks, row_ke, out)
+    _need(q, (torch.uint8,), "q", 3)
+    _need(w, _BF16, "w", 2)
+    _need(k_rows, (torch.uint8,), "k_rows")
+    for t, nm in ((q, "q"), (w, "w"), (k_rows, "k_rows"), (row_ks, "row_ks"), (row_ke, "row_ke")):
+        _contig(t, nm)
+    T, S = q.shape[0], k_rows.numel() // ROW_BYTES
+    if out is None:
+        out = torch.empty((T, S), dtype=torch.float32, device=dev)
+    _need(out, (torch.float32,), "out")
+    ld = _rows(out, "out")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_mqa_logits_prefill(_ptr(q), _ptr(w), T, _ptr(k_rows), S, _ptr(row_ks), _ptr(row_ke),
+                                            _ptr(out), ld, _stream(q)), "mqa_logits_prefill")
+    return out
+
+
+def paged_mqa_logits_decode(q, w, context_lens, pool, block_size, block_table, max_context_len, next_n=1,
+                            out=None, block_stride_bytes=None, num_blocks=None, bt_width=None):
+    """Decode logits straight from the paged pool; fp32 out [B*next_n, >=max_context_len]."""
+    dev = _dev(q, w, context_lens, pool, block_table, out)
+    _need(q, (torch.uint8,), "q", 3)
+    _need(w, _BF16, "w", 2)
+    _need(context_lens, _I32, "context_lens")
+    _need(block_table, _I32, "block_table")
+    for t, nm in ((q, "q"), (w, "w"), (context_lens, "context_lens"), (pool, "pool")):
+        _contig(t, nm)
+    B = context_lens.shape[0]
+    if block_stride_bytes is None:
+        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * ROW_BYTES
+    if num_blocks is None:
+        num_blocks = pool.numel() // block_stride_bytes
+    bt_ld = _rows(block_table, "block_table")
+    if bt_width is None:
+        bt_width = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B * next_n, max_context_len), dtype=torch.float32, device=dev)
+    _need(out, (torch.float32,), "out")
+    ld = _rows(out, "out")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_paged_mqa_logits_decode(_ptr(q), _ptr(w), B, next_n, _ptr(context_lens), _ptr(pool),
+                                                 num_blocks, block_size, block_stride_bytes, _ptr(block_table), bt_ld,
+                                                 bt_width, max_context_len, _ptr(out), ld, _stream(q)),
+               "paged_mqa_logits_decode")
+    return out
+
+
+def topk_workspace_bytes(rows, max_width, k):
+    return lib().dsi_topk_workspace_bytes(rows, max_width, k)
+
+
+def topk_select(logits, row_ends, k=MAX_TOPK, row_starts=None, max_width=None, out=None, workspace=None):
+    """Top-k per row of fp32 or bf16 logits -> int32 [rows, k], request-relative, -1 padded."""
+    dev = _dev(logits, row_ends, row_starts, out, workspace)
+    if logits.dtype == torch.float32:
+        dtype = F32
+    elif logits.dtype in _BF16:
+        dtype = BF16
+    else:
+        raise TypeError(f"logits: unsupported dtype {logits.dtype}")
+    ld = _rows(logits, "logits")
+    rows = logits.shape[0]
+    if max_width is None:
+        max_width = logits.shape[1]
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    _need(out, _I32, "out")
+    out_ld = _rows(out, "out")
+    need = topk_workspace_bytes(rows, max_width, k)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        _check(lib().dsi_topk_select(_ptr(logits), dtype, ld, rows, _ptr(row_starts), _ptr(row_ends), max_width, k,
+                                     _ptr(out), out_ld, ws_ptr, ws_bytes, _stream(logits)), "topk_select")
+    return out
+
+
+def _vec_stride(t, name):
+    if t.dim() != 1:
+        raise ValueError(f"{name}: need a 1-D tensor")
+    return t.stride(0)
+
+
+def expand_candidates(cand, row_ks, row_ke, candidate_block_size, sparse_block_kv, out=None):
+    """-> (sparse_indices int32 [rows, K*ratio], end int32 [rows]); strided inputs allowed."""
+    dev = _dev(cand, row_ks, row_ke)
+    _need(cand, _I32, "cand", 2)
+    cand_ld = _rows(cand, "cand")
+    rows, K = cand.shape
+    ratio = candidate_block_size // sparse_block_kv if sparse_block_kv else 0
+    if out is None:
+        out = (torch.empty((rows, K * max(ratio, 1)), dtype=torch.int32, device=dev),
+               torch.empty((rows,), dtype=torch.int32, device=dev))
+    si, end = out
+    with torch.cuda.device(dev):
+        _check(lib().dsi_expand_candidates(_ptr(cand), cand_ld, rows, K, _ptr(row_ks), _vec_stride(row_ks, "row_ks"),
+                                           _ptr(row_ke), _vec_stride(row_ke, "row_ke"), candidate_block_size,
+                                           sparse_block_kv, _ptr(si), _rows(si, "sparse_indices"), _ptr(end),
+                                           _vec_stride(end, "end"), _stream(cand)), "expand_candidates")
+    return si, end
+
+
+def sparse_mqa_logits(q, w, row_ks, row_ke, sparse_indices, end, sparse_block_kv, k_src, block_table=None,
+                      row_to_req=None, block_size=0, block_stride_bytes=None, num_k=None, bt_width=None,
+                      num_sparse_blocks=None, out=None):
+    """bf16 logits on the candidate columns: [rows, num_sparse_blocks*sbk] (as int16 bit patterns)."""
+    dev = _dev(q, w, row_ks, row_ke, sparse_indices, end, k_src, block_table, row_to_req, out)
+    _need(q, (torch.uint8,), "q", 3)
+    _need(w, _BF16, "w", 2)
+    for t, nm in ((q, "q"), (w, "w"), (row_ks, "row_ks"), (row_ke, "row_ke"), (end, "end"), (k_src, "k_src")):
+        _contig(t, nm)
+    rows = q.shape[0]
+    si_ld = _rows(sparse_indices, "sparse_indices")
+    if num_sparse_blocks is None:
+        num_sparse_blocks = sparse_indices.shape[1]
+    width = num_sparse_blocks * sparse_block_kv
+    bt_ld = 0
+    if block_table is not None:
+        bt_ld = _rows(block_table, "block_table")
+        if bt_width is None:
+            bt_width = block_table.shape[1]
+        if block_stride_bytes is None:
+            block_stride_bytes = k_src.stride(0) if k_src.dim() > 1 else block_size * ROW_BYTES
+        if num_k is None:
+            num_k = k_src.numel() // block_stride_bytes
+    else:
+        bt_width, block_stride_bytes = 0, 0
+        if num_k is None:
+            num_k = k_src.numel() // ROW_BYTES
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.int16, device=dev)
+    _need(out, _BF16, "out")
+    ld = _rows(out, "out")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_sparse_mqa_logits(_ptr(q), _ptr(w), rows, _ptr(row_ks), _ptr(row_ke), _ptr(sparse_indices),
+                                           si_ld, num_sparse_blocks, _ptr(end), sparse_block_kv, _ptr(k_src), num_k,
+                                           _ptr(block_table), bt_ld, bt_width, _ptr(row_to_req), block_size,
+                                           block_stride_bytes, _ptr(out), ld, _stream(q)), "sparse_mqa_logits")
+    return out
+
+
+def topk_remap(col, sparse_indices, row_ks, sparse_block_kv, out=None, num_sparse_blocks=None):
+    """Sparse columns -> request-local positions (out may be `col` itself)."""
+    dev = _dev(col, sparse_indices, row_ks, out)
+    _need(col, _I32, "col", 2)
+    rows, k = col.shape
+    if out is None:
+        out = torch.empty_like(col)
+    if num_sparse_blocks is None:
+        num_sparse_blocks = sparse_indices.shape[1]
+    _contig(row_ks, "row_ks")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_topk_remap(_ptr(col), _rows(col, "col"), rows, k, _ptr(sparse_indices),
+                                    _rows(sparse_indices, "sparse_indices"), num_sparse_blocks, _ptr(row_ks),
+                                    sparse_block_kv, _ptr(out), _rows(out, "out"), _stream(col)), "topk_remap")
+    return out
+
+
+def req_index_to_global_slot(idx, block_table, block_size, block_span, row_to_req=None, out=None, bt_width=None):
+    """Request-local positions -> physical slots block*block_span + offset (out may be `idx`)."""
+    dev = _dev(idx, block_table, row_to_req, out)
+    _need(idx, _I32, "idx", 2)
+    rows, k = idx.shape
+    if out is None:
+        out = torch.empty_like(idx)
+    if bt_width is None:
+        bt_width = block_table.shape[1]
+    with torch.cuda.device(dev):
+        _check(lib().dsi_req_index_to_global_slot(_ptr(idx), _rows(idx, "idx"), rows, k, _ptr(row_to_req),
+                                                  _ptr(block_table), _rows(block_table, "block_table"), bt_width,
+                                                  block_size, block_span, _ptr(out), _rows(out, "out"),
+                                                  _stream(idx)), "req_index_to_global_slot")
+    return out

@@ -1,0 +1,157 @@
+// Device helpers shared by the gfx950 indexer kernels.
+//
+// Scoring layout (used by every logits kernel).  The indexer score of P3
+// step ⑥ ("DeepSeek V3.2 稀疏注意力 DSA 推理流程图解") is a 64-head x 128-dim
+// FP8 contraction followed by a per-head weighted sum.  It runs on
+// v_mfma_f32_16x16x128_f8f6f4 with
+//   A = 16 heads x 128 dims of q   (lane l: head l%16, 32 bytes of chunk l/16)
+//   B = 128 dims x 16 keys of K    (lane l: key  l%16, the same 32-byte chunk)
+//   C = 16 heads x 16 keys, lane l holds heads 4*(l/16)+i, i<4, of key l%16.
+// Four head tiles cover the 64 heads, so after the MFMAs each lane holds 16
+// heads of one key; the head-weighted sum is 16 FMAs per lane followed by a
+// sum over the four lane groups (l/16).  That cross-lane sum is done for four
+// (row, key-group) outputs at once as a 4x4 transpose-reduce: two exchange
+// stages (lane^32, lane^16), after which each lane group owns one output.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsi.h"
+
+namespace dsi {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeads = 64;
+constexpr int kDim = 128;
+constexpr int kRow = 132;       // bytes per cache row
+constexpr int kLdsKeyStride = 144;  // bytes per key row in LDS: 128 codes + pad, 16-byte aligned,
+                                    // 36 dwords = 4 mod 32 banks -> conflict-free 16-byte reads
+
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  // cbsz = blgp = 0 selects E4M3 for both operands; no block scaling.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 on the bit pattern (finite or inf).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// fp32 -> OCP E4M3FN code: round to nearest even, saturate to +-448, keep the
+// sign of the input (also for results that round to zero).  Derived from the
+// format: a normal e4m3 value keeps 3 of the 23 fp32 mantissa bits and has a
+// biased exponent 120 below fp32's; below 2^-6 the format is the grid m*2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |x| >= 448 (and inf/nan, never produced here)
+  if (a >= 0x3C800000u) {                      // |x| >= 2^-6: normal range
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // round the 20 dropped mantissa bits to nearest even
+    return sign | ((r >> 20) - (120u << 3));
+  }
+  float m = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, then nearest-even integer 0..8
+  return sign | (uint32_t)m;
+}
+
+// Order-preserving unsigned keys (larger value <-> larger key).
+__device__ __forceinline__ uint32_t f32_key(uint32_t u) { return (u & 0x80000000u) ? ~u : (u | 0x80000000u); }
+__device__ __forceinline__ uint32_t bf16_key(uint32_t h) { return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u); }
+
+// 4x4 transpose-reduce across the lane groups g = lane/16.  v[j], j = 0..3, are
+// this lane's partial sums of four outputs; on return the lane holds the full
+// sum of output j = g (summed over the four lane groups of its column).
+__device__ __forceinline__ float transpose_reduce4(const float v[4], int lane) {
+  const bool hi = lane >= 32;             // g in {2,3}
+  const bool odd = (lane >> 4) & 1;       // g in {1,3}
+  float s0 = hi ? v[0] : v[2];
+  float s1 = hi ? v[1] : v[3];
+  float r0 = __shfl_xor(s0, 32);
+  float r1 = __shfl_xor(s1, 32);
+  float k0 = (hi ? v[2] : v[0]) + r0;     // output 2*hi + 0
+  float k1 = (hi ? v[3] : v[1]) + r1;     // output 2*hi + 1
+  float s = odd ? k0 : k1;
+  float r = __shfl_xor(s, 16);
+  return (odd ? k1 : k0) + r;
+}
+
+// A-operand fragments of one query row: four 16-head tiles.
+struct QFrag {
+  i32x8 a[4];
+};
+
+// Load q[row] (64 x 128 codes, contiguous) into this lane's A fragments.
+__device__ __forceinline__ void load_q(QFrag& f, const uint8_t* q_row, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) {
+    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 16 + n) * kDim + g * 32);
+    uint4 x0 = p[0], x1 = p[1];
+    f.a[hb] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+}
+
+// This lane's 16 head weights of one row: heads hb*16 + 4*(lane/16) + i.
+struct WFrag {
+  float w[4][4];
+};
+
+__device__ __forceinline__ void load_w(WFrag& f, const uint16_t* w_row, int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) {
+    uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 16 + g * 4);
+    f.w[hb][0] = bf16_to_f32(x.x & 0xFFFFu);
+    f.w[hb][1] = bf16_to_f32(x.x >> 16);
+    f.w[hb][2] = bf16_to_f32(x.y & 0xFFFFu);
+    f.w[hb][3] = bf16_to_f32(x.y >> 16);
+  }
+}
+
+// B-operand fragment for 16 keys whose LDS rows start at `keys` (kLdsKeyStride apart).
+__device__ __forceinline__ i32x8 load_kfrag(const uint8_t* keys, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint4* p = reinterpret_cast<const uint4*>(keys + n * kLdsKeyStride + g * 32);
+  uint4 x0 = p[0], x1 = p[1];
+  return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
+// Head-weighted partial of one (row, 16-key group): the 64-head contraction on
+// the matrix cores, then this lane's 16 heads weighted and summed.
+__device__ __forceinline__ float score_partial(const QFrag& q, const WFrag& w, const i32x8& kb) {
+  f32x4 c[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) c[hb] = mfma_fp8(q.a[hb], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+  float s = 0.f;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) s = fmaf(w.w[hb][i], c[hb][i], s);
+  return s;
+}
+
+// Copy one 16-byte chunk of a contiguous run of 132-byte cache rows into the
+// LDS key layout: dword d of the run belongs to row d/33, word d%33 (word 32
+// is the fp32 scale).  `chunk` is the chunk index within the run, `key0` the
+// LDS key slot of the run's first row.
+__device__ __forceinline__ void scatter_chunk(uint8_t* lds_codes, float* lds_scale, int key0, int chunk,
+                                              const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    int d = chunk * 4 + j;
+    int row = d / 33, word = d - row * 33;
+    if (word < 32)
+      *reinterpret_cast<uint32_t*>(lds_codes + (key0 + row) * kLdsKeyStride + word * 4) = w[j];
+    else
+      lds_scale[key0 + row] = __uint_as_float(w[j]);
+  }
+}
+
+}  // namespace dsi

@@ -1,0 +1,154 @@
+"""The C-ABI library loads without a GPU, exports every entry point include/dsi.h declares, and rejects
+bad host-known arguments before any HIP call (fail closed, never a slower fallback: vLLM PR 56254 summary,
+review highlights)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_token_amd as dsi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EINVAL, EUNSUP, EALIGN, EWS = -1, -2, -3, -5
+A16 = 0x10000  # a fake, 16-byte aligned non-null "device" pointer.  Every call below is either invalid
+# (rejected on the host) or empty (returns before any launch), so no kernel ever sees this pointer.
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "dsi.h")).read()
+    return sorted(set(re.findall(r"DSI_API\s+[\w\s\*]*?\b(dsi_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_eight_steps():
+    names = declared()
+    for step in ["k_quant_and_cache", "mqa_logits_prefill", "paged_mqa_logits_decode", "topk_select",
+                 "expand_candidates", "sparse_mqa_logits", "topk_remap", "req_index_to_global_slot"]:
+        assert "dsi_" + step in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dsi.lib()
+    for name in declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dsi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (dsi_\w+)", out)))
+    assert exported == declared()
+    assert sorted(dsi.ENTRY_POINTS) == declared()
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert dsi.status_string(code)
+    assert dsi.status_string(-99) == "unknown status"
+    assert dsi.lib().dsi_abi_version() >= 1
+
+
+def test_k_quant_validation():
+    L = dsi.lib()
+    assert L.dsi_k_quant_and_cache(None, -1, 128, None, None, 1, 64, 64 * 132, None) == EINVAL
+    assert L.dsi_k_quant_and_cache(None, 4, 127, None, None, 1, 64, 64 * 132, None) == EINVAL
+    assert L.dsi_k_quant_and_cache(None, 4, 128, None, None, 1, 64, 64 * 132, None) == EINVAL  # nulls
+    assert L.dsi_k_quant_and_cache(A16, 4, 128, A16, A16, 1, 64, 64 * 132 - 4, None) == EINVAL  # stride < row
+    assert L.dsi_k_quant_and_cache(A16, 4, 128, A16, A16, 1, 0, 0, None) == EINVAL
+    assert L.dsi_k_quant_and_cache(A16 + 2, 4, 128, A16, A16, 1, 64, 64 * 132, None) == EALIGN
+    assert L.dsi_k_quant_and_cache(A16, 4, 129, A16, A16, 1, 64, 64 * 132, None) == EALIGN
+    assert L.dsi_k_quant_and_cache(A16, 4, 128, A16, A16, 1, 64, 64 * 132 + 2, None) == EALIGN
+    assert L.dsi_k_quant_and_cache(None, 0, 128, None, None, 0, 64, 64 * 132, None) == 0  # empty: no-op
+
+
+def test_prefill_validation():
+    L = dsi.lib()
+    f = L.dsi_mqa_logits_prefill
+    assert f(None, None, -1, None, 10, None, None, None, 10, None) == EINVAL
+    assert f(A16, A16, 4, A16, 10, A16, A16, A16, 9, None) == EINVAL  # ld < S
+    assert f(A16, A16, 4, None, 10, A16, A16, A16, 10, None) == EINVAL
+    assert f(A16 + 8, A16, 4, A16, 10, A16, A16, A16, 10, None) == EALIGN
+    assert f(A16, A16, 4, A16 + 4, 10, A16, A16, A16, 10, None) == EALIGN
+    assert f(A16, A16 + 4, 4, A16, 10, A16, A16, A16, 10, None) == EALIGN
+    assert f(None, None, 0, None, 10, None, None, None, 10, None) == 0
+
+
+def test_decode_validation():
+    L = dsi.lib()
+
+    def call(**kw):
+        a = dict(q=A16, w=A16, B=2, next_n=1, cl=A16, pool=A16, nb=10, bs=64, stride=64 * 132, bt=A16, bt_ld=4,
+                 bt_w=4, maxc=256, out=A16, ld=256)
+        a.update(kw)
+        return L.dsi_paged_mqa_logits_decode(a["q"], a["w"], a["B"], a["next_n"], a["cl"], a["pool"], a["nb"],
+                                             a["bs"], a["stride"], a["bt"], a["bt_ld"], a["bt_w"], a["maxc"],
+                                             a["out"], a["ld"], None)
+    assert call(next_n=0) == EUNSUP and call(next_n=5) == EUNSUP
+    assert call(bs=8) == EUNSUP and call(bs=24) == EUNSUP
+    assert call(ld=255) == EINVAL and call(B=-1) == EINVAL and call(bt_ld=3) == EINVAL
+    assert call(stride=64 * 132 - 16) == EINVAL
+    assert call(pool=None) == EINVAL and call(bt=None) == EINVAL
+    assert call(stride=64 * 132 + 4) == EALIGN and call(q=A16 + 4) == EALIGN and call(pool=A16 + 8) == EALIGN
+    assert call(B=0) == 0
+
+
+def test_topk_validation():
+    L = dsi.lib()
+    f = L.dsi_topk_select
+    assert f(A16, 0, 10, 2, None, A16, 10, 0, A16, 10, None, 0, None) == EUNSUP  # k = 0
+    assert f(A16, 0, 10, 2, None, A16, 10, 2049, A16, 2049, None, 0, None) == EUNSUP
+    assert f(A16, 7, 10, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EUNSUP  # dtype
+    assert f(A16, 0, 9, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EINVAL  # ld < width
+    assert f(A16, 0, 10, 2, None, A16, 10, 4, A16, 3, None, 0, None) == EINVAL  # out_ld < k
+    assert f(None, 0, 10, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EINVAL
+    assert f(A16 + 2, 0, 10, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EALIGN
+    assert f(A16 + 1, 1, 10, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EALIGN
+    assert f(None, 0, 10, 0, None, None, 10, 4, None, 4, None, 0, None) == 0
+    assert L.dsi_topk_workspace_bytes(64, 131072, 2048) >= 0
+
+
+def test_expand_validation():
+    L = dsi.lib()
+
+    def call(cbs=16, sbk=16, K=4, cand_ld=4, si_ld=4, rows=2, cand=A16):
+        return L.dsi_expand_candidates(cand, cand_ld, rows, K, A16, 1, A16, 1, cbs, sbk, A16, si_ld, A16, 1, None)
+    assert call(cbs=48, sbk=16) == EUNSUP  # ratio 3
+    assert call(cbs=24, sbk=16) == EUNSUP  # not exact
+    assert call(sbk=12, cbs=12) == EUNSUP and call(sbk=256, cbs=256) == EUNSUP and call(sbk=4, cbs=4) == EUNSUP
+    assert call(cbs=32, sbk=16, si_ld=7) == EINVAL  # si_ld < K*ratio
+    assert call(cand_ld=3) == EINVAL and call(K=0) == EINVAL and call(cand=None) == EINVAL
+    assert call(K=1025, cand_ld=1025, si_ld=1025) == EUNSUP
+    assert call(rows=0) == 0
+
+
+def test_sparse_validation():
+    L = dsi.lib()
+
+    def call(sbk=16, nsb=4, si_ld=4, ld=64, bt=None, bs=0, stride=0, k_src=A16, q=A16):
+        return L.dsi_sparse_mqa_logits(q, A16, 2, A16, A16, A16, si_ld, nsb, A16, sbk, k_src, 100, bt, 4, 4, None,
+                                       bs, stride, A16, ld, None)
+    assert call(sbk=12) == EUNSUP and call(sbk=4) == EUNSUP
+    assert call(si_ld=3) == EINVAL and call(ld=63) == EINVAL and call(nsb=0) == EINVAL
+    assert call(bt=A16, bs=24, stride=24 * 132) == EUNSUP  # block_size not a multiple of sbk
+    assert call(bt=A16, bs=64, stride=64 * 132 - 16) == EINVAL
+    assert call(bt=A16, bs=64, stride=64 * 132 + 4) == EALIGN
+    assert call(k_src=None) == EINVAL
+    assert call(q=A16 + 4) == EALIGN
+
+
+def test_remap_and_slot_validation():
+    L = dsi.lib()
+    assert L.dsi_topk_remap(A16, 4, 2, 4, A16, 4, 4, A16, 0, A16, 4, None) == EUNSUP
+    assert L.dsi_topk_remap(A16, 3, 2, 4, A16, 4, 4, A16, 16, A16, 4, None) == EINVAL
+    assert L.dsi_topk_remap(None, 4, 2, 4, A16, 4, 4, A16, 16, A16, 4, None) == EINVAL
+    assert L.dsi_topk_remap(A16, 4, 0, 4, A16, 4, 4, A16, 16, A16, 4, None) == 0
+    f = L.dsi_req_index_to_global_slot
+    assert f(A16, 4, 2, 4, None, A16, 8, 8, 0, 64, A16, 4, None) == EUNSUP
+    assert f(A16, 4, 2, 4, None, A16, 8, 8, 64, 63, A16, 4, None) == EUNSUP  # span < block_size
+    assert f(A16, 4, 2, 4, None, A16, 7, 8, 64, 64, A16, 4, None) == EINVAL  # bt_ld < bt_width
+    assert f(A16, 4, 2, 4, None, None, 8, 8, 64, 64, A16, 4, None) == EINVAL
+    assert f(A16, 4, 2, 0, None, A16, 8, 8, 64, 64, A16, 4, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dsi, "_lib", None)
+    monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        dsi.lib()
