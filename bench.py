@@ -1,0 +1,332 @@
+"""Benchmark of the DSA lightning-indexer hot path on one MI355X.
+
+Headline line (stdout, one JSON object): the prefill-chunk workload — one request, T=2048 query tokens at
+positions 6144..8191 over S=8192 history tokens, 64 heads x 128 dims, FP8 q/k.  One step = quantize and
+insert the chunk's 2048 new k rows, dense indexer logits over the gathered K (causal), top-2048 per row.
+`value` = scored query-key pairs per second (masked pairs not counted).  Inputs are resident in HBM before
+the timed region; every step launches the same three kernels on the current stream.
+
+Also reported (same JSON line): the roofline of the dominant kernel (prefill logits, FP8 MFMA), the oracle's
+single-thread CPU rate on a bounded row sample, and the decode and hierarchical workloads (paged decode
+64 x U{4096..65536}; long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows
++ 1024 prefill rows) with their HBM roofline fractions.  Diagnostics go to stderr.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_attention_token_amd as dsi  # noqa: E402
+import synth  # noqa: E402
+
+ROW, K = 132, 2048
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0
+FLOP_PER_PAIR = 2 * 64 * 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+class EventTimer:
+    """Pairs of HIP events on the current stream around one kernel; averaged after a sync."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+# --------------------------------------------------------------------------- prefill chunk (headline)
+def bench_prefill(steps, warmup):
+    c = synth.workload(2)
+    T, S = c["T"], c["S"]
+    first = S - T
+    pairs = int((c["ke"] - c["ks"]).sum())
+    q, w, ks, ke = dev(c["q"]), dev(c["w"]), dev(c["ks"]), dev(c["ke"])
+    k_all = dev(c["k"])
+    rows = torch.zeros((S, ROW), dtype=torch.uint8, device="cuda")
+    slots = torch.arange(S, dtype=torch.int64, device="cuda")
+    # history already in the cache; each step inserts the chunk's own k rows
+    dsi.k_quant_and_cache(k_all[:first], slots[:first], rows.view(-1), S, S * ROW, 1)
+    k_chunk, s_chunk = k_all[first:], slots[first:]
+    logits = torch.empty((T, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    timer = EventTimer()
+
+    def step(timed):
+        dsi.k_quant_and_cache(k_chunk, s_chunk, rows.view(-1), S, S * ROW, 1)
+        s = timer.start() if timed else None
+        dsi.mqa_logits_prefill(q, w, rows, ks, ke, out=logits)
+        if timed:
+            timer.stop(s)
+        dsi.topk_select(logits, ke, k=K, row_starts=ks, out=idx)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    ms_logits = timer.mean_ms()
+    # top-k alone, for the report
+    tk = EventTimer()
+    for _ in range(steps):
+        s = tk.start()
+        dsi.topk_select(logits, ke, k=K, row_starts=ks, out=idx)
+        tk.stop(s)
+    ms_topk = tk.mean_ms()
+    return dict(c=c, pairs=pairs, ms_step=ms_step, ms_logits=ms_logits, ms_topk=ms_topk, T=T, S=S)
+
+
+def cpu_baseline(c, max_seconds):
+    """The oracle as it is, single thread, on a bounded sample of the same workload: the chunk's k rows
+    quantized, then logits and top-2048 for evenly spaced query rows until the time budget is used."""
+    import oracle
+    T, S = c["T"], c["S"]
+    t0 = time.perf_counter()
+    rows = np.zeros((S, ROW), np.uint8)
+    oracle.k_quant_and_cache(c["k"], np.arange(S), rows.reshape(-1), S, S * ROW)
+    order = np.random.default_rng(0).permutation(T)
+    done_rows, pairs = 0, 0
+    for t in order:
+        sl = slice(int(t), int(t) + 1)
+        lg = oracle.mqa_logits_gathered(c["q"][sl], c["w"][sl], rows, c["ks"][sl], c["ke"][sl])
+        oracle.topk_select(lg, c["ke"][sl], K, starts=c["ks"][sl])
+        pairs += int(c["ke"][t] - c["ks"][t])
+        done_rows += 1
+        if time.perf_counter() - t0 > max_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=pairs / dt, unit="pairs/s", cores=1, kind="oracle",
+                sample=f"{done_rows} of {T} query rows of the prefill chunk (plus quantizing all {S} k rows), "
+                       f"{dt:.1f} s, 1 thread, host {platform.processor() or platform.machine()} "
+                       f"with {os.cpu_count()} cores")
+
+
+# --------------------------------------------------------------------------- paged decode
+def bench_decode(n, steps, warmup, copies=4):
+    c = synth.workload(n)
+    bs, stride, nb, nn, B = c["block_size"], c["block_stride"], c["num_blocks"], c["next_n"], c["B"]
+    lens = c["context_lens"]
+    maxc = int(lens.max())
+    sumL = int(lens.sum())
+    q, w, cl = dev(c["q"]), dev(c["w"]), dev(lens)
+    ends_np = (np.repeat(lens, nn) - nn + np.tile(np.arange(nn), B) + 1).astype(np.int32)
+    ends = dev(ends_np)
+    r2r = dev(np.repeat(np.arange(B, dtype=np.int32), nn))
+    k_t, slot_t = dev(c["k"]), dev(c["slot_mapping"])
+    # independent pool copies, each with its own block permutation, so the 256 MB MALL cannot hold K
+    pools, tables = [], []
+    rng = np.random.default_rng(100 + n)
+    for i in range(copies):
+        perm = rng.permutation(nb).astype(np.int32)
+        bt = perm[c["block_table"]]
+        sl = (bt[np.repeat(np.arange(B), lens), np.concatenate([np.arange(L) for L in lens]) // bs].astype(np.int64)
+              * bs + np.concatenate([np.arange(L) for L in lens]) % bs)
+        pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+        dsi.k_quant_and_cache(k_t, dev(sl), pool, bs, stride, nb)
+        pools.append(pool)
+        tables.append(dev(bt))
+    del k_t, slot_t
+    rows = B * nn
+    logits = torch.empty((rows, maxc), dtype=torch.float32, device="cuda")
+    idx = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    slots = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    tl, tt, ts = EventTimer(), EventTimer(), EventTimer()
+
+    def step(i, timed):
+        p, bt = pools[i % copies], tables[i % copies]
+        s = tl.start() if timed else None
+        dsi.paged_mqa_logits_decode(q, w, cl, p, bs, bt, maxc, next_n=nn, out=logits, block_stride_bytes=stride,
+                                    num_blocks=nb)
+        if timed:
+            tl.stop(s)
+            s = tt.start()
+        dsi.topk_select(logits, ends, k=K, out=idx)
+        if timed:
+            tt.stop(s)
+            s = ts.start()
+        dsi.req_index_to_global_slot(idx, bt, bs, bs, row_to_req=r2r, out=slots)
+        if timed:
+            ts.stop(s)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(i, True)
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
+    ms_l, ms_t, ms_s = tl.mean_ms(), tt.mean_ms(), ts.mean_ms()
+    V = int(ends_np.sum())
+    nblk = int(sum((int(L) + bs - 1) // bs for L in lens))
+    bytes_logits = ROW * sumL + 4 * nblk + rows * (64 * 128 + 64 * 2) + 4 * V
+    bytes_topk = 4 * V + rows * K * 4
+    gbs = (bytes_logits + bytes_topk) / ((ms_l + ms_t) * 1e-3) / 1e9
+    return dict(workload=f"paged decode {B} x next_n {nn}, lengths U{{{int(lens.min())}..{int(lens.max())}}}",
+                rows=rows, sum_tokens=sumL, ms_step=round(ms_step, 4), ms_logits=round(ms_l, 4),
+                ms_topk=round(ms_t, 4), ms_slot=round(ms_s, 4),
+                logits_gbs=round(bytes_logits / (ms_l * 1e-3) / 1e9, 1),
+                logits_topk_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                rows_per_s=round(rows / ((ms_l + ms_t) * 1e-3), 1),
+                algorithmic_bytes=bytes_logits + bytes_topk)
+
+
+# --------------------------------------------------------------------------- hierarchical sparse
+def bench_sparse(steps, warmup):
+    c = synth.workload(5)
+    sbk, cbs, nd, rows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
+    bs, stride, nb = c["block_size"], c["block_stride"], c["num_blocks"]
+    q, w, ks, ke, cand = dev(c["q"]), dev(c["w"]), dev(c["ks"]), dev(c["ke"]), dev(c["cand"])
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(c["k_dec"]), dev(c["dec_slot_mapping"]), pool, bs, stride, nb)
+    Lp = c["Lp"]
+    pre = torch.zeros((Lp, ROW), dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(c["k_pre"]), torch.arange(Lp, dtype=torch.int64, device="cuda"), pre.view(-1), Lp,
+                          Lp * ROW, 1)
+    bt, r2r = dev(c["block_table"]), dev(c["row_to_req"])
+    nsb = cand.shape[1] * (cbs // sbk)
+    width = nsb * sbk
+    si = torch.empty((rows, nsb), dtype=torch.int32, device="cuda")
+    end = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    out = torch.empty((rows, width), dtype=torch.int16, device="cuda")
+    col = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    slots = torch.empty((nd, K), dtype=torch.int32, device="cuda")
+    te, tl, tt, tr = EventTimer(), EventTimer(), EventTimer(), EventTimer()
+
+    def step(timed):
+        s = te.start() if timed else None
+        dsi.expand_candidates(cand, ks, ke, cbs, sbk, out=(si, end))
+        if timed:
+            te.stop(s)
+            s = tl.start()
+        dsi.sparse_mqa_logits(q[:nd], w[:nd], ks[:nd], ke[:nd], si[:nd], end[:nd], sbk, pool, block_table=bt,
+                              row_to_req=r2r, block_size=bs, block_stride_bytes=stride, num_k=nb, out=out[:nd])
+        dsi.sparse_mqa_logits(q[nd:], w[nd:], ks[nd:], ke[nd:], si[nd:], end[nd:], sbk, pre, out=out[nd:])
+        if timed:
+            tl.stop(s)
+            s = tt.start()
+        dsi.topk_select(out, end, k=K, out=col)
+        if timed:
+            tt.stop(s)
+            s = tr.start()
+        dsi.topk_remap(col, si, ks, sbk, out=col)
+        dsi.req_index_to_global_slot(col[:nd], bt, bs, bs, row_to_req=r2r, out=slots)
+        if timed:
+            tr.stop(s)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step(True)
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
+    scored = int(host_end(end).sum())
+    ms_l = tl.mean_ms()
+    return dict(workload=f"hierarchical sparse: {nd} decode rows + {rows - nd} prefill rows, {nsb} sparse blocks "
+                         f"of {sbk}", rows=rows, ms_step=round(ms_step, 4), ms_expand=round(te.mean_ms(), 4),
+                ms_logits=round(ms_l, 4), ms_topk=round(tt.mean_ms(), 4), ms_remap_slot=round(tr.mean_ms(), 4),
+                scored_pairs=scored, pairs_per_s=round(scored / (ms_step * 1e-3), 1),
+                logits_tflops=round(scored * FLOP_PER_PAIR / (ms_l * 1e-3) / 1e12, 1),
+                effective_gathered_gbs=round(scored * ROW / (ms_l * 1e-3) / 1e9, 1))
+
+
+def host_end(t):
+    return t.cpu().numpy().astype(np.int64)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only-headline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the indexer path has no multi-GPU mode in this build "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dsi.lib()
+
+    log("prefill chunk ...")
+    pf = bench_prefill(args.steps, args.warmup)
+    value = pf["pairs"] / (pf["ms_step"] * 1e-3)
+    flops = pf["pairs"] * FLOP_PER_PAIR
+    achieved = flops / (pf["ms_logits"] * 1e-3) / 1e12
+    extra = {}
+    if not args.only_headline:
+        for n in (3, 4):
+            log(f"decode workload {n} ...")
+            extra[f"decode_w{n}"] = bench_decode(n, args.steps, args.warmup)
+        log("hierarchical sparse ...")
+        extra["sparse_w5"] = bench_sparse(args.steps, args.warmup)
+    log("cpu baseline ...")
+    cpu = cpu_baseline(pf["c"], args.cpu_seconds)
+    line = {
+        "metric": "indexer q.k pairs/s (prefill chunk: k insert + dense FP8 logits + top-2048)",
+        "value": round(value, 1),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3->f32",
+        "data": "synthetic (seeded numpy: q,k ~ N(0,1) to bf16, FP8 e4m3 with per-128 scales)",
+        "config": {"workload": "prefill chunk: 1 request, T=2048 query tokens at positions 6144..8191, S=8192, "
+                               "H=64, D=128, causal, top-2048", "T": pf["T"], "S": pf["S"], "pairs": pf["pairs"],
+                   "ms_logits": round(pf["ms_logits"], 4), "ms_topk": round(pf["ms_topk"], 4)},
+        "roofline": {"bound": "mfma", "kernel": "prefill_logits_kernel", "achieved": round(achieved, 1),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,10 +41,10 @@ _SIGNATURES = {
     "dsi_expand_candidates": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _p, _i64, _i32, _i32, _p, _i64, _p,
                                              _i64, _p]),
     "dsi_sparse_mqa_logits": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p, _i64,
-                                             _i32, _p, _i32, _i64, _p, _i64, _p]),
+                                             _i32, _i32, _p, _i32, _i64, _p, _i64, _p]),
     "dsi_topk_remap": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _i32, _p, _i32, _p, _i64, _p]),
-    "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _p, _i64,
-                                                    _p]),
+    "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _i32, _p,
+                                                    _i64, _p]),
 }
 
 ENTRY_POINTS = tuple(_SIGNATURES)
@@ -260,9 +260,10 @@ def sparse_mqa_logits(q, w, row_ks, row_ke, sparse_indices, end, sparse_block_kv
     if num_sparse_blocks is None:
         num_sparse_blocks = sparse_indices.shape[1]
     width = num_sparse_blocks * sparse_block_kv
-    bt_ld = 0
+    bt_ld, num_reqs = 0, 0
     if block_table is not None:
         bt_ld = _rows(block_table, "block_table")
+        num_reqs = block_table.shape[0]
         if bt_width is None:
             bt_width = block_table.shape[1]
         if block_stride_bytes is None:
@@ -280,7 +281,7 @@ def sparse_mqa_logits(q, w, row_ks, row_ke, sparse_indices, end, sparse_block_kv
     with torch.cuda.device(dev):
         _check(lib().dsi_sparse_mqa_logits(_ptr(q), _ptr(w), rows, _ptr(row_ks), _ptr(row_ke), _ptr(sparse_indices),
                                            si_ld, num_sparse_blocks, _ptr(end), sparse_block_kv, _ptr(k_src), num_k,
-                                           _ptr(block_table), bt_ld, bt_width, _ptr(row_to_req), block_size,
+                                           _ptr(block_table), bt_ld, bt_width, num_reqs, _ptr(row_to_req), block_size,
                                            block_stride_bytes, _ptr(out), ld, _stream(q)), "sparse_mqa_logits")
     return out
 
@@ -314,6 +315,6 @@ def req_index_to_global_slot(idx, block_table, block_size, block_span, row_to_re
     with torch.cuda.device(dev):
         _check(lib().dsi_req_index_to_global_slot(_ptr(idx), _rows(idx, "idx"), rows, k, _ptr(row_to_req),
                                                   _ptr(block_table), _rows(block_table, "block_table"), bt_width,
-                                                  block_size, block_span, _ptr(out), _rows(out, "out"),
+                                                  block_table.shape[0], block_size, block_span, _ptr(out), _rows(out, "out"),
                                                   _stream(idx)), "req_index_to_global_slot")
     return out

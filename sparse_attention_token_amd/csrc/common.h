@@ -1,17 +1,30 @@
 // Device helpers shared by the gfx950 indexer kernels.
 //
-// Scoring layout (used by every logits kernel).  The indexer score of P3
-// step ⑥ ("DeepSeek V3.2 稀疏注意力 DSA 推理流程图解") is a 64-head x 128-dim
-// FP8 contraction followed by a per-head weighted sum.  It runs on
-// v_mfma_f32_16x16x128_f8f6f4 with
-//   A = 16 heads x 128 dims of q   (lane l: head l%16, 32 bytes of chunk l/16)
-//   B = 128 dims x 16 keys of K    (lane l: key  l%16, the same 32-byte chunk)
+// Scoring layout (used by every logits kernel).  The indexer score of P3 step ⑥
+// ("DeepSeek V3.2 稀疏注意力 DSA 推理流程图解") is a 64-head x 128-dim contraction of
+// FP8 values followed by a per-head weighted sum.
+//
+// Matrix instruction.  The FP8 codes are decoded exactly to f16 and contracted with
+// v_mfma_f32_16x16x32_f16.  gfx950's FP8-operand MFMAs (16x16x128 f8f6f4 and
+// 16x16x32 fp8) were measured to drop product bits about 13 binades below the largest
+// product of their internal sum, with a one-sided (truncating) error that reaches
+// ~0.1 on indexer logits — beyond the path's 1e-3 (1 + |ref|) bar — while the f16
+// MFMA sums the same products exactly.  Every E4M3FN code shifted left by 7 bits (sign
+// moved to bit 15) is an f16 equal to the code's value times 2^-8, subnormals included
+// (they become f16 subnormals, which the f16 MFMA keeps); the 2^16 of the two factors
+// is folded into the key scale.
+//
+// Operands of one MFMA (k = 32 dims of a 128-dim slice):
+//   A = 16 heads x 32 dims of q   (lane l: head l%16, 8 dims of lane group g = l/16)
+//   B = 32 dims x 16 keys of K    (lane l: key  l%16, the same 8 dims)
 //   C = 16 heads x 16 keys, lane l holds heads 4*(l/16)+i, i<4, of key l%16.
-// Four head tiles cover the 64 heads, so after the MFMAs each lane holds 16
-// heads of one key; the head-weighted sum is 16 FMAs per lane followed by a
-// sum over the four lane groups (l/16).  That cross-lane sum is done for four
-// (row, key-group) outputs at once as a 4x4 transpose-reduce: two exchange
-// stages (lane^32, lane^16), after which each lane group owns one output.
+// Lane group g owns dims [32g, 32g+32) of the 128 and feeds 8 of them to each of the
+// four slices; A and B use the same assignment, so the sum over dims is complete.
+// Four head tiles cover the 64 heads, so after the MFMAs each lane holds 16 heads of
+// one key; the head-weighted sum is 16 FMAs per lane followed by a sum over the four
+// lane groups.  That cross-lane sum is done for four (row, key-group) outputs at once
+// as a 4x4 transpose-reduce: two exchange stages (lane^32, lane^16), after which each
+// lane group owns one output.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,18 +34,20 @@
 
 namespace dsi {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
-constexpr int kRow = 132;       // bytes per cache row
-constexpr int kLdsKeyStride = 144;  // bytes per key row in LDS: 128 codes + pad, 16-byte aligned,
-                                    // 36 dwords = 4 mod 32 banks -> conflict-free 16-byte reads
+constexpr int kRow = 132;              // bytes per cache row
+constexpr int kLdsKeyStride = 144;     // LDS bytes per FP8 key row: 128 codes + pad; 36 dwords = 4 mod 32
+                                       // banks, so 16-byte reads by 8 consecutive keys are conflict-free
+constexpr int kLdsKeyStrideF16 = 272;  // LDS bytes per f16 key row: 256 + pad, 68 dwords = 4 mod 32 banks
+constexpr float kF16Unscale = 65536.0f;  // 2^16: undoes the 2^-8 of both decoded operands
 
-__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
-  // cbsz = blgp = 0 selects E4M3 for both operands; no block scaling.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -60,6 +75,22 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (uint32_t)m;
 }
 
+// Four E4M3FN codes (one dword, little-endian) -> four f16 (two dwords), each the
+// code's value times 2^-8.  Exact for every finite code.
+__device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
+  uint32_t lo = (x & 0xFFu) | ((x & 0xFF00u) << 8);            // bytes b1, b0 into the two halves
+  uint32_t hi = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u);  // bytes b3, b2
+  lo = ((lo & 0x007F007Fu) << 7) | ((lo & 0x00800080u) << 8);
+  hi = ((hi & 0x007F007Fu) << 7) | ((hi & 0x00800080u) << 8);
+  return uint2{lo, hi};
+}
+
+// Eight codes (two dwords) -> one f16x8 operand.
+__device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t x0, uint32_t x1) {
+  const uint2 a = e4m3x4_to_f16x4(x0), b = e4m3x4_to_f16x4(x1);
+  return __builtin_bit_cast(f16x8, (u32x4{a.x, a.y, b.x, b.y}));
+}
+
 // Order-preserving unsigned keys (larger value <-> larger key).
 __device__ __forceinline__ uint32_t f32_key(uint32_t u) { return (u & 0x80000000u) ? ~u : (u | 0x80000000u); }
 __device__ __forceinline__ uint32_t bf16_key(uint32_t h) { return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u); }
@@ -68,32 +99,36 @@ __device__ __forceinline__ uint32_t bf16_key(uint32_t h) { return (h & 0x8000u) 
 // this lane's partial sums of four outputs; on return the lane holds the full
 // sum of output j = g (summed over the four lane groups of its column).
 __device__ __forceinline__ float transpose_reduce4(const float v[4], int lane) {
-  const bool hi = lane >= 32;             // g in {2,3}
-  const bool odd = (lane >> 4) & 1;       // g in {1,3}
+  const bool hi = lane >= 32;        // g in {2,3}
+  const bool odd = (lane >> 4) & 1;  // g in {1,3}
   float s0 = hi ? v[0] : v[2];
   float s1 = hi ? v[1] : v[3];
   float r0 = __shfl_xor(s0, 32);
   float r1 = __shfl_xor(s1, 32);
-  float k0 = (hi ? v[2] : v[0]) + r0;     // output 2*hi + 0
-  float k1 = (hi ? v[3] : v[1]) + r1;     // output 2*hi + 1
+  float k0 = (hi ? v[2] : v[0]) + r0;  // output 2*hi + 0
+  float k1 = (hi ? v[3] : v[1]) + r1;  // output 2*hi + 1
   float s = odd ? k0 : k1;
   float r = __shfl_xor(s, 16);
   return (odd ? k1 : k0) + r;
 }
 
-// A-operand fragments of one query row: four 16-head tiles.
+// A-operand fragments of one query row: four 16-head tiles x four 32-dim slices.
 struct QFrag {
-  i32x8 a[4];
+  f16x8 a[4][4];
 };
 
-// Load q[row] (64 x 128 codes, contiguous) into this lane's A fragments.
+// Load q[row] (64 x 128 codes, contiguous) and decode it into this lane's A fragments:
+// lane (head n, group g) reads the codes [32g, 32g+32) of head hb*16+n; slice s takes 8.
 __device__ __forceinline__ void load_q(QFrag& f, const uint8_t* q_row, int lane) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int hb = 0; hb < 4; hb++) {
     const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 16 + n) * kDim + g * 32);
-    uint4 x0 = p[0], x1 = p[1];
-    f.a[hb] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    const uint4 x0 = p[0], x1 = p[1];
+    f.a[hb][0] = e4m3x8_to_f16x8(x0.x, x0.y);
+    f.a[hb][1] = e4m3x8_to_f16x8(x0.z, x0.w);
+    f.a[hb][2] = e4m3x8_to_f16x8(x1.x, x1.y);
+    f.a[hb][3] = e4m3x8_to_f16x8(x1.z, x1.w);
   }
 }
 
@@ -114,32 +149,53 @@ __device__ __forceinline__ void load_w(WFrag& f, const uint16_t* w_row, int lane
   }
 }
 
-// B-operand fragment for 16 keys whose LDS rows start at `keys` (kLdsKeyStride apart).
-__device__ __forceinline__ i32x8 load_kfrag(const uint8_t* keys, int lane) {
+// B-operand fragments for 16 keys: four 32-dim slices.
+struct KFrag {
+  f16x8 b[4];
+};
+
+// From FP8 key rows in LDS (kLdsKeyStride apart): read this lane's 32 codes and decode.
+__device__ __forceinline__ void load_kfrag_fp8(KFrag& f, const uint8_t* keys, int lane) {
   const int n = lane & 15, g = lane >> 4;
   const uint4* p = reinterpret_cast<const uint4*>(keys + n * kLdsKeyStride + g * 32);
-  uint4 x0 = p[0], x1 = p[1];
-  return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  const uint4 x0 = p[0], x1 = p[1];
+  f.b[0] = e4m3x8_to_f16x8(x0.x, x0.y);
+  f.b[1] = e4m3x8_to_f16x8(x0.z, x0.w);
+  f.b[2] = e4m3x8_to_f16x8(x1.x, x1.y);
+  f.b[3] = e4m3x8_to_f16x8(x1.z, x1.w);
 }
 
-// Head-weighted partial of one (row, 16-key group): the 64-head contraction on
-// the matrix cores, then this lane's 16 heads weighted and summed.
-__device__ __forceinline__ float score_partial(const QFrag& q, const WFrag& w, const i32x8& kb) {
+// From key rows already decoded to f16 in LDS (kLdsKeyStrideF16 apart).
+__device__ __forceinline__ void load_kfrag_f16(KFrag& f, const uint8_t* keys, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  const f16x8* p = reinterpret_cast<const f16x8*>(keys + n * kLdsKeyStrideF16 + g * 64);
+#pragma unroll
+  for (int s = 0; s < 4; s++) f.b[s] = p[s];
+}
+
+// Head-weighted partial of one (row, 16-key group): the 64-head contraction on the
+// matrix cores, then this lane's 16 heads weighted and summed.  The result carries
+// the 2^-16 of the decoded operands.
+__device__ __forceinline__ float score_partial(const QFrag& q, const WFrag& w, const KFrag& kb) {
   f32x4 c[4];
 #pragma unroll
-  for (int hb = 0; hb < 4; hb++) c[hb] = mfma_fp8(q.a[hb], kb, f32x4{0.f, 0.f, 0.f, 0.f});
-  float s = 0.f;
+  for (int hb = 0; hb < 4; hb++) {
+    c[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; s++) c[hb] = mfma_f16(q.a[hb][s], kb.b[s], c[hb]);
+  }
+  float acc = 0.f;
 #pragma unroll
   for (int hb = 0; hb < 4; hb++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) s = fmaf(w.w[hb][i], c[hb][i], s);
-  return s;
+    for (int i = 0; i < 4; i++) acc = fmaf(w.w[hb][i], c[hb][i], acc);
+  return acc;
 }
 
-// Copy one 16-byte chunk of a contiguous run of 132-byte cache rows into the
-// LDS key layout: dword d of the run belongs to row d/33, word d%33 (word 32
-// is the fp32 scale).  `chunk` is the chunk index within the run, `key0` the
-// LDS key slot of the run's first row.
+// Copy one 16-byte chunk of a contiguous run of 132-byte cache rows into the FP8
+// LDS key layout: dword d of the run belongs to row d/33, word d%33 (word 32 is
+// the fp32 scale).  `chunk` is the chunk index within the run, `key0` the LDS key
+// slot of the run's first row.
 __device__ __forceinline__ void scatter_chunk(uint8_t* lds_codes, float* lds_scale, int key0, int chunk,
                                               const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -152,6 +208,15 @@ __device__ __forceinline__ void scatter_chunk(uint8_t* lds_codes, float* lds_sca
     else
       lds_scale[key0 + row] = __uint_as_float(w[j]);
   }
+}
+
+// The same for the decoded layout: each code dword becomes two f16 dwords.
+__device__ __forceinline__ void scatter_word_f16(uint8_t* lds_f16, float* lds_scale, int d, uint32_t x) {
+  int row = d / 33, word = d - row * 33;
+  if (word < 32)
+    *reinterpret_cast<uint2*>(lds_f16 + row * kLdsKeyStrideF16 + word * 8) = e4m3x4_to_f16x4(x);
+  else
+    lds_scale[row] = __uint_as_float(x);
 }
 
 }  // namespace dsi

@@ -8,7 +8,9 @@
 // HBM/L2-bound.  A workgroup gathers 256 keys (segments of 16, or 8, consecutive
 // tokens that are contiguous in memory) into LDS with 16-byte loads — all issued
 // before any is used — then each wavefront scores 4 groups of 16 keys on the
-// matrix cores (common.h) and writes its outputs.  Block-table entries are read
+// matrix cores, decoding the FP8 codes to f16 as it reads them (common.h), and
+// writes its outputs.  Query rows are held two at a time (next_n 3 and 4 take a
+// second pass over the staged keys).  Block-table entries are read
 // once per segment into LDS.  Out-of-range table entries or page ids never
 // produce an access outside the pool: those keys score -inf.
 #include "common.h"
@@ -60,7 +62,7 @@ __device__ __forceinline__ void gather_keys(uint8_t* s_codes, float* s_scale, co
 }
 
 // ------------------------------------------------------------------ paged decode
-// grid = (ceil(max_context_len / 256), B); R = next_n rounded up to 1, 2 or 4.
+// grid = (ceil(max_context_len / 256), B); R = 1 (next_n 1) or 2 (rows taken in pairs).
 template <int R>
 __global__ __launch_bounds__(256) void paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int next_n, const int* __restrict__ context_lens,
@@ -89,40 +91,43 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(
     }
     s_base[tid] = base;
   }
-
-  QFrag qf[R];
-  WFrag wf[R];
-#pragma unroll
-  for (int r = 0; r < R; r++) {
-    const int64_t row = (int64_t)b * next_n + min(r, next_n - 1);
-    load_q(qf[r], q + row * kHeads * kDim, lane);
-    load_w(wf[r], w + row * kHeads, lane);
-  }
   __syncthreads();
   gather_keys(s_codes, s_scale, s_base, pool, num_blocks * block_stride, 16, tid);
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
   constexpr int KPB = 4 / R;  // key groups per batch of four outputs
+  for (int r0 = 0; r0 < next_n; r0 += R) {
+    QFrag qf[R];
+    WFrag wf[R];
 #pragma unroll
-  for (int batch = 0; batch < R; batch++) {
-    float part[4];
-#pragma unroll
-    for (int kgi = 0; kgi < KPB; kgi++) {
-      const int grp = wave + 4 * (batch * KPB + kgi);
-      const i32x8 kb = load_kfrag(s_codes + grp * 16 * kLdsKeyStride, lane);
-#pragma unroll
-      for (int r = 0; r < R; r++) part[r * KPB + kgi] = score_partial(qf[r], wf[r], kb);
+    for (int r = 0; r < R; r++) {
+      const int64_t row = (int64_t)b * next_n + min(r0 + r, next_n - 1);
+      load_q(qf[r], q + row * kHeads * kDim, lane);
+      load_w(wf[r], w + row * kHeads, lane);
     }
-    const float v = transpose_reduce4(part, lane);
-    const int r = g / KPB, kgi = g - r * KPB;
-    const int grp = wave + 4 * (batch * KPB + kgi);
-    const int kslot = grp * 16 + n;
-    const int tok = tok0 + kslot;
-    if (r < next_n) {
-      const int ke = min(L - next_n + r + 1, max_ctx);
-      if (tok < ke)
-        logits[((int64_t)b * next_n + r) * ld + tok] = s_base[grp] >= 0 ? v * s_scale[kslot] : -INFINITY;
+#pragma unroll
+    for (int batch = 0; batch < R; batch++) {
+      float part[4];
+#pragma unroll
+      for (int kgi = 0; kgi < KPB; kgi++) {
+        const int grp = wave + 4 * (batch * KPB + kgi);
+        KFrag kb;
+        load_kfrag_fp8(kb, s_codes + grp * 16 * kLdsKeyStride, lane);
+#pragma unroll
+        for (int r = 0; r < R; r++) part[r * KPB + kgi] = score_partial(qf[r], wf[r], kb);
+      }
+      const float v = transpose_reduce4(part, lane);
+      const int r = r0 + g / KPB, kgi = g % KPB;
+      const int grp = wave + 4 * (batch * KPB + kgi);
+      const int kslot = grp * 16 + n;
+      const int tok = tok0 + kslot;
+      if (r < next_n) {
+        const int ke = min(L - next_n + r + 1, max_ctx);
+        if (tok < ke)
+          logits[((int64_t)b * next_n + r) * ld + tok] =
+              s_base[grp] >= 0 ? v * (s_scale[kslot] * kF16Unscale) : -INFINITY;
+      }
     }
   }
 }
@@ -133,8 +138,9 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
     const int* __restrict__ end, int sbk, const uint8_t* __restrict__ k_src, int64_t num_k,
-    const int* __restrict__ block_table, int64_t bt_ld, int bt_width, const int* __restrict__ row_to_req,
-    int block_size, int64_t block_stride, uint16_t* __restrict__ out, int64_t ld) {
+    const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
+    const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
+    int64_t ld) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[kKeys * kLdsKeyStride];
   __shared__ float s_scale[kKeys];
   __shared__ int64_t s_base[32];
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
         } else {
           const int req = row_to_req ? row_to_req[r] : r;
           const int blk = tok / block_size;
-          if (blk < bt_width) {
+          if (blk < bt_width && req >= 0 && req < num_reqs) {
             const int page = block_table[(int64_t)req * bt_ld + blk];
             if (page >= 0 && page < num_k) base = (int64_t)page * block_stride + (int64_t)(tok % block_size) * kRow;
           }
@@ -184,7 +190,8 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
 #pragma unroll
   for (int kgi = 0; kgi < 4; kgi++) {
     const int grp = wave + 4 * kgi;
-    const i32x8 kb = load_kfrag(s_codes + grp * 16 * kLdsKeyStride, lane);
+    KFrag kb;
+    load_kfrag_fp8(kb, s_codes + grp * 16 * kLdsKeyStride, lane);
     part[kgi] = score_partial(qf, wf, kb);
   }
   const float v = transpose_reduce4(part, lane);
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
     const int seg = kslot / G;
     const int tok = s_tok[seg] + (kslot - seg * G);
     const bool valid = c < e && s_base[seg] >= 0 && tok >= ks && tok < ke && (paged || tok < num_k);
-    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * s_scale[kslot]) : (uint16_t)0xFF80u;
+    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * (s_scale[kslot] * kF16Unscale)) : (uint16_t)0xFF80u;
   }
 }
 
@@ -214,6 +221,7 @@ extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, 
   if (block_stride_bytes < (int64_t)block_size * kRow) return DSI_EINVAL;
   if (B == 0 || max_context_len == 0) return DSI_OK;
   if (!q || !w || !context_lens || !pool || !block_table || !logits) return DSI_EINVAL;
+  if (B > 65535) return DSI_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(pool) & 15) ||
       (block_stride_bytes & 15) || (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits) & 3))
     return DSI_EALIGN;
@@ -222,12 +230,8 @@ extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, 
     hipLaunchKernelGGL(paged_decode_kernel<1>, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool,
                        num_blocks, block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
                        logits, ld);
-  else if (next_n == 2)
-    hipLaunchKernelGGL(paged_decode_kernel<2>, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool,
-                       num_blocks, block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
-                       logits, ld);
   else
-    hipLaunchKernelGGL(paged_decode_kernel<4>, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool,
+    hipLaunchKernelGGL(paged_decode_kernel<2>, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool,
                        num_blocks, block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
                        logits, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
@@ -237,7 +241,7 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
                                      const int32_t* row_ke, const int32_t* sparse_indices, int64_t si_ld,
                                      int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
                                      const uint8_t* k_src, int64_t num_k, const int32_t* block_table, int64_t bt_ld,
-                                     int32_t bt_width, const int32_t* row_to_req, int32_t block_size,
+                                     int32_t bt_width, int32_t num_reqs, const int32_t* row_to_req, int32_t block_size,
                                      int64_t block_stride_bytes, uint16_t* logits_bf16, int64_t ld,
                                      hipStream_t stream) {
   using namespace dsi;
@@ -248,7 +252,7 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
   if (width > 0x7FFFFFFF || ld < width) return DSI_EINVAL;
   const bool paged = block_table != nullptr;
   if (paged) {
-    if (bt_width < 0 || bt_ld < bt_width) return DSI_EINVAL;
+    if (bt_width < 0 || bt_ld < bt_width || num_reqs < 0) return DSI_EINVAL;
     if (block_size < 8 || (block_size % sbk) != 0 || (block_size % 8) != 0) return DSI_EUNSUPPORTED;
     if (block_stride_bytes < (int64_t)block_size * kRow) return DSI_EINVAL;
     if (block_stride_bytes & 15) return DSI_EALIGN;
@@ -261,7 +265,7 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
   if (rows > 65535) return DSI_EUNSUPPORTED;
   const dim3 grid((unsigned)((width + kKeys - 1) / kKeys), (unsigned)rows);
   hipLaunchKernelGGL(sparse_logits_kernel, grid, dim3(256), 0, stream, q, w, row_ks, row_ke, sparse_indices, si_ld,
-                     (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, row_to_req, block_size,
+                     (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req, block_size,
                      block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }

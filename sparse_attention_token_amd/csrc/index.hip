@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void remap_kernel(const int* __restrict__ col,
 __global__ __launch_bounds__(256) void slot_kernel(const int* idx, int64_t idx_ld, int k,
                                                    const int* __restrict__ row_to_req,
                                                    const int* __restrict__ block_table, int64_t bt_ld, int bt_width,
-                                                   int block_size, int block_span, int* out, int64_t out_ld) {
+                                                   int num_reqs, int block_size, int block_span, int* out,
+                                                   int64_t out_ld) {
   const int r = blockIdx.y;
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= k) return;
@@ -106,10 +107,9 @@ __global__ __launch_bounds__(256) void slot_kernel(const int* idx, int64_t idx_l
   int v = -1;
   if (p >= 0) {
     const int blk = p / block_size;
-    if (blk < bt_width) {
-      const int req = row_to_req ? row_to_req[r] : r;
+    const int req = row_to_req ? row_to_req[r] : r;
+    if (blk < bt_width && req >= 0 && req < num_reqs)
       v = block_table[(int64_t)req * bt_ld + blk] * block_span + p % block_size;
-    }
   }
   out[(int64_t)r * out_ld + j] = v;
 }
@@ -158,15 +158,17 @@ extern "C" int dsi_topk_remap(const int32_t* col, int64_t col_ld, int32_t rows, 
 
 extern "C" int dsi_req_index_to_global_slot(const int32_t* idx, int64_t idx_ld, int32_t rows, int32_t k,
                                             const int32_t* row_to_req, const int32_t* block_table, int64_t bt_ld,
-                                            int32_t bt_width, int32_t block_size, int32_t block_span, int32_t* out,
+                                            int32_t bt_width, int32_t num_reqs, int32_t block_size, int32_t block_span, int32_t* out,
                                             int64_t out_ld, hipStream_t stream) {
   using namespace dsi;
   if (block_size < 1 || block_span < block_size) return DSI_EUNSUPPORTED;
-  if (rows < 0 || k < 0 || idx_ld < k || out_ld < k || bt_width < 0 || bt_ld < bt_width) return DSI_EINVAL;
+  if (rows < 0 || k < 0 || idx_ld < k || out_ld < k || bt_width < 0 || bt_ld < bt_width || num_reqs < 0)
+    return DSI_EINVAL;
   if (rows == 0 || k == 0) return DSI_OK;
   if (!idx || !block_table || !out) return DSI_EINVAL;
   if (rows > 65535) return DSI_EUNSUPPORTED;
   hipLaunchKernelGGL(slot_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)rows), dim3(256), 0, stream, idx,
-                     idx_ld, k, row_to_req, block_table, bt_ld, bt_width, block_size, block_span, out, out_ld);
+                     idx_ld, k, row_to_req, block_table, bt_ld, bt_width, num_reqs, block_size, block_span, out,
+                     out_ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }

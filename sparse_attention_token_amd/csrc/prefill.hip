@@ -2,13 +2,15 @@
 // table of "DeepSeek V3.2 稀疏注意力 DSA 推理流程图解": prefill gathers the history
 // K, then scores every history token for every query token).
 //
-// The contraction [T*64, 128] x [128, S] runs on FP8 MFMA; the head-weighted sum
-// is the epilogue (see common.h).  A workgroup owns 8 query rows (two per
-// wavefront, q held in VGPRs for the whole kernel) and a chunk of 1024 keys,
-// streamed through LDS in double-buffered tiles of 64 keys; tiles wholly outside
-// the rows' [ks, ke) ranges are never loaded, so causal work above the diagonal
-// is skipped.  Consecutive workgroups on one XCD share the same rows (their q in
-// that XCD's L2); K (132 B per key) is re-read from L2 by each row tile.
+// The contraction [T*64, 128] x [128, S] runs on the matrix cores with the FP8 codes
+// decoded exactly to f16 (see common.h for why and how); the head-weighted sum is the
+// epilogue.  A workgroup owns 8 query rows (two per wavefront, q decoded once and
+// held in VGPRs) and a chunk of 1024 keys, streamed through LDS in double-buffered
+// tiles of 64 keys that are decoded to f16 as they are staged (each staged key is
+// then read by all 8 rows); tiles wholly outside the rows' [ks, ke) ranges are never
+// loaded, so causal work above the diagonal is skipped.  Consecutive workgroups on
+// one XCD share the same rows (their q in that XCD's L2); K (132 B per key) is
+// re-read from L2 by each row tile.
 #include "common.h"
 
 namespace dsi {
@@ -47,24 +49,22 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, uint8_t* codes, fl
 #pragma unroll
   for (int j = 0; j < kLoadsPerThread; j++) {
     int c = tid + j * 256;
-    if (c < full) scatter_chunk(codes, scale, 0, c, r.v[j]);
+    if (c < full) {
+      scatter_word_f16(codes, scale, c * 4 + 0, r.v[j].x);
+      scatter_word_f16(codes, scale, c * 4 + 1, r.v[j].y);
+      scatter_word_f16(codes, scale, c * 4 + 2, r.v[j].z);
+      scatter_word_f16(codes, scale, c * 4 + 3, r.v[j].w);
+    }
   }
   int tail_words = (bytes & 15) >> 2;
-  if (tid < tail_words) {
-    int d = full * 4 + tid;
-    int row = d / 33, word = d - row * 33;
-    if (word < 32)
-      *reinterpret_cast<uint32_t*>(codes + row * kLdsKeyStride + word * 4) = r.tail;
-    else
-      scale[row] = __uint_as_float(r.tail);
-  }
+  if (tid < tail_words) scatter_word_f16(codes, scale, full * 4 + tid, r.tail);
 }
 
 __global__ __launch_bounds__(256) void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int T, const uint8_t* __restrict__ k_rows, int S,
     const int* __restrict__ row_ks, const int* __restrict__ row_ke, float* __restrict__ logits, int64_t ld,
     int n_chunks) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTileKeys * kLdsKeyStride];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTileKeys * kLdsKeyStrideF16];
   __shared__ float s_scale[2][kTileKeys];
 
   // Workgroups are dealt to the 8 XCDs round-robin; renumber so that the chunks
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
       float part[4];
 #pragma unroll
       for (int kg = 0; kg < 2; kg++) {
-        const i32x8 kb = load_kfrag(s_codes[buf] + (pair * 2 + kg) * 16 * kLdsKeyStride, lane);
+        KFrag kb;
+        load_kfrag_f16(kb, s_codes[buf] + (pair * 2 + kg) * 16 * kLdsKeyStrideF16, lane);
 #pragma unroll
         for (int r = 0; r < kPfRowsPerWave; r++) part[r * 2 + kg] = score_partial(qf[r], wf[r], kb);
       }
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
       const int kslot = (pair * 2 + (g & 1)) * 16 + n;
       const int key = key0 + kslot;
       const int rk = r ? rks[1] : rks[0], re = r ? rke[1] : rke[0], t = r ? trow[1] : trow[0];
-      if (key >= rk && key < re) logits[(int64_t)t * ld + key] = v * s_scale[buf][kslot];
+      if (key >= rk && key < re) logits[(int64_t)t * ld + key] = v * (s_scale[buf][kslot] * kF16Unscale);
     }
 
     if (has_next) store_tile(regs, s_codes[buf ^ 1], s_scale[buf ^ 1], nnk, tid);

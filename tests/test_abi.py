@@ -122,8 +122,8 @@ def test_sparse_validation():
     L = dsi.lib()
 
     def call(sbk=16, nsb=4, si_ld=4, ld=64, bt=None, bs=0, stride=0, k_src=A16, q=A16):
-        return L.dsi_sparse_mqa_logits(q, A16, 2, A16, A16, A16, si_ld, nsb, A16, sbk, k_src, 100, bt, 4, 4, None,
-                                       bs, stride, A16, ld, None)
+        return L.dsi_sparse_mqa_logits(q, A16, 2, A16, A16, A16, si_ld, nsb, A16, sbk, k_src, 100, bt, 4, 4, 2,
+                                       None, bs, stride, A16, ld, None)
     assert call(sbk=12) == EUNSUP and call(sbk=4) == EUNSUP
     assert call(si_ld=3) == EINVAL and call(ld=63) == EINVAL and call(nsb=0) == EINVAL
     assert call(bt=A16, bs=24, stride=24 * 132) == EUNSUP  # block_size not a multiple of sbk
@@ -140,11 +140,11 @@ def test_remap_and_slot_validation():
     assert L.dsi_topk_remap(None, 4, 2, 4, A16, 4, 4, A16, 16, A16, 4, None) == EINVAL
     assert L.dsi_topk_remap(A16, 4, 0, 4, A16, 4, 4, A16, 16, A16, 4, None) == 0
     f = L.dsi_req_index_to_global_slot
-    assert f(A16, 4, 2, 4, None, A16, 8, 8, 0, 64, A16, 4, None) == EUNSUP
-    assert f(A16, 4, 2, 4, None, A16, 8, 8, 64, 63, A16, 4, None) == EUNSUP  # span < block_size
-    assert f(A16, 4, 2, 4, None, A16, 7, 8, 64, 64, A16, 4, None) == EINVAL  # bt_ld < bt_width
-    assert f(A16, 4, 2, 4, None, None, 8, 8, 64, 64, A16, 4, None) == EINVAL
-    assert f(A16, 4, 2, 0, None, A16, 8, 8, 64, 64, A16, 4, None) == 0
+    assert f(A16, 4, 2, 4, None, A16, 8, 8, 2, 0, 64, A16, 4, None) == EUNSUP
+    assert f(A16, 4, 2, 4, None, A16, 8, 8, 2, 64, 63, A16, 4, None) == EUNSUP  # span < block_size
+    assert f(A16, 4, 2, 4, None, A16, 7, 8, 2, 64, 64, A16, 4, None) == EINVAL  # bt_ld < bt_width
+    assert f(A16, 4, 2, 4, None, None, 8, 8, 2, 64, 64, A16, 4, None) == EINVAL
+    assert f(A16, 4, 2, 0, None, A16, 8, 8, 2, 64, 64, A16, 4, None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

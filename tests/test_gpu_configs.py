@@ -1,0 +1,188 @@
+"""The five workloads end to end on the GPU, at their full sizes, in the launch configuration the bench times.
+
+The GPU runs every step for every row; the oracle recomputes sampled rows one by one from the same generator
+inputs (its own quantized K, never bytes produced by the GPU).  Workloads:
+  1 tiny dense indexer (T=8 at positions 3064..3071, S=3072),
+  2 prefill chunk (T=2048 at 6144..8191, S=8192),
+  3 paged decode (64 requests, lengths U{4096..65536}, 64-token pages, random block tables),
+  4 long-context decode (16 requests x next_n 2, lengths U{98304..131072}),
+  5 hierarchical sparse (32 decode requests + a 1024-row prefill chunk, lengths U{32768..131072},
+    64 candidate blocks of 128 tokens per row with duplicates and out-of-range ids).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_amd as dsi
+import synth
+from parity_util import (ROW, assert_close, bf16_value, check_selection, dev, gathered_rows_oracle, host,
+                         tol_bf16)
+
+pytestmark = pytest.mark.gpu
+K = 2048
+
+
+def _gpu_gathered_rows(k_bf16):
+    S = k_bf16.shape[0]
+    rows = torch.zeros((S, ROW), dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(k_bf16), dev(np.arange(S, dtype=np.int64)), rows.view(-1), S, S * ROW, 1)
+    return rows
+
+
+def _prefill_workload(n, sample_rows):
+    c = synth.workload(n)
+    T, S = c["T"], c["S"]
+    rows_ref = gathered_rows_oracle(c["k"])
+    rows_gpu = _gpu_gathered_rows(c["k"])
+    assert np.array_equal(host(rows_gpu), rows_ref), "k quantization is not bit-exact"
+    ks, ke = c["ks"], c["ke"]
+    logits = dsi.mqa_logits_prefill(dev(c["q"]), dev(c["w"]), rows_gpu, dev(ks), dev(ke))
+    idx = host(dsi.topk_select(logits, dev(ke), k=K, row_starts=dev(ks)))
+    got = host(logits)
+    for t in sample_rows:
+        ref = oracle.mqa_logits_gathered(c["q"][t:t + 1], c["w"][t:t + 1], rows_ref, ks[t:t + 1], ke[t:t + 1])[0]
+        valid = np.isfinite(ref)
+        assert_close(got[t][valid], ref[valid], what=f"row {t} logits")
+        ref_idx = oracle.topk_select(ref[None, :], ke[t:t + 1], K, starts=ks[t:t + 1])[0]
+        check_selection(idx[t], ref_idx, ref, start=ks[t], end=ke[t])
+    return c, got, idx
+
+
+def test_workload1_tiny_dense():
+    c, got, idx = _prefill_workload(1, range(8))
+    # identical-input top-k: GPU selection over the oracle's own logits has the oracle's exact value multiset
+    rows_ref = gathered_rows_oracle(c["k"])
+    ref = oracle.mqa_logits_gathered(c["q"], c["w"], rows_ref, c["ks"], c["ke"])
+    same = host(dsi.topk_select(dev(ref), dev(c["ke"]), k=K))
+    ref_idx = oracle.topk_select(ref, c["ke"], K)
+    for t in range(8):
+        assert np.array_equal(np.sort(ref[t, same[t][same[t] >= 0]]), np.sort(ref[t, ref_idx[t][ref_idx[t] >= 0]]))
+
+
+def test_workload2_prefill_chunk():
+    rng = np.random.default_rng(2)
+    sample = sorted(set([0, 1, 7, 8, 1023, 1024, 2040, 2047] + rng.integers(0, 2048, 8).tolist()))
+    _prefill_workload(2, sample)
+
+
+def _decode_workload(n, n_sample):
+    c = synth.workload(n)
+    bs, stride, nb = c["block_size"], c["block_stride"], c["num_blocks"]
+    nn, B = c["next_n"], c["B"]
+    lens = c["context_lens"]
+    maxc = int(lens.max())
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(c["k"]), dev(c["slot_mapping"]), pool, bs, stride, nb)
+    bt = dev(c["block_table"])
+    logits = dsi.paged_mqa_logits_decode(dev(c["q"]), dev(c["w"]), dev(lens), pool, bs, bt, maxc, next_n=nn,
+                                         block_stride_bytes=stride, num_blocks=nb)
+    ends = np.repeat(lens, nn) - nn + np.tile(np.arange(nn), B) + 1
+    idx_t = dsi.topk_select(logits, dev(ends.astype(np.int32)), k=K)
+    row_to_req = np.repeat(np.arange(B, dtype=np.int32), nn)
+    slots = host(dsi.req_index_to_global_slot(idx_t, bt, bs, bs, row_to_req=dev(row_to_req)))
+    idx = host(idx_t)
+    got = host(logits)
+    pool_gpu = host(pool)
+    order = np.argsort(lens)
+    sample = [int(order[0]), int(order[-1])] + [int(b) for b in np.random.default_rng(n).choice(B, n_sample - 2,
+                                                                                               replace=False)]
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for b in sorted(set(sample)):
+        L = int(lens[b])
+        # oracle: quantize this request's tokens into its own pool, compare the bytes, then score its rows
+        pool_ref = np.zeros(nb * stride, np.uint8)
+        sl = c["slot_mapping"][starts[b]:starts[b + 1]]
+        oracle.k_quant_and_cache(c["k"][starts[b]:starts[b + 1]], sl, pool_ref, bs, stride)
+        toks = (c["block_table"][b, np.arange(L) // bs].astype(np.int64) * stride + (np.arange(L) % bs) * ROW)
+        rowbytes = toks[:, None] + np.arange(ROW)[None, :]
+        assert np.array_equal(pool_gpu[rowbytes], pool_ref[rowbytes]), f"request {b}: k rows differ"
+        rr = slice(b * nn, (b + 1) * nn)
+        ref = oracle.mqa_logits_paged(c["q"][rr], c["w"][rr], nn, lens[b:b + 1], pool_ref, bs, stride,
+                                      c["block_table"][b:b + 1], maxc)
+        for i in range(nn):
+            r = b * nn + i
+            valid = np.isfinite(ref[i])
+            assert_close(got[r][valid], ref[i][valid], what=f"row {r} logits")
+            assert valid.sum() == ends[r]
+            ref_idx = oracle.topk_select(ref[i:i + 1], ends[r:r + 1], K)[0]
+            check_selection(idx[r], ref_idx, ref[i], end=int(ends[r]))
+            if int(ends[r]) < K:
+                assert np.all(idx[r][int(ends[r]):] == -1)
+            # slot conversion of the selected positions (consistency with the block table)
+            p = idx[r]
+            exp = np.where(p >= 0, c["block_table"][b, np.maximum(p, 0) // bs] * bs + np.maximum(p, 0) % bs, -1)
+            assert np.array_equal(slots[r], exp)
+
+
+def test_workload3_paged_decode():
+    _decode_workload(3, 4)
+
+
+def test_workload4_long_context_decode():
+    _decode_workload(4, 3)
+
+
+def test_workload5_hierarchical_sparse():
+    c = synth.workload(5)
+    sbk, cbs, nd, chunk, rows = c["sbk"], c["cbs"], c["n_decode"], c["chunk"], c["rows"]
+    bs, stride, nb = c["block_size"], c["block_stride"], c["num_blocks"]
+    ks, ke, cand = c["ks"], c["ke"], c["cand"]
+    # expansion for every row: bit-exact
+    si_ref, end_ref = oracle.expand_candidates(cand, ks, ke, cbs, sbk)
+    si_t, end_t = dsi.expand_candidates(dev(cand), dev(ks), dev(ke), cbs, sbk)
+    assert np.array_equal(host(si_t), si_ref) and np.array_equal(host(end_t), end_ref)
+    # K: decode requests in the paged pool (128-token pages), prefill request gathered
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(c["k_dec"]), dev(c["dec_slot_mapping"]), pool, bs, stride, nb)
+    pre_rows = _gpu_gathered_rows(c["k_pre"])
+    width = si_ref.shape[1] * sbk
+    out = torch.empty((rows, width), dtype=torch.int16, device="cuda")
+    q, w = dev(c["q"]), dev(c["w"])
+    ks_t, ke_t = dev(ks), dev(ke)
+    bt = dev(c["block_table"])
+    dsi.sparse_mqa_logits(q[:nd], w[:nd], ks_t[:nd], ke_t[:nd], si_t[:nd], end_t[:nd], sbk, pool, block_table=bt,
+                          row_to_req=dev(c["row_to_req"]), block_size=bs, block_stride_bytes=stride, num_k=nb,
+                          out=out[:nd])
+    dsi.sparse_mqa_logits(q[nd:], w[nd:], ks_t[nd:], ke_t[nd:], si_t[nd:], end_t[nd:], sbk, pre_rows,
+                          out=out[nd:])
+    col_t = dsi.topk_select(out, end_t, k=K)
+    pos_t = dsi.topk_remap(col_t, si_t, ks_t, sbk)
+    slot_t = dsi.req_index_to_global_slot(pos_t[:nd], bt, bs, bs, row_to_req=dev(c["row_to_req"]))
+    got, col, pos, slot = host(out), host(col_t), host(pos_t), host(slot_t)
+    # every row: remap and slot outputs are consistent with their own inputs
+    for r in range(rows):
+        cr = col[r]
+        exp = np.where(cr >= 0, (si_ref[r, np.maximum(cr, 0) // sbk] - ks[r] // sbk) * sbk + np.maximum(cr, 0) % sbk,
+                       -1)
+        assert np.array_equal(pos[r], exp)
+    # sampled rows against the oracle
+    rng = np.random.default_rng(5)
+    dec_rows = sorted(set([0, nd - 1] + rng.integers(0, nd, 2).tolist()))
+    pre_rows_s = sorted(set([nd, rows - 1] + rng.integers(nd, rows, 6).tolist()))
+    pre_ref = gathered_rows_oracle(c["k_pre"])
+    assert np.array_equal(host(pre_rows), pre_ref), "prefill k rows differ"
+    starts = np.concatenate([[0], np.cumsum(c["dec_lens"])])
+    for r in dec_rows + pre_rows_s:
+        if r < nd:
+            pool_ref = np.zeros(nb * stride, np.uint8)
+            oracle.k_quant_and_cache(c["k_dec"][starts[r]:starts[r + 1]], c["dec_slot_mapping"][starts[r]:starts[r + 1]],
+                                     pool_ref, bs, stride)
+            kw = dict(k_src=pool_ref, block_table=c["block_table"], row_to_req=c["row_to_req"][r:r + 1],
+                      block_size=bs, block_stride=stride)
+        else:
+            kw = dict(k_src=pre_ref)
+        sl = slice(r, r + 1)
+        ref_f32 = oracle.sparse_mqa_logits(c["q"][sl], c["w"][sl], ks[sl], ke[sl], si_ref[sl], end_ref[sl], sbk,
+                                           out_f32=True, **kw)[0]
+        ref_bits = oracle.sparse_mqa_logits(c["q"][sl], c["w"][sl], ks[sl], ke[sl], si_ref[sl], end_ref[sl], sbk,
+                                            **kw)[0]
+        valid = np.isfinite(ref_f32)
+        assert np.all(got[r][~valid] == 0xFF80)
+        assert_close(bf16_value(got[r][valid]), ref_f32[valid], tol_fn=tol_bf16, what=f"row {r} sparse logits")
+        ref_col = oracle.topk_select(ref_bits[None, :], end_ref[sl], K, bf16=True)[0]
+        check_selection(col[r], ref_col, ref_f32, tol_fn=tol_bf16, end=int(end_ref[r]))
+        if r < nd:
+            p = pos[r]
+            exp = np.where(p >= 0, c["block_table"][r, np.maximum(p, 0) // bs] * bs + np.maximum(p, 0) % bs, -1)
+            assert np.array_equal(slot[r], exp)

@@ -1,0 +1,337 @@
+"""GPU parity, one kernel at a time, against the oracle on identical input bytes.
+
+Sizes are small enough for the oracle to finish in seconds but span several tiles and a ragged tail.
+Integer and byte outputs must be bit-exact; logits use the tolerance rules in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_amd as dsi
+import synth
+from parity_util import (ROW, assert_close, bf16_value, check_selection, dev, gathered_rows_oracle, host,
+                         paged_pool_oracle, tol_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------------------- k quant + cache insert
+def test_k_quant_every_bf16_value_bit_exact():
+    # amax = 448 makes the scale exactly 1, so every bf16 value in [-448, 448] is encoded as itself:
+    # an exhaustive check of the device rounding (ties, subnormals, saturation edge).
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    x = (bits << 16).view(np.float32)
+    vals = x[np.isfinite(x) & (np.abs(x) <= 448)]
+    n = (vals.size + 126) // 127
+    k = np.zeros((n, 128), np.float32)
+    flat = np.zeros(n * 127, np.float32)
+    flat[:vals.size] = vals
+    k[:, :127] = flat.reshape(n, 127)
+    k[:, 127] = 448.0
+    kb = synth._bf16_bits(k)
+    bs, stride = 16, 16 * ROW
+    nb = (n + bs - 1) // bs
+    slots = np.arange(n, dtype=np.int64)
+    ref = paged_pool_oracle(kb, slots, nb, bs, stride)
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(kb), dev(slots), pool, bs, stride, nb)
+    assert np.array_equal(host(pool), ref)
+
+
+@pytest.mark.parametrize("n,bs,extra", [(1, 16, 0), (1000, 64, 16), (4099, 128, 48)])
+def test_k_quant_random_rows_packed_pool(n, bs, extra):
+    rng = np.random.default_rng(n)
+    kb = synth.draw_k(rng, n)
+    kb[: min(n, 3)] = synth._bf16_bits(rng.standard_normal((min(n, 3), 128)).astype(np.float32) * 1e-6)  # tiny
+    if n > 5:
+        kb[4] = 0
+    stride = bs * ROW + extra
+    nb = (n + bs - 1) // bs + 2
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    slots[::7] = -1  # padding tokens
+    ref = paged_pool_oracle(kb, slots, nb, bs, stride)
+    # the kernel only writes the rows of valid slots: start both from the same sentinel
+    ref_s = np.full_like(ref, 0xA5)
+    written = np.zeros(ref.size, bool)
+    for s in slots[slots >= 0]:
+        a = (s // bs) * stride + (s % bs) * ROW
+        written[a:a + ROW] = True
+    ref_s[written] = ref[written]
+    pool = torch.full((nb * stride,), 0xA5, dtype=torch.uint8, device="cuda")
+    wide = np.zeros((n, 160), np.uint16)
+    wide[:, :128] = kb
+    dsi.k_quant_and_cache(dev(wide)[:, :128], dev(slots), pool, bs, stride, nb)
+    assert np.array_equal(host(pool), ref_s)
+
+
+# ----------------------------------------------------------------------------- dense prefill logits
+def _exact_int_inputs(rng, T, S):
+    table = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C, 7: 0x4E, 8: 0x50}
+    enc = np.vectorize(lambda v: table[abs(int(v))] | (0x80 if v < 0 else 0))
+    q = enc(rng.integers(-8, 9, size=(T, 64, 128))).astype(np.uint8)
+    rows = np.zeros((S, ROW), np.uint8)
+    rows[:, :128] = enc(rng.integers(-8, 9, size=(S, 128))).astype(np.uint8)
+    rows[:, 128:] = np.ones(S, np.float32).view(np.uint8).reshape(S, 4)
+    w = synth._bf16_bits((rng.choice([-1.0, 1.0], (T, 64)) * 2.0 ** rng.integers(-3, 4, (T, 64))).astype(np.float32))
+    return q, w, rows
+
+
+def test_prefill_exact_integer_bit_exact():
+    rng = np.random.default_rng(100)
+    T, S = 19, 333
+    q, w, rows = _exact_int_inputs(rng, T, S)
+    ks = np.zeros(T, np.int32)
+    ke = np.full(T, S, np.int32)
+    ref = oracle.mqa_logits_gathered(q, w, rows, ks, ke)
+    out = dsi.mqa_logits_prefill(dev(q), dev(w), dev(rows), dev(ks), dev(ke))
+    assert np.array_equal(host(out), ref)
+
+
+@pytest.mark.parametrize("T,S,seed", [(37, 1001, 1), (8, 3072, 2), (5, 64, 3), (16, 1027, 4)])
+def test_prefill_ragged_ranges_and_guards(T, S, seed):
+    rng = np.random.default_rng(seed)
+    c = synth.prefill_case(seed, T=T, S=S, first_pos=max(S - T, 0))
+    rows = gathered_rows_oracle(c["k"])
+    ks = rng.integers(0, S, T).astype(np.int32)
+    ke = (ks + rng.integers(-5, S, T)).astype(np.int32)
+    ks[0], ke[0] = 0, S + 50  # ke beyond S is clipped
+    ks[1], ke[1] = 10, 10 if T > 1 else ke[1]  # empty row
+    ref = oracle.mqa_logits_gathered(c["q"], c["w"], rows, ks, np.minimum(ke, S))
+    ld = S + 13
+    out = torch.full((T, ld), 7.25, dtype=torch.float32, device="cuda")
+    dsi.mqa_logits_prefill(dev(c["q"]), dev(c["w"]), dev(rows), dev(ks), dev(ke), out=out[:, :S])
+    got = host(out)
+    valid = np.isfinite(ref)
+    assert_close(got[:, :S][valid], ref[valid])
+    assert np.all(got[:, :S][~valid] == 7.25), "entries outside [ks, ke) must stay untouched"
+    assert np.all(got[:, S:] == 7.25)
+
+
+def test_prefill_uses_the_k_scale_per_row():
+    # same codes, per-row scales of 2^j: logits scale exactly with the row scale
+    rng = np.random.default_rng(5)
+    c = synth.prefill_case(6, T=4, S=96, first_pos=92)
+    rows = gathered_rows_oracle(c["k"])
+    ks, ke = np.zeros(4, np.int32), np.full(4, 96, np.int32)
+    base = host(dsi.mqa_logits_prefill(dev(c["q"]), dev(c["w"]), dev(rows), dev(ks), dev(ke)))
+    rows2 = rows.copy()
+    sc = rows2[:, 128:].copy().view(np.float32)[:, 0] * (2.0 ** (np.arange(96) % 5)).astype(np.float32)
+    rows2[:, 128:] = sc.astype(np.float32).view(np.uint8).reshape(96, 4)
+    got = host(dsi.mqa_logits_prefill(dev(c["q"]), dev(c["w"]), dev(rows2), dev(ks), dev(ke)))
+    assert np.array_equal(got, base * (2.0 ** (np.arange(96) % 5)).astype(np.float32)[None, :])
+
+
+# ----------------------------------------------------------------------------- paged decode logits
+@pytest.mark.parametrize("next_n,bs,extra", [(1, 64, 0), (2, 64, 16), (3, 16, 0), (4, 32, 32)])
+def test_decode_parity_ragged(next_n, bs, extra):
+    lens = [1, 15, 16, 17, 300, 1000 + next_n, 2049]
+    c = synth.decode_case(10 + next_n, B=len(lens), next_n=next_n, lmin=0, lmax=0, block_size=bs, lens=lens)
+    stride = bs * ROW + extra
+    nb = c["num_blocks"]
+    pool_np = paged_pool_oracle(c["k"], c["slot_mapping"], nb, bs, stride)
+    width = max(lens) + 3
+    ref = oracle.mqa_logits_paged(c["q"], c["w"], next_n, c["context_lens"], pool_np, bs, stride,
+                                  c["block_table"], width)
+    ld = width + 5
+    out = torch.full((len(lens) * next_n, ld), -3.5, dtype=torch.float32, device="cuda")
+    dsi.paged_mqa_logits_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(pool_np), bs,
+                                dev(c["block_table"]), width, next_n=next_n, out=out[:, :width],
+                                block_stride_bytes=stride, num_blocks=nb)
+    got = host(out)
+    valid = np.isfinite(ref)
+    assert_close(got[:, :width][valid], ref[valid])
+    assert np.all(got[:, :width][~valid] == -3.5) and np.all(got[:, width:] == -3.5)
+
+
+def test_decode_bad_page_ids_score_minus_inf():
+    c = synth.decode_case(20, B=2, next_n=1, lmin=0, lmax=0, block_size=16, lens=[64, 64])
+    bs, stride, nb = 16, 16 * ROW, c["num_blocks"]
+    pool_np = paged_pool_oracle(c["k"], c["slot_mapping"], nb, bs, stride)
+    bt = c["block_table"].copy()
+    bt[0, 1] = nb + 100  # out of range page
+    bt[1, 2] = -7
+    out = dsi.paged_mqa_logits_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(pool_np), bs, dev(bt),
+                                      64, block_stride_bytes=stride, num_blocks=nb)
+    got = host(out)
+    assert np.all(np.isneginf(got[0, 16:32])) and np.all(np.isneginf(got[1, 32:48]))
+    ref = oracle.mqa_logits_paged(c["q"], c["w"], 1, c["context_lens"], pool_np, bs, stride, c["block_table"], 64)
+    keep = np.ones((2, 64), bool)
+    keep[0, 16:32] = False
+    keep[1, 32:48] = False
+    assert_close(got[keep], ref[keep])
+
+
+# ----------------------------------------------------------------------------- top-k
+def _rows_with_ties(rng, rows, width):
+    x = (rng.standard_normal((rows, width)) * 50).astype(np.float32)
+    x[:, ::3] = np.round(x[:, ::3])
+    x[0, :] = 1.5  # all equal
+    return x
+
+
+@pytest.mark.parametrize("width,k", [(3000, 2048), (2048, 2048), (2049, 2048), (700, 2048), (8192, 2048),
+                                     (100, 7), (40000, 2048)])
+def test_topk_f32_same_input_exact_values(width, k):
+    rng = np.random.default_rng(width + k)
+    rows = 6
+    x = _rows_with_ties(rng, rows, width)
+    x[1, 5] = np.nan
+    x[1, 6] = np.inf
+    x[2, 7] = -np.inf
+    x[3, :] = 0.0
+    x[3, ::2] = -0.0
+    starts = rng.integers(0, max(width // 4, 1), rows).astype(np.int32)
+    ends = np.minimum(starts + rng.integers(0, width, rows), width).astype(np.int32)
+    ends[0] = width
+    starts[0] = 0
+    ref = oracle.topk_select(x, ends, k, starts=starts)
+    got = host(dsi.topk_select(dev(x), dev(ends), k=k, row_starts=dev(starts)))
+    for r in range(rows):
+        check_selection(got[r], ref[r], x[r], tol_fn=lambda v: 0.0 * v, start=starts[r], end=ends[r])
+        g = got[r][got[r] >= 0] + starts[r]
+        o = ref[r][ref[r] >= 0] + starts[r]
+        assert np.array_equal(np.sort(x[r, g]), np.sort(x[r, o]))
+
+
+def test_topk_bf16_exact_values():
+    rng = np.random.default_rng(7)
+    vals = (rng.standard_normal((9, 8192)) * 8).astype(np.float32)
+    bits = synth._bf16_bits(vals)
+    bits[1, :4000] = 0xFF80
+    bits[2, :] = 0xFF80
+    ends = np.array([8192, 8192, 8192, 100, 2048, 2047, 8192, 5000, 0], np.int32)
+    ref = oracle.topk_select(bits, ends, 2048, bf16=True)
+    got = host(dsi.topk_select(dev(bits), dev(ends), k=2048))
+    f = bf16_value(bits)
+    for r in range(9):
+        check_selection(got[r], ref[r], f[r], tol_fn=lambda v: 0.0 * v, end=ends[r])
+        assert np.array_equal(np.sort(f[r, got[r][got[r] >= 0]]), np.sort(f[r, ref[r][ref[r] >= 0]]))
+
+
+def test_topk_strided_rows_and_out():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((4, 5000)) * 3).astype(np.float32)
+    big = torch.zeros((4, 6000), dtype=torch.float32, device="cuda")
+    big[:, 100:5100] = dev(x)
+    out = torch.full((4, 2100), -9, dtype=torch.int32, device="cuda")
+    ends = np.full(4, 5000, np.int32)
+    dsi.topk_select(big[:, 100:5100], dev(ends), k=2048, out=out[:, 10:2058], max_width=5000)
+    got = host(out)
+    assert np.all(got[:, :10] == -9) and np.all(got[:, 2058:] == -9)
+    ref = oracle.topk_select(x, ends, 2048)
+    for r in range(4):
+        check_selection(got[r, 10:2058], ref[r], x[r], tol_fn=lambda v: 0.0 * v)
+
+
+# ----------------------------------------------------------------------------- expansion / remap / slot
+@pytest.mark.parametrize("sbk,ratio,K", [(16, 1, 4), (8, 2, 16), (128, 1, 64), (64, 2, 256), (32, 1, 512)])
+def test_expand_bit_exact(sbk, ratio, K):
+    rng = np.random.default_rng(sbk * 7 + K)
+    rows, cbs = 300, sbk * ratio
+    ks = (rng.integers(0, 30, rows) * sbk).astype(np.int32)
+    ks[::5] += rng.integers(0, sbk, ks[::5].size).astype(np.int32)  # unaligned starts too
+    ke = (ks + rng.integers(-10, 60 * cbs, rows)).astype(np.int32)
+    maxc = (np.maximum(ke - ks, 0) + cbs - 1) // cbs
+    cand = np.stack([rng.integers(-2, int(m) + 3, K) for m in maxc]).astype(np.int32)
+    cand[::3, : K // 2] = cand[::3, K // 2:K // 2 * 2]  # duplicates
+    si_ref, end_ref = oracle.expand_candidates(cand, ks, ke, cbs, sbk)
+    wide = np.full((rows, K + 9), 555, np.int32)
+    wide[:, 3:3 + K] = cand
+    ks2 = np.zeros((rows, 2), np.int32)
+    ks2[:, 1] = ks
+    si, end = dsi.expand_candidates(dev(wide)[:, 3:3 + K], dev(ks2)[:, 1], dev(ke), cbs, sbk)
+    assert np.array_equal(host(si), si_ref) and np.array_equal(host(end), end_ref)
+
+
+def test_expand_golden_cases():
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "expand_cases.json")))["cases"]
+    for c in cases:
+        si, end = dsi.expand_candidates(dev(np.array([c["cand"]], np.int32)), dev(np.array([c["ks"]], np.int32)),
+                                        dev(np.array([c["ke"]], np.int32)), c["cbs"], c["sbk"])
+        assert host(si)[0].tolist() == c["si"] and int(host(end)[0]) == c["end"], c["name"]
+
+
+def test_remap_bit_exact_and_alias():
+    rng = np.random.default_rng(9)
+    rows, nsb, sbk, k = 50, 64, 128, 2048
+    si = np.sort(rng.integers(0, 1000, (rows, nsb)), axis=1).astype(np.int32)
+    ks = (rng.integers(0, 8, rows) * sbk).astype(np.int32)
+    col = rng.integers(-1, nsb * sbk, (rows, k)).astype(np.int32)
+    ref = oracle.topk_remap(col, si, ks, sbk)
+    got = host(dsi.topk_remap(dev(col), dev(si), dev(ks), sbk))
+    assert np.array_equal(got, ref)
+    t = dev(col)
+    dsi.topk_remap(t, dev(si), dev(ks), sbk, out=t)  # in place
+    assert np.array_equal(host(t), ref)
+
+
+def test_slot_bit_exact_packed_and_alias():
+    import json
+    import os
+    rng = np.random.default_rng(10)
+    rows, k, bs, nreq = 40, 2048, 64, 7
+    bt = np.stack([rng.permutation(2000)[:1100] for _ in range(nreq)]).astype(np.int32)
+    r2r = rng.integers(0, nreq, rows).astype(np.int32)
+    idx = rng.integers(-1, 1100 * bs, (rows, k)).astype(np.int32)
+    for span in (64, 68):
+        ref = oracle.req_index_to_global_slot(idx, bt, bs, span, row_to_req=r2r)
+        got = host(dsi.req_index_to_global_slot(dev(idx), dev(bt), bs, span, row_to_req=dev(r2r)))
+        assert np.array_equal(got, ref)
+    t = dev(idx)
+    dsi.req_index_to_global_slot(t, dev(bt), bs, 64, row_to_req=dev(r2r), out=t)
+    assert np.array_equal(host(t), oracle.req_index_to_global_slot(idx, bt, bs, 64, row_to_req=r2r))
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "slot_cases.json")))["cases"]
+    for c in cases:
+        got = host(dsi.req_index_to_global_slot(dev(np.array([c["p"]], np.int32)),
+                                                dev(np.array([c["table"]], np.int32)), c["block_size"],
+                                                c["block_span"]))
+        assert got[0].tolist() == c["slot"], c["name"]
+
+
+# ----------------------------------------------------------------------------- sparse MQA logits
+@pytest.mark.parametrize("sbk,ratio", [(128, 1), (16, 1), (8, 2), (32, 2)])
+def test_sparse_gathered_parity(sbk, ratio):
+    rng = np.random.default_rng(sbk + ratio)
+    cbs, S, T, K = sbk * ratio, 3001, 12, 16
+    c = synth.prefill_case(30 + sbk, T=T, S=S, first_pos=S - T)
+    rows = gathered_rows_oracle(c["k"])
+    ks = np.zeros(T, np.int32)
+    ks[3] = sbk * 2
+    ke = c["ke"].copy()
+    ke[5] = 40
+    maxb = (np.maximum(ke - ks, 0) + cbs - 1) // cbs
+    cand = synth.draw_candidates(rng, maxb, num=K, distinct=min(12, int(maxb.min())), dup=2)
+    si, end = oracle.expand_candidates(cand, ks, ke, cbs, sbk)
+    ref_bits = oracle.sparse_mqa_logits(c["q"], c["w"], ks, ke, si, end, sbk, rows)
+    ref_f32 = oracle.sparse_mqa_logits(c["q"], c["w"], ks, ke, si, end, sbk, rows, out_f32=True)
+    got = host(dsi.sparse_mqa_logits(dev(c["q"]), dev(c["w"]), dev(ks), dev(ke), dev(si), dev(end), sbk, dev(rows)))
+    valid = np.isfinite(ref_f32)
+    assert np.array_equal(got[~valid], ref_bits[~valid])  # same -inf pattern
+    assert_close(bf16_value(got[valid]), ref_f32[valid], tol_fn=tol_bf16, what="sparse logits")
+
+
+@pytest.mark.parametrize("sbk,bs", [(128, 128), (16, 64), (8, 16)])
+def test_sparse_paged_parity(sbk, bs):
+    rng = np.random.default_rng(sbk * 3 + bs)
+    lens = [700, 1, 129, 3000, 2048]
+    c = synth.decode_case(40 + sbk, B=len(lens), next_n=1, lmin=0, lmax=0, block_size=bs, lens=lens)
+    stride, nb = bs * ROW, c["num_blocks"]
+    pool_np = paged_pool_oracle(c["k"], c["slot_mapping"], nb, bs, stride)
+    rows = len(lens)
+    ks = np.zeros(rows, np.int32)
+    ke = np.array(lens, np.int32)
+    maxb = (np.maximum(ke - ks, 0) + sbk - 1) // sbk
+    cand = synth.draw_candidates(rng, maxb, num=8, distinct=6, dup=1)
+    si, end = oracle.expand_candidates(cand, ks, ke, sbk, sbk)
+    r2r = np.arange(rows, dtype=np.int32)
+    ref_f32 = oracle.sparse_mqa_logits(c["q"], c["w"], ks, ke, si, end, sbk, pool_np, block_table=c["block_table"],
+                                       row_to_req=r2r, block_size=bs, block_stride=stride, out_f32=True)
+    got = host(dsi.sparse_mqa_logits(dev(c["q"]), dev(c["w"]), dev(ks), dev(ke), dev(si), dev(end), sbk,
+                                     dev(pool_np), block_table=dev(c["block_table"]), row_to_req=dev(r2r),
+                                     block_size=bs, block_stride_bytes=stride, num_k=nb))
+    valid = np.isfinite(ref_f32)
+    assert np.all(got[~valid] == 0xFF80)
+    assert_close(bf16_value(got[valid]), ref_f32[valid], tol_fn=tol_bf16, what="sparse paged logits")
