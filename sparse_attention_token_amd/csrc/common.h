@@ -9,10 +9,9 @@
 // 16x16x32 fp8) were measured to drop product bits about 13 binades below the largest
 // product of their internal sum, with a one-sided (truncating) error that reaches
 // ~0.1 on indexer logits — beyond the path's 1e-3 (1 + |ref|) bar — while the f16
-// MFMA sums the same products exactly.  Every E4M3FN code shifted left by 7 bits (sign
-// moved to bit 15) is an f16 equal to the code's value times 2^-8, subnormals included
-// (they become f16 subnormals, which the f16 MFMA keeps); the 2^16 of the two factors
-// is folded into the key scale.
+// MFMA sums the same products exactly.  Every E4M3FN value is a normal f16 (2^-9 to
+// 448), so the decode (v_cvt_scalef32_pk_f16_fp8 with scale 1, two codes per
+// instruction) is exact.
 //
 // Operands of one MFMA (k = 32 dims of a 128-dim slice):
 //   A = 16 heads x 32 dims of q   (lane l: head l%16, 8 dims of lane group g = l/16)
@@ -44,7 +43,6 @@ constexpr int kRow = 132;              // bytes per cache row
 constexpr int kLdsKeyStride = 144;     // LDS bytes per FP8 key row: 128 codes + pad; 36 dwords = 4 mod 32
                                        // banks, so 16-byte reads by 8 consecutive keys are conflict-free
 constexpr int kLdsKeyStrideF16 = 272;  // LDS bytes per f16 key row: 256 + pad, 68 dwords = 4 mod 32 banks
-constexpr float kF16Unscale = 65536.0f;  // 2^16: undoes the 2^-8 of both decoded operands
 
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -75,14 +73,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (uint32_t)m;
 }
 
-// Four E4M3FN codes (one dword, little-endian) -> four f16 (two dwords), each the
-// code's value times 2^-8.  Exact for every finite code.
+// Four E4M3FN codes (one dword, little-endian) -> four f16 (two dwords), exact.
 __device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
-  uint32_t lo = (x & 0xFFu) | ((x & 0xFF00u) << 8);            // bytes b1, b0 into the two halves
-  uint32_t hi = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u);  // bytes b3, b2
-  lo = ((lo & 0x007F007Fu) << 7) | ((lo & 0x00800080u) << 8);
-  hi = ((hi & 0x007F007Fu) << 7) | ((hi & 0x00800080u) << 8);
-  return uint2{lo, hi};
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);  // codes 0, 1
+  const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);   // codes 2, 3
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // Eight codes (two dwords) -> one f16x8 operand.
@@ -173,23 +169,33 @@ __device__ __forceinline__ void load_kfrag_f16(KFrag& f, const uint8_t* keys, in
   for (int s = 0; s < 4; s++) f.b[s] = p[s];
 }
 
-// Head-weighted partial of one (row, 16-key group): the 64-head contraction on the
-// matrix cores, then this lane's 16 heads weighted and summed.  The result carries
-// the 2^-16 of the decoded operands.
-__device__ __forceinline__ float score_partial(const QFrag& q, const WFrag& w, const KFrag& kb) {
-  f32x4 c[4];
+// Head-weighted partials of four (row, 16-key group) outputs at once: out j uses
+// q[rows[j]] and kb[kgs[j]].  The 64 MFMAs run as 16 independent accumulator chains
+// (4 outputs x 4 head tiles) taken slice by slice, so consecutive MFMAs never wait on
+// each other; then each lane weights and sums its 16 heads per output.
+template <int NQ, int NK>
+__device__ __forceinline__ void score4(const QFrag (&q)[NQ], const WFrag (&w)[NQ], const KFrag (&kb)[NK],
+                                       const int (&rows)[4], const int (&kgs)[4], float (&part)[4]) {
+  f32x4 c[4][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; hb++) {
-    c[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; j++)
 #pragma unroll
-    for (int s = 0; s < 4; s++) c[hb] = mfma_f16(q.a[hb][s], kb.b[s], c[hb]);
+    for (int hb = 0; hb < 4; hb++) c[j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; s++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int hb = 0; hb < 4; hb++) c[j][hb] = mfma_f16(q[rows[j]].a[hb][s], kb[kgs[j]].b[s], c[j][hb]);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    float acc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; hb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc = fmaf(w[rows[j]].w[hb][i], c[j][hb][i], acc);
+    part[j] = acc;
   }
-  float acc = 0.f;
-#pragma unroll
-  for (int hb = 0; hb < 4; hb++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) acc = fmaf(w.w[hb][i], c[hb][i], acc);
-  return acc;
 }
 
 // Copy one 16-byte chunk of a contiguous run of 132-byte cache rows into the FP8
@@ -208,15 +214,6 @@ __device__ __forceinline__ void scatter_chunk(uint8_t* lds_codes, float* lds_sca
     else
       lds_scale[key0 + row] = __uint_as_float(w[j]);
   }
-}
-
-// The same for the decoded layout: each code dword becomes two f16 dwords.
-__device__ __forceinline__ void scatter_word_f16(uint8_t* lds_f16, float* lds_scale, int d, uint32_t x) {
-  int row = d / 33, word = d - row * 33;
-  if (word < 32)
-    *reinterpret_cast<uint2*>(lds_f16 + row * kLdsKeyStrideF16 + word * 8) = e4m3x4_to_f16x4(x);
-  else
-    lds_scale[row] = __uint_as_float(x);
 }
 
 }  // namespace dsi

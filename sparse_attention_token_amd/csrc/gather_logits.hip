@@ -108,15 +108,15 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(
     }
 #pragma unroll
     for (int batch = 0; batch < R; batch++) {
+      KFrag kb[KPB];
+#pragma unroll
+      for (int kgi = 0; kgi < KPB; kgi++)
+        load_kfrag_fp8(kb[kgi], s_codes + (wave + 4 * (batch * KPB + kgi)) * 16 * kLdsKeyStride, lane);
+      // output j: row j / KPB of the pair, key group j % KPB of the batch
+      constexpr int orow[4] = {0, R == 1 ? 0 : 0, R == 1 ? 0 : 1, R == 1 ? 0 : 1};
+      constexpr int okg[4] = {0, R == 1 ? 1 : 1, R == 1 ? 2 : 0, R == 1 ? 3 : 1};
       float part[4];
-#pragma unroll
-      for (int kgi = 0; kgi < KPB; kgi++) {
-        const int grp = wave + 4 * (batch * KPB + kgi);
-        KFrag kb;
-        load_kfrag_fp8(kb, s_codes + grp * 16 * kLdsKeyStride, lane);
-#pragma unroll
-        for (int r = 0; r < R; r++) part[r * KPB + kgi] = score_partial(qf[r], wf[r], kb);
-      }
+      score4(qf, wf, kb, orow, okg, part);
       const float v = transpose_reduce4(part, lane);
       const int r = r0 + g / KPB, kgi = g % KPB;
       const int grp = wave + 4 * (batch * KPB + kgi);
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(
         const int ke = min(L - next_n + r + 1, max_ctx);
         if (tok < ke)
           logits[((int64_t)b * next_n + r) * ld + tok] =
-              s_base[grp] >= 0 ? v * (s_scale[kslot] * kF16Unscale) : -INFINITY;
+              s_base[grp] >= 0 ? v * s_scale[kslot] : -INFINITY;
       }
     }
   }
@@ -186,14 +186,15 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
-  float part[4];
+  KFrag kb[4];
 #pragma unroll
-  for (int kgi = 0; kgi < 4; kgi++) {
-    const int grp = wave + 4 * kgi;
-    KFrag kb;
-    load_kfrag_fp8(kb, s_codes + grp * 16 * kLdsKeyStride, lane);
-    part[kgi] = score_partial(qf, wf, kb);
-  }
+  for (int kgi = 0; kgi < 4; kgi++) load_kfrag_fp8(kb[kgi], s_codes + (wave + 4 * kgi) * 16 * kLdsKeyStride, lane);
+  QFrag qa[1] = {qf};
+  WFrag wa[1] = {wf};
+  constexpr int orow[4] = {0, 0, 0, 0};
+  constexpr int okg[4] = {0, 1, 2, 3};
+  float part[4];
+  score4(qa, wa, kb, orow, okg, part);
   const float v = transpose_reduce4(part, lane);
   const int grp = wave + 4 * g;
   const int kslot = grp * 16 + n;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
     const int seg = kslot / G;
     const int tok = s_tok[seg] + (kslot - seg * G);
     const bool valid = c < e && s_base[seg] >= 0 && tok >= ks && tok < ke && (paged || tok < num_k);
-    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * (s_scale[kslot] * kF16Unscale)) : (uint16_t)0xFF80u;
+    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * s_scale[kslot]) : (uint16_t)0xFF80u;
   }
 }
 

@@ -88,6 +88,20 @@ def test_prefill_exact_integer_bit_exact():
     assert np.array_equal(host(out), ref)
 
 
+def test_prefill_subnormal_codes_bit_exact():
+    # q codes drawn from the E4M3 subnormals (m * 2^-9) and zero, k small integers, unit scales and
+    # power-of-two weights: every partial sum is exact, so the device decode of subnormals must be exact
+    rng = np.random.default_rng(101)
+    T, S = 9, 200
+    q, w, rows = _exact_int_inputs(rng, T, S)
+    sub = np.array([0x00, 0x01, 0x02, 0x03, 0x04, 0x05, 0x06, 0x07, 0x81, 0x82, 0x83, 0x84, 0x85, 0x86, 0x87], np.uint8)
+    q = sub[rng.integers(0, sub.size, size=q.shape)]
+    ks, ke = np.zeros(T, np.int32), np.full(T, S, np.int32)
+    ref = oracle.mqa_logits_gathered(q, w, rows, ks, ke)
+    out = dsi.mqa_logits_prefill(dev(q), dev(w), dev(rows), dev(ks), dev(ke))
+    assert np.array_equal(host(out), ref)
+
+
 @pytest.mark.parametrize("T,S,seed", [(37, 1001, 1), (8, 3072, 2), (5, 64, 3), (16, 1027, 4)])
 def test_prefill_ragged_ranges_and_guards(T, S, seed):
     rng = np.random.default_rng(seed)
