@@ -4,73 +4,127 @@
 // 索引器接入稀疏 MQA logits", motivation and implementation: consumer layers score
 // only the candidate blocks, into bf16 logits).
 //
-// Both are a stream of 132-byte K rows scored against one to four query rows:
-// HBM/L2-bound.  A workgroup gathers 256 keys (segments of 16, or 8, consecutive
-// tokens that are contiguous in memory) into LDS with 16-byte loads — all issued
-// before any is used — then each wavefront scores 4 groups of 16 keys on the
-// matrix cores, decoding the FP8 codes to f16 as it reads them (common.h), and
-// writes its outputs.  Query rows are held two at a time (next_n 3 and 4 take a
-// second pass over the staged keys).  Block-table entries are read
-// once per segment into LDS.  Out-of-range table entries or page ids never
-// produce an access outside the pool: those keys score -inf.
+// Both stream 132-byte K rows past one to four query rows: HBM/L2-bound.  A
+// workgroup gathers 256 keys — segments of 16 (or 8) consecutive tokens, each
+// contiguous in memory — straight into LDS with global->LDS DMA loads
+// (global_load_lds_dwordx4: no VGPR staging, no LDS write instructions; all 33 KB
+// in flight at once).  The segments sit back to back, so key slot k is always the
+// 132 bytes at LDS offset 132*k.  Each wavefront then scores 4 groups of 16 keys on
+// the matrix cores one group at a time (raw codes read with 4-byte LDS loads and
+// decoded to f16 per use, common.h), keeping its register footprint small so that
+// several workgroups per CU keep loads in flight.  Block-table entries are read
+// once per segment.  Out-of-range table entries or page ids never produce an access
+// outside the pool: those keys score -inf.
 #include "common.h"
 
 namespace dsi {
 namespace {
 
-constexpr int kKeys = 256;                   // keys per workgroup
-constexpr int kChunks16 = kKeys * kRow / 16;  // 2112 sixteen-byte chunks
-constexpr int kLoads = (kChunks16 + 255) / 256;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glob_ptr_t;
 
-// Load up to 16 bytes at p, stopping at `limit` bytes from `base` (dword granular).
-__device__ __forceinline__ uint4 load_bounded(const uint8_t* base, int64_t off, int64_t limit) {
-  if (off + 16 <= limit) return *reinterpret_cast<const uint4*>(base + off);
-  uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-    if (off + 4 * j + 4 <= limit) w[j] = *reinterpret_cast<const uint32_t*>(base + off + 4 * j);
-  return uint4{w[0], w[1], w[2], w[3]};
-}
+constexpr int kKeys = 256;                         // keys per workgroup
+constexpr int kGatherBytes = kKeys * kRow;         // 33792 = 33 x 1024
+constexpr int kGatherSlabs = kGatherBytes / 1024;  // one DMA instruction of a wavefront fills 1 KB
 
-// Gather segments of `seg_tokens` rows (byte offsets in s_base, -1 = absent) into LDS.
-__device__ __forceinline__ void gather_keys(uint8_t* s_codes, float* s_scale, const int64_t* s_base,
-                                            const uint8_t* src, int64_t limit, int seg_tokens, int tid) {
-  const int cps = seg_tokens * kRow / 16;  // chunks per segment (132 or 66)
-  uint4 v[kLoads];
-  bool ok[kLoads];
+// Issue the DMA loads of a 256-key gather into s_keys.  s_base[seg] is the byte
+// offset in src of segment seg (seg_bytes long) or -1 when absent; limit is the byte
+// size of src.  A 16-byte piece that would cross `limit` is copied dword by dword.
+__device__ __forceinline__ void gather_keys_dma(uint8_t* s_keys, const int64_t* s_base, const uint8_t* src,
+                                                int64_t limit, int seg_bytes, int wave, int lane) {
+  for (int i = wave; i < kGatherSlabs; i += 4) {
+    const int o = i * 1024 + lane * 16;  // this lane's LDS bytes
+    const int seg = o / seg_bytes, within = o - seg * seg_bytes;
+    const int64_t base = s_base[seg];
+    const int64_t goff = base + within;
+    if (base >= 0 && goff + 16 <= limit) {
+      __builtin_amdgcn_global_load_lds((glob_ptr_t)(src + goff), (lds_ptr_t)(s_keys + i * 1024), 16, 0, 0);
+    } else if (base >= 0 && goff < limit) {
 #pragma unroll
-  for (int j = 0; j < kLoads; j++) {
-    const int c = tid + j * 256;
-    ok[j] = false;
-    if (c < kChunks16) {
-      const int seg = c / cps, cc = c - seg * cps;
-      const int64_t base = s_base[seg];
-      if (base >= 0) {
-        v[j] = load_bounded(src, base + cc * 16, limit);
-        ok[j] = true;
-      }
+      for (int j = 0; j < 4; j++)
+        if (goff + 4 * j + 4 <= limit)
+          *reinterpret_cast<uint32_t*>(s_keys + o + 4 * j) = *reinterpret_cast<const uint32_t*>(src + goff + 4 * j);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // every load of this wavefront has landed in LDS
+}
+
+// B fragments of 16 keys from raw rows at LDS offset 132*k: lane (key n, group g)
+// reads its 32 codes as 8 dwords and decodes them.
+__device__ __forceinline__ void load_kfrag_raw(KFrag& f, const uint8_t* keys, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(keys + n * kRow + g * 32);
+  uint32_t x[8];
 #pragma unroll
-  for (int j = 0; j < kLoads; j++) {
-    const int c = tid + j * 256;
-    if (ok[j]) {
-      const int seg = c / cps, cc = c - seg * cps;
-      scatter_chunk(s_codes, s_scale, seg * seg_tokens, cc, v[j]);
-    }
+  for (int j = 0; j < 8; j++) x[j] = p[j];
+  f.b[0] = e4m3x8_to_f16x8(x[0], x[1]);
+  f.b[1] = e4m3x8_to_f16x8(x[2], x[3]);
+  f.b[2] = e4m3x8_to_f16x8(x[4], x[5]);
+  f.b[3] = e4m3x8_to_f16x8(x[6], x[7]);
+}
+
+// One (row, 16-key group) output: 16 MFMAs as 4 interleaved head-tile chains, then
+// this lane's 16 heads weighted and summed.
+__device__ __forceinline__ float score1(const QFrag& q, const WFrag& w, const KFrag& kb) {
+  f32x4 c[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) c[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; s++)
+#pragma unroll
+    for (int hb = 0; hb < 4; hb++) c[hb] = mfma_f16(q.a[hb][s], kb.b[s], c[hb]);
+  float acc = 0.f;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc = fmaf(w.w[hb][i], c[hb][i], acc);
+  return acc;
+}
+
+__device__ __forceinline__ float key_scale(const uint8_t* s_keys, int kslot) {
+  return *reinterpret_cast<const float*>(s_keys + kslot * kRow + kDim);
+}
+
+// Stage one q row (64 x 128 codes) into 8 KB of LDS by DMA, permuted into the order
+// the A fragments are read: 16-byte unit (hb*2 + p)*64 + lane holds codes
+// [32g + 16p, +16) of head hb*16 + n (lane = 16g + n), so each fragment read of a
+// wavefront is one contiguous, conflict-free 1 KB.  Issued by one wavefront.
+__device__ __forceinline__ void stage_q_dma(uint8_t* s_q, const uint8_t* q_row, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int hb = i >> 1, p = i & 1;
+    __builtin_amdgcn_global_load_lds((glob_ptr_t)(q_row + (hb * 16 + n) * kDim + g * 32 + p * 16),
+                                     (lds_ptr_t)(s_q + i * 1024), 16, 0, 0);
+  }
+}
+
+// A fragments of one q row staged by stage_q_dma, decoded to f16.
+__device__ __forceinline__ void load_q_lds(QFrag& f, const uint8_t* s_q, int lane) {
+  const uint4* p = reinterpret_cast<const uint4*>(s_q) + lane;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) {
+    const uint4 x0 = p[(hb * 2 + 0) * 64], x1 = p[(hb * 2 + 1) * 64];
+    f.a[hb][0] = e4m3x8_to_f16x8(x0.x, x0.y);
+    f.a[hb][1] = e4m3x8_to_f16x8(x0.z, x0.w);
+    f.a[hb][2] = e4m3x8_to_f16x8(x1.x, x1.y);
+    f.a[hb][3] = e4m3x8_to_f16x8(x1.z, x1.w);
   }
 }
 
 // ------------------------------------------------------------------ paged decode
-// grid = (ceil(max_context_len / 256), B); R = 1 (next_n 1) or 2 (rows taken in pairs).
-template <int R>
+// grid = (ceil(max_context_len / 256), B).  Dynamic LDS: the 256 gathered keys, then
+// up to two of the request's q rows (8 KB each), all loaded by DMA and waited for
+// once.  Rows are then scored one after the other against the staged keys (rows 2
+// and 3 of a four-row request are staged after the first two are done).
 __global__ __launch_bounds__(256) void paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int next_n, const int* __restrict__ context_lens,
     const uint8_t* __restrict__ pool, int64_t num_blocks, int block_size, int64_t block_stride,
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int max_ctx, float* __restrict__ logits,
     int64_t ld) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kKeys * kLdsKeyStride];
-  __shared__ float s_scale[kKeys];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  uint8_t* s_keys = s_dyn;
+  uint8_t* s_q = s_dyn + kGatherBytes;
   __shared__ int64_t s_base[16];
 
   const int b = blockIdx.y, tok0 = blockIdx.x * kKeys;
@@ -91,44 +145,41 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(
     }
     s_base[tid] = base;
   }
+  // q rows of this request, two at a time: waves 0 and 1 stage rows 0 and 1
+  if (wave < min(next_n, 2)) stage_q_dma(s_q + wave * 8192, q + ((int64_t)b * next_n + wave) * kHeads * kDim, lane);
   __syncthreads();
-  gather_keys(s_codes, s_scale, s_base, pool, num_blocks * block_stride, 16, tid);
+  gather_keys_dma(s_keys, s_base, pool, num_blocks * block_stride, 16 * kRow, wave, lane);
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
-  constexpr int KPB = 4 / R;  // key groups per batch of four outputs
-  for (int r0 = 0; r0 < next_n; r0 += R) {
-    QFrag qf[R];
-    WFrag wf[R];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-      const int64_t row = (int64_t)b * next_n + min(r0 + r, next_n - 1);
-      load_q(qf[r], q + row * kHeads * kDim, lane);
-      load_w(wf[r], w + row * kHeads, lane);
+  const int grp = wave + 4 * g;  // after the transpose-reduce lane group g owns key group wave + 4g
+  const int kslot = grp * 16 + n;
+  const int tok = tok0 + kslot;
+  const float ks = key_scale(s_keys, kslot);
+  const bool present = s_base[grp] >= 0;
+  for (int row = 0; row < next_n; row++) {
+    if (row == 2) {  // rows 2 and 3 replace rows 0 and 1 in LDS
+      __syncthreads();
+      if (wave < next_n - 2)
+        stage_q_dma(s_q + wave * 8192, q + ((int64_t)b * next_n + 2 + wave) * kHeads * kDim, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
+    QFrag qf;
+    WFrag wf;
+    load_q_lds(qf, s_q + (row & 1) * 8192, lane);
+    load_w(wf, w + ((int64_t)b * next_n + row) * kHeads, lane);
+    float part[4];
 #pragma unroll
-    for (int batch = 0; batch < R; batch++) {
-      KFrag kb[KPB];
-#pragma unroll
-      for (int kgi = 0; kgi < KPB; kgi++)
-        load_kfrag_fp8(kb[kgi], s_codes + (wave + 4 * (batch * KPB + kgi)) * 16 * kLdsKeyStride, lane);
-      // output j: row j / KPB of the pair, key group j % KPB of the batch
-      constexpr int orow[4] = {0, R == 1 ? 0 : 0, R == 1 ? 0 : 1, R == 1 ? 0 : 1};
-      constexpr int okg[4] = {0, R == 1 ? 1 : 1, R == 1 ? 2 : 0, R == 1 ? 3 : 1};
-      float part[4];
-      score4(qf, wf, kb, orow, okg, part);
-      const float v = transpose_reduce4(part, lane);
-      const int r = r0 + g / KPB, kgi = g % KPB;
-      const int grp = wave + 4 * (batch * KPB + kgi);
-      const int kslot = grp * 16 + n;
-      const int tok = tok0 + kslot;
-      if (r < next_n) {
-        const int ke = min(L - next_n + r + 1, max_ctx);
-        if (tok < ke)
-          logits[((int64_t)b * next_n + r) * ld + tok] =
-              s_base[grp] >= 0 ? v * s_scale[kslot] : -INFINITY;
-      }
+    for (int kg = 0; kg < 4; kg++) {
+      KFrag kb;
+      load_kfrag_raw(kb, s_keys + (wave + 4 * kg) * 16 * kRow, lane);
+      part[kg] = score1(qf, wf, kb);
+      __builtin_amdgcn_sched_barrier(0);  // one key group in flight: a small register footprint
     }
+    const float v = transpose_reduce4(part, lane);
+    const int ke = min(L - next_n + row + 1, max_ctx);
+    if (tok < ke) logits[((int64_t)b * next_n + row) * ld + tok] = present ? v * ks : -INFINITY;
   }
 }
 
@@ -141,8 +192,8 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
     const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
     int64_t ld) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kKeys * kLdsKeyStride];
-  __shared__ float s_scale[kKeys];
+  __shared__ __attribute__((aligned(16))) uint8_t s_keys[kGatherBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[8192];
   __shared__ int64_t s_base[32];
   __shared__ int s_tok[32];
 
@@ -176,25 +227,24 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
     s_base[tid] = base;
     s_tok[tid] = tok;
   }
-
-  QFrag qf;
+  if (wave == 0) stage_q_dma(s_q, q + (int64_t)r * kHeads * kDim, lane);
+  __syncthreads();
+  gather_keys_dma(s_keys, s_base, k_src, limit, G * kRow, wave, lane);
   WFrag wf;
-  load_q(qf, q + (int64_t)r * kHeads * kDim, lane);
   load_w(wf, w + (int64_t)r * kHeads, lane);
   __syncthreads();
-  gather_keys(s_codes, s_scale, s_base, k_src, limit, G, tid);
-  __syncthreads();
+  QFrag qf;
+  load_q_lds(qf, s_q, lane);
 
   const int n = lane & 15, g = lane >> 4;
-  KFrag kb[4];
-#pragma unroll
-  for (int kgi = 0; kgi < 4; kgi++) load_kfrag_fp8(kb[kgi], s_codes + (wave + 4 * kgi) * 16 * kLdsKeyStride, lane);
-  QFrag qa[1] = {qf};
-  WFrag wa[1] = {wf};
-  constexpr int orow[4] = {0, 0, 0, 0};
-  constexpr int okg[4] = {0, 1, 2, 3};
   float part[4];
-  score4(qa, wa, kb, orow, okg, part);
+#pragma unroll
+  for (int kg = 0; kg < 4; kg++) {
+    KFrag kb;
+    load_kfrag_raw(kb, s_keys + (wave + 4 * kg) * 16 * kRow, lane);
+    part[kg] = score1(qf, wf, kb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const float v = transpose_reduce4(part, lane);
   const int grp = wave + 4 * g;
   const int kslot = grp * 16 + n;
@@ -203,7 +253,7 @@ __global__ __launch_bounds__(256) void sparse_logits_kernel(
     const int seg = kslot / G;
     const int tok = s_tok[seg] + (kslot - seg * G);
     const bool valid = c < e && s_base[seg] >= 0 && tok >= ks && tok < ke && (paged || tok < num_k);
-    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * s_scale[kslot]) : (uint16_t)0xFF80u;
+    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * key_scale(s_keys, kslot)) : (uint16_t)0xFF80u;
   }
 }
 
@@ -227,14 +277,9 @@ extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, 
       (block_stride_bytes & 15) || (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits) & 3))
     return DSI_EALIGN;
   const dim3 grid((unsigned)((max_context_len + kKeys - 1) / kKeys), (unsigned)B);
-  if (next_n == 1)
-    hipLaunchKernelGGL(paged_decode_kernel<1>, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool,
-                       num_blocks, block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
-                       logits, ld);
-  else
-    hipLaunchKernelGGL(paged_decode_kernel<2>, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool,
-                       num_blocks, block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
-                       logits, ld);
+  const size_t lds = (size_t)kGatherBytes + (size_t)(next_n < 2 ? next_n : 2) * 8192;
+  hipLaunchKernelGGL(paged_decode_kernel, grid, dim3(256), lds, stream, q, w, next_n, context_lens, pool, num_blocks,
+                     block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
@@ -242,9 +287,9 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
                                      const int32_t* row_ke, const int32_t* sparse_indices, int64_t si_ld,
                                      int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
                                      const uint8_t* k_src, int64_t num_k, const int32_t* block_table, int64_t bt_ld,
-                                     int32_t bt_width, int32_t num_reqs, const int32_t* row_to_req, int32_t block_size,
-                                     int64_t block_stride_bytes, uint16_t* logits_bf16, int64_t ld,
-                                     hipStream_t stream) {
+                                     int32_t bt_width, int32_t num_reqs, const int32_t* row_to_req,
+                                     int32_t block_size, int64_t block_stride_bytes, uint16_t* logits_bf16,
+                                     int64_t ld, hipStream_t stream) {
   using namespace dsi;
   const int sbk = sparse_block_kv;
   if (sbk < 8 || sbk > 128 || (sbk & (sbk - 1))) return DSI_EUNSUPPORTED;
@@ -266,7 +311,7 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
   if (rows > 65535) return DSI_EUNSUPPORTED;
   const dim3 grid((unsigned)((width + kKeys - 1) / kKeys), (unsigned)rows);
   hipLaunchKernelGGL(sparse_logits_kernel, grid, dim3(256), 0, stream, q, w, row_ks, row_ke, sparse_indices, si_ld,
-                     (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req, block_size,
-                     block_stride_bytes, logits_bf16, ld);
+                     (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
+                     block_size, block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
