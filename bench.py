@@ -6,12 +6,19 @@ insert the chunk's 2048 new k rows, dense indexer logits over the gathered K (ca
 `value` = scored query-key pairs per second (masked pairs not counted).  Inputs are resident in HBM before
 the timed region; every step launches the same three kernels on the current stream.
 
-Also reported (same JSON line): the roofline of the dominant kernel (prefill logits, FP8 MFMA), the oracle's
-single-thread CPU rate on a bounded row sample, and the decode and hierarchical workloads (paged decode
-64 x U{4096..65536}; long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows
-+ 1024 prefill rows) with their HBM roofline fractions.  Diagnostics go to stderr.
+Also reported (same JSON line): the roofline of the dominant kernel (prefill logits: FP8 codes decoded
+exactly to f16 and contracted on the f16 matrix cores, so its peak is the dense f16 MFMA peak), ceilings
+measured on this device (register-only MFMA loops, a 4 GiB streaming read), the oracle's single-thread CPU
+rate on a bounded row sample, and the decode and hierarchical workloads (paged decode 64 x U{4096..65536};
+long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows + 1024 prefill rows)
+with their HBM roofline fractions.  Diagnostics go to stderr.
+
+`roofline.traffic` (HBM bytes per launch of the prefill logits kernel) comes from the committed counter
+summary in profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads for a plain copy
+of known size); it is null when the kernel's sources no longer hash to the ones the counters were taken on.
 """
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -25,11 +32,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import sparse_attention_token_amd as dsi  # noqa: E402
+from sparse_attention_token_amd import ceiling  # noqa: E402
 import synth  # noqa: E402
 
 ROW, K = 132, 2048
-FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
-HBM_PEAK_GBS = 8000.0
+F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA (published)
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E (published)
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_logits_T2048_S8192_traffic.md")
+PREFILL_SOURCES = [os.path.join(ROOT, "sparse_attention_token_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
 FLOP_PER_PAIR = 2 * 64 * 128
 
 
@@ -61,6 +72,81 @@ class EventTimer:
     def mean_ms(self):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+# --------------------------------------------------------------------------- measured ceilings
+def timed_ms(fn, reps=5):
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    return best
+
+
+def measure_ceilings():
+    """Register-only MFMA loops (f16 16x16x32, FP8 16x16x128), a streaming read of 4 GiB (16x the 256 MB
+    Infinity Cache) and a 1 GiB copy.  The copy is also the calibration dispatch of the byte counters."""
+    out = {}
+    wg = 256 * 8
+    sink = torch.empty(wg * ceiling.THREADS, dtype=torch.float32, device="cuda")
+    for kind, name, iters in ((0, "mfma_f16_tflops", 1000), (1, "mfma_fp8_tflops", 500)):
+        flop = [0]
+
+        def run():
+            flop[0] = ceiling.mfma_loop(kind, wg, iters, sink)
+        run()
+        out[name] = round(flop[0] / (timed_ms(run) * 1e-3) / 1e12, 1)
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    isink = torch.empty(4096 * ceiling.THREADS, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for wg in (1024, 2048, 4096):
+        nb = [0]
+
+        def run():
+            nb[0] = ceiling.stream_read(big, wg, isink)
+        run()
+        best = max(best, nb[0] / (timed_ms(run) * 1e-3) / 1e9)
+    out["hbm_read_gbs"] = round(best, 1)
+    src, dst = big[: 1 << 30], big[2 << 30: 3 << 30]
+    nb = [0]
+
+    def run():
+        nb[0] = ceiling.copy(src, dst, 4096)
+    out["copy_gbs"] = round(2 * (1 << 30) / (timed_ms(run) * 1e-3) / 1e9, 1)
+    out["copy_bytes"] = 1 << 30
+    del big
+    torch.cuda.empty_cache()
+    return out
+
+
+def sources_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per prefill-logits launch from the committed counter summary, or None when it is missing or
+    was taken on other kernel sources.  The summary holds `key: value` lines."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and line.startswith("- `"):
+            k, v = line[3:].split("`", 1)
+            kv[k] = v.split(":", 1)[1].strip().strip("`")
+    if kv.get("kernel_sources_sha256") != sources_digest(PREFILL_SOURCES):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # --------------------------------------------------------------------------- prefill chunk (headline)
@@ -281,6 +367,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the indexer path has no multi-GPU mode in this build "
@@ -289,6 +376,11 @@ def main():
     torch.cuda.set_device(0)
     dsi.lib()
 
+    ceil = None
+    if not args.no_ceilings:
+        log("measured ceilings ...")
+        ceil = measure_ceilings()
+        log(ceil)
     log("prefill chunk ...")
     pf = bench_prefill(args.steps, args.warmup)
     value = pf["pairs"] / (pf["ms_step"] * 1e-3)
@@ -314,14 +406,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3->f32",
+        "dtype": "fp8e4m3 (decoded exactly to f16 for the f16 MFMA) -> f32 accumulate",
         "data": "synthetic (seeded numpy: q,k ~ N(0,1) to bf16, FP8 e4m3 with per-128 scales)",
         "config": {"workload": "prefill chunk: 1 request, T=2048 query tokens at positions 6144..8191, S=8192, "
                                "H=64, D=128, causal, top-2048", "T": pf["T"], "S": pf["S"], "pairs": pf["pairs"],
                    "ms_logits": round(pf["ms_logits"], 4), "ms_topk": round(pf["ms_topk"], 4)},
         "roofline": {"bound": "mfma", "kernel": "prefill_logits_kernel", "achieved": round(achieved, 1),
-                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": flops},
+                     "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / F16_PEAK_TFLOPS, 4),
+                     "traffic": committed_traffic(), "algorithmic_flops_per_launch": flops,
+                     "mfma_dtype": "f16 (v_mfma_f32_16x16x32_f16)",
+                     "frac_of_fp8_peak": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "measured_ceiling": ceil},
         "cpu_baseline": cpu,
         "workloads": extra,
     }

@@ -1,0 +1,61 @@
+/*
+ * dsi_ceiling.h — on-device ceilings that the indexer kernels' rooflines are
+ * read against, and the plain copy that calibrates the HBM byte counters.
+ *
+ * Not part of the indexer path: a separate library (libdsi_ceiling.so) that
+ * the benchmark loads.  The published MI355X peaks (HBM3E 8 TB/s, dense f16
+ * MFMA 2.5 PFLOP/s, dense FP8 MFMA 5.0 PFLOP/s) are the roofline
+ * denominators; these kernels measure what one process actually reaches:
+ *   - matrix-core throughput with every operand in registers (no memory
+ *     traffic, 16 independent accumulator chains per wavefront);
+ *   - HBM streaming read bandwidth over a caller-sized buffer (sized well
+ *     above the 256 MB Infinity Cache, so the bytes come from HBM);
+ *   - a plain 16-byte-per-lane copy of a known number of bytes, whose
+ *     FETCH_SIZE / WRITE_SIZE counter readings give the factor between those
+ *     counters and real bytes.
+ *
+ * Conventions: device pointers owned by the caller; each call enqueues one
+ * kernel on `stream` and returns 0, or a negative dsi status (dsi.h) for
+ * rejected arguments (nothing is enqueued then).
+ */
+#ifndef DSI_CEILING_H
+#define DSI_CEILING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSIC_API __attribute__((visibility("default")))
+
+/* Register-only matrix-core loop.  kind 0 = v_mfma_f32_16x16x32_f16 (16,384
+ * flop per instruction), kind 1 = v_mfma_scale_f32_16x16x128_f8f6f4 with FP8
+ * E4M3 operands (65,536 flop per instruction).  `workgroups` workgroups of 256
+ * threads each run `iters` rounds of 16 instructions per wavefront, so the
+ * total is workgroups * 4 * iters * 16 instructions.  `sink` receives one
+ * float per thread (workgroups * 256 floats) so that nothing is optimised away.
+ * EINVAL: kind not 0/1, workgroups < 1, iters < 1, sink NULL. */
+DSIC_API int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, float* sink, hipStream_t stream);
+
+/* Stream-read `bytes` bytes from `src` (16-byte aligned, bytes a multiple of
+ * 16) with 16-byte loads, grid-stride, and fold them into one word per thread
+ * written to `sink` (workgroups * 256 uint32 = at most 4 MB).  EINVAL: null
+ * pointer, bytes 0 or not a multiple of 16, workgroups < 1; EALIGN: src not
+ * 16-byte aligned. */
+DSIC_API int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                              hipStream_t stream);
+
+/* Copy `bytes` bytes from `src` to `dst` (both 16-byte aligned, not
+ * overlapping, bytes a multiple of 16) with 16-byte loads and stores,
+ * grid-stride.  Errors as dsic_stream_read. */
+DSIC_API int dsic_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSI_CEILING_H */

@@ -1,8 +1,10 @@
-"""Compile the gfx950 HIP sources of the indexer library into libdsi.so (in-tree).
+"""Compile the gfx950 HIP sources into in-tree shared libraries.
 
+libdsi.so is the indexer library (include/dsi.h); libdsi_ceiling.so holds the
+measurement kernels the benchmark reads rooflines against (include/dsi_ceiling.h).
 Each source compiles to its own object under _build/ (in parallel), then one
-hipcc link produces sparse_attention_token_amd/libdsi.so.  Packed FP32 ops are
-disabled for every device compilation.
+hipcc link per library.  Packed FP32 ops are disabled for every device
+compilation.
 """
 import concurrent.futures
 import os
@@ -13,10 +15,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsi.so")
+LIB_CEILING = os.path.join(HERE, "libdsi_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["quant.hip", "prefill.hip", "gather_logits.hip", "topk.hip", "index.hip", "status.cpp"]
+CEILING_SOURCES = ["ceiling.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,16 +40,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEILING_SOURCES], LIB_CEILING, verbose)
     return LIB
 
 

@@ -1,0 +1,98 @@
+// Measured ceilings for the indexer rooflines: register-only matrix-core loops
+// and HBM streaming read / copy.  Built into its own library; the indexer path
+// does not use it.
+#include <hip/hip_runtime.h>
+
+#include "dsi.h"
+#include "dsi_ceiling.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kChains = 16;
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float* __restrict__ sink, int iters) {
+  f32x4 c[kChains];
+#pragma unroll
+  for (int j = 0; j < kChains; j++) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Operands depend on the thread id so the compiler cannot fold the loop; their
+  // values are small and finite (f16 halves, FP8 codes 0x30..0x37 = 0.5..0.9375).
+  f16x8 a16, b16;
+  i32x8 a8, b8;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    a16[j] = (_Float16)((threadIdx.x & 7) * 0.125f + j * 0.0625f);
+    b16[j] = (_Float16)(0.5f + j * 0.03125f);
+    a8[j] = 0x30303030 | ((threadIdx.x + j) & 7);
+    b8[j] = 0x30303030 | (j & 7);
+  }
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int j = 0; j < kChains; j++) {
+      if constexpr (KIND == 0)
+        c[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a16, b16, c[j], 0, 0, 0);
+      else
+        c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c[j], 0, 0, 0, 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kChains; j++) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  // four independent loads in flight per thread
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
+    acc ^= x0 ^ x1 ^ x2 ^ x3;
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        size_t n16) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH; }
+
+}  // namespace
+
+extern "C" int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, float* sink, hipStream_t stream) {
+  if ((kind != 0 && kind != 1) || workgroups < 1 || iters < 1 || !sink) return DSI_EINVAL;
+  if (kind == 0)
+    hipLaunchKernelGGL(mfma_loop_kernel<0>, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
+  else
+    hipLaunchKernelGGL(mfma_loop_kernel<1>, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
+  return launched();
+}
+
+extern "C" int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                                hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || (bytes & 15) || workgroups < 1 || workgroups > 4096) return DSI_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) & 15) return DSI_EALIGN;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  return launched();
+}
+
+extern "C" int dsic_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, hipStream_t stream) {
+  if (!src || !dst || bytes == 0 || (bytes & 15) || workgroups < 1) return DSI_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return DSI_EALIGN;
+  hipLaunchKernelGGL(copy_kernel, dim3(workgroups), dim3(kThreads), 0, stream, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), bytes / 16);
+  return launched();
+}

@@ -152,3 +152,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         dsi.lib()
+
+
+def test_ceiling_library_exports_and_validation():
+    from sparse_attention_token_amd import ceiling
+    src = open(os.path.join(ROOT, "include", "dsi_ceiling.h")).read()
+    names = sorted(set(re.findall(r"DSIC_API\s+[\w\s\*]*?\b(dsic_\w+)\s*\(", src)))
+    assert names == sorted(ceiling.ENTRY_POINTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", ceiling.LIB_PATH], capture_output=True, text=True).stdout
+    assert sorted(set(re.findall(r" T (dsic_\w+)", out))) == names
+    L = ceiling.lib()
+    assert L.dsic_mfma_loop(2, 1, 1, A16, None) == EINVAL
+    assert L.dsic_mfma_loop(0, 0, 1, A16, None) == EINVAL
+    assert L.dsic_mfma_loop(0, 1, 1, None, None) == EINVAL
+    assert L.dsic_stream_read(A16, 24, 1, A16, None) == EINVAL
+    assert L.dsic_stream_read(A16 + 4, 32, 1, A16, None) == EALIGN
+    assert L.dsic_copy(A16, A16 + 8, 32, 1, None) == EALIGN
+    assert L.dsic_copy(None, A16, 32, 1, None) == EINVAL
