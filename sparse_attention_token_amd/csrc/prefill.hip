@@ -1,39 +1,128 @@
-// Dense prefill indexer logits over gathered K (P3 step ⑥ and the prefill/decode
-// table of "DeepSeek V3.2 稀疏注意力 DSA 推理流程图解": prefill gathers the history
-// K, then scores every history token for every query token).
+// Dense prefill indexer logits over gathered K (P3 step ⑥ and the prefill/decode table of
+// "DeepSeek V3.2 稀疏注意力 DSA 推理流程图解": prefill gathers the history K, then scores
+// every history token for every query token).
 //
 // The contraction [T*64, 128] x [128, S] runs on the matrix cores with the FP8 codes
 // decoded exactly to f16 (common.h); the head-weighted sum is the epilogue.
 //
-// A workgroup owns 8 query rows, one per wavefront (its q decoded once into VGPRs),
-// and a chunk of 1024 keys streamed through LDS in double-buffered tiles of 64 keys.
-// Each tile is loaded as 4-byte words (consecutive lanes take consecutive words, so
-// the decoded 8-byte LDS writes of a wavefront are contiguous and conflict-free),
-// decoded to f16 once, and read by all 8 rows.  Per tile a wavefront runs one batch:
-// its row against the tile's 4 groups of 16 keys (64 MFMAs in 16 independent chains),
-// then one 4x4 transpose-reduce and one coalesced 256-byte store.  Tiles wholly
-// outside the rows' [ks, ke) ranges are never loaded, so causal work above the
-// diagonal is skipped.  Workgroups are renumbered so that the chunks of one row tile
-// run on the same XCD (their q stays in that XCD's L2); K (132 B per key) is re-read
-// from L2 by each row tile.
+// Matrix instruction: v_mfma_f32_32x32x16_f16 (measured on gfx950 to sustain a higher
+// rate than the 16x16x32 form, with only two independent accumulator chains).
+//   A = 32 heads x 16 dims of q   (lane l: head l%32, 8 dims of lane half h = l/32)
+//   B = 16 dims x 32 keys of K    (lane l: key  l%32, the same 8 dims)
+//   C = 32 heads x 32 keys, lane l holds heads 8*(i/4) + 4*h + i%4 (i < 16) of key l%32.
+// Lane half h owns dims [64h, 64h+64) of the 128 and feeds 8 of them to each of eight
+// slices; A and B use the same assignment, so the sum over dims is complete.  Two head
+// blocks cover the 64 heads, so after 16 MFMAs each lane holds 32 heads of one key and
+// the head-weighted sum is 32 FMAs.  The two lane halves hold the other 32 heads of the
+// same key: for a 64-key tile, one v_permlane32_swap exchanges the halves' partial sums
+// of the tile's two 32-key groups, and one add leaves lane l with key l of the tile.
+//
+// A workgroup of 4 wavefronts owns 4 query rows, one per wavefront, its q decoded once into
+// VGPRs, and a chunk of keys streamed through LDS in double-buffered 128-key tiles: each
+// tile is staged once (each wavefront loads a quarter of every row's codes), decoded to f16
+// once and read by all 4 rows.  Two workgroups share a CU, so one workgroup's barrier and
+// epilogue overlap the other's matrix work.  Tiles wholly outside the rows' [ks, ke)
+// ranges are never loaded, so causal work above the diagonal is skipped.  Workgroups are
+// renumbered so that the chunks of one row tile run on the same XCD (their q stays in that
+// XCD's L2); K (132 B per key) is re-read from L2 by each row tile.
 #include "common.h"
 
 namespace dsi {
 namespace {
 
-constexpr int kPfThreads = 512;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPfThreads = 256;
 constexpr int kPfRows = kPfThreads / 64;  // one query row per wavefront
-constexpr int kTileKeys = 64;             // keys per LDS tile
+constexpr int kGroups = 4;                // 32-key groups per tile
+constexpr int kTileKeys = 32 * kGroups;   // keys per LDS tile
 constexpr int kChunkTiles = 16;           // tiles per workgroup
 constexpr int kChunkKeys = kTileKeys * kChunkTiles;
-constexpr int kTileWords = kTileKeys * kRow / 4;  // 2112 dwords per full tile
-constexpr int kWordsPerThread = (kTileWords + kPfThreads - 1) / kPfThreads;
-constexpr int kTileLdsBytes = kTileKeys * kLdsKeyStrideF16 + kTileKeys * 4;  // f16 rows, then the fp32 scales
-constexpr int kScaleOffset = kTileKeys * kLdsKeyStrideF16;
-constexpr int kOutRow[4] = {0, 0, 0, 0};
-constexpr int kOutKg[4] = {0, 1, 2, 3};
+constexpr int kScaleOffset = kTileKeys * kLdsKeyStrideF16;  // f16 rows, then the fp32 scales
+constexpr int kTileLdsBytes = kScaleOffset + kTileKeys * 4;
+constexpr int kRowsPerLane = kTileKeys / 64;  // staging: lane r of wave p takes rows r + 64j, dims [32p, 32p+32)
+static_assert(kPfRows * 32 == kDim, "one wavefront per 32-dim quarter of the staged rows");
 
-__global__ __launch_bounds__(kPfThreads) void prefill_logits_kernel(
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// q[row] decoded into this lane's A fragments: head hb*32 + l%32, dims [64h + 8s, +8) for
+// slice s.
+struct Q32 {
+  f16x8 a[2][8];
+};
+
+__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint4 x = p[j];
+      f.a[hb][2 * j] = e4m3x8_to_f16x8(x.x, x.y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x.z, x.w);
+    }
+  }
+}
+
+// The weights of the 32 heads this lane holds in C: w[hb][i] is head hb*32 + 8*(i/4) + 4h + i%4.
+struct W32 {
+  float w[2][16];
+};
+
+__device__ __forceinline__ void load_w32(W32& f, const uint16_t* w_row, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
+      f.w[hb][4 * b + 0] = bf16_to_f32(x.x & 0xFFFFu);
+      f.w[hb][4 * b + 1] = bf16_to_f32(x.x >> 16);
+      f.w[hb][4 * b + 2] = bf16_to_f32(x.y & 0xFFFFu);
+      f.w[hb][4 * b + 3] = bf16_to_f32(x.y >> 16);
+    }
+}
+
+// B fragments of one 32-key group from the f16 tile: key l%32, dims [64h + 8s, +8).
+struct K32 {
+  f16x8 b[8];
+};
+
+__device__ __forceinline__ void load_k32(K32& f, const uint8_t* keys, int lane) {
+  const int n = lane & 31, h = lane >> 5;
+  const f16x8* p = reinterpret_cast<const f16x8*>(keys + n * kLdsKeyStrideF16 + h * 128);
+#pragma unroll
+  for (int s = 0; s < 8; s++) f.b[s] = p[s];
+}
+
+// Head-weighted partial of one 32-key group: 16 MFMAs in two chains (one per head block),
+// then 32 FMAs over the lane's heads.
+__device__ __forceinline__ float score32(const Q32& q, const W32& w, const K32& kb) {
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    c0 = mfma32(q.a[0][s], kb.b[s], c0);
+    c1 = mfma32(q.a[1][s], kb.b[s], c1);
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[0][i], c0[i], acc[i & 3]);
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[1][i], c1[i], acc[i & 3]);
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Sum of the two lane halves for two 32-key groups at once: on return lane l holds the
+// full sum of key l of the 64-key tile (group l/32, key l%32).
+__device__ __forceinline__ float combine_halves(float g0, float g1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(g0), __float_as_uint(g1), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int T, const uint8_t* __restrict__ k_rows, int S,
     const int* __restrict__ row_ks, const int* __restrict__ row_ke, float* __restrict__ logits, int64_t ld,
     int n_chunks) {
@@ -65,47 +154,48 @@ __global__ __launch_bounds__(kPfThreads) void prefill_logits_kernel(
   if (c_lo >= c_hi) return;  // uniform across the workgroup
   const int tile_first = c_lo / kTileKeys, tile_end = (c_hi + kTileKeys - 1) / kTileKeys;
 
-  // This thread's staging words: the same positions in every tile.
-  int lds_off[kWordsPerThread];
-  bool is_code[kWordsPerThread];
-#pragma unroll
-  for (int j = 0; j < kWordsPerThread; j++) {
-    const int d = tid + j * kPfThreads;
-    const int row = d / 33, word = d - row * 33;
-    is_code[j] = word < 32;
-    lds_off[j] = word < 32 ? row * kLdsKeyStrideF16 + word * 8 : kScaleOffset + row * 4;
-  }
-
   // This wavefront's row.
   const int t = t_first + wave;
   const int tc = min(t, T - 1);
-  QFrag qf[1];
-  WFrag wf[1];
-  load_q(qf[0], q + (int64_t)tc * kHeads * kDim, lane);
-  load_w(wf[0], w + (int64_t)tc * kHeads, lane);
+  Q32 qf;
+  W32 wf;
+  load_q32(qf, q + (int64_t)tc * kHeads * kDim, lane);
+  load_w32(wf, w + (int64_t)tc * kHeads, lane);
   const int rks = t < T ? max(row_ks[t], 0) : 0;
   const int rke = t < T ? min(row_ke[t], S) : 0;
 
-  uint32_t regs[kWordsPerThread];
+  // Staging: lane r of wavefront p loads the codes [32p, 32p+32) of rows r + 64j of the tile
+  // (two 16-byte loads per row), decodes them and writes 64 bytes of f16; wavefront 0 also
+  // copies the rows' scales.  Writes by consecutive lanes go to consecutive rows, 272 bytes
+  // apart, so they are conflict-free.
+  uint4 regs[kRowsPerLane][2];
+  uint32_t sregs[kRowsPerLane];
   auto load_tile = [&](int tile) {
-    const int nwords = min(kTileKeys, S - tile * kTileKeys) * (kRow / 4);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(k_rows + (int64_t)tile * kTileKeys * kRow);
+    const int nrows = min(kTileKeys, S - tile * kTileKeys);
+    const uint8_t* src = k_rows + (int64_t)tile * kTileKeys * kRow;
 #pragma unroll
-    for (int j = 0; j < kWordsPerThread; j++) {
-      const int d = tid + j * kPfThreads;
-      if (d < nwords) regs[j] = src[d];
+    for (int j = 0; j < kRowsPerLane; j++) {
+      const int r = lane + 64 * j;
+      if (r < nrows) {
+        const uint4* p = reinterpret_cast<const uint4*>(src + r * kRow + wave * 32);
+        regs[j][0] = p[0];
+        regs[j][1] = p[1];
+        if (wave == 0) sregs[j] = *reinterpret_cast<const uint32_t*>(src + r * kRow + kDim);
+      }
     }
   };
   auto store_tile = [&](int tile, uint8_t* dst) {
-    const int nwords = min(kTileKeys, S - tile * kTileKeys) * (kRow / 4);
+    const int nrows = min(kTileKeys, S - tile * kTileKeys);
 #pragma unroll
-    for (int j = 0; j < kWordsPerThread; j++) {
-      const int d = tid + j * kPfThreads;
-      if (d < nwords) {
-        if (is_code[j])
-          *reinterpret_cast<uint2*>(dst + lds_off[j]) = e4m3x4_to_f16x4(regs[j]);
-        else
-          *reinterpret_cast<uint32_t*>(dst + lds_off[j]) = regs[j];
+    for (int j = 0; j < kRowsPerLane; j++) {
+      const int r = lane + 64 * j;
+      if (r < nrows) {
+        f16x8* d = reinterpret_cast<f16x8*>(dst + r * kLdsKeyStrideF16 + wave * 64);
+        d[0] = e4m3x8_to_f16x8(regs[j][0].x, regs[j][0].y);
+        d[1] = e4m3x8_to_f16x8(regs[j][0].z, regs[j][0].w);
+        d[2] = e4m3x8_to_f16x8(regs[j][1].x, regs[j][1].y);
+        d[3] = e4m3x8_to_f16x8(regs[j][1].z, regs[j][1].w);
+        if (wave == 0) reinterpret_cast<uint32_t*>(dst + kScaleOffset)[r] = sregs[j];
       }
     }
   };
@@ -114,24 +204,24 @@ __global__ __launch_bounds__(kPfThreads) void prefill_logits_kernel(
   store_tile(tile_first, s_tile[0]);
   __syncthreads();
 
-  const int n = lane & 15, g = lane >> 4;
   for (int tile = tile_first; tile < tile_end; tile++) {
     const int buf = (tile - tile_first) & 1;
     const bool has_next = tile + 1 < tile_end;
     if (has_next) load_tile(tile + 1);
 
     const uint8_t* cur = s_tile[buf];
-    KFrag kb[4];
+    const float* scale = reinterpret_cast<const float*>(cur + kScaleOffset);
 #pragma unroll
-    for (int kg = 0; kg < 4; kg++) load_kfrag_f16(kb[kg], cur + kg * 16 * kLdsKeyStrideF16, lane);
-    float part[4];
-    score4(qf, wf, kb, kOutRow, kOutKg, part);
-    const float v = transpose_reduce4(part, lane);
-    // lane group g owns key group g: keys g*16 + n of the tile
-    const int kslot = g * 16 + n;
-    const int key = tile * kTileKeys + kslot;
-    if (key >= rks && key < rke)
-      logits[(int64_t)t * ld + key] = v * reinterpret_cast<const float*>(cur + kScaleOffset)[kslot];
+    for (int half = 0; half < kGroups / 2; half++) {
+      K32 kb;
+      load_k32(kb, cur + (2 * half) * 32 * kLdsKeyStrideF16, lane);
+      const float g0 = score32(qf, wf, kb);
+      load_k32(kb, cur + (2 * half + 1) * 32 * kLdsKeyStrideF16, lane);
+      const float g1 = score32(qf, wf, kb);
+      const float v = combine_halves(g0, g1);
+      const int key = tile * kTileKeys + half * 64 + lane;
+      if (key >= rks && key < rke) logits[(int64_t)t * ld + key] = v * scale[half * 64 + lane];
+    }
 
     if (has_next) store_tile(tile + 1, s_tile[buf ^ 1]);
     __syncthreads();
