@@ -98,15 +98,26 @@ __device__ __forceinline__ void load_k32(K32& f, const uint8_t* keys, int lane) 
   for (int s = 0; s < 8; s++) f.b[s] = p[s];
 }
 
-// Head-weighted partial of one 32-key group: 16 MFMAs in two chains (one per head block),
-// then 32 FMAs over the lane's heads.
-__device__ __forceinline__ float score32(const Q32& q, const W32& w, const K32& kb) {
-  f32x16 c0 = {}, c1 = {};
+// Half of one 32-key group's matrix work: slices [s0, s0+4) for both head blocks, two
+// independent accumulator chains.
+__device__ __forceinline__ void mfma_half(f32x16& c0, f32x16& c1, const Q32& q, const K32& kb, int s0) {
 #pragma unroll
-  for (int s = 0; s < 8; s++) {
+  for (int s = s0; s < s0 + 4; s++) {
     c0 = mfma32(q.a[0][s], kb.b[s], c0);
     c1 = mfma32(q.a[1][s], kb.b[s], c1);
   }
+}
+
+// Slices [s0, s0+4) of the B fragments of one 32-key group.
+__device__ __forceinline__ void load_k32_half(K32& f, const uint8_t* keys, int lane, int s0) {
+  const int n = lane & 31, h = lane >> 5;
+  const f16x8* p = reinterpret_cast<const f16x8*>(keys + n * kLdsKeyStrideF16 + h * 128);
+#pragma unroll
+  for (int s = s0; s < s0 + 4; s++) f.b[s] = p[s];
+}
+
+// Head-weighted sum over the 32 heads this lane holds for its key: 32 FMAs in four chains.
+__device__ __forceinline__ float head_sum(const W32& w, const f32x16& c0, const f32x16& c1) {
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[0][i], c0[i], acc[i & 3]);
@@ -133,7 +144,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);  // chunks of a row tile on one XCD
   const int rt = id / n_chunks, chunk = id - rt * n_chunks;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront: row values live in SGPRs
   const int t_first = rt * kPfRows;
 
   // Union of the workgroup's row ranges, clipped to this chunk.
@@ -164,67 +176,116 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
   const int rks = t < T ? max(row_ks[t], 0) : 0;
   const int rke = t < T ? min(row_ke[t], S) : 0;
 
+  // Output: a raw buffer over this row's logits whose record size ends at the row's range
+  // end; a lane whose key is below the range start (or below this workgroup's first tile)
+  // gets an offset past the end, so the hardware drops its store and the pipelined loop
+  // below has no branches.
+  const int key_lo = max(rks, tile_first * kTileKeys);
+  const __amdgpu_buffer_rsrc_t out_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(logits + (int64_t)tc * ld, (short)0, rke * 4, 0x00020000);
+  auto store_logit = [&](int key, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rsrc, key >= key_lo ? key * 4 : 0x7FFFFFFC, 0, 0);
+  };
+
   // Staging: lane r of wavefront p loads the codes [32p, 32p+32) of rows r + 64j of the tile
-  // (two 16-byte loads per row), decodes them and writes 64 bytes of f16; wavefront 0 also
-  // copies the rows' scales.  Writes by consecutive lanes go to consecutive rows, 272 bytes
-  // apart, so they are conflict-free.
+  // (two 16-byte loads per row), decodes them and writes 64 bytes of f16; the row's scale is
+  // copied by wavefronts p and p+2 (same value).  Writes by consecutive lanes go to
+  // consecutive rows, 272 bytes apart, so they are conflict-free.  Rows past the end of a
+  // partial tile repeat its last row; their keys are never stored.
   uint4 regs[kRowsPerLane][2];
-  uint32_t sregs[kRowsPerLane];
+  uint32_t sreg;
   auto load_tile = [&](int tile) {
-    const int nrows = min(kTileKeys, S - tile * kTileKeys);
+    const int last = min(kTileKeys, S - tile * kTileKeys) - 1;
     const uint8_t* src = k_rows + (int64_t)tile * kTileKeys * kRow;
 #pragma unroll
     for (int j = 0; j < kRowsPerLane; j++) {
-      const int r = lane + 64 * j;
-      if (r < nrows) {
-        const uint4* p = reinterpret_cast<const uint4*>(src + r * kRow + wave * 32);
-        regs[j][0] = p[0];
-        regs[j][1] = p[1];
-        if (wave == 0) sregs[j] = *reinterpret_cast<const uint32_t*>(src + r * kRow + kDim);
-      }
+      const uint4* p = reinterpret_cast<const uint4*>(src + min(lane + 64 * j, last) * kRow + wave * 32);
+      regs[j][0] = p[0];
+      regs[j][1] = p[1];
     }
+    sreg = *reinterpret_cast<const uint32_t*>(src + min(lane + 64 * (wave & 1), last) * kRow + kDim);
   };
-  auto store_tile = [&](int tile, uint8_t* dst) {
-    const int nrows = min(kTileKeys, S - tile * kTileKeys);
+  auto store_tile = [&](uint8_t* dst) {
 #pragma unroll
     for (int j = 0; j < kRowsPerLane; j++) {
-      const int r = lane + 64 * j;
-      if (r < nrows) {
-        f16x8* d = reinterpret_cast<f16x8*>(dst + r * kLdsKeyStrideF16 + wave * 64);
-        d[0] = e4m3x8_to_f16x8(regs[j][0].x, regs[j][0].y);
-        d[1] = e4m3x8_to_f16x8(regs[j][0].z, regs[j][0].w);
-        d[2] = e4m3x8_to_f16x8(regs[j][1].x, regs[j][1].y);
-        d[3] = e4m3x8_to_f16x8(regs[j][1].z, regs[j][1].w);
-        if (wave == 0) reinterpret_cast<uint32_t*>(dst + kScaleOffset)[r] = sregs[j];
-      }
+      f16x8* d = reinterpret_cast<f16x8*>(dst + (lane + 64 * j) * kLdsKeyStrideF16 + wave * 64);
+      d[0] = e4m3x8_to_f16x8(regs[j][0].x, regs[j][0].y);
+      d[1] = e4m3x8_to_f16x8(regs[j][0].z, regs[j][0].w);
+      d[2] = e4m3x8_to_f16x8(regs[j][1].x, regs[j][1].y);
+      d[3] = e4m3x8_to_f16x8(regs[j][1].z, regs[j][1].w);
     }
+    reinterpret_cast<uint32_t*>(dst + kScaleOffset)[lane + 64 * (wave & 1)] = sreg;
   };
 
   load_tile(tile_first);
-  store_tile(tile_first, s_tile[0]);
+  store_tile(s_tile[0]);
   __syncthreads();
 
+  // Software pipeline over 32-key groups.  While the matrix cores run group g, the wavefront
+  // computes the head sums of group g-1, loads the B fragments of group g+1 (the first half
+  // once the first half of group g is issued) and, for the last group of a tile, writes the
+  // next tile into the other LDS buffer.  The head sums of a tile's last group are taken
+  // during the next tile's first group, so the matrix work never waits for an epilogue.
+  f32x16 a0 = {}, a1 = {}, b0 = {}, b1 = {};
+  float p_even = 0.f;   // head sum of group 0 or 2, waiting for its partner
+  float scale_hi = 0.f;  // scale of key 64 + lane of the previous tile
+  K32 kb;
+  load_k32_half(kb, s_tile[0], lane, 0);
+  load_k32_half(kb, s_tile[0], lane, 4);
   for (int tile = tile_first; tile < tile_end; tile++) {
     const int buf = (tile - tile_first) & 1;
-    const bool has_next = tile + 1 < tile_end;
-    if (has_next) load_tile(tile + 1);
-
     const uint8_t* cur = s_tile[buf];
     const float* scale = reinterpret_cast<const float*>(cur + kScaleOffset);
-#pragma unroll
-    for (int half = 0; half < kGroups / 2; half++) {
-      K32 kb;
-      load_k32(kb, cur + (2 * half) * 32 * kLdsKeyStrideF16, lane);
-      const float g0 = score32(qf, wf, kb);
-      load_k32(kb, cur + (2 * half + 1) * 32 * kLdsKeyStrideF16, lane);
-      const float g1 = score32(qf, wf, kb);
-      const float v = combine_halves(g0, g1);
-      const int key = tile * kTileKeys + half * 64 + lane;
-      if (key >= rks && key < rke) logits[(int64_t)t * ld + key] = v * scale[half * 64 + lane];
-    }
+    load_tile(min(tile + 1, tile_end - 1));
 
-    if (has_next) store_tile(tile + 1, s_tile[buf ^ 1]);
+    // group 0 -> a; finish the previous tile's keys 64..127 from b
+    a0 = f32x16{};
+    a1 = f32x16{};
+    mfma_half(a0, a1, qf, kb, 0);
+    load_k32_half(kb, cur + 32 * kLdsKeyStrideF16, lane, 0);
+    {
+      const float v = combine_halves(p_even, head_sum(wf, b0, b1));
+      store_logit((tile - 1) * kTileKeys + 64 + lane, v * scale_hi);
+    }
+    mfma_half(a0, a1, qf, kb, 4);
+    load_k32_half(kb, cur + 32 * kLdsKeyStrideF16, lane, 4);
+
+    // group 1 -> b; head sums of group 0
+    b0 = f32x16{};
+    b1 = f32x16{};
+    mfma_half(b0, b1, qf, kb, 0);
+    load_k32_half(kb, cur + 64 * kLdsKeyStrideF16, lane, 0);
+    p_even = head_sum(wf, a0, a1);
+    mfma_half(b0, b1, qf, kb, 4);
+    load_k32_half(kb, cur + 64 * kLdsKeyStrideF16, lane, 4);
+
+    // group 2 -> a; keys 0..63 of this tile from groups 0 and 1
+    a0 = f32x16{};
+    a1 = f32x16{};
+    mfma_half(a0, a1, qf, kb, 0);
+    load_k32_half(kb, cur + 96 * kLdsKeyStrideF16, lane, 0);
+    {
+      const float v = combine_halves(p_even, head_sum(wf, b0, b1));
+      store_logit(tile * kTileKeys + lane, v * scale[lane]);
+    }
+    mfma_half(a0, a1, qf, kb, 4);
+    load_k32_half(kb, cur + 96 * kLdsKeyStrideF16, lane, 4);
+
+    // group 3 -> b; head sums of group 2; stage the next tile
+    b0 = f32x16{};
+    b1 = f32x16{};
+    mfma_half(b0, b1, qf, kb, 0);
+    p_even = head_sum(wf, a0, a1);
+    scale_hi = scale[64 + lane];
+    mfma_half(b0, b1, qf, kb, 4);
+    store_tile(s_tile[buf ^ 1]);
     __syncthreads();
+    load_k32_half(kb, s_tile[buf ^ 1], lane, 0);
+    load_k32_half(kb, s_tile[buf ^ 1], lane, 4);
+  }
+  {
+    const float v = combine_halves(p_even, head_sum(wf, b0, b1));
+    store_logit((tile_end - 1) * kTileKeys + 64 + lane, v * scale_hi);
   }
 }
 
