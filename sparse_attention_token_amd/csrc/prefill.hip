@@ -91,39 +91,47 @@ struct K32 {
   f16x8 b[8];
 };
 
-__device__ __forceinline__ void load_k32(K32& f, const uint8_t* keys, int lane) {
-  const int n = lane & 31, h = lane >> 5;
-  const f16x8* p = reinterpret_cast<const f16x8*>(keys + n * kLdsKeyStrideF16 + h * 128);
+// One 32-key group on the matrix cores, with the previous group's head sum and other work
+// threaded between its 16 MFMAs in a fixed order (sched_barrier fences keep the compiler
+// from regrouping them).  Step i issues MFMA i (slice i/2, head block i%2) into x, then two
+// of the 32 FMAs of the head sum of y (the previous group's accumulators), then, after the
+// second MFMA of a slice has read it, the same slice of the next group's B fragments (when
+// kLoadNext), then extra(i).
+template <bool kLoadNext, typename Extra>
+__device__ __forceinline__ void group_phase(f32x16& x0, f32x16& x1, const Q32& q, K32& kb, const uint8_t* next,
+                                            int lane, const W32& w, const f32x16& y0, const f32x16& y1,
+                                            float (&acc)[4], Extra&& extra) {
+  const f16x8* np = reinterpret_cast<const f16x8*>(next + (lane & 31) * kLdsKeyStrideF16 + (lane >> 5) * 128);
 #pragma unroll
-  for (int s = 0; s < 8; s++) f.b[s] = p[s];
-}
-
-// Half of one 32-key group's matrix work: slices [s0, s0+4) for both head blocks, two
-// independent accumulator chains.
-__device__ __forceinline__ void mfma_half(f32x16& c0, f32x16& c1, const Q32& q, const K32& kb, int s0) {
+  for (int j = 0; j < 4; j++) acc[j] = 0.f;
 #pragma unroll
-  for (int s = s0; s < s0 + 4; s++) {
-    c0 = mfma32(q.a[0][s], kb.b[s], c0);
-    c1 = mfma32(q.a[1][s], kb.b[s], c1);
+  for (int i = 0; i < 16; i++) {
+    const int sl = i >> 1;
+    if ((i & 1) == 0)
+      x0 = mfma32(q.a[0][sl], kb.b[sl], i == 0 ? f32x16{} : x0);
+    else
+      x1 = mfma32(q.a[1][sl], kb.b[sl], i == 1 ? f32x16{} : x1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 2 * i; e < 2 * i + 2; e++) {
+      if (e < 16)
+        acc[e & 3] = fmaf(w.w[0][e], y0[e], acc[e & 3]);
+      else
+        acc[e & 3] = fmaf(w.w[1][e - 16], y1[e - 16], acc[e & 3]);
+    }
+    if (kLoadNext && (i & 1)) kb.b[sl] = np[sl];
+    extra(i);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Slices [s0, s0+4) of the B fragments of one 32-key group.
-__device__ __forceinline__ void load_k32_half(K32& f, const uint8_t* keys, int lane, int s0) {
-  const int n = lane & 31, h = lane >> 5;
-  const f16x8* p = reinterpret_cast<const f16x8*>(keys + n * kLdsKeyStrideF16 + h * 128);
-#pragma unroll
-  for (int s = s0; s < s0 + 4; s++) f.b[s] = p[s];
-}
+__device__ __forceinline__ float acc_sum(const float (&acc)[4]) { return (acc[0] + acc[1]) + (acc[2] + acc[3]); }
 
-// Head-weighted sum over the 32 heads this lane holds for its key: 32 FMAs in four chains.
-__device__ __forceinline__ float head_sum(const W32& w, const f32x16& c0, const f32x16& c1) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+// All eight slices of one group's B fragments (after a barrier, when nothing else can run).
+__device__ __forceinline__ void load_k32(K32& f, const uint8_t* keys, int lane) {
+  const f16x8* p = reinterpret_cast<const f16x8*>(keys + (lane & 31) * kLdsKeyStrideF16 + (lane >> 5) * 128);
 #pragma unroll
-  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[0][i], c0[i], acc[i & 3]);
-#pragma unroll
-  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[1][i], c1[i], acc[i & 3]);
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  for (int s = 0; s < 8; s++) f.b[s] = p[s];
 }
 
 // Sum of the two lane halves for two 32-key groups at once: on return lane l holds the
@@ -194,99 +202,85 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
   // partial tile repeat its last row; their keys are never stored.
   uint4 regs[kRowsPerLane][2];
   uint32_t sreg;
-  auto load_tile = [&](int tile) {
+  auto load_piece = [&](int tile, int i) {  // i = 0..4: the two 16-byte loads of each row, then the scale
     const int last = min(kTileKeys, S - tile * kTileKeys) - 1;
     const uint8_t* src = k_rows + (int64_t)tile * kTileKeys * kRow;
-#pragma unroll
-    for (int j = 0; j < kRowsPerLane; j++) {
-      const uint4* p = reinterpret_cast<const uint4*>(src + min(lane + 64 * j, last) * kRow + wave * 32);
-      regs[j][0] = p[0];
-      regs[j][1] = p[1];
+    if (i < 2 * kRowsPerLane) {
+      const int j = i >> 1;
+      regs[j][i & 1] = reinterpret_cast<const uint4*>(src + min(lane + 64 * j, last) * kRow + wave * 32)[i & 1];
+    } else if (i == 2 * kRowsPerLane) {
+      sreg = *reinterpret_cast<const uint32_t*>(src + min(lane + 64 * (wave & 1), last) * kRow + kDim);
     }
-    sreg = *reinterpret_cast<const uint32_t*>(src + min(lane + 64 * (wave & 1), last) * kRow + kDim);
   };
-  auto store_tile = [&](uint8_t* dst) {
-#pragma unroll
-    for (int j = 0; j < kRowsPerLane; j++) {
-      f16x8* d = reinterpret_cast<f16x8*>(dst + (lane + 64 * j) * kLdsKeyStrideF16 + wave * 64);
-      d[0] = e4m3x8_to_f16x8(regs[j][0].x, regs[j][0].y);
-      d[1] = e4m3x8_to_f16x8(regs[j][0].z, regs[j][0].w);
-      d[2] = e4m3x8_to_f16x8(regs[j][1].x, regs[j][1].y);
-      d[3] = e4m3x8_to_f16x8(regs[j][1].z, regs[j][1].w);
+  auto store_piece = [&](uint8_t* dst, int i) {  // i = 0..8: one f16x8 (4 conversions, one LDS write), then the scale
+    if (i < 4 * kRowsPerLane) {
+      const int j = i >> 2, c = i & 3;
+      const uint4& x = regs[j][c >> 1];
+      const uint32_t lo = (c & 1) ? x.z : x.x, hi = (c & 1) ? x.w : x.y;
+      reinterpret_cast<f16x8*>(dst + (lane + 64 * j) * kLdsKeyStrideF16 + wave * 64)[c] = e4m3x8_to_f16x8(lo, hi);
+    } else if (i == 4 * kRowsPerLane) {
+      reinterpret_cast<uint32_t*>(dst + kScaleOffset)[lane + 64 * (wave & 1)] = sreg;
     }
-    reinterpret_cast<uint32_t*>(dst + kScaleOffset)[lane + 64 * (wave & 1)] = sreg;
   };
 
-  load_tile(tile_first);
-  store_tile(s_tile[0]);
+#pragma unroll
+  for (int i = 0; i <= 2 * kRowsPerLane; i++) load_piece(tile_first, i);
+#pragma unroll
+  for (int i = 0; i <= 4 * kRowsPerLane; i++) store_piece(s_tile[0], i);
   __syncthreads();
 
   // Software pipeline over 32-key groups.  While the matrix cores run group g, the wavefront
-  // computes the head sums of group g-1, loads the B fragments of group g+1 (the first half
-  // once the first half of group g is issued) and, for the last group of a tile, writes the
-  // next tile into the other LDS buffer.  The head sums of a tile's last group are taken
+  // computes the head sums of group g-1, loads the B fragments of group g+1 slice by slice
+  // and does its share of staging the next tile (global loads during the first group,
+  // decode and LDS writes during the last).  The head sums of a tile's last group are taken
   // during the next tile's first group, so the matrix work never waits for an epilogue.
   f32x16 a0 = {}, a1 = {}, b0 = {}, b1 = {};
-  float p_even = 0.f;   // head sum of group 0 or 2, waiting for its partner
+  float acc[4];
+  float p_even = 0.f;    // head sum of group 0 or 2, waiting for its partner
+  float scale_lo = 0.f;  // scale of key lane of the current tile
   float scale_hi = 0.f;  // scale of key 64 + lane of the previous tile
   K32 kb;
-  load_k32_half(kb, s_tile[0], lane, 0);
-  load_k32_half(kb, s_tile[0], lane, 4);
+  load_k32(kb, s_tile[0], lane);
   for (int tile = tile_first; tile < tile_end; tile++) {
     const int buf = (tile - tile_first) & 1;
     const uint8_t* cur = s_tile[buf];
+    uint8_t* nxt = s_tile[buf ^ 1];
     const float* scale = reinterpret_cast<const float*>(cur + kScaleOffset);
-    load_tile(min(tile + 1, tile_end - 1));
+    const int next_tile = min(tile + 1, tile_end - 1);
 
-    // group 0 -> a; finish the previous tile's keys 64..127 from b
-    a0 = f32x16{};
-    a1 = f32x16{};
-    mfma_half(a0, a1, qf, kb, 0);
-    load_k32_half(kb, cur + 32 * kLdsKeyStrideF16, lane, 0);
-    {
-      const float v = combine_halves(p_even, head_sum(wf, b0, b1));
-      store_logit((tile - 1) * kTileKeys + 64 + lane, v * scale_hi);
-    }
-    mfma_half(a0, a1, qf, kb, 4);
-    load_k32_half(kb, cur + 32 * kLdsKeyStrideF16, lane, 4);
+    // group 0 -> a; head sums of the previous tile's group 3; global loads of the next tile
+    group_phase<true>(a0, a1, qf, kb, cur + 32 * kLdsKeyStrideF16, lane, wf, b0, b1, acc, [&](int i) {
+      if (i >= 2 && i <= 2 + 2 * kRowsPerLane) load_piece(next_tile, i - 2);
+      if (i == 12) scale_lo = scale[lane];
+    });
+    store_logit((tile - 1) * kTileKeys + 64 + lane, combine_halves(p_even, acc_sum(acc)) * scale_hi);
 
     // group 1 -> b; head sums of group 0
-    b0 = f32x16{};
-    b1 = f32x16{};
-    mfma_half(b0, b1, qf, kb, 0);
-    load_k32_half(kb, cur + 64 * kLdsKeyStrideF16, lane, 0);
-    p_even = head_sum(wf, a0, a1);
-    mfma_half(b0, b1, qf, kb, 4);
-    load_k32_half(kb, cur + 64 * kLdsKeyStrideF16, lane, 4);
+    group_phase<true>(b0, b1, qf, kb, cur + 64 * kLdsKeyStrideF16, lane, wf, a0, a1, acc, [&](int) {});
+    p_even = acc_sum(acc);
 
-    // group 2 -> a; keys 0..63 of this tile from groups 0 and 1
-    a0 = f32x16{};
-    a1 = f32x16{};
-    mfma_half(a0, a1, qf, kb, 0);
-    load_k32_half(kb, cur + 96 * kLdsKeyStrideF16, lane, 0);
-    {
-      const float v = combine_halves(p_even, head_sum(wf, b0, b1));
-      store_logit(tile * kTileKeys + lane, v * scale[lane]);
-    }
-    mfma_half(a0, a1, qf, kb, 4);
-    load_k32_half(kb, cur + 96 * kLdsKeyStrideF16, lane, 4);
+    // group 2 -> a; head sums of group 1; keys 0..63 of this tile
+    group_phase<true>(a0, a1, qf, kb, cur + 96 * kLdsKeyStrideF16, lane, wf, b0, b1, acc, [&](int i) {
+      if (i == 12) scale_hi = scale[64 + lane];
+    });
+    store_logit(tile * kTileKeys + lane, combine_halves(p_even, acc_sum(acc)) * scale_lo);
 
-    // group 3 -> b; head sums of group 2; stage the next tile
-    b0 = f32x16{};
-    b1 = f32x16{};
-    mfma_half(b0, b1, qf, kb, 0);
-    p_even = head_sum(wf, a0, a1);
-    scale_hi = scale[64 + lane];
-    mfma_half(b0, b1, qf, kb, 4);
-    store_tile(s_tile[buf ^ 1]);
+    // group 3 -> b; head sums of group 2; decode the next tile into the other buffer
+    group_phase<false>(b0, b1, qf, kb, cur, lane, wf, a0, a1, acc, [&](int i) {
+      if (i >= 4 && i <= 4 + 4 * kRowsPerLane) store_piece(nxt, i - 4);
+    });
+    p_even = acc_sum(acc);
     __syncthreads();
-    load_k32_half(kb, s_tile[buf ^ 1], lane, 0);
-    load_k32_half(kb, s_tile[buf ^ 1], lane, 4);
+    load_k32(kb, nxt, lane);
   }
-  {
-    const float v = combine_halves(p_even, head_sum(wf, b0, b1));
-    store_logit((tile_end - 1) * kTileKeys + 64 + lane, v * scale_hi);
-  }
+  // head sums of the last tile's group 3
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; e++) acc[e & 3] = fmaf(wf.w[0][e], b0[e], acc[e & 3]);
+#pragma unroll
+  for (int e = 0; e < 16; e++) acc[e & 3] = fmaf(wf.w[1][e], b1[e], acc[e & 3]);
+  store_logit((tile_end - 1) * kTileKeys + 64 + lane, combine_halves(p_even, acc_sum(acc)) * scale_hi);
 }
 
 }  // namespace
