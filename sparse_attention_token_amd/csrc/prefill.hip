@@ -17,14 +17,13 @@
 // same key: for a 64-key tile, one v_permlane32_swap exchanges the halves' partial sums
 // of the tile's two 32-key groups, and one add leaves lane l with key l of the tile.
 //
-// A workgroup of 4 wavefronts owns 4 query rows, one per wavefront, its q decoded once into
-// VGPRs, and a chunk of keys streamed through LDS in double-buffered 128-key tiles: each
-// tile is staged once (each wavefront loads a quarter of every row's codes), decoded to f16
-// once and read by all 4 rows.  Two workgroups share a CU, so one workgroup's barrier and
-// epilogue overlap the other's matrix work.  Tiles wholly outside the rows' [ks, ke)
-// ranges are never loaded, so causal work above the diagonal is skipped.  Workgroups are
-// renumbered so that the chunks of one row tile run on the same XCD (their q stays in that
-// XCD's L2); K (132 B per key) is re-read from L2 by each row tile.
+// A workgroup of 8 wavefronts (one per CU) owns 8 query rows, one per wavefront, its q
+// decoded once into VGPRs, and a share of the keys streamed through LDS in double-buffered
+// 128-key tiles: each tile is staged once (each wavefront loads an eighth of every row's
+// codes), decoded to f16 once and read by all 8 rows.  Tiles wholly outside the rows'
+// [ks, ke) ranges are never loaded, so causal work above the diagonal is skipped; the tiles
+// a row tile does need are split evenly between its workgroups.  K (132 B per key) is
+// re-read from L2 by each row tile.
 #include "common.h"
 
 namespace dsi {
@@ -32,16 +31,17 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfThreads = 256;
+constexpr int kPfThreads = 512;
 constexpr int kPfRows = kPfThreads / 64;  // one query row per wavefront
 constexpr int kGroups = 4;                // 32-key groups per tile
 constexpr int kTileKeys = 32 * kGroups;   // keys per LDS tile
-constexpr int kChunkTiles = 16;           // tiles per workgroup
+constexpr int kChunkTiles = 32;           // tiles per workgroup at most (S sets the split count)
 constexpr int kChunkKeys = kTileKeys * kChunkTiles;
 constexpr int kScaleOffset = kTileKeys * kLdsKeyStrideF16;  // f16 rows, then the fp32 scales
 constexpr int kTileLdsBytes = kScaleOffset + kTileKeys * 4;
-constexpr int kRowsPerLane = kTileKeys / 64;  // staging: lane r of wave p takes rows r + 64j, dims [32p, 32p+32)
-static_assert(kPfRows * 32 == kDim, "one wavefront per 32-dim quarter of the staged rows");
+constexpr int kRowsPerLane = kTileKeys / 64;  // staging: lane r of wave p takes rows r + 64j,
+constexpr int kStageDims = kDim / kPfRows;     // dims [kStageDims*p, kStageDims*(p+1))
+static_assert(kStageDims % 16 == 0, "staging moves whole 16-byte pieces");
 
 __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -141,22 +141,25 @@ __device__ __forceinline__ float combine_halves(float g0, float g1) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int T, const uint8_t* __restrict__ k_rows, int S,
     const int* __restrict__ row_ks, const int* __restrict__ row_ke, float* __restrict__ logits, int64_t ld,
-    int n_chunks) {
+    int n_parts) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][kTileLdsBytes];
 
-  const int nwg = gridDim.x;
-  int id = blockIdx.x;
-  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);  // chunks of a row tile on one XCD
-  const int rt = id / n_chunks, chunk = id - rt * n_chunks;
+  // Workgroup -> (part, row tile): parts outermost and row tiles in descending order, so the
+  // larger causal row tiles are dispatched first, and the parts of one row tile (which share
+  // its q) land on the same XCD whenever the row-tile count is a multiple of the 8 XCDs.
+  const int row_tiles = (T + kPfRows - 1) / kPfRows;
+  const int part = blockIdx.x / row_tiles;
+  const int rt = row_tiles - 1 - (int)(blockIdx.x - part * row_tiles);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront: row values live in SGPRs
   const int t_first = rt * kPfRows;
 
-  // Union of the workgroup's row ranges, clipped to this chunk.
+  // Union of the workgroup's row ranges; this workgroup takes an equal share (part `part` of
+  // n_parts) of the tiles that cover it.
   int lo = 0x7FFFFFFF, hi = 0;
 #pragma unroll
   for (int i = 0; i < kPfRows; i++) {
@@ -169,10 +172,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
       }
     }
   }
-  const int c_lo = max(chunk * kChunkKeys, lo);
-  const int c_hi = min(chunk * kChunkKeys + kChunkKeys, hi);
-  if (c_lo >= c_hi) return;  // uniform across the workgroup
-  const int tile_first = c_lo / kTileKeys, tile_end = (c_hi + kTileKeys - 1) / kTileKeys;
+  if (lo >= hi) return;  // uniform across the workgroup
+  const int t0 = lo / kTileKeys, nt = (hi + kTileKeys - 1) / kTileKeys - t0;
+  const int tile_first = t0 + part * nt / n_parts, tile_end = t0 + (part + 1) * nt / n_parts;
+  if (tile_first >= tile_end) return;
 
   // This wavefront's row.
   const int t = t_first + wave;
@@ -195,45 +198,51 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rsrc, key >= key_lo ? key * 4 : 0x7FFFFFFC, 0, 0);
   };
 
-  // Staging: lane r of wavefront p loads the codes [32p, 32p+32) of rows r + 64j of the tile
-  // (two 16-byte loads per row), decodes them and writes 64 bytes of f16; the row's scale is
-  // copied by wavefronts p and p+2 (same value).  Writes by consecutive lanes go to
-  // consecutive rows, 272 bytes apart, so they are conflict-free.  Rows past the end of a
-  // partial tile repeat its last row; their keys are never stored.
-  uint4 regs[kRowsPerLane][2];
+  // Staging: lane r of wavefront p loads the codes [16p, 16p+16) of rows r + 64j of the tile
+  // (one 16-byte load per row), decodes them and writes 32 bytes of f16; the row's scale is
+  // copied by every wavefront of the same parity (same value).  Writes by consecutive lanes
+  // go to consecutive rows, 272 bytes apart, so they are conflict-free.  Rows past the end of
+  // a partial tile repeat its last row; their keys are never stored.
+  constexpr int kLoads = kStageDims / 16;  // 16-byte loads per row
+  constexpr int kVecs = kStageDims / 8;    // f16x8 writes per row
+  uint4 regs[kRowsPerLane][kLoads];
   uint32_t sreg;
-  auto load_piece = [&](int tile, int i) {  // i = 0..4: the two 16-byte loads of each row, then the scale
+  auto load_piece = [&](int tile, int i) {  // i < kRowsPerLane*kLoads: one 16-byte load; then the scale
     const int last = min(kTileKeys, S - tile * kTileKeys) - 1;
     const uint8_t* src = k_rows + (int64_t)tile * kTileKeys * kRow;
-    if (i < 2 * kRowsPerLane) {
-      const int j = i >> 1;
-      regs[j][i & 1] = reinterpret_cast<const uint4*>(src + min(lane + 64 * j, last) * kRow + wave * 32)[i & 1];
-    } else if (i == 2 * kRowsPerLane) {
-      sreg = *reinterpret_cast<const uint32_t*>(src + min(lane + 64 * (wave & 1), last) * kRow + kDim);
+    if (i < kRowsPerLane * kLoads) {
+      const int j = i / kLoads, c = i % kLoads;
+      const uint32_t off = __umul24((uint32_t)min(lane + 64 * j, last), (uint32_t)kRow) + wave * kStageDims + 16 * c;
+      regs[j][c] = *reinterpret_cast<const uint4*>(src + off);
+    } else if (i == kRowsPerLane * kLoads) {
+      sreg = *reinterpret_cast<const uint32_t*>(src + __umul24((uint32_t)min(lane + 64 * (wave & 1), last), (uint32_t)kRow) + kDim);
     }
   };
-  auto store_piece = [&](uint8_t* dst, int i) {  // i = 0..8: one f16x8 (4 conversions, one LDS write), then the scale
-    if (i < 4 * kRowsPerLane) {
-      const int j = i >> 2, c = i & 3;
+  auto store_piece = [&](uint8_t* dst, int i) {  // i < kRowsPerLane*kVecs: one f16x8 (4 conversions); then the scale
+    if (i < kRowsPerLane * kVecs) {
+      const int j = i / kVecs, c = i % kVecs;
       const uint4& x = regs[j][c >> 1];
       const uint32_t lo = (c & 1) ? x.z : x.x, hi = (c & 1) ? x.w : x.y;
-      reinterpret_cast<f16x8*>(dst + (lane + 64 * j) * kLdsKeyStrideF16 + wave * 64)[c] = e4m3x8_to_f16x8(lo, hi);
-    } else if (i == 4 * kRowsPerLane) {
+      reinterpret_cast<f16x8*>(dst + (lane + 64 * j) * kLdsKeyStrideF16 + wave * (2 * kStageDims))[c] =
+          e4m3x8_to_f16x8(lo, hi);
+    } else if (i == kRowsPerLane * kVecs) {
       reinterpret_cast<uint32_t*>(dst + kScaleOffset)[lane + 64 * (wave & 1)] = sreg;
     }
   };
 
 #pragma unroll
-  for (int i = 0; i <= 2 * kRowsPerLane; i++) load_piece(tile_first, i);
+  for (int i = 0; i <= kRowsPerLane * kLoads; i++) load_piece(tile_first, i);
 #pragma unroll
-  for (int i = 0; i <= 4 * kRowsPerLane; i++) store_piece(s_tile[0], i);
+  for (int i = 0; i <= kRowsPerLane * kVecs; i++) store_piece(s_tile[0], i);
   __syncthreads();
 
   // Software pipeline over 32-key groups.  While the matrix cores run group g, the wavefront
   // computes the head sums of group g-1, loads the B fragments of group g+1 slice by slice
   // and does its share of staging the next tile (global loads during the first group,
-  // decode and LDS writes during the last).  The head sums of a tile's last group are taken
-  // during the next tile's first group, so the matrix work never waits for an epilogue.
+  // decode and LDS writes during the third).  The tile's one barrier sits before its last
+  // group, whose fragments are already in registers, so the next tile's first fragments
+  // load under that group's MFMAs.  The head sums of a tile's last group are taken during
+  // the next tile's first group, so the matrix work never waits for an epilogue.
   f32x16 a0 = {}, a1 = {}, b0 = {}, b1 = {};
   float acc[4];
   float p_even = 0.f;    // head sum of group 0 or 2, waiting for its partner
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
 
     // group 0 -> a; head sums of the previous tile's group 3; global loads of the next tile
     group_phase<true>(a0, a1, qf, kb, cur + 32 * kLdsKeyStrideF16, lane, wf, b0, b1, acc, [&](int i) {
-      if (i >= 2 && i <= 2 + 2 * kRowsPerLane) load_piece(next_tile, i - 2);
+      if (i >= 2 && i <= 2 + kRowsPerLane * kLoads) load_piece(next_tile, i - 2);
       if (i == 12) scale_lo = scale[lane];
     });
     store_logit((tile - 1) * kTileKeys + 64 + lane, combine_halves(p_even, acc_sum(acc)) * scale_hi);
@@ -259,19 +268,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_logits_kernel(
     group_phase<true>(b0, b1, qf, kb, cur + 64 * kLdsKeyStrideF16, lane, wf, a0, a1, acc, [&](int) {});
     p_even = acc_sum(acc);
 
-    // group 2 -> a; head sums of group 1; keys 0..63 of this tile
+    // group 2 -> a; head sums of group 1; decode the next tile into the other buffer
     group_phase<true>(a0, a1, qf, kb, cur + 96 * kLdsKeyStrideF16, lane, wf, b0, b1, acc, [&](int i) {
+      if (i >= 2 && i <= 2 + kRowsPerLane * kVecs) store_piece(nxt, i - 2);
       if (i == 12) scale_hi = scale[64 + lane];
     });
-    store_logit(tile * kTileKeys + lane, combine_halves(p_even, acc_sum(acc)) * scale_lo);
-
-    // group 3 -> b; head sums of group 2; decode the next tile into the other buffer
-    group_phase<false>(b0, b1, qf, kb, cur, lane, wf, a0, a1, acc, [&](int i) {
-      if (i >= 4 && i <= 4 + 4 * kRowsPerLane) store_piece(nxt, i - 4);
-    });
-    p_even = acc_sum(acc);
+    const float v_lo = combine_halves(p_even, acc_sum(acc)) * scale_lo;
+    // Every wavefront is done with this tile's buffer (group 3's fragments and both scale
+    // halves are in registers) and has written its part of the next tile.
     __syncthreads();
-    load_k32(kb, nxt, lane);
+
+    // group 3 -> b; head sums of group 2; fragments of the next tile's group 0
+    store_logit(tile * kTileKeys + lane, v_lo);
+    group_phase<true>(b0, b1, qf, kb, nxt, lane, wf, a0, a1, acc, [&](int) {});
+    p_even = acc_sum(acc);
   }
   // head sums of the last tile's group 3
 #pragma unroll
@@ -297,10 +307,10 @@ extern "C" int dsi_mqa_logits_prefill(const uint8_t* q, const uint16_t* w, int32
       (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits) & 3))
     return DSI_EALIGN;
   const int row_tiles = (T + kPfRows - 1) / kPfRows;
-  const int n_chunks = (S + kChunkKeys - 1) / kChunkKeys;
-  const int64_t grid = (int64_t)row_tiles * n_chunks;
+  const int n_parts = (S + kChunkKeys - 1) / kChunkKeys;  // each row tile's key range is split n_parts ways
+  const int64_t grid = (int64_t)row_tiles * n_parts;
   if (grid > 0x7FFFFFFF) return DSI_EUNSUPPORTED;
   hipLaunchKernelGGL(prefill_logits_kernel, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, q, w, T, k_rows, S,
-                     row_ks, row_ke, logits, ld, n_chunks);
+                     row_ks, row_ke, logits, ld, n_parts);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
