@@ -250,6 +250,7 @@ def bench_decode(n, steps, warmup, copies=4):
     logits = torch.empty((rows, maxc), dtype=torch.float32, device="cuda")
     idx = torch.empty((rows, K), dtype=torch.int32, device="cuda")
     slots = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(dsi.topk_workspace_bytes(rows, maxc, K), 16), dtype=torch.uint8, device="cuda")
     tl, tt, ts = EventTimer(), EventTimer(), EventTimer()
 
     def step(i, timed):
@@ -260,7 +261,7 @@ def bench_decode(n, steps, warmup, copies=4):
         if timed:
             tl.stop(s)
             s = tt.start()
-        dsi.topk_select(logits, ends, k=K, out=idx)
+        dsi.topk_select(logits, ends, k=K, out=idx, workspace=ws)
         if timed:
             tt.stop(s)
             s = ts.start()

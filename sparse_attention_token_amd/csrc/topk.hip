@@ -6,8 +6,8 @@
 // Radix select, no sort.  Values map to order-preserving unsigned keys (non-finite
 // values are dropped).  One workgroup per row — 1024 threads for rows longer than
 // 16K columns, else 256 threads with a smaller LDS footprint so that several rows
-// share a CU — and the row is read twice, with 16-byte loads, four per thread in
-// flight:
+// share a CU — and the row is read twice, with 16-byte loads, 16 elements per thread
+// in flight:
 //   pass 1 builds an LDS histogram of the top 11 key bits and finds the bin b1 where
 //          the count from the top reaches k;
 //   pass 2 writes every column whose bin is above b1 and collects the columns of bin
@@ -17,28 +17,48 @@
 // slots are reserved per wavefront (ballot + popcount, one LDS atomic).  A row whose
 // boundary bin holds more candidates than LDS can keep (heavy ties) resolves the
 // remaining digits with passes over the row instead.
+//
+// Long rows that are too few to fill the CUs are split between up to 16 workgroups per
+// row, in four launches that communicate through the caller's workspace: per-slice
+// histograms; per row, their sum, the boundary bin and each slice's output offsets; every
+// slice writes its columns above the boundary bin from its offset (no atomics across
+// workgroups) and appends its boundary-bin columns to a per-row candidate list; one
+// workgroup per row resolves the candidates as above.
+#include <algorithm>
+
 #include "common.h"
 
 namespace dsi {
 namespace {
 
 constexpr int kHistBins = 2048;
-constexpr int kUnroll = 4;  // 16-byte loads in flight per thread
 constexpr int kShortRow = 16384;  // rows up to this width use the small configuration
+constexpr int kSplitCap = 12288;  // boundary-bin candidates kept per row when rows are split
+constexpr int kMaxSplit = 16;     // workgroups per row at most
 
 // Workgroup size and the number of boundary-bin candidates kept in LDS.
-template <int THREADS, int CAP>
+// Histograms may keep kCopies lane-interleaved copies of every bin (bin b, copy lane %
+// kCopies at b * kCopies + copy); select_bin sums the copies.  Measured on the indexer
+// workloads, one copy is fastest (more copies cost occupancy and buy nothing).
+template <int THREADS, int CAP, int COPIES>
 struct Cfg {
   static constexpr int kThreads = THREADS;
   static constexpr int kWaves = THREADS / 64;
   static constexpr int kCap = CAP;
+  static constexpr int kCopies = COPIES;
   static constexpr int kBinsPerThread = kHistBins / THREADS;
 };
-using LongRows = Cfg<1024, 12288>;  // 96 KB of candidates
-using ShortRows = Cfg<256, 2048>;   // 16 KB of candidates
+using LongRows = Cfg<1024, 12288, 1>;  // 96 KB of candidates
+using ShortRows = Cfg<256, 2048, 1>;   // 16 KB of candidates
+
+template <int C>
+__device__ __forceinline__ void hist_add(int* h, uint32_t bin, int lane) {
+  atomicAdd(&h[bin * C + (lane & (C - 1))], 1);
+}
 
 template <bool BF16>
 struct Keys {
+  static constexpr int kUnroll = BF16 ? 2 : 4;  // 16-byte loads in flight per thread: 16 elements
   static constexpr int kBits = BF16 ? 16 : 32;
   static constexpr int kElemBytes = BF16 ? 2 : 4;
   static constexpr int kPerVec = 16 / kElemBytes;
@@ -62,26 +82,27 @@ struct Keys {
   }
 };
 
-// Visit every column of [st, en) once: f(active, column, raw bits).  Every lane of
-// the workgroup calls f the same number of times (active = false for padding), so
-// f may use wavefront ballots.  Columns between 16-byte boundaries use 16-byte loads,
-// kUnroll per thread at a time; the unaligned head and tail use element loads.
+// Visit every column of [st, en) once, in batches: f(n, active[], column[], raw[]) with
+// n = 2 (the unaligned head and tail, fewer than 16 bytes each, element loads) and then
+// n = 16 per round of 16-byte loads (K::kUnroll per thread in flight).  Every lane of the workgroup makes the same calls (active = false for
+// padding), so f may use wavefront ballots.
 template <bool BF16, int THREADS, typename F>
 __device__ __forceinline__ void scan_row(const uint8_t* row, int st, int en, int tid, F&& f) {
   using K = Keys<BF16>;
   constexpr int E = K::kPerVec;
+  constexpr int kUnroll = K::kUnroll;
+  constexpr int N = kUnroll * E;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + (uintptr_t)st * K::kElemBytes;
   int c0 = st + (int)(((16 - (addr & 15)) & 15) / K::kElemBytes);
   if (c0 > en) c0 = en;
   const int nvec = (en - c0) / E;
   const int c1 = c0 + nvec * E;
-  // head and tail (fewer than E columns each)
   {
     const int nh = c0 - st, nt = en - c1;
-    const bool ah = tid < nh, at = tid < nt;
-    const int ch = st + tid, ct = c1 + tid;
-    f(ah, ch, ah ? K::load1(row, ch) : 0u);
-    f(at, ct, at ? K::load1(row, ct) : 0u);
+    const bool act[2] = {tid < nh, tid < nt};
+    const int col[2] = {st + tid, c1 + tid};
+    const uint32_t raw[2] = {act[0] ? K::load1(row, col[0]) : 0u, act[1] ? K::load1(row, col[1]) : 0u};
+    f(act, col, raw);
   }
   const uint4* vec = reinterpret_cast<const uint4*>(row + (size_t)c0 * K::kElemBytes);
   for (int base = 0; base < nvec; base += THREADS * kUnroll) {
@@ -91,24 +112,46 @@ __device__ __forceinline__ void scan_row(const uint8_t* row, int st, int en, int
       const int vi = base + u * THREADS + tid;
       if (vi < nvec) v[u] = vec[vi];
     }
+    bool act[N];
+    int col[N];
+    uint32_t raw[N];
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
       const int vi = base + u * THREADS + tid;
       const bool a = vi < nvec;
 #pragma unroll
-      for (int e = 0; e < E; e++) f(a, c0 + vi * E + e, a ? K::elem(v[u], e) : 0u);
+      for (int e = 0; e < E; e++) {
+        act[u * E + e] = a;
+        col[u * E + e] = c0 + vi * E + e;
+        raw[u * E + e] = a ? K::elem(v[u], e) : 0u;
+      }
     }
+    f(act, col, raw);
   }
 }
 
-// Reserve consecutive slots for the lanes whose pred is set; returns this lane's slot.
-__device__ __forceinline__ int wave_reserve(bool pred, int* counter, int lane) {
-  const uint64_t m = __ballot(pred);
+// Reserve consecutive slots for the set predicates of a batch, one LDS atomic per
+// wavefront: pos[i] is this lane's slot for element i (meaningful where pred[i]).
+// Slots follow the element order of the batch, lanes in order within an element.
+template <int N>
+__device__ __forceinline__ void reserve_batch(const bool (&pred)[N], int* counter, int lane, int (&pos)[N]) {
+  uint64_t m[N];
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    m[i] = __ballot(pred[i]);
+    total += __popcll(m[i]);
+  }
   int base = 0;
-  if (lane == 0 && m) base = atomicAdd(counter, __popcll(m));
-  base = __shfl(base, 0);
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  return base + __popcll(m & below);
+  if (total) {  // uniform
+    if (lane == 0) base = atomicAdd(counter, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+  }
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    pos[i] = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[i], 0u));
+    base += __popcll(m[i]);
+  }
 }
 
 // Exclusive suffix sum over threads (thread i gets the sum of `x` of all threads > i).
@@ -129,18 +172,21 @@ __device__ __forceinline__ int block_suffix_excl(int x, int* s_wave, int tid) {
   return v - x + above;
 }
 
-// Given an LDS histogram of nb bins (already filled), find the bin where the count
+// Given an LDS histogram of nb bins (COPIES copies each, already filled), find the bin where the count
 // from the top reaches `need`.  Writes the bin and the count strictly above it to
 // s_sel[0..1]; s_sel[2] = total count.  Each thread owns kBinsPerThread consecutive
 // bins.  Call with all threads; ends synchronised.
-template <typename C>
+template <typename C, int COPIES = C::kCopies>
 __device__ __forceinline__ void select_bin(const int* hist, int nb, int need, int* s_wave, int* s_sel, int tid) {
   constexpr int BPT = C::kBinsPerThread;
   int h[BPT], local = 0;
 #pragma unroll
   for (int j = 0; j < BPT; j++) {
     const int bin = tid * BPT + j;
-    h[j] = bin < nb ? hist[bin] : 0;
+    h[j] = 0;
+    if (bin < nb)
+#pragma unroll
+      for (int c = 0; c < COPIES; c++) h[j] += hist[bin * COPIES + c];
     local += h[j];
   }
   const int above = block_suffix_excl<C::kWaves>(local, s_wave, tid);
@@ -160,91 +206,52 @@ __device__ __forceinline__ void select_bin(const int* hist, int nb, int need, in
   __syncthreads();
 }
 
+// Columns [a, b) of slice g of G of a row's range [st, en): contiguous, nearly equal.
+__device__ __forceinline__ void slice_range(int st, int en, int g, int G, int& a, int& b) {
+  const int w = (en - st + G - 1) / G;
+  a = min(st + g * w, en);
+  b = min(a + w, en);
+}
+
+// The boundary bin b1 (top 11 key bits) is known, `above1` columns above it are written
+// to out[0, above1), and the m columns of bin b1 are in s_ckey/s_ccol (when m <= cap).
+// Resolves the remaining key bits (fp32: 11 then 10, bf16: 5) by histograms over the
+// candidates — or over the row when m > cap — and writes the k - above1 selected
+// boundary-bin columns to out[above1, k).  Call with all threads.
 template <bool BF16, typename C>
-__global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __restrict__ logits, int64_t row_bytes,
-                                                          const int* __restrict__ row_starts,
-                                                          const int* __restrict__ row_ends, int max_width, int k,
-                                                          int* __restrict__ out, int64_t out_ld) {
+__device__ __forceinline__ void resolve_boundary(const uint8_t* row, int st, int en, int k, uint32_t b1, int above1,
+                                                 int m, int cap, const uint32_t* s_ckey, const int* s_ccol,
+                                                 int* s_hist, int* s_wave, int* s_sel, int* s_cnt, int* orow,
+                                                 int tid) {
   using K = Keys<BF16>;
-  __shared__ int s_hist[kHistBins];
-  constexpr int kTkThreads = C::kThreads, kCandCap = C::kCap;
-  __shared__ uint32_t s_ckey[kCandCap];
-  __shared__ int s_ccol[kCandCap];
-  __shared__ int s_wave[C::kWaves];
-  __shared__ int s_sel[4];
-  __shared__ int s_cnt[4];  // 0: written above the boundary, 1: candidates, 2: written from candidates
-
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
-  const uint8_t* row = logits + (int64_t)r * row_bytes;
-  int* orow = out + (int64_t)r * out_ld;
-
-  for (int i = tid; i < kHistBins; i += kTkThreads) s_hist[i] = 0;
-  if (tid < 4) s_cnt[tid] = 0;
-  __syncthreads();
-
-  // pass 1: histogram of the top 11 key bits
-  scan_row<BF16, kTkThreads>(row, st, en, tid, [&](bool a, int, uint32_t raw) {
-    uint32_t key;
-    if (a && K::key(raw, key)) atomicAdd(&s_hist[key >> K::kTopShift], 1);
-  });
-  __syncthreads();
-  select_bin<C>(s_hist, kHistBins, k, s_wave, s_sel, tid);
-  const int total = s_sel[2];
-
-  if (total <= k) {  // every valid value is selected
-    scan_row<BF16, kTkThreads>(row, st, en, tid, [&](bool a, int c, uint32_t raw) {
-      uint32_t key;
-      const bool take = a && K::key(raw, key);
-      const int pos = wave_reserve(take, &s_cnt[0], lane);
-      if (take && pos < k) orow[pos] = c - st;
-    });
-    for (int j = total + tid; j < k; j += kTkThreads) orow[j] = -1;
-    return;
-  }
-
-  const uint32_t b1 = (uint32_t)s_sel[0];
-  const int above1 = s_sel[1];
-  // pass 2: columns above the boundary bin are selected; the boundary bin's are candidates
-  scan_row<BF16, kTkThreads>(row, st, en, tid, [&](bool a, int c, uint32_t raw) {
-    uint32_t key = 0;
-    const bool valid = a && K::key(raw, key);
-    const uint32_t d = key >> K::kTopShift;
-    const bool gt = valid && d > b1, eq = valid && d == b1;
-    const int pos = wave_reserve(gt, &s_cnt[0], lane);
-    if (gt && pos < k) orow[pos] = c - st;
-    const int slot = wave_reserve(eq, &s_cnt[1], lane);
-    if (eq && slot < kCandCap) {
-      s_ckey[slot] = key;
-      s_ccol[slot] = c;
-    }
-  });
-  __syncthreads();
-  const int m = s_cnt[1];
+  constexpr int kTkThreads = C::kThreads;
+  const int lane = tid & 63;
   int need = k - above1;
-
-  // remaining digits below the top 11 bits: fp32 (11, 10), bf16 (5)
   constexpr int kLow = K::kTopShift;
   const int nd = BF16 ? 1 : 2;
   const int shifts[2] = {BF16 ? 0 : 10, 0};
   const int widths[2] = {BF16 ? 5 : 11, 10};
   uint32_t prefix = b1 << kLow;  // known high bits of the threshold key
-  const bool in_lds = m <= kCandCap;
+  const bool in_lds = m <= cap;
   for (int p = 0; p < nd; p++) {
     const int sh = shifts[p], wd = widths[p], nb = 1 << wd;
     const int hs = sh + wd;  // bits at and above hs are fixed by `prefix`
-    for (int i = tid; i < nb; i += kTkThreads) s_hist[i] = 0;
+    for (int i = tid; i < nb * C::kCopies; i += kTkThreads) s_hist[i] = 0;
     __syncthreads();
     if (in_lds) {
       for (int i = tid; i < m; i += kTkThreads) {
         const uint32_t key = s_ckey[i];
-        if ((key >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1);
+        if ((key >> hs) == (prefix >> hs)) hist_add<C::kCopies>(s_hist, (key >> sh) & (nb - 1), lane);
       }
     } else {
-      scan_row<BF16, kTkThreads>(row, st, en, tid, [&](bool a, int, uint32_t raw) {
-        uint32_t key;
-        if (a && K::key(raw, key) && (key >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1);
+      scan_row<BF16, kTkThreads>(row, st, en, tid, [&](const auto& act, const auto&, const auto& raw) {
+        constexpr int n = sizeof(act) / sizeof(act[0]);
+#pragma unroll
+        for (int i = 0; i < n; i++) {
+          uint32_t key;
+          if (act[i] && K::key(raw[i], key) && (key >> hs) == (prefix >> hs))
+            hist_add<C::kCopies>(s_hist, (key >> sh) & (nb - 1), lane);
+        }
       });
     }
     __syncthreads();
@@ -254,40 +261,364 @@ __global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __rest
     __syncthreads();
   }
   // tau = prefix: select the boundary-bin keys above tau, and `need` of those equal to it
-  const int base = above1;  // slots [0, above1) hold the columns above the boundary bin
+  const int base = above1;
   const int n_above_tau = (k - base) - need;
+  auto emit = [&](const auto& gt, const auto& eq, const auto& col) {
+    constexpr int n = sizeof(gt) / sizeof(gt[0]);
+    int pg[n], pe[n];
+    reserve_batch(gt, &s_cnt[2], lane, pg);
+    reserve_batch(eq, &s_cnt[3], lane, pe);
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      if (gt[i] && base + pg[i] < k) orow[base + pg[i]] = col[i] - st;
+      if (eq[i] && pe[i] < need && base + n_above_tau + pe[i] < k) orow[base + n_above_tau + pe[i]] = col[i] - st;
+    }
+  };
   if (in_lds) {
     for (int i0 = 0; i0 < m; i0 += kTkThreads) {
       const int i = i0 + tid;
       const bool a = i < m;
       const uint32_t key = a ? s_ckey[i] : 0u;
-      const bool gt = a && key > prefix, eq = a && key == prefix;
-      const int pg = wave_reserve(gt, &s_cnt[2], lane);
-      if (gt && base + pg < k) orow[base + pg] = s_ccol[i] - st;
-      const int pe = wave_reserve(eq, &s_cnt[3], lane);
-      if (eq && pe < need && base + n_above_tau + pe < k) orow[base + n_above_tau + pe] = s_ccol[i] - st;
+      const bool gt[1] = {a && key > prefix}, eq[1] = {a && key == prefix};
+      const int col[1] = {a ? s_ccol[i] : 0};
+      emit(gt, eq, col);
     }
   } else {
-    scan_row<BF16, kTkThreads>(row, st, en, tid, [&](bool a, int c, uint32_t raw) {
-      uint32_t key = 0;
-      const bool valid = a && K::key(raw, key) && (key >> kLow) == b1;
-      const bool gt = valid && key > prefix, eq = valid && key == prefix;
-      const int pg = wave_reserve(gt, &s_cnt[2], lane);
-      if (gt && base + pg < k) orow[base + pg] = c - st;
-      const int pe = wave_reserve(eq, &s_cnt[3], lane);
-      if (eq && pe < need && base + n_above_tau + pe < k) orow[base + n_above_tau + pe] = c - st;
+    scan_row<BF16, kTkThreads>(row, st, en, tid, [&](const auto& act, const auto& col, const auto& raw) {
+      constexpr int n = sizeof(act) / sizeof(act[0]);
+      bool gt[n], eq[n];
+#pragma unroll
+      for (int i = 0; i < n; i++) {
+        uint32_t key = 0;
+        const bool valid = act[i] && K::key(raw[i], key) && (key >> kLow) == b1;
+        gt[i] = valid && key > prefix;
+        eq[i] = valid && key == prefix;
+      }
+      emit(gt, eq, col);
     });
   }
+}
+
+// ---------------------------------------------------------------- one workgroup per row
+template <bool BF16, typename C>
+__global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __restrict__ logits, int64_t row_bytes,
+                                                          const int* __restrict__ row_starts,
+                                                          const int* __restrict__ row_ends, int max_width, int k,
+                                                          int* __restrict__ out, int64_t out_ld) {
+  using K = Keys<BF16>;
+  __shared__ int s_hist[kHistBins * C::kCopies];
+  constexpr int kTkThreads = C::kThreads, kCandCap = C::kCap;
+  __shared__ uint32_t s_ckey[kCandCap];
+  __shared__ int s_ccol[kCandCap];
+  __shared__ int s_wave[C::kWaves];
+  __shared__ int s_sel[4];
+  __shared__ int s_cnt[4];  // 0: written above the boundary, 1: candidates, 2/3: written from candidates
+
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int st = row_starts ? max(row_starts[r], 0) : 0;
+  const int en = max(min(row_ends[r], max_width), st);
+  const uint8_t* row = logits + (int64_t)r * row_bytes;
+  int* orow = out + (int64_t)r * out_ld;
+
+  for (int i = tid; i < kHistBins * C::kCopies; i += kTkThreads) s_hist[i] = 0;
+  if (tid < 4) s_cnt[tid] = 0;
+  __syncthreads();
+
+  // pass 1: histogram of the top 11 key bits
+  scan_row<BF16, kTkThreads>(row, st, en, tid, [&](const auto& act, const auto&, const auto& raw) {
+    constexpr int n = sizeof(act) / sizeof(act[0]);
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      uint32_t key;
+      if (act[i] && K::key(raw[i], key)) hist_add<C::kCopies>(s_hist, key >> K::kTopShift, lane);
+    }
+  });
+  __syncthreads();
+  select_bin<C>(s_hist, kHistBins, k, s_wave, s_sel, tid);
+  const int total = s_sel[2];
+  const uint32_t b1 = (uint32_t)s_sel[0];
+  const int above1 = s_sel[1];
+  const bool all = total <= k;  // every valid value is selected
+
+  // pass 2: columns above the boundary bin (or every valid column) are written; the
+  // boundary bin's are candidates
+  scan_row<BF16, kTkThreads>(row, st, en, tid, [&](const auto& act, const auto& col, const auto& raw) {
+    constexpr int n = sizeof(act) / sizeof(act[0]);
+    bool gt[n], eq[n];
+    uint32_t keys[n];
+    int pos[n], slot[n];
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      uint32_t key = 0;
+      const bool valid = act[i] && K::key(raw[i], key);
+      const uint32_t d = key >> K::kTopShift;
+      gt[i] = valid && (all || d > b1);
+      eq[i] = valid && !all && d == b1;
+      keys[i] = key;
+    }
+    reserve_batch(gt, &s_cnt[0], lane, pos);
+    reserve_batch(eq, &s_cnt[1], lane, slot);
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      if (gt[i] && pos[i] < k) orow[pos[i]] = col[i] - st;
+      if (eq[i] && slot[i] < kCandCap) {
+        s_ckey[slot[i]] = keys[i];
+        s_ccol[slot[i]] = col[i];
+      }
+    }
+  });
+  if (all) {
+    for (int j = total + tid; j < k; j += kTkThreads) orow[j] = -1;
+    return;
+  }
+  __syncthreads();
+  resolve_boundary<BF16, C>(row, st, en, k, b1, above1, s_cnt[1], kCandCap, s_ckey, s_ccol, s_hist, s_wave, s_sel,
+                            s_cnt, orow, tid);
+}
+
+// ---------------------------------------------------------------- long rows split G ways
+// Workspace: per (row, slice) an 11-bit histogram; per row {b1, above1, total, m}; per row
+// up to kSplitCap boundary-bin candidates (key, column).
+using SliceCfg = Cfg<512, 0, 1>;
+
+struct SplitWs {
+  int* hist;      // [rows][G][2048]
+  int* meta;      // [rows][4]: b1, above1, total, m
+  int* off;       // [rows][kMaxSplit][4]: columns of the earlier slices above b1, at b1, valid
+  uint32_t* key;  // [rows][kSplitCap]
+  int* col;       // [rows][kSplitCap]
+};
+
+__host__ __device__ inline size_t split_ws_bytes(int rows, int G) {
+  return (size_t)rows * G * kHistBins * 4 + (size_t)rows * 16 + (size_t)rows * kMaxSplit * 16 +
+         (size_t)rows * kSplitCap * 8;
+}
+
+__device__ __forceinline__ SplitWs split_ws(void* ws, int rows, int G) {
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  SplitWs w;
+  w.hist = reinterpret_cast<int*>(p);
+  p += (size_t)rows * G * kHistBins * 4;
+  w.meta = reinterpret_cast<int*>(p);
+  p += (size_t)rows * 16;
+  w.off = reinterpret_cast<int*>(p);
+  p += (size_t)rows * kMaxSplit * 16;
+  w.key = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * kSplitCap * 4;
+  w.col = reinterpret_cast<int*>(p);
+  return w;
+}
+
+// Step 1: the 11-bit histogram of each slice.  grid = (G, rows).
+template <bool BF16>
+__global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
+    const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
+    const int* __restrict__ row_ends, int max_width, void* ws, int rows, int G) {
+  using K = Keys<BF16>;
+  constexpr int kC = SliceCfg::kCopies;
+  __shared__ int s_hist[kHistBins * kC];
+  const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int st = row_starts ? max(row_starts[r], 0) : 0;
+  const int en = max(min(row_ends[r], max_width), st);
+  int a, b;
+  slice_range(st, en, g, G, a, b);
+  for (int i = tid; i < kHistBins * kC; i += SliceCfg::kThreads) s_hist[i] = 0;
+  __syncthreads();
+  scan_row<BF16, SliceCfg::kThreads>(logits + (int64_t)r * row_bytes, a, b, tid,
+                                     [&](const auto& act, const auto&, const auto& raw) {
+    constexpr int n = sizeof(act) / sizeof(act[0]);
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      uint32_t key;
+      if (act[i] && K::key(raw[i], key)) hist_add<kC>(s_hist, key >> K::kTopShift, lane);
+    }
+  });
+  __syncthreads();
+  int* dst = split_ws(ws, rows, G).hist + ((int64_t)r * G + g) * kHistBins;
+  for (int i = tid; i < kHistBins; i += SliceCfg::kThreads) {
+    int h = 0;
+#pragma unroll
+    for (int c = 0; c < kC; c++) h += s_hist[i * kC + c];
+    dst[i] = h;
+  }
+}
+
+// Step 2: one workgroup per row sums the slice histograms, finds the boundary bin b1 and
+// gives every slice the number of columns the slices before it hold above b1, at b1, and
+// valid (the offsets its writes start at).  grid = rows.
+__global__ __launch_bounds__(LongRows::kThreads) void topk_split_reduce_kernel(void* ws, int rows, int G, int k) {
+  using C = LongRows;
+  constexpr int kT = C::kThreads;
+  static_assert(C::kWaves >= kMaxSplit, "one wavefront per slice");
+  __shared__ int s_all[kMaxSplit][kHistBins];  // the slice histograms
+  __shared__ int s_hist[kHistBins];            // their sum
+  __shared__ int s_wave[C::kWaves];
+  __shared__ int s_sel[4];
+  __shared__ int s_slice[3][kMaxSplit];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SplitWs w = split_ws(ws, rows, G);
+  const int* hist = w.hist + (int64_t)r * G * kHistBins;
+  for (int i = tid; i < kHistBins; i += kT) {
+    int v[kMaxSplit], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxSplit; j++) v[j] = j < G ? hist[j * kHistBins + i] : 0;  // all loads in flight
+#pragma unroll
+    for (int j = 0; j < kMaxSplit; j++) {
+      s_all[j][i] = v[j];
+      sum += v[j];
+    }
+    s_hist[i] = sum;
+  }
+  __syncthreads();
+  select_bin<C, 1>(s_hist, kHistBins, k, s_wave, s_sel, tid);
+  const uint32_t b1 = (uint32_t)s_sel[0];
+  if (wave < kMaxSplit) {  // wavefront j: columns of slice j above b1, at b1, valid
+    int gt = 0, eq = 0, valid = 0;
+    for (int i = lane; i < kHistBins; i += 64) {
+      const int h = s_all[wave][i];
+      valid += h;
+      gt += (uint32_t)i > b1 ? h : 0;
+      eq += (uint32_t)i == b1 ? h : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      gt += __shfl_xor(gt, o);
+      eq += __shfl_xor(eq, o);
+      valid += __shfl_xor(valid, o);
+    }
+    if (lane == 0) {
+      s_slice[0][wave] = gt;
+      s_slice[1][wave] = eq;
+      s_slice[2][wave] = valid;
+    }
+  }
+  __syncthreads();
+  if (tid < 3) {  // exclusive prefix over the slices
+    int acc = 0;
+    for (int j = 0; j < G; j++) {
+      w.off[((int64_t)r * kMaxSplit + j) * 4 + tid] = acc;
+      acc += s_slice[tid][j];
+    }
+  }
+  if (tid == 0) {
+    int* meta = w.meta + (int64_t)r * 4;
+    meta[0] = (int)b1;
+    meta[1] = s_sel[1];
+    meta[2] = s_sel[2];
+    meta[3] = s_hist[b1];
+  }
+}
+
+// Step 3: every slice writes its columns above the boundary bin from its offset (or, when
+// every valid value is selected, all its valid columns, and the last slice the -1
+// padding); its boundary-bin columns go to the row's candidate list from its offset.
+// grid = (G, rows).
+template <bool BF16>
+__global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
+    const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
+    const int* __restrict__ row_ends, int max_width, int k, int* __restrict__ out, int64_t out_ld, void* ws, int rows,
+    int G) {
+  using K = Keys<BF16>;
+  constexpr int kT = SliceCfg::kThreads;
+  __shared__ int s_cnt[2];
+  const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const SplitWs w = split_ws(ws, rows, G);
+  const int* meta = w.meta + (int64_t)r * 4;
+  const int* off = w.off + ((int64_t)r * kMaxSplit + g) * 4;
+  const uint32_t b1 = (uint32_t)meta[0];
+  const int total = meta[2];
+  const bool all = total <= k;
+  const int out_base = all ? off[2] : off[0];
+  const int cand_base = off[1];
+  if (tid < 2) s_cnt[tid] = 0;
+  __syncthreads();
+  const int st = row_starts ? max(row_starts[r], 0) : 0;
+  const int en = max(min(row_ends[r], max_width), st);
+  int a, b;
+  slice_range(st, en, g, G, a, b);
+  int* orow = out + (int64_t)r * out_ld;
+  uint32_t* ckey = w.key + (int64_t)r * kSplitCap;
+  int* ccol = w.col + (int64_t)r * kSplitCap;
+  scan_row<BF16, kT>(logits + (int64_t)r * row_bytes, a, b, tid, [&](const auto& act, const auto& col, const auto& raw) {
+    constexpr int n = sizeof(act) / sizeof(act[0]);
+    bool gt[n], eq[n];
+    uint32_t keys[n];
+    int pos[n], slot[n];
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      uint32_t key = 0;
+      const bool valid = act[i] && K::key(raw[i], key);
+      const uint32_t d = key >> K::kTopShift;
+      gt[i] = valid && (all || d > b1);
+      eq[i] = valid && !all && d == b1;
+      keys[i] = key;
+    }
+    reserve_batch(gt, &s_cnt[0], lane, pos);
+    reserve_batch(eq, &s_cnt[1], lane, slot);
+#pragma unroll
+    for (int i = 0; i < n; i++) {
+      if (gt[i] && out_base + pos[i] < k) orow[out_base + pos[i]] = col[i] - st;
+      if (eq[i] && cand_base + slot[i] < kSplitCap) {
+        ckey[cand_base + slot[i]] = keys[i];
+        ccol[cand_base + slot[i]] = col[i];
+      }
+    }
+  });
+  if (all && g == G - 1)
+    for (int j = total + tid; j < k; j += kT) orow[j] = -1;
+}
+
+// Step 4: one workgroup per row resolves the boundary bin from the candidate list.
+template <bool BF16>
+__global__ __launch_bounds__(LongRows::kThreads) void topk_split_resolve_kernel(
+    const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
+    const int* __restrict__ row_ends, int max_width, int k, int* __restrict__ out, int64_t out_ld, void* ws, int rows,
+    int G) {
+  using C = LongRows;
+  static_assert(kSplitCap <= C::kCap, "the candidate list must fit in LDS");
+  __shared__ int s_hist[kHistBins * C::kCopies];
+  __shared__ uint32_t s_ckey[kSplitCap];
+  __shared__ int s_ccol[kSplitCap];
+  __shared__ int s_wave[C::kWaves];
+  __shared__ int s_sel[4];
+  __shared__ int s_cnt[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const SplitWs w = split_ws(ws, rows, G);
+  const int* meta = w.meta + (int64_t)r * 4;
+  const uint32_t b1 = (uint32_t)meta[0];
+  const int above1 = meta[1], total = meta[2], m = meta[3];
+  if (total <= k) return;  // uniform: the slices wrote everything
+  if (m <= kSplitCap)
+    for (int i = tid; i < m; i += C::kThreads) {
+      s_ckey[i] = w.key[(int64_t)r * kSplitCap + i];
+      s_ccol[i] = w.col[(int64_t)r * kSplitCap + i];
+    }
+  if (tid < 4) s_cnt[tid] = 0;
+  __syncthreads();
+  const int st = row_starts ? max(row_starts[r], 0) : 0;
+  const int en = max(min(row_ends[r], max_width), st);
+  resolve_boundary<BF16, C>(logits + (int64_t)r * row_bytes, st, en, k, b1, above1, m, kSplitCap, s_ckey, s_ccol,
+                            s_hist, s_wave, s_sel, s_cnt, out + (int64_t)r * out_ld, tid);
+}
+
+// Workgroups per row: split long rows when there are too few rows to fill the CUs.
+inline int split_count(int rows, int max_width) {
+  if (max_width <= kShortRow || rows >= 512) return 1;
+  int g = (512 + rows - 1) / rows;
+  g = std::min(g, kMaxSplit);
+  g = std::min(g, (max_width + 8191) / 8192);  // at least ~8K columns per slice
+  return std::max(g, 1);
 }
 
 }  // namespace
 }  // namespace dsi
 
 extern "C" size_t dsi_topk_workspace_bytes(int32_t rows, int32_t max_width, int32_t k) {
-  (void)rows;
-  (void)max_width;
+  using namespace dsi;
   (void)k;
-  return 0;
+  if (rows <= 0 || max_width <= 0) return 0;
+  const int G = split_count(rows, max_width);
+  return G > 1 ? split_ws_bytes(rows, G) : 0;
 }
 
 extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, int32_t rows,
@@ -295,20 +626,46 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
                                int32_t* out, int64_t out_ld, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   using namespace dsi;
-  (void)workspace;
   if (dtype != DSI_F32 && dtype != DSI_BF16) return DSI_EUNSUPPORTED;
   if (k < 1 || k > DSI_MAX_TOPK) return DSI_EUNSUPPORTED;
   if (rows < 0 || max_width < 0 || ld < max_width || out_ld < k) return DSI_EINVAL;
-  if (workspace_bytes < dsi_topk_workspace_bytes(rows, max_width, k)) return DSI_EWORKSPACE;
+  const size_t need = dsi_topk_workspace_bytes(rows, max_width, k);
+  if (workspace_bytes < need || (need && !workspace)) return DSI_EWORKSPACE;
   if (rows == 0) return DSI_OK;
   if (!logits || !row_ends || !out) return DSI_EINVAL;
   if (dtype == DSI_F32 && (reinterpret_cast<uintptr_t>(logits) & 3)) return DSI_EALIGN;
   if (dtype == DSI_BF16 && (reinterpret_cast<uintptr_t>(logits) & 1)) return DSI_EALIGN;
-  if (reinterpret_cast<uintptr_t>(out) & 3) return DSI_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(out) & 3) || (reinterpret_cast<uintptr_t>(workspace) & 15)) return DSI_EALIGN;
+  if (rows > 65535) return DSI_EUNSUPPORTED;
   const int64_t row_bytes = ld * (dtype == DSI_F32 ? 4 : 2);
   const uint8_t* src = reinterpret_cast<const uint8_t*>(logits);
+  const int G = split_count(rows, max_width);
+  const bool bf = dtype == DSI_BF16;
+  if (G > 1) {
+    const dim3 grid((unsigned)G, (unsigned)rows);
+    if (bf) {
+      hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
+                         row_starts, row_ends, max_width, workspace, rows, G);
+      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream, workspace,
+                         rows, G, k);
+      hipLaunchKernelGGL(topk_slice_select_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
+                         row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
+      hipLaunchKernelGGL(topk_split_resolve_kernel<true>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
+                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
+    } else {
+      hipLaunchKernelGGL(topk_slice_hist_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
+                         row_starts, row_ends, max_width, workspace, rows, G);
+      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream, workspace,
+                         rows, G, k);
+      hipLaunchKernelGGL(topk_slice_select_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
+                         row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
+      hipLaunchKernelGGL(topk_split_resolve_kernel<false>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
+                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
+    }
+    return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+  }
   const bool small = max_width <= kShortRow;
-  if (dtype == DSI_F32) {
+  if (!bf) {
     if (small)
       hipLaunchKernelGGL((topk_kernel<false, ShortRows>), dim3((unsigned)rows), dim3(ShortRows::kThreads), 0, stream,
                          src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld);

@@ -101,7 +101,12 @@ def test_topk_validation():
     assert f(A16 + 2, 0, 10, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EALIGN
     assert f(A16 + 1, 1, 10, 2, None, A16, 10, 4, A16, 4, None, 0, None) == EALIGN
     assert f(None, 0, 10, 0, None, None, 10, 4, None, 4, None, 0, None) == 0
-    assert L.dsi_topk_workspace_bytes(64, 131072, 2048) >= 0
+    assert L.dsi_topk_workspace_bytes(64, 131072, 2048) > 0  # few long rows are split: workspace needed
+    assert L.dsi_topk_workspace_bytes(2048, 8192, 2048) == 0  # one workgroup per row
+    assert f(A16, 0, 40000, 4, None, A16, 40000, 2048, A16, 2048, None, 0, None) == EWS
+    need = L.dsi_topk_workspace_bytes(4, 40000, 2048)
+    assert f(A16, 0, 40000, 4, None, A16, 40000, 2048, A16, 2048, A16, need - 1, None) == EWS
+    assert f(A16, 0, 40000, 4, None, A16, 40000, 2048, A16, 2048, A16 + 4, need, None) == EALIGN
 
 
 def test_expand_validation():

@@ -223,6 +223,37 @@ def test_topk_bf16_exact_values():
         assert np.array_equal(np.sort(f[r, got[r][got[r] >= 0]]), np.sort(f[r, ref[r][ref[r] >= 0]]))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_topk_split_long_rows(bf16):
+    """Few long rows are split between workgroups; cover the take-all, all-invalid, heavy-tie
+    (boundary bin larger than the candidate list) and ordinary rows."""
+    rng = np.random.default_rng(21 + bf16)
+    rows, width = 8, 50000
+    x = (rng.standard_normal((rows, width)) * 40).astype(np.float32)
+    x[1, 1000:] = -np.inf           # 1000 valid: take all, pad with -1
+    x[2, :] = np.nan                # nothing valid
+    x[3, :] = 2.5                   # one value everywhere
+    x[4, ::2] = 7.0                 # a heavy tie inside the top 2048
+    x[5] = np.round(x[5] / 8) * 8   # many ties
+    ends = np.array([width, width, width, width, width, 30001, 20000, 49999], np.int32)
+    starts = np.array([0, 0, 0, 0, 3, 17, 0, 12345], np.int32)
+    if bf16:
+        bits = synth._bf16_bits(x)
+        vals = bf16_value(bits)
+        ref = oracle.topk_select(bits, ends, 2048, starts=starts, bf16=True)
+        got = host(dsi.topk_select(dev(bits), dev(ends), k=2048, row_starts=dev(starts)))
+    else:
+        vals = x
+        ref = oracle.topk_select(x, ends, 2048, starts=starts)
+        got = host(dsi.topk_select(dev(x), dev(ends), k=2048, row_starts=dev(starts)))
+    for r in range(rows):
+        check_selection(got[r], ref[r], vals[r], tol_fn=lambda v: 0.0 * v, start=starts[r], end=ends[r])
+        g = got[r][got[r] >= 0] + starts[r]
+        o = ref[r][ref[r] >= 0] + starts[r]
+        assert np.array_equal(np.sort(vals[r, g]), np.sort(vals[r, o]))
+    assert np.all(got[2] == -1) and np.sum(got[1] >= 0) == 1000
+
+
 def test_topk_strided_rows_and_out():
     rng = np.random.default_rng(8)
     x = (rng.standard_normal((4, 5000)) * 3).astype(np.float32)
