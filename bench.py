@@ -88,12 +88,13 @@ def timed_ms(fn, reps=5):
 
 
 def measure_ceilings():
-    """Register-only MFMA loops (f16 16x16x32, FP8 16x16x128), a streaming read of 4 GiB (16x the 256 MB
+    """Register-only MFMA loops (f16 16x16x32 and 32x32x16, FP8 16x16x128), a streaming read of 4 GiB (16x the 256 MB
     Infinity Cache) and a 1 GiB copy.  The copy is also the calibration dispatch of the byte counters."""
     out = {}
     wg = 256 * 8
     sink = torch.empty(wg * ceiling.THREADS, dtype=torch.float32, device="cuda")
-    for kind, name, iters in ((0, "mfma_f16_tflops", 1000), (1, "mfma_fp8_tflops", 500)):
+    for kind, name, iters in ((0, "mfma_f16_tflops", 1000), (2, "mfma_f16_32x32x16_tflops", 1000),
+                              (1, "mfma_fp8_tflops", 500)):
         flop = [0]
 
         def run():
@@ -415,7 +416,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_logits_kernel", "achieved": round(achieved, 1),
                      "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / F16_PEAK_TFLOPS, 4),
                      "traffic": committed_traffic(), "algorithmic_flops_per_launch": flops,
-                     "mfma_dtype": "f16 (v_mfma_f32_16x16x32_f16)",
+                     "mfma_dtype": "f16 (v_mfma_f32_32x32x16_f16)",
                      "frac_of_fp8_peak": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "measured_ceiling": ceil},
         "cpu_baseline": cpu,

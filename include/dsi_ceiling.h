@@ -34,11 +34,13 @@ extern "C" {
 
 /* Register-only matrix-core loop.  kind 0 = v_mfma_f32_16x16x32_f16 (16,384
  * flop per instruction), kind 1 = v_mfma_scale_f32_16x16x128_f8f6f4 with FP8
- * E4M3 operands (65,536 flop per instruction).  `workgroups` workgroups of 256
- * threads each run `iters` rounds of 16 instructions per wavefront, so the
- * total is workgroups * 4 * iters * 16 instructions.  `sink` receives one
- * float per thread (workgroups * 256 floats) so that nothing is optimised away.
- * EINVAL: kind not 0/1, workgroups < 1, iters < 1, sink NULL. */
+ * E4M3 operands (65,536 flop per instruction), both with 16 chains per
+ * wavefront; kind 2 = v_mfma_f32_32x32x16_f16 (32,768 flop per instruction)
+ * with 8 chains.  `workgroups` workgroups of 256 threads each run `iters`
+ * rounds of one instruction per chain per wavefront, so the total is
+ * workgroups * 4 * iters * chains instructions.  `sink` receives one float
+ * per thread (workgroups * 256 floats) so that nothing is optimised away.
+ * EINVAL: kind not 0..2, workgroups < 1, iters < 1, sink NULL. */
 DSIC_API int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, float* sink, hipStream_t stream);
 
 /* Stream-read `bytes` bytes from `src` (16-byte aligned, bytes a multiple of

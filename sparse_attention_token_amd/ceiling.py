@@ -8,7 +8,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsi_ceiling.so")
 THREADS = 256
-FLOP_PER_INSTR = {0: 16 * 16 * 32 * 2, 1: 16 * 16 * 128 * 2}  # f16 16x16x32, FP8 16x16x128
+FLOP_PER_INSTR = {0: 16 * 16 * 32 * 2, 1: 16 * 16 * 128 * 2, 2: 32 * 32 * 16 * 2}  # f16 16x16x32, FP8 16x16x128,
+CHAINS = {0: 16, 1: 16, 2: 8}                                                      # f16 32x32x16
 
 _p, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGNATURES = {
@@ -46,7 +47,7 @@ def mfma_loop(kind: int, workgroups: int, iters: int, sink: torch.Tensor) -> int
     """Enqueue the register-only loop; returns its flop count."""
     assert sink.dtype == torch.float32 and sink.numel() >= workgroups * THREADS and sink.is_contiguous()
     _check(lib().dsic_mfma_loop(kind, workgroups, iters, sink.data_ptr(), _stream(sink)), "dsic_mfma_loop")
-    return workgroups * 4 * iters * 16 * FLOP_PER_INSTR[kind]
+    return workgroups * 4 * iters * CHAINS[kind] * FLOP_PER_INSTR[kind]
 
 
 def stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor) -> int:

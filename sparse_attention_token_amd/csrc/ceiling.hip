@@ -9,6 +9,7 @@
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -47,6 +48,30 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float* __restrict__
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// The 32x32x16 f16 form (32,768 flop per instruction) with 8 independent chains; the
+// accumulators (128 registers) live in the accumulation registers.
+constexpr int kChains32 = 8;
+
+__global__ __launch_bounds__(kThreads) void mfma32_loop_kernel(float* __restrict__ sink, int iters) {
+  f32x16 c[kChains32];
+#pragma unroll
+  for (int j = 0; j < kChains32; j++) c[j] = f32x16{};
+  f16x8 a16, b16;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    a16[j] = (_Float16)((threadIdx.x & 7) * 0.125f + j * 0.0625f);
+    b16[j] = (_Float16)(0.5f + j * 0.03125f);
+  }
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int j = 0; j < kChains32; j++) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a16, b16, c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kChains32; j++) s += c[j][0] + c[j][5] + c[j][10] + c[j][15];
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
                                                                uint32_t* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * kThreads;
@@ -72,8 +97,10 @@ int launched() { return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH; 
 }  // namespace
 
 extern "C" int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, float* sink, hipStream_t stream) {
-  if ((kind != 0 && kind != 1) || workgroups < 1 || iters < 1 || !sink) return DSI_EINVAL;
-  if (kind == 0)
+  if (kind < 0 || kind > 2 || workgroups < 1 || iters < 1 || !sink) return DSI_EINVAL;
+  if (kind == 2)
+    hipLaunchKernelGGL(mfma32_loop_kernel, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
+  else if (kind == 0)
     hipLaunchKernelGGL(mfma_loop_kernel<0>, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
   else
     hipLaunchKernelGGL(mfma_loop_kernel<1>, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);

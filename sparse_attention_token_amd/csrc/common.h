@@ -216,4 +216,71 @@ __device__ __forceinline__ void scatter_chunk(uint8_t* lds_codes, float* lds_sca
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// 32x32x16 layout (v_mfma_f32_32x32x16_f16), used where a wavefront scores one query row
+// against 32-key groups:
+//   A = 32 heads x 16 dims of q   (lane l: head l%32, 8 dims of lane half h = l/32)
+//   B = 16 dims x 32 keys of K    (lane l: key  l%32, the same 8 dims)
+//   C = 32 heads x 32 keys, lane l holds heads 8*(i/4) + 4*h + i%4 (i < 16) of key l%32.
+// Lane half h owns dims [64h, 64h+64) of the 128 and feeds 8 of them to each of eight
+// slices.  Two head blocks cover the 64 heads, so 16 MFMAs leave each lane 32 heads of one
+// key: the head-weighted sum is 32 FMAs, and the other lane half holds the other 32 heads.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// q[row] decoded into this lane's A fragments: head hb*32 + l%32, dims [64h + 8s, +8) for
+// slice s.
+struct Q32 {
+  f16x8 a[2][8];
+};
+
+__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint4 x = p[j];
+      f.a[hb][2 * j] = e4m3x8_to_f16x8(x.x, x.y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x.z, x.w);
+    }
+  }
+}
+
+// The weights of the 32 heads this lane holds in C: w[hb][i] is head hb*32 + 8*(i/4) + 4h + i%4.
+struct W32 {
+  float w[2][16];
+};
+
+__device__ __forceinline__ void load_w32(W32& f, const uint16_t* w_row, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
+      f.w[hb][4 * b + 0] = bf16_to_f32(x.x & 0xFFFFu);
+      f.w[hb][4 * b + 1] = bf16_to_f32(x.x >> 16);
+      f.w[hb][4 * b + 2] = bf16_to_f32(x.y & 0xFFFFu);
+      f.w[hb][4 * b + 3] = bf16_to_f32(x.y >> 16);
+    }
+}
+
+// B fragments of one 32-key group from the f16 tile: key l%32, dims [64h + 8s, +8).
+struct K32 {
+  f16x8 b[8];
+};
+
+// Sum of the two lane halves for two 32-key groups at once: on return lane l holds the
+// full sum of key l of the 64-key tile (group l/32, key l%32).
+__device__ __forceinline__ float combine_halves(float g0, float g1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(g0), __float_as_uint(g1), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace dsi

@@ -113,28 +113,119 @@ __device__ __forceinline__ void load_q_lds(QFrag& f, const uint8_t* s_q, int lan
 }
 
 // ------------------------------------------------------------------ paged decode
-// grid = (ceil(max_context_len / 256), B).  Dynamic LDS: the 256 gathered keys, then
-// up to two of the request's q rows (8 KB each), all loaded by DMA and waited for
-// once.  Rows are then scored one after the other against the staged keys (rows 2
-// and 3 of a four-row request are staged after the first two are done).
-__global__ __launch_bounds__(256) void paged_decode_kernel(
+// A workgroup (4 wavefronts) streams a job of up to 8 chunks of 256 keys of one request
+// through a ring of LDS buffers: the DMA gathers of the next chunks are in flight while
+// one chunk is scored, and the request's q rows stay decoded in VGPRs for the whole job.
+// Rows are spread over the wavefronts (1 row: 4 wavefronts share each chunk's keys; 2
+// rows: 2 wavefronts per row; 3-4 rows: one wavefront per row, all keys).  Each key row
+// lands in LDS as nine 16-byte pieces at a 144-byte stride (bytes 0..127, then 116..131
+// so that the scale sits at byte 140 and nothing past the row is read), which makes
+// every B-fragment read a conflict-free 16-byte LDS load.
+constexpr int kDcChunk = 256;                       // keys per LDS buffer
+constexpr int kDcRow = 144;                         // LDS bytes per key
+constexpr int kDcBuf = kDcChunk * kDcRow;           // 36864
+constexpr int kDcSlabsPerWave = kDcBuf / 1024 / 4;  // 9 DMA instructions per wavefront per chunk
+constexpr int kDcJob = 8;                           // chunks per workgroup
+constexpr int kDcSegs = kDcJob * kDcChunk / 16;     // 16-token segments per job
+
+// Issue this wavefront's DMA pieces of one chunk.  Piece s of the chunk (16 bytes) is key
+// s/9, piece s%9; absent segments read the pool's first bytes (their keys score -inf).
+// The loads are issued as inline assembly (M0 = the LDS destination of the wavefront's
+// 1 KB, one wait state, global_load_lds_dwordx4), so the compiler does not treat them as
+// writes to the other buffer that the scoring of the current chunk has to wait for; the
+// kernel orders them itself with an explicit vmcnt wait and a barrier.  No other code in
+// the kernel uses M0.
+__device__ __forceinline__ void dc_gather(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
+                                          int lane) {
+#pragma unroll
+  for (int i = 0; i < kDcSlabsPerWave; i++) {
+    const int slab = wave + 4 * i;
+    const int piece = slab * 64 + lane;
+    const int key = piece / 9, p = piece - key * 9;
+    const int64_t base = seg_base[key >> 4];
+    const uint8_t* src = base >= 0 ? pool + base + (key & 15) * kRow + (p < 8 ? 16 * p : 116) : pool;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+  }
+}
+
+// Piece i (0..8) of this wavefront's share of dc_gather.
+__device__ __forceinline__ void dc_gather_piece(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
+                                                int lane, int i) {
+  const int slab = wave + 4 * i;
+  const int piece = slab * 64 + lane;
+  const int key = piece / 9, p = piece - key * 9;
+  const int64_t base = seg_base[key >> 4];
+  const uint8_t* src = base >= 0 ? pool + base + (key & 15) * kRow + (p < 8 ? 16 * p : 116) : pool;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+
+// Wait until at most `n` of this wavefront's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// B fragments of one 32-key group from raw rows in a chunk buffer: key l%32, codes
+// [64h, 64h+64) as four 16-byte loads, decoded to f16.
+__device__ __forceinline__ void load_k32_raw(K32& f, const uint8_t* keys, int lane) {
+  const uint4* p = reinterpret_cast<const uint4*>(keys + (lane & 31) * kDcRow + (lane >> 5) * 64);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint4 x = p[j];
+    f.b[2 * j] = e4m3x8_to_f16x8(x.x, x.y);
+    f.b[2 * j + 1] = e4m3x8_to_f16x8(x.z, x.w);
+  }
+}
+
+// Head-weighted score of one 32-key group for one row (lane half partial); hook(s) runs
+// after the two MFMAs of slice s.
+template <typename Hook>
+__device__ __forceinline__ float dc_group(const Q32& q, const W32& w, const K32& kb, Hook&& hook) {
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    c0 = mfma32(q.a[0][s], kb.b[s], c0);
+    c1 = mfma32(q.a[1][s], kb.b[s], c1);
+    hook(s);
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[0][i], c0[i], acc[i & 3]);
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[1][i], c1[i], acc[i & 3]);
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// WPR = wavefronts per row (4, 2 or 1): each scores 256 / WPR keys of every chunk.  NB =
+// chunk buffers in LDS: NB - 1 gathers are in flight while one chunk is scored.
+template <int WPR, int NB>
+__global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int next_n, const int* __restrict__ context_lens,
     const uint8_t* __restrict__ pool, int64_t num_blocks, int block_size, int64_t block_stride,
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int max_ctx, float* __restrict__ logits,
     int64_t ld) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
-  uint8_t* s_keys = s_dyn;
-  uint8_t* s_q = s_dyn + kGatherBytes;
-  __shared__ int64_t s_base[16];
+  constexpr int kKeysPerWave = kDcChunk / WPR;
+  constexpr int kGroups = kKeysPerWave / 32;
+  constexpr int kStores = kKeysPerWave / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kDcBuf];
+  __shared__ int64_t s_base[kDcSegs];
 
-  const int b = blockIdx.y, tok0 = blockIdx.x * kKeys;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = context_lens[b];
   const int Lc = min(L, max_ctx);  // the last row of the request sees [0, L)
-  if (tok0 >= Lc) return;
+  const int c_first = blockIdx.x * kDcJob;
+  const int c_end = min(c_first + kDcJob, (Lc + kDcChunk - 1) / kDcChunk);
+  if (c_first >= c_end) return;  // uniform
+  const bool has_pool = num_blocks > 0;
 
-  if (tid < 16) {
-    const int s = tok0 + 16 * tid;
+  // Segment bases of the whole job (-1: absent).
+  for (int sg = tid; sg < kDcSegs; sg += 256) {
+    const int s = (c_first * kDcChunk) + 16 * sg;
     int64_t base = -1;
     if (s < Lc) {
       const int blk = s / block_size;
@@ -143,43 +234,71 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(
         if (page >= 0 && page < num_blocks) base = (int64_t)page * block_stride + (int64_t)(s % block_size) * kRow;
       }
     }
-    s_base[tid] = base;
+    s_base[sg] = base;
   }
-  // q rows of this request, two at a time: waves 0 and 1 stage rows 0 and 1
-  if (wave < min(next_n, 2)) stage_q_dma(s_q + wave * 8192, q + ((int64_t)b * next_n + wave) * kHeads * kDim, lane);
-  __syncthreads();
-  gather_keys_dma(s_keys, s_base, pool, num_blocks * block_stride, 16 * kRow, wave, lane);
-  __syncthreads();
 
-  const int n = lane & 15, g = lane >> 4;
-  const int grp = wave + 4 * g;  // after the transpose-reduce lane group g owns key group wave + 4g
-  const int kslot = grp * 16 + n;
-  const int tok = tok0 + kslot;
-  const float ks = key_scale(s_keys, kslot);
-  const bool present = s_base[grp] >= 0;
-  for (int row = 0; row < next_n; row++) {
-    if (row == 2) {  // rows 2 and 3 replace rows 0 and 1 in LDS
-      __syncthreads();
-      if (wave < next_n - 2)
-        stage_q_dma(s_q + wave * 8192, q + ((int64_t)b * next_n + 2 + wave) * kHeads * kDim, lane);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-    QFrag qf;
-    WFrag wf;
-    load_q_lds(qf, s_q + (row & 1) * 8192, lane);
-    load_w(wf, w + ((int64_t)b * next_n + row) * kHeads, lane);
-    float part[4];
+  // This wavefront's row and key range within each chunk.
+  const int row = wave / WPR;
+  const int kbase = (wave % WPR) * kKeysPerWave;
+  const bool active = row < next_n;  // 3 rows: the fourth wavefront only gathers
+  const int rr = min(row, next_n - 1);
+  Q32 qf;
+  W32 wf;
+  load_q32(qf, q + ((int64_t)b * next_n + rr) * kHeads * kDim, lane);
+  load_w32(wf, w + ((int64_t)b * next_n + rr) * kHeads, lane);
+  const int ke = active ? min(L - next_n + rr + 1, max_ctx) : 0;
+  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      logits + ((int64_t)b * next_n + rr) * ld, (short)0, max(ke, 0) * 4, 0x00020000);
+  __syncthreads();  // segment bases visible
+
+  auto gather = [&](int c) {  // chunk c into its buffer
+    if (has_pool) dc_gather(s_buf[(c - c_first) % NB], s_base + (c - c_first) * 16, pool, wave, lane);
+  };
+  // Score chunk c; the gather of chunk `next` (if any) is issued piece by piece between
+  // the MFMAs, so that a busy vector-memory queue never holds up the matrix work.
+  auto score_chunk = [&](int c, const uint8_t* buf, int next) {
+    const int64_t* seg = s_base + (c - c_first) * 16;
+    float part[2];
 #pragma unroll
-    for (int kg = 0; kg < 4; kg++) {
-      KFrag kb;
-      load_kfrag_raw(kb, s_keys + (wave + 4 * kg) * 16 * kRow, lane);
-      part[kg] = score1(qf, wf, kb);
-      __builtin_amdgcn_sched_barrier(0);  // one key group in flight: a small register footprint
+    for (int g = 0; g < kGroups; g++) {
+      K32 kb;
+      load_k32_raw(kb, buf + (kbase + 32 * g) * kDcRow, lane);
+      part[g & 1] = dc_group(qf, wf, kb, [&](int sl) {
+        const int i = g * 8 + sl;
+        if (i < kDcSlabsPerWave && has_pool && next < c_end)
+          dc_gather_piece(s_buf[(next - c_first) % NB], s_base + (next - c_first) * 16, pool, wave, lane, i);
+      });
+      if (g & 1) {
+        const float v = combine_halves(part[0], part[1]);
+        const int key = kbase + 64 * (g >> 1) + lane;  // key within the chunk
+        const float scale = *reinterpret_cast<const float*>(buf + key * kDcRow + 140);
+        const float out = seg[key >> 4] >= 0 ? v * scale : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_rsrc, (c * kDcChunk + key) * 4, 0, 0);
+      }
     }
-    const float v = transpose_reduce4(part, lane);
-    const int ke = min(L - next_n + row + 1, max_ctx);
-    if (tok < ke) logits[((int64_t)b * next_n + row) * ld + tok] = present ? v * ks : -INFINITY;
+  };
+
+#pragma unroll
+  for (int j = 0; j < NB - 1; j++)
+    if (c_first + j < c_end) gather(c_first + j);
+  for (int cc = c_first; cc < c_end; cc++) {
+    // Wait for chunk cc's gather.  In the steady state this wavefront has since issued the
+    // gathers of the NB - 2 chunks after it and, for each of the NB - 1 chunks scored since,
+    // its stores; near the start or the end of the job it waits for everything.
+    const bool steady = cc - c_first >= NB - 1 && cc + NB - 2 < c_end;
+    if (steady) {
+      if (active)
+        wait_vm<(NB - 2) * kDcSlabsPerWave + (NB - 1) * kStores>();
+      else
+        wait_vm<(NB - 2) * kDcSlabsPerWave>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();  // every wavefront's part has landed; and everyone is done with chunk cc - 1's buffer
+    if (active)
+      score_chunk(cc, s_buf[(cc - c_first) % NB], cc + NB - 1);
+    else if (cc + NB - 1 < c_end)
+      gather(cc + NB - 1);
   }
 }
 
@@ -276,10 +395,13 @@ extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, 
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(pool) & 15) ||
       (block_stride_bytes & 15) || (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits) & 3))
     return DSI_EALIGN;
-  const dim3 grid((unsigned)((max_context_len + kKeys - 1) / kKeys), (unsigned)B);
-  const size_t lds = (size_t)kGatherBytes + (size_t)(next_n < 2 ? next_n : 2) * 8192;
-  hipLaunchKernelGGL(paged_decode_kernel, grid, dim3(256), lds, stream, q, w, next_n, context_lens, pool, num_blocks,
-                     block_size, block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld);
+  const dim3 grid((unsigned)((max_context_len + kDcChunk * kDcJob - 1) / (kDcChunk * kDcJob)), (unsigned)B);
+  const int wpr = next_n == 1 ? 4 : next_n == 2 ? 2 : 1;
+  constexpr int kNB = 2;
+  auto k = wpr == 4 ? paged_decode_kernel<4, kNB> : wpr == 2 ? paged_decode_kernel<2, kNB>
+                                                             : paged_decode_kernel<1, kNB>;
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool, num_blocks, block_size,
+                     block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 

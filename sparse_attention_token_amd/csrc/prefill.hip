@@ -29,8 +29,6 @@
 namespace dsi {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kPfThreads = 512;
 constexpr int kPfRows = kPfThreads / 64;  // one query row per wavefront
 constexpr int kGroups = 4;                // 32-key groups per tile
@@ -42,54 +40,6 @@ constexpr int kTileLdsBytes = kScaleOffset + kTileKeys * 4;
 constexpr int kRowsPerLane = kTileKeys / 64;  // staging: lane r of wave p takes rows r + 64j,
 constexpr int kStageDims = kDim / kPfRows;     // dims [kStageDims*p, kStageDims*(p+1))
 static_assert(kStageDims % 16 == 0, "staging moves whole 16-byte pieces");
-
-__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// q[row] decoded into this lane's A fragments: head hb*32 + l%32, dims [64h + 8s, +8) for
-// slice s.
-struct Q32 {
-  f16x8 a[2][8];
-};
-
-__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
-  const int m = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int hb = 0; hb < 2; hb++) {
-    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint4 x = p[j];
-      f.a[hb][2 * j] = e4m3x8_to_f16x8(x.x, x.y);
-      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x.z, x.w);
-    }
-  }
-}
-
-// The weights of the 32 heads this lane holds in C: w[hb][i] is head hb*32 + 8*(i/4) + 4h + i%4.
-struct W32 {
-  float w[2][16];
-};
-
-__device__ __forceinline__ void load_w32(W32& f, const uint16_t* w_row, int lane) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int hb = 0; hb < 2; hb++)
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
-      f.w[hb][4 * b + 0] = bf16_to_f32(x.x & 0xFFFFu);
-      f.w[hb][4 * b + 1] = bf16_to_f32(x.x >> 16);
-      f.w[hb][4 * b + 2] = bf16_to_f32(x.y & 0xFFFFu);
-      f.w[hb][4 * b + 3] = bf16_to_f32(x.y >> 16);
-    }
-}
-
-// B fragments of one 32-key group from the f16 tile: key l%32, dims [64h + 8s, +8).
-struct K32 {
-  f16x8 b[8];
-};
 
 // One 32-key group on the matrix cores, with the previous group's head sum and other work
 // threaded between its 16 MFMAs in a fixed order (sched_barrier fences keep the compiler
@@ -132,13 +82,6 @@ __device__ __forceinline__ void load_k32(K32& f, const uint8_t* keys, int lane) 
   const f16x8* p = reinterpret_cast<const f16x8*>(keys + (lane & 31) * kLdsKeyStrideF16 + (lane >> 5) * 128);
 #pragma unroll
   for (int s = 0; s < 8; s++) f.b[s] = p[s];
-}
-
-// Sum of the two lane halves for two 32-key groups at once: on return lane l holds the
-// full sum of key l of the 64-key tile (group l/32, key l%32).
-__device__ __forceinline__ float combine_halves(float g0, float g1) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(g0), __float_as_uint(g1), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(

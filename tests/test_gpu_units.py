@@ -137,9 +137,13 @@ def test_prefill_uses_the_k_scale_per_row():
 
 
 # ----------------------------------------------------------------------------- paged decode logits
-@pytest.mark.parametrize("next_n,bs,extra", [(1, 64, 0), (2, 64, 16), (3, 16, 0), (4, 32, 32)])
-def test_decode_parity_ragged(next_n, bs, extra):
-    lens = [1, 15, 16, 17, 300, 1000 + next_n, 2049]
+@pytest.mark.parametrize("next_n,bs,extra,long", [(1, 64, 0, False), (2, 64, 16, False), (3, 16, 0, False),
+                                                   (4, 32, 32, False), (1, 64, 0, True), (2, 16, 0, True),
+                                                   (4, 64, 16, True)])
+def test_decode_parity_ragged(next_n, bs, extra, long):
+    """Short ragged lengths, and long ones that span many 256-key chunks and several jobs per
+    request (the double-buffered gather alternates buffers across job boundaries)."""
+    lens = [4099, 2048 * 8 + 1, 2048 * 8, 2048 * 3 + 257, 9000] if long else [1, 15, 16, 17, 300, 1000 + next_n, 2049]
     c = synth.decode_case(10 + next_n, B=len(lens), next_n=next_n, lmin=0, lmax=0, block_size=bs, lens=lens)
     stride = bs * ROW + extra
     nb = c["num_blocks"]
