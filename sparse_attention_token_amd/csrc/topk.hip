@@ -32,7 +32,7 @@ namespace dsi {
 namespace {
 
 constexpr int kHistBins = 2048;
-constexpr int kShortRow = 16384;  // rows up to this width use the small configuration
+constexpr int kShortRow = 16384;  // rows up to this width are held in registers, one workgroup per row
 constexpr int kSplitCap = 12288;  // boundary-bin candidates kept per row when rows are split
 constexpr int kMaxSplit = 16;     // workgroups per row at most
 
@@ -49,7 +49,6 @@ struct Cfg {
   static constexpr int kBinsPerThread = kHistBins / THREADS;
 };
 using LongRows = Cfg<1024, 12288, 1>;  // 96 KB of candidates
-using ShortRows = Cfg<256, 2048, 1>;   // 16 KB of candidates
 
 template <int C>
 __device__ __forceinline__ void hist_add(int* h, uint32_t bin, int lane) {
@@ -376,6 +375,339 @@ __global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __rest
                             s_cnt, orow, tid);
 }
 
+// ---------------------------------------------------------------- rows held in registers
+// A row of at most THREADS * VPT 16-byte vectors (plus an unaligned head and tail of fewer
+// than 16 bytes each) is read from memory once: thread t keeps vectors i*THREADS + t of the
+// row in registers, converted to keys, and every pass runs on them.
+//
+// Non-finite values and the empty slots past the row fall into histogram bins no finite
+// value reaches — the four lowest (negative NaN/inf; key 0 for empty slots) and the four
+// highest (positive inf/NaN) — which the bin search ignores.  Output slots are reserved
+// once per wavefront: each thread counts its columns above the boundary bin and in it, a
+// wavefront prefix sum of the two counts packed into one word (wavefront totals stay below
+// 2^16, so the halves never carry into each other) gives every thread its offsets, and two
+// LDS atomics per wavefront reserve the ranges.  Columns above the boundary bin go straight
+// to their slots (lanes with nothing to write store to a spare slot instead of branching);
+// the boundary bin's columns are kept in LDS and resolved there by further key digits, or
+// from the registers when there are more than the LDS list holds.  The selected columns are
+// assembled in LDS and the finished row is written in one coalesced pass.
+template <int THREADS, int VPT, int WAVES_PER_SIMD>
+struct RegCfg {
+  static constexpr int kThreads = THREADS;
+  static constexpr int kVpt = VPT;
+  static constexpr int kCap = 1024;                  // boundary-bin columns kept in LDS
+  static constexpr int kWavesPerSimd = WAVES_PER_SIMD;  // occupancy asked of the register allocator
+};
+using RegSmall = RegCfg<256, 8, 4>;  // fp32 rows up to 8192 columns, bf16 rows up to 16384
+using RegMid = RegCfg<256, 16, 2>;   // fp32 rows up to 16384 columns
+
+template <bool BF16, typename C>
+constexpr int reg_capacity() {
+  return C::kThreads * C::kVpt * Keys<BF16>::kPerVec;
+}
+
+// Bin search by wavefront 0 alone: lane l sums bins [l*B, l*B + B) of hist (B = nb / 64, or
+// bin l when nb < 64), a wavefront suffix sum gives each lane the count above its bins, and
+// the lane whose bins hold the `need`-th largest writes s_sel[0] = that bin, s_sel[1] = the
+// count strictly above it, s_sel[2] = the total.  Bins outside [lo, hi) count as empty.
+// Call with all threads (after the histogram is complete); ends synchronised.
+template <int NB>
+__device__ __forceinline__ void find_bin_w0(const int* hist, int lo, int hi, int need, int* s_sel, int tid) {
+  constexpr int B = NB >= 64 ? NB / 64 : 1;
+  if (tid < 64) {
+    int h[B], local = 0;
+    if (B % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < B; j += 4) {
+        const int4 x = *reinterpret_cast<const int4*>(hist + tid * B + j);
+        h[j] = x.x;
+        h[j + 1] = x.y;
+        h[j + 2] = x.z;
+        h[j + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < B; j++) h[j] = tid * B + j < NB ? hist[tid * B + j] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < B; j++) {
+      const int bin = tid * B + j;
+      h[j] = (bin < NB && bin >= lo && bin < hi) ? h[j] : 0;
+      local += h[j];
+    }
+    // suffix sum over lanes: above = sum of `local` over lanes > tid
+    int v = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_down(v, off);
+      if (tid + off < 64) v += y;
+    }
+    const int above = v - local;
+    if (tid == 0) s_sel[2] = v;
+    // the bin j with acc_j < need <= acc_j + h[j], acc_j = above + (bins above j): one
+    // lane holds it, found without branches
+    int acc = above, sel = -1, sel_acc = 0;
+#pragma unroll
+    for (int j = B - 1; j >= 0; j--) {
+      const bool hit = acc < need && need <= acc + h[j];
+      sel = hit ? tid * B + j : sel;
+      sel_acc = hit ? acc : sel_acc;
+      acc += h[j];
+    }
+    if (sel >= 0) {
+      s_sel[0] = sel;
+      s_sel[1] = sel_acc;
+    }
+  }
+  __syncthreads();
+}
+
+// Makes the compiler treat the values as redefined here, so that predicates computed from
+// them in an earlier unrolled loop are recomputed rather than kept alive (as one 64-bit
+// lane mask each) until a later loop.
+template <int M>
+__device__ __forceinline__ void launder(uint32_t (&a)[M]) {
+#pragma unroll
+  for (int j = 0; j < M; j++) asm volatile("" : "+v"(a[j]));
+}
+
+// Reserve output ranges for one wavefront: this thread has `a` items for range A and `b`
+// for range B (each below 2^16 per wavefront); returns the thread's first slots in pa, pb,
+// counted from the running totals *ca, *cb (LDS), which grow by the wavefront's sums.
+__device__ __forceinline__ void reserve2(int a, int b, int* ca, int* cb, int lane, int& pa, int& pb) {
+  const int packed = (a << 16) | b;
+  int incl = packed;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  int ba = 0, bb = 0;
+  if (lane == 63) {
+    ba = atomicAdd(ca, incl >> 16);
+    bb = atomicAdd(cb, incl & 0xFFFF);
+  }
+  ba = __shfl(ba, 63);
+  bb = __shfl(bb, 63);
+  const int excl = incl - packed;
+  pa = ba + (excl >> 16);
+  pb = bb + (excl & 0xFFFF);
+}
+
+// The same search with every thread of the workgroup owning kHistBins / T consecutive bins
+// (fewer registers per thread than find_bin_w0, one more barrier).  s_wave: one int per
+// wavefront.
+template <int T>
+__device__ __forceinline__ void find_bin_all(const int* hist, int nb, int lo, int hi, int need, int* s_wave,
+                                             int* s_sel, int tid) {
+  constexpr int B = kHistBins / T;
+  int h[B], local = 0;
+#pragma unroll
+  for (int j = 0; j < B; j++) {
+    const int bin = tid * B + j;
+    h[j] = (bin < nb && bin >= lo && bin < hi) ? hist[bin] : 0;
+    local += h[j];
+  }
+  const int above = block_suffix_excl<T / 64>(local, s_wave, tid);
+  if (tid == T - 1) s_sel[2] = above + local;
+  int acc = above, sel = -1, sel_acc = 0;
+#pragma unroll
+  for (int j = B - 1; j >= 0; j--) {
+    const bool hit = acc < need && need <= acc + h[j];
+    sel = hit ? tid * B + j : sel;
+    sel_acc = hit ? acc : sel_acc;
+    acc += h[j];
+  }
+  if (sel >= 0) {
+    s_sel[0] = sel;
+    s_sel[1] = sel_acc;
+  }
+  __syncthreads();
+}
+
+template <bool BF16, typename C>
+__global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __restrict__ logits, int64_t row_bytes,
+                                                              const int* __restrict__ row_starts,
+                                                              const int* __restrict__ row_ends, int max_width, int k,
+                                                              int* __restrict__ out, int64_t out_ld) {
+  using K = Keys<BF16>;
+  constexpr int T = C::kThreads, E = K::kPerVec, V = C::kVpt, N = V * E;
+  constexpr int kShift = K::kTopShift;
+  constexpr int kCap = C::kCap;
+  constexpr uint32_t kLoBin = 4, kHiBin = kHistBins - 4;  // finite values have bins in [kLoBin, kHiBin)
+  static_assert((N + 2) * 64 < 65536, "packed per-wavefront counts must stay below 2^16");
+  // Arrays carry 64 spare slots past their end: a lane with nothing to store (or add)
+  // writes its own spare slot instead of branching.
+  __shared__ __attribute__((aligned(16))) int s_hist[kHistBins + 64];
+  __shared__ uint32_t s_ckey[kCap + 64];  // boundary-bin keys and columns
+  __shared__ int s_ccol[kCap + 64];
+  __shared__ int s_out[DSI_MAX_TOPK + 64];  // the selected columns
+  __shared__ int s_sel[4];
+  __shared__ int s_cnt[4];  // 0: written, 3: boundary bin; 1/2: resolution
+
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int st = row_starts ? max(row_starts[r], 0) : 0;
+  const int en = max(min(row_ends[r], max_width), st);
+  const uint8_t* row = logits + (int64_t)r * row_bytes;
+  int* orow = out + (int64_t)r * out_ld;
+
+  for (int i = tid; i < kHistBins; i += T) s_hist[i] = 0;
+  if (tid < 4) s_cnt[tid] = 0;
+
+  // Head [st, c0) and tail [c1, en): fewer than E columns each, one element per thread;
+  // nvec aligned vectors in between (the host guarantees nvec <= T * V).
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + (uintptr_t)st * K::kElemBytes;
+  const int c0 = min(st + (int)(((16 - (addr & 15)) & 15) / K::kElemBytes), en);
+  const int nvec = (en - c0) / E;
+  const int c1 = c0 + nvec * E;
+  const uint4* vec = reinterpret_cast<const uint4*>(row + (size_t)c0 * K::kElemBytes);
+  uint32_t kk[N + 2];  // keys; 0 (an ignored bin) for slots outside the row
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    const int vi = i * T + tid;
+    uint4 x = uint4{0u, 0u, 0u, 0u};
+    if (vi < nvec) x = vec[vi];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      uint32_t key;
+      K::key(K::elem(x, e), key);
+      kk[i * E + e] = vi < nvec ? key : 0u;
+    }
+  }
+  const bool ha = tid < c0 - st, ta = tid < en - c1;
+  {
+    uint32_t key;
+    K::key(ha ? K::load1(row, st + tid) : 0u, key);
+    kk[N] = ha ? key : 0u;
+    K::key(ta ? K::load1(row, c1 + tid) : 0u, key);
+    kk[N + 1] = ta ? key : 0u;
+  }
+  // column of kk[j] relative to st
+  const int col_base = c0 - st + tid * E;
+  auto column = [&](int j) { return j < N ? col_base + (j / E) * T * E + (j % E) : (j == N ? tid : c1 - st + tid); };
+
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    const bool in = i * T + tid < nvec;
+#pragma unroll
+    for (int e = 0; e < E; e++) atomicAdd(&s_hist[in ? kk[i * E + e] >> kShift : kHistBins + lane], 1);
+  }
+  atomicAdd(&s_hist[ha ? kk[N] >> kShift : kHistBins + lane], 1);
+  atomicAdd(&s_hist[ta ? kk[N + 1] >> kShift : kHistBins + lane], 1);
+  __syncthreads();
+  find_bin_w0<kHistBins>(s_hist, kLoBin, kHiBin, k, s_sel, tid);
+  const int total = s_sel[2];
+  const bool all = total <= k;  // every finite value is selected
+  const uint32_t b1 = all ? 0xFFFFFFFFu : (uint32_t)s_sel[0];
+  const int above1 = all ? total : s_sel[1];
+  // written: bins in (lo_w, kHiBin), i.e. (d - lo_w - 1) < (kHiBin - lo_w - 1) unsigned
+  const uint32_t lo_w = all ? kLoBin - 1 : b1;
+  const uint32_t span_w = kHiBin - lo_w - 1;
+
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int j = 0; j < N + 2; j++) {
+    const uint32_t d = kk[j] >> kShift;
+    ngt += (d - lo_w - 1u) < span_w ? 1 : 0;
+    neq += d == b1 ? 1 : 0;
+  }
+  int pg, pe;
+  reserve2(ngt, neq, &s_cnt[0], &s_cnt[3], lane, pg, pe);
+  launder(kk);
+#pragma unroll
+  for (int j = 0; j < N + 2; j++) {
+    const uint32_t d = kk[j] >> kShift;
+    const bool gt = (d - lo_w - 1u) < span_w;
+    const bool eq = d == b1;
+    const int col = column(j);
+    s_out[gt ? pg : DSI_MAX_TOPK + lane] = col;
+    const int cs = (eq && pe < kCap) ? pe : kCap + lane;
+    s_ckey[cs] = kk[j];
+    s_ccol[cs] = col;
+    pg += gt ? 1 : 0;
+    pe += eq ? 1 : 0;
+    __builtin_amdgcn_sched_barrier(0);  // one element at a time: keeps register pressure low
+  }
+  __syncthreads();
+  if (!all) {
+    launder(kk);
+    const int m = s_cnt[3];
+    const int need = k - above1;
+    // Further digits of the key (fp32: 11 then 10 bits; bf16: 5 bits) by histograms over
+    // the boundary bin's columns — from LDS when they all fit, else from the registers.
+    constexpr int kDigits = BF16 ? 1 : 2;
+    constexpr int kSh[2] = {BF16 ? 0 : 10, 0};
+    constexpr int kWd[2] = {BF16 ? 5 : 11, 10};
+    const bool in_lds = m <= kCap;
+    uint32_t prefix = b1 << kShift;
+    int rem = need;
+#pragma unroll
+    for (int p = 0; p < kDigits; p++) {
+      const int sh = kSh[p], nb = 1 << kWd[p], hs = sh + kWd[p];
+      for (int i = tid; i < nb; i += T) s_hist[i] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (int i = tid; i < m; i += T) {
+          const uint32_t key = s_ckey[i];
+          if ((key >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < N + 2; j++) {
+          const bool match = (kk[j] >> hs) == (prefix >> hs);
+          atomicAdd(&s_hist[match ? (kk[j] >> sh) & (nb - 1) : kHistBins + lane], 1);
+        }
+      }
+      __syncthreads();
+      if (p == 0)
+        find_bin_w0<(BF16 ? 32 : 2048)>(s_hist, 0, nb, rem, s_sel, tid);
+      else
+        find_bin_w0<1024>(s_hist, 0, nb, rem, s_sel, tid);
+      prefix |= (uint32_t)s_sel[0] << sh;
+      rem -= s_sel[1];
+    }
+    // prefix is the threshold key: boundary-bin keys above it are taken, and `rem` of
+    // those equal to it
+    const int n_above_tau = need - rem;
+    if (in_lds) {
+      for (int i = tid; i < m; i += T) {
+        const uint32_t key = s_ckey[i];
+        if (key > prefix) {
+          s_out[above1 + atomicAdd(&s_cnt[1], 1)] = s_ccol[i];
+        } else if (key == prefix) {
+          const int t = atomicAdd(&s_cnt[2], 1);
+          if (t < rem) s_out[above1 + n_above_tau + t] = s_ccol[i];
+        }
+      }
+    } else {
+      int na = 0, ne = 0;
+#pragma unroll
+      for (int j = 0; j < N + 2; j++) {
+        na += ((kk[j] >> kShift) == b1 && kk[j] > prefix) ? 1 : 0;
+        ne += kk[j] == prefix ? 1 : 0;
+      }
+      int qa, qe;
+      reserve2(na, ne, &s_cnt[1], &s_cnt[2], lane, qa, qe);
+      launder(kk);
+#pragma unroll
+      for (int j = 0; j < N + 2; j++) {
+        const bool a = (kk[j] >> kShift) == b1 && kk[j] > prefix;
+        const bool e = kk[j] == prefix && qe < rem;
+        const int col = column(j);
+        s_out[a ? above1 + qa : DSI_MAX_TOPK + lane] = col;
+        s_out[e ? above1 + n_above_tau + qe : DSI_MAX_TOPK + lane] = col;
+        qa += a ? 1 : 0;
+        qe += kk[j] == prefix ? 1 : 0;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+  }
+  const int n = all ? total : k;
+  for (int j = tid; j < k; j += T) orow[j] = j < n ? s_out[j] : -1;
+}
+
 // ---------------------------------------------------------------- long rows split G ways
 // Workspace: per (row, slice) an 11-bit histogram; per row {b1, above1, total, m}; per row
 // up to kSplitCap boundary-bin candidates (key, column).
@@ -664,21 +996,25 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
     }
     return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
   }
-  const bool small = max_width <= kShortRow;
+  const dim3 grid((unsigned)rows);
+#define DSI_TOPK_REG(B, CFG)                                                                                        \
+  hipLaunchKernelGGL((topk_reg_kernel<B, CFG>), grid, dim3(CFG::kThreads), 0, stream, src, row_bytes, row_starts, \
+                     row_ends, max_width, k, out, out_ld)
   if (!bf) {
-    if (small)
-      hipLaunchKernelGGL((topk_kernel<false, ShortRows>), dim3((unsigned)rows), dim3(ShortRows::kThreads), 0, stream,
-                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld);
+    if (max_width <= reg_capacity<false, RegSmall>())
+      DSI_TOPK_REG(false, RegSmall);
+    else if (max_width <= reg_capacity<false, RegMid>())
+      DSI_TOPK_REG(false, RegMid);
     else
-      hipLaunchKernelGGL((topk_kernel<false, LongRows>), dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
-                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld);
+      hipLaunchKernelGGL((topk_kernel<false, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
+                         row_starts, row_ends, max_width, k, out, out_ld);
   } else {
-    if (small)
-      hipLaunchKernelGGL((topk_kernel<true, ShortRows>), dim3((unsigned)rows), dim3(ShortRows::kThreads), 0, stream,
-                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld);
+    if (max_width <= reg_capacity<true, RegSmall>())
+      DSI_TOPK_REG(true, RegSmall);
     else
-      hipLaunchKernelGGL((topk_kernel<true, LongRows>), dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
-                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld);
+      hipLaunchKernelGGL((topk_kernel<true, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
+                         row_starts, row_ends, max_width, k, out, out_ld);
   }
+#undef DSI_TOPK_REG
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }

@@ -189,7 +189,7 @@ def _rows_with_ties(rng, rows, width):
 
 
 @pytest.mark.parametrize("width,k", [(3000, 2048), (2048, 2048), (2049, 2048), (700, 2048), (8192, 2048),
-                                     (100, 7), (40000, 2048)])
+                                     (100, 7), (8193, 2048), (16384, 1000), (40000, 2048)])
 def test_topk_f32_same_input_exact_values(width, k):
     rng = np.random.default_rng(width + k)
     rows = 6
@@ -212,13 +212,15 @@ def test_topk_f32_same_input_exact_values(width, k):
         assert np.array_equal(np.sort(x[r, g]), np.sort(x[r, o]))
 
 
-def test_topk_bf16_exact_values():
+@pytest.mark.parametrize("width", [8192, 16384])
+def test_topk_bf16_exact_values(width):
     rng = np.random.default_rng(7)
-    vals = (rng.standard_normal((9, 8192)) * 8).astype(np.float32)
+    vals = (rng.standard_normal((9, width)) * 8).astype(np.float32)
     bits = synth._bf16_bits(vals)
     bits[1, :4000] = 0xFF80
     bits[2, :] = 0xFF80
-    ends = np.array([8192, 8192, 8192, 100, 2048, 2047, 8192, 5000, 0], np.int32)
+    bits[6, :] = 0x4000  # one value everywhere: the boundary bin outgrows the candidate list
+    ends = np.array([width, width, width, 100, 2048, 2047, width, 5000, 0], np.int32)
     ref = oracle.topk_select(bits, ends, 2048, bf16=True)
     got = host(dsi.topk_select(dev(bits), dev(ends), k=2048))
     f = bf16_value(bits)
