@@ -4,26 +4,23 @@
 // 索引器接入稀疏 MQA logits": the compressed-space top-k runs on bf16 logits).
 //
 // Radix select, no sort.  Values map to order-preserving unsigned keys (non-finite
-// values are dropped).  One workgroup per row — 1024 threads for rows longer than
-// 16K columns, else 256 threads with a smaller LDS footprint so that several rows
-// share a CU — and the row is read twice, with 16-byte loads, 16 elements per thread
-// in flight:
-//   pass 1 builds an LDS histogram of the top 11 key bits and finds the bin b1 where
-//          the count from the top reaches k;
-//   pass 2 writes every column whose bin is above b1 and collects the columns of bin
-//          b1 (key, column) into LDS;
-// the remaining key bits (21 for fp32, 5 for bf16) are then resolved on those
-// candidates in LDS, digit by digit, and the selected candidates written.  Output
-// slots are reserved per wavefront (ballot + popcount, one LDS atomic).  A row whose
-// boundary bin holds more candidates than LDS can keep (heavy ties) resolves the
-// remaining digits with passes over the row instead.
-//
-// Long rows that are too few to fill the CUs are split between up to 16 workgroups per
-// row, in four launches that communicate through the caller's workspace: per-slice
-// histograms; per row, their sum, the boundary bin and each slice's output offsets; every
-// slice writes its columns above the boundary bin from its offset (no atomics across
-// workgroups) and appends its boundary-bin columns to a per-row candidate list; one
-// workgroup per row resolves the candidates as above.
+// values are dropped).  Three shapes, by row width and row count:
+//   * rows of at most 16K columns (fp32) or 16K (bf16): one 256-thread workgroup per row
+//     reads the row once into registers (topk_reg_kernel below);
+//   * longer rows, when there are enough of them to fill the CUs: one 1024-thread
+//     workgroup per row reads the row twice — pass 1 builds an LDS histogram of the top
+//     11 key bits and finds the bin b1 where the count from the top reaches k; pass 2
+//     writes every column whose bin is above b1 and collects the columns of bin b1 (key,
+//     column) into LDS; the remaining key bits (21 for fp32, 5 for bf16) are resolved on
+//     those candidates, digit by digit (by passes over the row when the boundary bin
+//     outgrows LDS).  Output slots are reserved per wavefront (ballot + popcount, one LDS
+//     atomic);
+//   * few long rows are split between up to 16 workgroups per row, in four launches that
+//     communicate through the caller's workspace: per-slice histograms; per row, their
+//     sum, the boundary bin and each slice's output offsets; every slice writes its
+//     columns above the boundary bin from its offset (no atomics across workgroups) and
+//     appends its boundary-bin columns to a per-row candidate list; one workgroup per row
+//     resolves the candidates as above.
 #include <algorithm>
 
 #include "common.h"
@@ -492,37 +489,6 @@ __device__ __forceinline__ void reserve2(int a, int b, int* ca, int* cb, int lan
   const int excl = incl - packed;
   pa = ba + (excl >> 16);
   pb = bb + (excl & 0xFFFF);
-}
-
-// The same search with every thread of the workgroup owning kHistBins / T consecutive bins
-// (fewer registers per thread than find_bin_w0, one more barrier).  s_wave: one int per
-// wavefront.
-template <int T>
-__device__ __forceinline__ void find_bin_all(const int* hist, int nb, int lo, int hi, int need, int* s_wave,
-                                             int* s_sel, int tid) {
-  constexpr int B = kHistBins / T;
-  int h[B], local = 0;
-#pragma unroll
-  for (int j = 0; j < B; j++) {
-    const int bin = tid * B + j;
-    h[j] = (bin < nb && bin >= lo && bin < hi) ? hist[bin] : 0;
-    local += h[j];
-  }
-  const int above = block_suffix_excl<T / 64>(local, s_wave, tid);
-  if (tid == T - 1) s_sel[2] = above + local;
-  int acc = above, sel = -1, sel_acc = 0;
-#pragma unroll
-  for (int j = B - 1; j >= 0; j--) {
-    const bool hit = acc < need && need <= acc + h[j];
-    sel = hit ? tid * B + j : sel;
-    sel_acc = hit ? acc : sel_acc;
-    acc += h[j];
-  }
-  if (sel >= 0) {
-    s_sel[0] = sel;
-    s_sel[1] = sel_acc;
-  }
-  __syncthreads();
 }
 
 template <bool BF16, typename C>
