@@ -15,6 +15,8 @@
 // several workgroups per CU keep loads in flight.  Block-table entries are read
 // once per segment.  Out-of-range table entries or page ids never produce an access
 // outside the pool: those keys score -inf.
+#include <algorithm>
+
 #include "common.h"
 
 namespace dsi {
@@ -24,6 +26,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glob_ptr_t;
 
 constexpr int kKeys = 256;                         // keys per workgroup
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
 constexpr int kGatherBytes = kKeys * kRow;         // 33792 = 33 x 1024
 constexpr int kGatherSlabs = kGatherBytes / 1024;  // one DMA instruction of a wavefront fills 1 KB
 
@@ -113,9 +127,11 @@ __device__ __forceinline__ void load_q_lds(QFrag& f, const uint8_t* s_q, int lan
 }
 
 // ------------------------------------------------------------------ paged decode
-// A workgroup (4 wavefronts) streams a job of up to 8 chunks of 256 keys of one request
+// A workgroup (4 wavefronts) streams segments of up to 8 chunks of 256 keys of one request
 // through a ring of LDS buffers: the DMA gathers of the next chunks are in flight while
-// one chunk is scored, and the request's q rows stay decoded in VGPRs for the whole job.
+// one chunk is scored, and the request's q rows stay decoded in VGPRs for the segment.
+// Scoring decodes a 32-key group's FP8 codes under the previous group's MFMAs and sums
+// heads under the next group's.
 // Rows are spread over the wavefronts (1 row: 4 wavefronts share each chunk's keys; 2
 // rows: 2 wavefronts per row; 3-4 rows: one wavefront per row, all keys).  Each key row
 // lands in LDS as nine 16-byte pieces at a 144-byte stride (bytes 0..127, then 116..131
@@ -168,6 +184,22 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait_vm<kDcSlabsPerWave * (idx / NB) + KS * (idx % NB)>() for a wavefront-uniform idx
+// in [0, (NB - 1) * NB): the wait for a chunk's gather when idx / NB gathers of this
+// wavefront and the stores of idx % NB scored chunks were issued after it.
+template <int NB, int KS, int I = 0>
+__device__ __forceinline__ void wait_gather(int idx) {
+  if constexpr (I < (NB - 1) * NB) {
+    if (idx == I) {
+      wait_vm<kDcSlabsPerWave * (I / NB) + KS * (I % NB)>();
+      return;
+    }
+    wait_gather<NB, KS, I + 1>(idx);
+  } else {
+    wait_vm<0>();
+  }
+}
+
 // B fragments of one 32-key group from raw rows in a chunk buffer: key l%32, codes
 // [64h, 64h+64) as four 16-byte loads, decoded to f16.
 __device__ __forceinline__ void load_k32_raw(K32& f, const uint8_t* keys, int lane) {
@@ -180,48 +212,117 @@ __device__ __forceinline__ void load_k32_raw(K32& f, const uint8_t* keys, int la
   }
 }
 
-// Head-weighted score of one 32-key group for one row (lane half partial); hook(s) runs
-// after the two MFMAs of slice s.
-template <typename Hook>
-__device__ __forceinline__ float dc_group(const Q32& q, const W32& w, const K32& kb, Hook&& hook) {
-  f32x16 c0 = {}, c1 = {};
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    c0 = mfma32(q.a[0][s], kb.b[s], c0);
-    c1 = mfma32(q.a[1][s], kb.b[s], c1);
-    hook(s);
+// The 32 head weights of load_w32's layout kept as bf16 pairs (16 registers instead of 32):
+// w[hb][e / 2] holds weights e (low half) and e + 1 (high half) of head block hb.
+struct W32p {
+  uint32_t w[2][8];
+  __device__ __forceinline__ float get(int hb, int e) const {
+    const uint32_t x = w[hb][e >> 1];
+    return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
   }
+};
+
+__device__ __forceinline__ void load_w32p(W32p& f, const uint16_t* w_row, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
+      f.w[hb][2 * b] = x.x;
+      f.w[hb][2 * b + 1] = x.y;
+    }
+}
+
+// One 32-key group on the matrix cores with the neighbouring groups' work threaded between
+// its 16 MFMAs in a fixed order (sched_barrier fences keep the compiler from regrouping):
+// step i issues MFMA i (slice i/2, head block i%2) into x, then two of the 32 FMAs of the
+// head sum of y (the previous group's accumulators) when kEpi, then — when kNext — the
+// decode of the next group's slices 2j and 2j+1 into kb once MFMA 4j+3 has read them
+// (their raw codes are read from LDS two slice pairs ahead), then extra(i).
+template <bool kEpi, bool kNext, typename Extra>
+__device__ __forceinline__ void dc_phase(f32x16& x0, f32x16& x1, const Q32& q, K32& kb, const uint8_t* next,
+                                         int lane, const W32p& w, const f32x16& y0, const f32x16& y1,
+                                         float (&acc)[4], Extra&& extra) {
+  const uint4* np = reinterpret_cast<const uint4*>(next + (lane & 31) * kDcRow + (lane >> 5) * 64);
+  uint4 raw[2];
+  if (kNext) {
+    raw[0] = np[0];
+    raw[1] = np[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int sl = i >> 1;
+    if ((i & 1) == 0)
+      x0 = mfma32(q.a[0][sl], kb.b[sl], i == 0 ? f32x16{} : x0);
+    else
+      x1 = mfma32(q.a[1][sl], kb.b[sl], i == 1 ? f32x16{} : x1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kEpi) {
+#pragma unroll
+      for (int e = 2 * i; e < 2 * i + 2; e++) {
+        if (e < 16)
+          acc[e & 3] = fmaf(w.get(0, e), y0[e], acc[e & 3]);
+        else
+          acc[e & 3] = fmaf(w.get(1, e - 16), y1[e - 16], acc[e & 3]);
+      }
+    }
+    if (kNext && (i & 3) == 3) {
+      const int j = i >> 2;
+      kb.b[2 * j] = e4m3x8_to_f16x8(raw[j & 1].x, raw[j & 1].y);
+      kb.b[2 * j + 1] = e4m3x8_to_f16x8(raw[j & 1].z, raw[j & 1].w);
+      if (j < 2) raw[j] = np[j + 2];  // codes of slices 2j+4 and 2j+5
+    }
+    extra(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__device__ __forceinline__ float dc_acc_sum(const float (&acc)[4]) { return (acc[0] + acc[1]) + (acc[2] + acc[3]); }
+
+// The head sum of one group's accumulators on its own (no MFMAs to hide it behind).
+__device__ __forceinline__ float dc_head_sum(const W32p& w, const f32x16& y0, const f32x16& y1) {
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[0][i], c0[i], acc[i & 3]);
+  for (int e = 0; e < 16; e++) acc[e & 3] = fmaf(w.get(0, e), y0[e], acc[e & 3]);
 #pragma unroll
-  for (int i = 0; i < 16; i++) acc[i & 3] = fmaf(w.w[1][i], c1[i], acc[i & 3]);
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  for (int e = 0; e < 16; e++) acc[e & 3] = fmaf(w.get(1, e), y1[e], acc[e & 3]);
+  return dc_acc_sum(acc);
 }
 
 // WPR = wavefronts per row (4, 2 or 1): each scores 256 / WPR keys of every chunk.  NB =
 // chunk buffers in LDS: NB - 1 gathers are in flight while one chunk is scored.
+// Work split.  persistent = 0: workgroup (x, y) takes chunks [8x, 8x + 8) of request y
+// (grid = (ceil(max_context_len / 2048), B)).  persistent = 1 (B <= kDcMaxReqs): the grid is
+// one-dimensional (two workgroups per CU) and workgroup i takes the i-th of gridDim.x equal
+// shares of all requests' chunks in request order, as segments of at most kDcJob chunks of
+// one request each, so that no CU idles while a few long jobs finish.
+constexpr int kDcMaxReqs = 1024;
+
 template <int WPR, int NB>
 __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
-    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int next_n, const int* __restrict__ context_lens,
-    const uint8_t* __restrict__ pool, int64_t num_blocks, int block_size, int64_t block_stride,
-    const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int max_ctx, float* __restrict__ logits,
-    int64_t ld) {
+    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int B, int next_n,
+    const int* __restrict__ context_lens, const uint8_t* __restrict__ pool, int64_t num_blocks, int block_size,
+    int64_t block_stride, const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int max_ctx,
+    float* __restrict__ logits, int64_t ld, int persistent) {
   constexpr int kKeysPerWave = kDcChunk / WPR;
   constexpr int kGroups = kKeysPerWave / 32;
   constexpr int kStores = kKeysPerWave / 64;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kDcBuf];
   __shared__ int64_t s_base[kDcSegs];
 
-  const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_pool = num_blocks > 0;
+  auto chunks_of = [&](int L) { return (min(max(L, 0), max_ctx) + kDcChunk - 1) / kDcChunk; };
+
+  // Score chunks [c_first, c_end) (at most kDcJob) of request b.
+  auto run = [&](int b, int c_first, int c_end) {
   const int L = context_lens[b];
   const int Lc = min(L, max_ctx);  // the last row of the request sees [0, L)
-  const int c_first = blockIdx.x * kDcJob;
-  const int c_end = min(c_first + kDcJob, (Lc + kDcChunk - 1) / kDcChunk);
-  if (c_first >= c_end) return;  // uniform
-  const bool has_pool = num_blocks > 0;
+  __syncthreads();  // the previous segment's buffers and segment bases are no longer read
 
   // Segment bases of the whole job (-1: absent).
   for (int sg = tid; sg < kDcSegs; sg += 256) {
@@ -243,9 +344,9 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   const bool active = row < next_n;  // 3 rows: the fourth wavefront only gathers
   const int rr = min(row, next_n - 1);
   Q32 qf;
-  W32 wf;
+  W32p wf;
   load_q32(qf, q + ((int64_t)b * next_n + rr) * kHeads * kDim, lane);
-  load_w32(wf, w + ((int64_t)b * next_n + rr) * kHeads, lane);
+  load_w32p(wf, w + ((int64_t)b * next_n + rr) * kHeads, lane);
   const int ke = active ? min(L - next_n + rr + 1, max_ctx) : 0;
   const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       logits + ((int64_t)b * next_n + rr) * ld, (short)0, max(ke, 0) * 4, 0x00020000);
@@ -254,27 +355,33 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   auto gather = [&](int c) {  // chunk c into its buffer
     if (has_pool) dc_gather(s_buf[(c - c_first) % NB], s_base + (c - c_first) * 16, pool, wave, lane);
   };
-  // Score chunk c; the gather of chunk `next` (if any) is issued piece by piece between
-  // the MFMAs, so that a busy vector-memory queue never holds up the matrix work.
+  // Score chunk c: this wavefront's keys as kGroups / 2 pairs of 32-key groups, each pair
+  // software-pipelined (dc_phase: the first group's MFMAs carry the second group's decode,
+  // the second group's MFMAs the first group's head sum).  With two buffers the gather of
+  // chunk `next` (if any) is issued piece by piece between the first MFMAs, so that a busy
+  // vector-memory queue never holds up the matrix work; with more buffers it was issued
+  // whole right after the barrier.
   auto score_chunk = [&](int c, const uint8_t* buf, int next) {
     const int64_t* seg = s_base + (c - c_first) * 16;
-    float part[2];
 #pragma unroll
-    for (int g = 0; g < kGroups; g++) {
-      K32 kb;
-      load_k32_raw(kb, buf + (kbase + 32 * g) * kDcRow, lane);
-      part[g & 1] = dc_group(qf, wf, kb, [&](int sl) {
-        const int i = g * 8 + sl;
-        if (i < kDcSlabsPerWave && has_pool && next < c_end)
+    for (int h = 0; h < kGroups / 2; h++) {
+      const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
+      auto dma = [&](int i) {
+        if (NB == 2 && h == 0 && i < kDcSlabsPerWave && has_pool && next < c_end)
           dc_gather_piece(s_buf[(next - c_first) % NB], s_base + (next - c_first) * 16, pool, wave, lane, i);
-      });
-      if (g & 1) {
-        const float v = combine_halves(part[0], part[1]);
-        const int key = kbase + 64 * (g >> 1) + lane;  // key within the chunk
-        const float scale = *reinterpret_cast<const float*>(buf + key * kDcRow + 140);
-        const float out = seg[key >> 4] >= 0 ? v * scale : -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_rsrc, (c * kDcChunk + key) * 4, 0, 0);
-      }
+      };
+      K32 kb;
+      load_k32_raw(kb, keys, lane);
+      f32x16 a0, a1, b0 = {}, b1 = {};
+      float acc[4];
+      dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, dma);
+      dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+      const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
+      const int key = kbase + 64 * h + lane;  // key within the chunk
+      const float scale = *reinterpret_cast<const float*>(buf + key * kDcRow + 140);
+      const float out = seg[key >> 4] >= 0 ? v * scale : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_rsrc, (c * kDcChunk + key) * 4, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -282,23 +389,83 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   for (int j = 0; j < NB - 1; j++)
     if (c_first + j < c_end) gather(c_first + j);
   for (int cc = c_first; cc < c_end; cc++) {
-    // Wait for chunk cc's gather.  In the steady state this wavefront has since issued the
-    // gathers of the NB - 2 chunks after it and, for each of the NB - 1 chunks scored since,
-    // its stores; near the start or the end of the job it waits for everything.
-    const bool steady = cc - c_first >= NB - 1 && cc + NB - 2 < c_end;
-    if (steady) {
+    // Wait for chunk cc's gather.  Issued after it by this wavefront: the gathers of the
+    // chunks up to cc + NB - 2 that exist, and the stores of the chunks scored since —
+    // all of them before the loop when cc's gather was issued in the prologue, else the
+    // NB - 1 chunks before cc.
+    const int ng = min(c_end - 1 - cc, NB - 2);
+    const int ns = min(cc - c_first, NB - 1);
+    if (has_pool) {
       if (active)
-        wait_vm<(NB - 2) * kDcSlabsPerWave + (NB - 1) * kStores>();
+        wait_gather<NB, kStores>(ng * NB + ns);
       else
-        wait_vm<(NB - 2) * kDcSlabsPerWave>();
-    } else {
-      wait_vm<0>();
+        wait_gather<NB, 0>(ng * NB + ns);
     }
     __syncthreads();  // every wavefront's part has landed; and everyone is done with chunk cc - 1's buffer
+    if (NB > 2 && cc + NB - 1 < c_end) gather(cc + NB - 1);  // into chunk cc - 1's buffer
     if (active)
       score_chunk(cc, s_buf[(cc - c_first) % NB], cc + NB - 1);
-    else if (cc + NB - 1 < c_end)
+    else if (NB == 2 && cc + NB - 1 < c_end)
       gather(cc + NB - 1);
+  }
+  };  // run
+
+  // Persistent: every wavefront finds this workgroup's share from all requests' chunk counts
+  // (lane l holds requests l, l + 64, ...; a running prefix over them), then walks it.
+  int b = B, start = 0, g0 = 0, g1 = 0;  // the request holding chunk g0 and its first global chunk
+  if (persistent) {
+    constexpr int kBlocks = kDcMaxReqs / 64;
+    const int nblk = (B + 63) / 64;  // uniform
+    int incl[kBlocks], cnt[kBlocks];
+    int carry = 0;
+#pragma unroll
+    for (int i = 0; i < kBlocks; i++) {
+      cnt[i] = 0;
+      incl[i] = carry;
+      if (i < nblk) {
+        const int r = i * 64 + lane;
+        cnt[i] = r < B ? chunks_of(context_lens[r]) : 0;
+        int v = cnt[i];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(v, off);
+          if (lane >= off) v += y;
+        }
+        incl[i] = carry + v;
+        carry += __shfl(v, 63);
+      }
+    }
+    const int64_t total = carry;
+    g0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
+    g1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+#pragma unroll
+    for (int i = kBlocks - 1; i >= 0; i--) {
+      const uint64_t m = __ballot(incl[i] > g0);
+      if (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        b = i * 64 + l;
+        start = __shfl(incl[i] - cnt[i], l);
+      }
+    }
+  } else {
+    b = blockIdx.y;
+    start = -(int)blockIdx.x * kDcJob;  // local chunk = g0 - start
+    g1 = kDcJob;
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  int lc = __builtin_amdgcn_readfirstlane(g0 - start);
+  int remaining = g1 - g0;
+  while (remaining > 0 && b < B) {  // uniform
+    const int cb = __builtin_amdgcn_readfirstlane(chunks_of(context_lens[b]));
+    const int len = min(remaining, min(cb - lc, kDcJob));
+    if (len > 0) run(b, lc, lc + len);
+    remaining -= max(len, 0);
+    lc += max(len, 0);
+    if (lc >= cb) {
+      if (!persistent) break;
+      b++;
+      lc = 0;
+    }
   }
 }
 
@@ -395,13 +562,24 @@ extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, 
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(pool) & 15) ||
       (block_stride_bytes & 15) || (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits) & 3))
     return DSI_EALIGN;
-  const dim3 grid((unsigned)((max_context_len + kDcChunk * kDcJob - 1) / (kDcChunk * kDcJob)), (unsigned)B);
+  const int64_t max_chunks = (max_context_len + kDcChunk - 1) / kDcChunk;
+  // Persistent shares pay off where scoring a chunk is cheap (one row per request: the
+  // tail of unequal jobs dominated); with two or more rows per request the per-request
+  // grid measured faster.
+  const bool persistent = B <= kDcMaxReqs && next_n == 1;
+  dim3 grid;
+  if (persistent) {  // two workgroups per CU, each an equal share of the chunks
+    const int64_t slots = 2 * (int64_t)cu_count();
+    grid = dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, max_chunks * B)));
+  } else {
+    grid = dim3((unsigned)((max_chunks + kDcJob - 1) / kDcJob), (unsigned)B);
+  }
   const int wpr = next_n == 1 ? 4 : next_n == 2 ? 2 : 1;
   constexpr int kNB = 2;
   auto k = wpr == 4 ? paged_decode_kernel<4, kNB> : wpr == 2 ? paged_decode_kernel<2, kNB>
                                                              : paged_decode_kernel<1, kNB>;
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, q, w, next_n, context_lens, pool, num_blocks, block_size,
-                     block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld);
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                     block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld, (int)persistent);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
