@@ -4,17 +4,13 @@
 // 索引器接入稀疏 MQA logits", motivation and implementation: consumer layers score
 // only the candidate blocks, into bf16 logits).
 //
-// Both stream 132-byte K rows past one to four query rows: HBM/L2-bound.  A
-// workgroup gathers 256 keys — segments of 16 (or 8) consecutive tokens, each
-// contiguous in memory — straight into LDS with global->LDS DMA loads
-// (global_load_lds_dwordx4: no VGPR staging, no LDS write instructions; all 33 KB
-// in flight at once).  The segments sit back to back, so key slot k is always the
-// 132 bytes at LDS offset 132*k.  Each wavefront then scores 4 groups of 16 keys on
-// the matrix cores one group at a time (raw codes read with 4-byte LDS loads and
-// decoded to f16 per use, common.h), keeping its register footprint small so that
-// several workgroups per CU keep loads in flight.  Block-table entries are read
-// once per segment.  Out-of-range table entries or page ids never produce an access
-// outside the pool: those keys score -inf.
+// Both stream 132-byte K rows past one to four query rows.  A workgroup gathers chunks of
+// 256 keys straight into LDS with global->LDS DMA loads (global_load_lds_dwordx4: no VGPR
+// staging, no LDS write instructions), double-buffered so that the next chunk is in flight
+// while one is scored, and scores them on the matrix cores with the query rows decoded in
+// VGPRs (common.h's 32x32x16 layout): each wavefront takes 32-key groups in pipelined
+// pairs, decoding the FP8 codes from LDS per use.  Out-of-range table entries, page ids
+// or tokens never produce an access outside the source: those keys score -inf.
 #include <algorithm>
 
 #include "common.h"
@@ -24,8 +20,6 @@ namespace {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glob_ptr_t;
-
-constexpr int kKeys = 256;                         // keys per workgroup
 
 // Compute units of the current device (queried once per device).
 int cu_count() {
@@ -38,94 +32,6 @@ int cu_count() {
   }
   return cached[dev];
 }
-constexpr int kGatherBytes = kKeys * kRow;         // 33792 = 33 x 1024
-constexpr int kGatherSlabs = kGatherBytes / 1024;  // one DMA instruction of a wavefront fills 1 KB
-
-// Issue the DMA loads of a 256-key gather into s_keys.  s_base[seg] is the byte
-// offset in src of segment seg (seg_bytes long) or -1 when absent; limit is the byte
-// size of src.  A 16-byte piece that would cross `limit` is copied dword by dword.
-__device__ __forceinline__ void gather_keys_dma(uint8_t* s_keys, const int64_t* s_base, const uint8_t* src,
-                                                int64_t limit, int seg_bytes, int wave, int lane) {
-  for (int i = wave; i < kGatherSlabs; i += 4) {
-    const int o = i * 1024 + lane * 16;  // this lane's LDS bytes
-    const int seg = o / seg_bytes, within = o - seg * seg_bytes;
-    const int64_t base = s_base[seg];
-    const int64_t goff = base + within;
-    if (base >= 0 && goff + 16 <= limit) {
-      __builtin_amdgcn_global_load_lds((glob_ptr_t)(src + goff), (lds_ptr_t)(s_keys + i * 1024), 16, 0, 0);
-    } else if (base >= 0 && goff < limit) {
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (goff + 4 * j + 4 <= limit)
-          *reinterpret_cast<uint32_t*>(s_keys + o + 4 * j) = *reinterpret_cast<const uint32_t*>(src + goff + 4 * j);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // every load of this wavefront has landed in LDS
-}
-
-// B fragments of 16 keys from raw rows at LDS offset 132*k: lane (key n, group g)
-// reads its 32 codes as 8 dwords and decodes them.
-__device__ __forceinline__ void load_kfrag_raw(KFrag& f, const uint8_t* keys, int lane) {
-  const int n = lane & 15, g = lane >> 4;
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(keys + n * kRow + g * 32);
-  uint32_t x[8];
-#pragma unroll
-  for (int j = 0; j < 8; j++) x[j] = p[j];
-  f.b[0] = e4m3x8_to_f16x8(x[0], x[1]);
-  f.b[1] = e4m3x8_to_f16x8(x[2], x[3]);
-  f.b[2] = e4m3x8_to_f16x8(x[4], x[5]);
-  f.b[3] = e4m3x8_to_f16x8(x[6], x[7]);
-}
-
-// One (row, 16-key group) output: 16 MFMAs as 4 interleaved head-tile chains, then
-// this lane's 16 heads weighted and summed.
-__device__ __forceinline__ float score1(const QFrag& q, const WFrag& w, const KFrag& kb) {
-  f32x4 c[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; hb++) c[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; s++)
-#pragma unroll
-    for (int hb = 0; hb < 4; hb++) c[hb] = mfma_f16(q.a[hb][s], kb.b[s], c[hb]);
-  float acc = 0.f;
-#pragma unroll
-  for (int hb = 0; hb < 4; hb++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) acc = fmaf(w.w[hb][i], c[hb][i], acc);
-  return acc;
-}
-
-__device__ __forceinline__ float key_scale(const uint8_t* s_keys, int kslot) {
-  return *reinterpret_cast<const float*>(s_keys + kslot * kRow + kDim);
-}
-
-// Stage one q row (64 x 128 codes) into 8 KB of LDS by DMA, permuted into the order
-// the A fragments are read: 16-byte unit (hb*2 + p)*64 + lane holds codes
-// [32g + 16p, +16) of head hb*16 + n (lane = 16g + n), so each fragment read of a
-// wavefront is one contiguous, conflict-free 1 KB.  Issued by one wavefront.
-__device__ __forceinline__ void stage_q_dma(uint8_t* s_q, const uint8_t* q_row, int lane) {
-  const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int hb = i >> 1, p = i & 1;
-    __builtin_amdgcn_global_load_lds((glob_ptr_t)(q_row + (hb * 16 + n) * kDim + g * 32 + p * 16),
-                                     (lds_ptr_t)(s_q + i * 1024), 16, 0, 0);
-  }
-}
-
-// A fragments of one q row staged by stage_q_dma, decoded to f16.
-__device__ __forceinline__ void load_q_lds(QFrag& f, const uint8_t* s_q, int lane) {
-  const uint4* p = reinterpret_cast<const uint4*>(s_q) + lane;
-#pragma unroll
-  for (int hb = 0; hb < 4; hb++) {
-    const uint4 x0 = p[(hb * 2 + 0) * 64], x1 = p[(hb * 2 + 1) * 64];
-    f.a[hb][0] = e4m3x8_to_f16x8(x0.x, x0.y);
-    f.a[hb][1] = e4m3x8_to_f16x8(x0.z, x0.w);
-    f.a[hb][2] = e4m3x8_to_f16x8(x1.x, x1.y);
-    f.a[hb][3] = e4m3x8_to_f16x8(x1.z, x1.w);
-  }
-}
-
 // ------------------------------------------------------------------ paged decode
 // A workgroup (4 wavefronts) streams segments of up to 8 chunks of 256 keys of one request
 // through a ring of LDS buffers: the DMA gathers of the next chunks are in flight while
@@ -414,38 +320,35 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   // (lane l holds requests l, l + 64, ...; a running prefix over them), then walks it.
   int b = B, start = 0, g0 = 0, g1 = 0;  // the request holding chunk g0 and its first global chunk
   if (persistent) {
-    constexpr int kBlocks = kDcMaxReqs / 64;
     const int nblk = (B + 63) / 64;  // uniform
-    int incl[kBlocks], cnt[kBlocks];
-    int carry = 0;
+    // lane l holds requests l, l + 64, ...: first the total, then the request holding g0
+    int total = 0;
+    for (int i = 0; i < nblk; i++) {
+      const int r = i * 64 + lane;
+      int v = r < B ? chunks_of(context_lens[r]) : 0;
 #pragma unroll
-    for (int i = 0; i < kBlocks; i++) {
-      cnt[i] = 0;
-      incl[i] = carry;
-      if (i < nblk) {
-        const int r = i * 64 + lane;
-        cnt[i] = r < B ? chunks_of(context_lens[r]) : 0;
-        int v = cnt[i];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(v, off);
-          if (lane >= off) v += y;
-        }
-        incl[i] = carry + v;
-        carry += __shfl(v, 63);
-      }
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      total += v;
     }
-    const int64_t total = carry;
     g0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
     g1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+    int carry = 0;
+    for (int i = 0; i < nblk && b == B; i++) {
+      const int r = i * 64 + lane;
+      const int c = r < B ? chunks_of(context_lens[r]) : 0;
+      int v = c;
 #pragma unroll
-    for (int i = kBlocks - 1; i >= 0; i--) {
-      const uint64_t m = __ballot(incl[i] > g0);
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(v, off);
+        if (lane >= off) v += y;
+      }
+      const uint64_t m = __ballot(carry + v > g0);
       if (m) {
         const int l = __ffsll((unsigned long long)m) - 1;
         b = i * 64 + l;
-        start = __shfl(incl[i] - cnt[i], l);
+        start = carry + __shfl(v - c, l);
       }
+      carry += __shfl(v, 63);
     }
   } else {
     b = blockIdx.y;
@@ -470,76 +373,133 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
 }
 
 // ------------------------------------------------------------------ sparse columns
-// grid = (ceil(width / 256), rows); one query row per workgroup.
-__global__ __launch_bounds__(256) void sparse_logits_kernel(
-    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, const int* __restrict__ row_ks,
+// The paged-decode machinery on the hierarchical path's candidate columns.  Every row's
+// columns form nch = ceil(width / 256) chunks; the grid (two workgroups per CU) takes equal
+// shares of all (row, chunk) pairs, as segments of up to kSpJob chunks of one row.  A
+// segment starts by computing each of its columns' source offset — the column's token
+// through sparse_indices, then the gathered row or the page through the block table, or
+// "absent" when the column scores -inf — so blocks, pages and invalid columns need no
+// special case later.  It then streams its chunks through the DMA ring and scores them as
+// the decode kernel scores one row (four wavefronts x 64 keys per chunk), rounding to bf16.
+constexpr int kSpJob = 4;                     // chunks per segment
+constexpr int kSpKeys = kSpJob * kDcChunk;    // columns per segment
+constexpr uint32_t kSpAbsent = 0xFFFFFFFFu;   // source offsets are in 4-byte units
+
+// Piece i (0..8) of this wavefront's share of one chunk's gather (as dc_gather_piece, with
+// one source offset per key).
+__device__ __forceinline__ void sp_gather_piece(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
+                                                int lane, int i) {
+  const int slab = wave + 4 * i;
+  const int piece = slab * 64 + lane;
+  const int key = piece / 9, p = piece - key * 9;
+  const uint32_t off = key_off[key];
+  const uint8_t* a = off != kSpAbsent ? src + (int64_t)off * 4 + (p < 8 ? 16 * p : 116) : src;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(lds) : "memory");
+}
+
+__global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
+    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
     const int* __restrict__ end, int sbk, const uint8_t* __restrict__ k_src, int64_t num_k,
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
     const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
     int64_t ld) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_keys[kGatherBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[8192];
-  __shared__ int64_t s_base[32];
-  __shared__ int s_tok[32];
+  constexpr int NB = 2;
+  constexpr int kKeysPerWave = kDcChunk / 4;
+  constexpr int kGroups = kKeysPerWave / 32;
+  constexpr int kStores = kKeysPerWave / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kDcBuf];
+  __shared__ uint32_t s_off[kSpKeys];
 
-  const int r = blockIdx.y, c0 = blockIdx.x * kKeys;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = sbk < 16 ? sbk : 16;  // tokens per contiguous segment
-  const int nseg = kKeys / G;
-  const int ks = row_ks[r], ke = row_ke[r], e = end[r];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_src = num_k > 0;
   const bool paged = block_table != nullptr;
-  const int64_t limit = paged ? num_k * block_stride : num_k * kRow;
+  const int sbk_shift = __builtin_ctz(sbk);
+  const int nch = (width + kDcChunk - 1) / kDcChunk;
+  const int kbase = wave * kKeysPerWave;
 
-  if (tid < nseg) {
-    const int c = c0 + tid * G;
-    int64_t base = -1;
-    int tok = -1;
-    if (c < width && c < e) {
-      tok = sparse_indices[(int64_t)r * si_ld + c / sbk] * sbk + c % sbk;
-      if (tok >= 0) {
-        if (!paged) {
-          if (tok < num_k) base = (int64_t)tok * kRow;
-        } else {
-          const int req = row_to_req ? row_to_req[r] : r;
-          const int blk = tok / block_size;
-          if (blk < bt_width && req >= 0 && req < num_reqs) {
-            const int page = block_table[(int64_t)req * bt_ld + blk];
-            if (page >= 0 && page < num_k) base = (int64_t)page * block_stride + (int64_t)(tok % block_size) * kRow;
+  // Score chunks [c_first, c_end) (at most kSpJob) of row r.
+  auto run = [&](int r, int c_first, int c_end) {
+    __syncthreads();  // the previous segment's buffers and offsets are no longer read
+    const int ks = row_ks[r], ke = row_ke[r], e = end[r];
+    const int req = paged ? (row_to_req ? row_to_req[r] : r) : 0;
+    const bool req_ok = !paged || (req >= 0 && req < num_reqs);
+    for (int t = tid; t < (c_end - c_first) * kDcChunk; t += 256) {
+      const int c = c_first * kDcChunk + t;
+      uint32_t off = kSpAbsent;
+      if (c < width && c < e) {
+        const int tok = sparse_indices[(int64_t)r * si_ld + (c >> sbk_shift)] * sbk + (c & (sbk - 1));
+        if (tok >= ks && tok < ke && tok >= 0) {
+          if (!paged) {
+            if (tok < num_k) off = (uint32_t)tok * (kRow / 4);
+          } else {
+            const int blk = tok / block_size;
+            if (req_ok && blk < bt_width) {
+              const int page = block_table[(int64_t)req * bt_ld + blk];
+              if (page >= 0 && page < num_k)
+                off = (uint32_t)(((int64_t)page * block_stride + (int64_t)(tok % block_size) * kRow) >> 2);
+            }
           }
         }
       }
+      s_off[t] = off;
     }
-    s_base[tid] = base;
-    s_tok[tid] = tok;
-  }
-  if (wave == 0) stage_q_dma(s_q, q + (int64_t)r * kHeads * kDim, lane);
-  __syncthreads();
-  gather_keys_dma(s_keys, s_base, k_src, limit, G * kRow, wave, lane);
-  WFrag wf;
-  load_w(wf, w + (int64_t)r * kHeads, lane);
-  __syncthreads();
-  QFrag qf;
-  load_q_lds(qf, s_q, lane);
+    Q32 qf;
+    W32p wf;
+    load_q32(qf, q + (int64_t)r * kHeads * kDim, lane);
+    load_w32p(wf, w + (int64_t)r * kHeads, lane);
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)r * ld, (short)0, width * 2, 0x00020000);
+    __syncthreads();  // offsets visible
 
-  const int n = lane & 15, g = lane >> 4;
-  float part[4];
+    auto gather_piece = [&](int c, int i) {
+      if (has_src)
+        sp_gather_piece(s_buf[(c - c_first) % NB], s_off + (c - c_first) * kDcChunk, k_src, wave, lane, i);
+    };
+    auto score_chunk = [&](int c, const uint8_t* buf, int next) {
+      const uint32_t* coff = s_off + (c - c_first) * kDcChunk;
 #pragma unroll
-  for (int kg = 0; kg < 4; kg++) {
-    KFrag kb;
-    load_kfrag_raw(kb, s_keys + (wave + 4 * kg) * 16 * kRow, lane);
-    part[kg] = score1(qf, wf, kb);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const float v = transpose_reduce4(part, lane);
-  const int grp = wave + 4 * g;
-  const int kslot = grp * 16 + n;
-  const int c = c0 + kslot;
-  if (c < width) {
-    const int seg = kslot / G;
-    const int tok = s_tok[seg] + (kslot - seg * G);
-    const bool valid = c < e && s_base[seg] >= 0 && tok >= ks && tok < ke && (paged || tok < num_k);
-    out[(int64_t)r * ld + c] = valid ? f32_to_bf16_rne(v * key_scale(s_keys, kslot)) : (uint16_t)0xFF80u;
+      for (int h = 0; h < kGroups / 2; h++) {
+        const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
+        auto dma = [&](int i) {
+          if (h == 0 && i < kDcSlabsPerWave && next < c_end) gather_piece(next, i);
+        };
+        K32 kb;
+        load_k32_raw(kb, keys, lane);
+        f32x16 a0, a1, b0 = {}, b1 = {};
+        float acc[4];
+        dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, dma);
+        dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+        const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
+        const int key = kbase + 64 * h + lane;  // key within the chunk
+        const float scale = *reinterpret_cast<const float*>(buf + key * kDcRow + 140);
+        const uint16_t o = coff[key] != kSpAbsent ? f32_to_bf16_rne(v * scale) : (uint16_t)0xFF80u;
+        __builtin_amdgcn_raw_buffer_store_b16(o, out_rsrc, (c * kDcChunk + key) * 2, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+#pragma unroll
+    for (int i = 0; i < kDcSlabsPerWave; i++) gather_piece(c_first, i);
+    for (int cc = c_first; cc < c_end; cc++) {
+      // as in the decode kernel: after chunk cc's gather this wavefront issued the stores of
+      // the chunk before it (when cc is not the segment's first)
+      if (has_src) wait_gather<NB, kStores>(min(cc - c_first, 1));
+      __syncthreads();
+      score_chunk(cc, s_buf[(cc - c_first) % NB], cc + 1);
+    }
+  };
+
+  const int64_t total = (int64_t)rows * nch;
+  int64_t g = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t g1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
+  while (g < g1) {  // uniform
+    const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
+    const int len = (int)min((int64_t)min(nch - lc, kSpJob), g1 - g);
+    run(r, lc, lc + len);
+    g += len;
   }
 }
 
@@ -609,9 +569,14 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
       (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits_bf16) & 1))
     return DSI_EALIGN;
   if (rows > 65535) return DSI_EUNSUPPORTED;
-  const dim3 grid((unsigned)((width + kKeys - 1) / kKeys), (unsigned)rows);
-  hipLaunchKernelGGL(sparse_logits_kernel, grid, dim3(256), 0, stream, q, w, row_ks, row_ke, sparse_indices, si_ld,
-                     (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
+  // source offsets are kept in 4-byte units in 32 bits
+  const int64_t src_bytes = paged ? num_k * block_stride_bytes : num_k * kRow;
+  if (src_bytes >= ((int64_t)1 << 34)) return DSI_EUNSUPPORTED;
+  const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
+  const int64_t slots = 2 * (int64_t)cu_count();
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
+  hipLaunchKernelGGL(sparse_logits_kernel, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
+                     si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
                      block_size, block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
