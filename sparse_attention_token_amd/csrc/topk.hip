@@ -386,17 +386,21 @@ __global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __rest
 // LDS atomics per wavefront reserve the ranges.  Columns above the boundary bin go straight
 // to their slots (lanes with nothing to write store to a spare slot instead of branching);
 // the boundary bin's columns are kept in LDS and resolved there by further key digits, or
-// from the registers when there are more than the LDS list holds.  The selected columns are
+// by passes over the row in memory when there are more than the LDS list holds (heavy
+// ties).  The keys are laundered between passes so that the compiler recomputes their
+// bins instead of keeping a second register per key.  The selected columns are
 // assembled in LDS and the finished row is written in one coalesced pass.
-template <int THREADS, int VPT, int WAVES_PER_SIMD>
+template <int THREADS, int VPT>
 struct RegCfg {
   static constexpr int kThreads = THREADS;
   static constexpr int kVpt = VPT;
-  static constexpr int kCap = 1024;                  // boundary-bin columns kept in LDS
-  static constexpr int kWavesPerSimd = WAVES_PER_SIMD;  // occupancy asked of the register allocator
+  static constexpr int kCap = 1024;  // boundary-bin columns kept in LDS
+  static constexpr int kWaves = THREADS / 64;
+  static constexpr int kCopies = 1;
+  static constexpr int kBinsPerThread = kHistBins / THREADS;
 };
-using RegSmall = RegCfg<256, 8, 4>;  // fp32 rows up to 8192 columns, bf16 rows up to 16384
-using RegMid = RegCfg<256, 16, 2>;   // fp32 rows up to 16384 columns
+using RegSmall = RegCfg<256, 8>;   // fp32 rows up to 8192 columns, bf16 rows up to 16384
+using RegMid = RegCfg<256, 16>;    // fp32 rows up to 16384 columns
 
 template <bool BF16, typename C>
 constexpr int reg_capacity() {
@@ -509,6 +513,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   __shared__ int s_ccol[kCap + 64];
   __shared__ int s_out[DSI_MAX_TOPK + 64];  // the selected columns
   __shared__ int s_sel[4];
+  __shared__ int s_wave[C::kWaves];
   __shared__ int s_cnt[4];  // 0: written, 3: boundary bin; 1/2: resolution
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -561,6 +566,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   }
   atomicAdd(&s_hist[ha ? kk[N] >> kShift : kHistBins + lane], 1);
   atomicAdd(&s_hist[ta ? kk[N + 1] >> kShift : kHistBins + lane], 1);
+  launder(kk);  // the bins are recomputed where needed rather than kept, one register per key
   __syncthreads();
   find_bin_w0<kHistBins>(s_hist, kLoBin, kHiBin, k, s_sel, tid);
   const int total = s_sel[2];
@@ -597,46 +603,36 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   }
   __syncthreads();
   if (!all) {
-    launder(kk);
     const int m = s_cnt[3];
     const int need = k - above1;
-    // Further digits of the key (fp32: 11 then 10 bits; bf16: 5 bits) by histograms over
-    // the boundary bin's columns — from LDS when they all fit, else from the registers.
-    constexpr int kDigits = BF16 ? 1 : 2;
-    constexpr int kSh[2] = {BF16 ? 0 : 10, 0};
-    constexpr int kWd[2] = {BF16 ? 5 : 11, 10};
-    const bool in_lds = m <= kCap;
-    uint32_t prefix = b1 << kShift;
-    int rem = need;
+    if (m <= kCap) {
+      // Further digits of the key (fp32: 11 then 10 bits; bf16: 5 bits) by histograms over
+      // the boundary bin's columns in LDS.
+      constexpr int kDigits = BF16 ? 1 : 2;
+      constexpr int kSh[2] = {BF16 ? 0 : 10, 0};
+      constexpr int kWd[2] = {BF16 ? 5 : 11, 10};
+      uint32_t prefix = b1 << kShift;
+      int rem = need;
 #pragma unroll
-    for (int p = 0; p < kDigits; p++) {
-      const int sh = kSh[p], nb = 1 << kWd[p], hs = sh + kWd[p];
-      for (int i = tid; i < nb; i += T) s_hist[i] = 0;
-      __syncthreads();
-      if (in_lds) {
+      for (int p = 0; p < kDigits; p++) {
+        const int sh = kSh[p], nb = 1 << kWd[p], hs = sh + kWd[p];
+        for (int i = tid; i < nb; i += T) s_hist[i] = 0;
+        __syncthreads();
         for (int i = tid; i < m; i += T) {
           const uint32_t key = s_ckey[i];
           if ((key >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < N + 2; j++) {
-          const bool match = (kk[j] >> hs) == (prefix >> hs);
-          atomicAdd(&s_hist[match ? (kk[j] >> sh) & (nb - 1) : kHistBins + lane], 1);
-        }
+        __syncthreads();
+        if (p == 0)
+          find_bin_w0<(BF16 ? 32 : 2048)>(s_hist, 0, nb, rem, s_sel, tid);
+        else
+          find_bin_w0<1024>(s_hist, 0, nb, rem, s_sel, tid);
+        prefix |= (uint32_t)s_sel[0] << sh;
+        rem -= s_sel[1];
       }
-      __syncthreads();
-      if (p == 0)
-        find_bin_w0<(BF16 ? 32 : 2048)>(s_hist, 0, nb, rem, s_sel, tid);
-      else
-        find_bin_w0<1024>(s_hist, 0, nb, rem, s_sel, tid);
-      prefix |= (uint32_t)s_sel[0] << sh;
-      rem -= s_sel[1];
-    }
-    // prefix is the threshold key: boundary-bin keys above it are taken, and `rem` of
-    // those equal to it
-    const int n_above_tau = need - rem;
-    if (in_lds) {
+      // prefix is the threshold key: boundary-bin keys above it are taken, and `rem` of
+      // those equal to it
+      const int n_above_tau = need - rem;
       for (int i = tid; i < m; i += T) {
         const uint32_t key = s_ckey[i];
         if (key > prefix) {
@@ -647,26 +643,13 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
         }
       }
     } else {
-      int na = 0, ne = 0;
-#pragma unroll
-      for (int j = 0; j < N + 2; j++) {
-        na += ((kk[j] >> kShift) == b1 && kk[j] > prefix) ? 1 : 0;
-        ne += kk[j] == prefix ? 1 : 0;
-      }
-      int qa, qe;
-      reserve2(na, ne, &s_cnt[1], &s_cnt[2], lane, qa, qe);
-      launder(kk);
-#pragma unroll
-      for (int j = 0; j < N + 2; j++) {
-        const bool a = (kk[j] >> kShift) == b1 && kk[j] > prefix;
-        const bool e = kk[j] == prefix && qe < rem;
-        const int col = column(j);
-        s_out[a ? above1 + qa : DSI_MAX_TOPK + lane] = col;
-        s_out[e ? above1 + n_above_tau + qe : DSI_MAX_TOPK + lane] = col;
-        qa += a ? 1 : 0;
-        qe += kk[j] == prefix ? 1 : 0;
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // The boundary bin holds more columns than the LDS list: resolve it with passes over
+      // the row in memory (heavy ties), writing relative columns into s_out.
+      __syncthreads();
+      if (tid < 4) s_cnt[tid] = 0;
+      __syncthreads();
+      resolve_boundary<BF16, C>(row, st, en, k, b1, above1, m, 0, s_ckey, s_ccol, s_hist, s_wave, s_sel, s_cnt, s_out,
+                                tid);
     }
     __syncthreads();
   }
