@@ -51,6 +51,7 @@ def _load():
         "orc_sparse_mqa_logits": (None, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _p, _i64, _p, _i32,
                                          _i64, _i32, _p, _i64]),
         "orc_topk_remap": (None, [_p, _i64, _i32, _i32, _p, _i64, _p, _i32, _p, _i64]),
+        "orc_gather_prefill_k": (None, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -256,3 +257,22 @@ def dense_masked_topk(q, w, k_rows, ks, ke, cand, candidate_block_size, k):
     logits = np.where(mask, logits, np.float32(-np.inf)).astype(np.float32)
     idx = topk_select(logits, ke, k, starts=ks)
     return idx, logits
+
+
+# ---------------------------------------------------------------- O9
+def gather_prefill_k(pool, num_blocks, block_size, block_stride, block_table, cu_seq_lens, S, bt_width=None):
+    """Paged pool (uint8) -> contiguous cache rows uint8 [S,132] of the requests laid end to end (cu_seq_lens
+    int32 [num_reqs+1]); rows no request owns and tokens without a valid page are zero."""
+    lib = _load()
+    pool = _c(pool, np.uint8)
+    assert pool.size >= num_blocks * block_stride
+    bt, bt_ld = _rows(np.asarray(block_table, dtype=np.int32), np.int32)
+    cu = _c(cu_seq_lens, np.int32)
+    num_reqs = cu.size - 1
+    assert num_reqs <= bt.shape[0]
+    if bt_width is None:
+        bt_width = bt.shape[1]
+    out = np.empty((S, ROW), dtype=np.uint8)
+    lib.orc_gather_prefill_k(_ptr(pool), num_blocks, block_size, block_stride, _ptr(bt), bt_ld, bt_width, _ptr(cu),
+                             num_reqs, _ptr(out), S)
+    return out

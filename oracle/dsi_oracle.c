@@ -443,3 +443,31 @@ void orc_topk_remap(const int32_t* col, int64_t col_ld, int32_t rows, int32_t k,
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* O9 prefill K gather (P3 prefill/decode table: a prefill chunk first      */
+/* collects its requests' history K out of the paged cache and then scores  */
+/* it, while decode reads the cache where it lies; P1 implementation        */
+/* breakdown: the indexer's forward chains the prefill K gather with the    */
+/* paged decode path).  The requests of the chunk are laid end to end:      */
+/* request r owns output rows [cu[r], cu[r+1]) and its row cu[r] + p is its */
+/* token p, found through row r of the block table.  The output is the     */
+/* cache rows copied byte for byte; rows that no request owns, and tokens   */
+/* whose block index or page id is out of range, are zero rows.             */
+/* ------------------------------------------------------------------------ */
+void orc_gather_prefill_k(const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                          const int32_t* block_table, int64_t bt_ld, int32_t bt_width, const int32_t* cu,
+                          int32_t num_reqs, uint8_t* out, int32_t S) {
+  int32_t r, p;
+  memset(out, 0, (size_t)S * ORC_ROW);
+  for (r = 0; r < num_reqs; r++) {
+    for (p = 0; p < cu[r + 1] - cu[r]; p++) {
+      int64_t row = (int64_t)cu[r] + p;
+      int32_t blk = p / block_size, page;
+      if (row < 0 || row >= S || blk >= bt_width) continue;
+      page = block_table[(int64_t)r * bt_ld + blk];
+      if (page < 0 || page >= num_blocks) continue;
+      memcpy(out + row * ORC_ROW, pool + (int64_t)page * block_stride + (int64_t)(p % block_size) * ORC_ROW, ORC_ROW);
+    }
+  }
+}

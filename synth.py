@@ -109,6 +109,20 @@ def decode_case(seed, B, next_n, lmin, lmax, block_size=64, lens=None):
                 slot_mapping=slots_for(lens, bt, block_size))
 
 
+def gather_case(seed, lens, block_size, span=None, extra_blocks=3):
+    """Prefill requests laid end to end (cu_seq_lens) over a paged pool whose blocks are a random permutation;
+    span = tokens per block stride (>= block_size: a packed pool leaves span - block_size unused rows)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    k = draw_k(rng, int(lens.sum()))
+    bt, nblocks = paged_layout(rng, lens, block_size, extra_blocks)
+    span = block_size if span is None else span
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    return dict(k=k, lens=lens, cu=cu, block_table=bt, num_blocks=nblocks, block_size=block_size,
+                block_stride=span * ROW, slot_mapping=slots_for(lens, bt, block_size), S=int(cu[-1]))
+
+
 # --------------------------------------------------------------------------- hierarchical sparse
 def draw_candidates(rng, maxb, num=64, distinct=60, dup=2):
     """Per row: `distinct` different ids from [0, maxb), `dup` repeats of those, one -1 and one id >= maxb,
