@@ -11,7 +11,8 @@ exactly to f16 and contracted on the f16 matrix cores, so its peak is the dense 
 measured on this device (register-only MFMA loops, a 4 GiB streaming read), the oracle's single-thread CPU
 rate on a bounded row sample, and the decode and hierarchical workloads (paged decode 64 x U{4096..65536};
 long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows + 1024 prefill rows)
-with their HBM roofline fractions.  Diagnostics go to stderr.
+with their HBM roofline fractions, and the prefill K gather out of the paged cache (8192 and 131072 tokens).
+Diagnostics go to stderr.
 
 `roofline.traffic` (HBM bytes per launch of the prefill logits kernel) comes from the committed counter
 summary in profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads for a plain copy
@@ -72,6 +73,12 @@ class EventTimer:
     def mean_ms(self):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def queue_ahead(steps, us_per_step=250):
+    """Occupy the GPU with a spin kernel (about us_per_step per step to come) so that the host enqueues the
+    timed launches while it runs: the events then bracket device time, not the binding's Python overhead."""
+    torch.cuda._sleep(int(steps * us_per_step * 2200))
 
 
 # --------------------------------------------------------------------------- measured ceilings
@@ -180,6 +187,7 @@ def bench_prefill(steps, warmup):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    queue_ahead(steps)
     t0.record()
     for _ in range(steps):
         step(True)
@@ -189,6 +197,7 @@ def bench_prefill(steps, warmup):
     ms_logits = timer.mean_ms()
     # top-k alone, for the report
     tk = EventTimer()
+    queue_ahead(steps)
     for _ in range(steps):
         s = tk.start()
         dsi.topk_select(logits, ke, k=K, row_starts=ks, out=idx)
@@ -274,6 +283,7 @@ def bench_decode(n, steps, warmup, copies=4):
         step(i, False)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_ahead(steps)
     a.record()
     for i in range(steps):
         step(i, True)
@@ -293,6 +303,43 @@ def bench_decode(n, steps, warmup, copies=4):
                 logits_topk_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
                 rows_per_s=round(rows / ((ms_l + ms_t) * 1e-3), 1),
                 algorithmic_bytes=bytes_logits + bytes_topk)
+
+
+# --------------------------------------------------------------------------- prefill K gather
+def bench_gather(steps, warmup, pool_bytes=512 << 20):
+    """Prefill K gather out of a paged pool: the prefill chunk's 8192-token history (64-token pages) and the
+    longest hierarchical prefill request (131072 tokens, 128-token pages).  The pool holds 512 MB of random
+    cache rows; each timed call reads a different, disjoint random set of its blocks, so K comes from HBM."""
+    res = {}
+    for name, L, bs in (("prefill_chunk_history", 8192, 64), ("longest_prefill_request", 131072, 128)):
+        stride = bs * ROW
+        nblk = (L + bs - 1) // bs
+        nb = pool_bytes // stride
+        copies = nb // nblk
+        pool = torch.randint(0, 256, (nb * stride,), dtype=torch.uint8, device="cuda")
+        perm = np.random.default_rng(L).permutation(nb)[:copies * nblk].astype(np.int32).reshape(copies, 1, nblk)
+        tables = [dev(perm[i]) for i in range(copies)]
+        cu = dev(np.array([0, L], dtype=np.int32))
+        out = torch.empty((L, ROW), dtype=torch.uint8, device="cuda")
+        tg = EventTimer()
+        for i in range(warmup):
+            dsi.gather_prefill_k(pool, bs, tables[i % copies], cu, out=out, block_stride_bytes=stride,
+                                 num_blocks=nb)
+        torch.cuda.synchronize()
+        queue_ahead(steps, 50)
+        for i in range(warmup, warmup + steps):
+            s = tg.start() if i >= warmup else None
+            dsi.gather_prefill_k(pool, bs, tables[i % copies], cu, out=out, block_stride_bytes=stride,
+                                 num_blocks=nb)
+            if i >= warmup:
+                tg.stop(s)
+        ms = tg.mean_ms()
+        nbytes = 2 * ROW * L + 4 * nblk + 8
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = dict(tokens=L, block_size=bs, us=round(ms * 1e3, 2), algorithmic_bytes=nbytes,
+                         gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        del pool, tables, out
+    return res
 
 
 # --------------------------------------------------------------------------- hierarchical sparse
@@ -342,6 +389,7 @@ def bench_sparse(steps, warmup):
         step(False)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_ahead(steps)
     a.record()
     for _ in range(steps):
         step(True)
@@ -395,6 +443,8 @@ def main():
             extra[f"decode_w{n}"] = bench_decode(n, args.steps, args.warmup)
         log("hierarchical sparse ...")
         extra["sparse_w5"] = bench_sparse(args.steps, args.warmup)
+        log("prefill K gather ...")
+        extra["prefill_gather"] = bench_gather(args.steps, args.warmup)
     log("cpu baseline ...")
     cpu = cpu_baseline(pf["c"], args.cpu_seconds)
     line = {

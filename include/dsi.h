@@ -253,6 +253,37 @@ DSI_API int dsi_req_index_to_global_slot(const int32_t* idx, int64_t idx_ld, int
                                  int32_t bt_width, int32_t num_reqs, int32_t block_size, int32_t block_span, int32_t* out,
                                  int64_t out_ld, hipStream_t stream);
 
+/*
+ * Prefill K gather: the history K of a prefill chunk's requests copied out of
+ * the paged cache into contiguous 132-byte rows, the input of
+ * dsi_mqa_logits_prefill and of the gathered form of dsi_sparse_mqa_logits
+ * (P3 prefill/decode table: prefill collects the history K before scoring,
+ * decode reads the cache where it lies; P1 implementation breakdown: the
+ * indexer's forward chains the prefill K gather with paged decode).
+ * The requests lie end to end: request r owns rows [cu_seq_lens[r],
+ * cu_seq_lens[r+1]) of k_rows and its row cu_seq_lens[r] + p is its token p,
+ * read from
+ *   pool + block_table[r*bt_ld + p/block_size]*block_stride_bytes
+ *        + (p % block_size)*132
+ * and copied byte for byte.  Rows that no request owns, and tokens whose
+ * block index p/block_size >= bt_width or whose page id is outside
+ * [0, num_blocks), are written as zero rows.  Exactly rows [0, S) are written.
+ *   pool         paged cache, num_blocks blocks of block_stride_bytes.
+ *   block_table  int32 [num_reqs][bt_ld]: the chunk's requests' tables.
+ *   cu_seq_lens  int32 [num_reqs + 1], non-decreasing (precondition: with
+ *                decreasing entries the rows they touch are unspecified, but
+ *                no memory outside the arguments is read or written).
+ *   k_rows       [S][132] output, 16-byte aligned.
+ * Errors: EINVAL (nulls with S > 0, S < 0, num_reqs < 0, num_blocks < 0,
+ * block_size < 1, bt_width < 0, bt_ld < bt_width, block_stride_bytes <
+ * block_size*132); EUNSUPPORTED (S > 2^31 - 129); EALIGN (k_rows not 16-byte
+ * aligned, pool or block_stride_bytes not multiples of 4).
+ */
+DSI_API int dsi_gather_prefill_k(const uint8_t* pool, int64_t num_blocks, int32_t block_size,
+                                 int64_t block_stride_bytes, const int32_t* block_table, int64_t bt_ld,
+                                 int32_t bt_width, const int32_t* cu_seq_lens, int32_t num_reqs, uint8_t* k_rows,
+                                 int32_t S, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

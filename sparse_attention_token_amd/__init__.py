@@ -45,6 +45,7 @@ _SIGNATURES = {
     "dsi_topk_remap": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _i32, _p, _i32, _p, _i64, _p]),
     "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _i32, _p,
                                                     _i64, _p]),
+    "dsi_gather_prefill_k": (ctypes.c_int, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32, _p]),
 }
 
 ENTRY_POINTS = tuple(_SIGNATURES)
@@ -317,4 +318,40 @@ def req_index_to_global_slot(idx, block_table, block_size, block_span, row_to_re
                                                   _ptr(block_table), _rows(block_table, "block_table"), bt_width,
                                                   block_table.shape[0], block_size, block_span, _ptr(out), _rows(out, "out"),
                                                   _stream(idx)), "req_index_to_global_slot")
+    return out
+
+
+def gather_prefill_k(pool, block_size, block_table, cu_seq_lens, S=None, out=None, block_stride_bytes=None,
+                     num_blocks=None, bt_width=None):
+    """Paged cache -> contiguous K rows uint8 [S,132] of the chunk's requests laid end to end
+    (cu_seq_lens int32 [num_reqs+1]; S defaults to the row count of `out`)."""
+    dev = _dev(pool, block_table, cu_seq_lens, out)
+    _need(pool, (torch.uint8,), "pool")
+    _need(block_table, _I32, "block_table", 2)
+    _need(cu_seq_lens, _I32, "cu_seq_lens", 1)
+    _contig(pool, "pool")
+    _contig(cu_seq_lens, "cu_seq_lens")
+    if block_stride_bytes is None:
+        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * ROW_BYTES
+    if num_blocks is None:
+        num_blocks = pool.numel() // block_stride_bytes
+    if bt_width is None:
+        bt_width = block_table.shape[1]
+    num_reqs = cu_seq_lens.shape[0] - 1
+    if num_reqs > block_table.shape[0]:
+        raise ValueError("block_table: fewer rows than requests")
+    if out is None:
+        if S is None:
+            raise ValueError("give S (rows to write) or out")
+        out = torch.empty((S, ROW_BYTES), dtype=torch.uint8, device=dev)
+    _need(out, (torch.uint8,), "out")
+    _contig(out, "out")
+    if S is None:
+        S = out.numel() // ROW_BYTES
+    if out.numel() < S * ROW_BYTES:
+        raise ValueError("out: fewer than S rows")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_gather_prefill_k(_ptr(pool), num_blocks, block_size, block_stride_bytes, _ptr(block_table),
+                                          _rows(block_table, "block_table"), bt_width, _ptr(cu_seq_lens), num_reqs,
+                                          _ptr(out), S, _stream(pool)), "gather_prefill_k")
     return out

@@ -152,6 +152,21 @@ def test_remap_and_slot_validation():
     assert f(A16, 4, 2, 0, None, A16, 8, 8, 2, 64, 64, A16, 4, None) == 0
 
 
+def test_gather_validation():
+    f = dsi.lib().dsi_gather_prefill_k
+
+    def call(pool=A16, nb=4, bs=64, stride=64 * 132, bt=A16, bt_ld=8, bt_width=8, cu=A16, nreq=2, out=A16, S=10):
+        return f(pool, nb, bs, stride, bt, bt_ld, bt_width, cu, nreq, out, S, None)
+
+    assert call(S=-1) == EINVAL and call(nreq=-1) == EINVAL and call(bs=0) == EINVAL and call(nb=-1) == EINVAL
+    assert call(bt_ld=7) == EINVAL and call(stride=64 * 132 - 4) == EINVAL and call(bt_width=-1) == EINVAL
+    assert call(pool=None) == EINVAL and call(bt=None) == EINVAL and call(cu=None) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(out=A16 + 4) == EALIGN and call(pool=A16 + 2) == EALIGN and call(stride=64 * 132 + 2) == EALIGN
+    assert call(S=0x7FFFFFFF) == EUNSUP
+    assert call(S=0, pool=None, out=None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsi, "_lib", None)
     monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))

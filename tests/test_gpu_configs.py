@@ -186,3 +186,16 @@ def test_workload5_hierarchical_sparse():
             p = pos[r]
             exp = np.where(p >= 0, c["block_table"][r, np.maximum(p, 0) // bs] * bs + np.maximum(p, 0) % bs, -1)
             assert np.array_equal(slot[r], exp)
+
+
+@pytest.mark.parametrize("L,bs", [(8192, 64), (131072, 128)])
+def test_prefill_gather_full_size(L, bs):
+    """The prefill chunk's history (8192 tokens of 64-token pages) and the longest hierarchical prefill
+    request (131072 tokens of 128-token pages) gathered from a randomly permuted pool, whole output compared
+    with the oracle's gather of the same pool bytes."""
+    c = synth.gather_case(L, [L], bs)
+    pool = np.random.default_rng(L).integers(0, 256, size=c["num_blocks"] * c["block_stride"], dtype=np.uint8)
+    oracle.k_quant_and_cache(c["k"], c["slot_mapping"], pool, bs, c["block_stride"])
+    ref = oracle.gather_prefill_k(pool, c["num_blocks"], bs, c["block_stride"], c["block_table"], c["cu"], L)
+    got = host(dsi.gather_prefill_k(dev(pool), bs, dev(c["block_table"]), dev(c["cu"]), S=L))
+    assert np.array_equal(got, ref)

@@ -386,3 +386,52 @@ def test_sparse_paged_parity(sbk, bs):
     valid = np.isfinite(ref_f32)
     assert np.all(got[~valid] == 0xFF80)
     assert_close(bf16_value(got[valid]), ref_f32[valid], tol_fn=tol_bf16, what="sparse paged logits")
+
+
+# ----------------------------------------------------------------------------- prefill K gather
+def _gather_inputs(seed, lens, bs, span=None):
+    c = synth.gather_case(seed, lens, bs, span)
+    rng = np.random.default_rng(seed + 1000)
+    pool = rng.integers(0, 256, size=c["num_blocks"] * c["block_stride"], dtype=np.uint8)  # garbage elsewhere
+    oracle.k_quant_and_cache(c["k"], c["slot_mapping"], pool, bs, c["block_stride"])
+    return c, pool
+
+
+def _gather_both(c, pool, bs, bt, cu, S, bt_width=None, extra_rows=5):
+    ref = oracle.gather_prefill_k(pool, c["num_blocks"], bs, c["block_stride"], bt, cu, S, bt_width=bt_width)
+    out = torch.full(((S + extra_rows) * ROW,), 0xEE, dtype=torch.uint8, device="cuda")
+    dsi.gather_prefill_k(dev(pool), bs, dev(bt), dev(cu), S=S, out=out, block_stride_bytes=c["block_stride"],
+                         num_blocks=c["num_blocks"], bt_width=bt_width)
+    got = host(out)
+    assert np.all(got[S * ROW:] == 0xEE), "wrote past row S"
+    return got[:S * ROW].reshape(S, ROW), ref
+
+
+@pytest.mark.parametrize("lens,bs,span", [([37, 130, 1], 16, None), ([64, 64, 200], 64, 68), ([5], 8, 9),
+                                          ([0, 17, 0, 33], 16, None), ([3000, 1, 8191, 777], 64, None),
+                                          ([301, 250], 6, 7), ([129, 4, 128], 128, None)])
+def test_gather_bit_exact(lens, bs, span):
+    c, pool = _gather_inputs(sum(lens) + bs, lens, bs, span)
+    got, ref = _gather_both(c, pool, bs, c["block_table"], c["cu"], c["S"])
+    assert np.array_equal(got, ref)
+    # and it is exactly the contiguous quantization of the same k rows
+    assert np.array_equal(got, gathered_rows_oracle(c["k"]))
+
+
+def test_gather_missing_pages_offsets_and_truncation():
+    lens, bs = [100, 45, 260], 16
+    c, pool = _gather_inputs(77, lens, bs)
+    bt = c["block_table"].copy()
+    bt[0, 2] = -1                      # missing page
+    bt[1, 1] = c["num_blocks"] + 3     # page beyond the pool
+    bt[2, 5] = c["num_blocks"]
+    got, ref = _gather_both(c, pool, bs, bt, c["cu"], c["S"])
+    assert np.array_equal(got, ref) and np.all(got[32:48] == 0)
+    # a narrower table, a chunk that starts at row 7, an output longer and one shorter than the chunk
+    for cu, S, width in [(c["cu"], c["S"], 3), (c["cu"] + 7, c["S"] + 20, None), (c["cu"], 150, None),
+                         (c["cu"] + 1, 3, None)]:
+        got, ref = _gather_both(c, pool, bs, bt, cu, S, bt_width=width)
+        assert np.array_equal(got, ref), (S, width)
+    # no requests: every row is zero
+    got, ref = _gather_both(c, pool, bs, bt, np.zeros(1, dtype=np.int32), 9)
+    assert np.array_equal(got, ref) and not got.any()
