@@ -52,6 +52,7 @@ def _load():
                                          _i64, _i32, _p, _i64]),
         "orc_topk_remap": (None, [_p, _i64, _i32, _i32, _p, _i64, _p, _i32, _p, _i64]),
         "orc_gather_prefill_k": (None, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32]),
+        "orc_q_rope_quant": (None, [_p, _p, _i32, _p, _i64, _i32, _p, ctypes.c_float, ctypes.c_float, _p, _p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -276,3 +277,23 @@ def gather_prefill_k(pool, num_blocks, block_size, block_stride, block_table, cu
     lib.orc_gather_prefill_k(_ptr(pool), num_blocks, block_size, block_stride, _ptr(bt), bt_ld, bt_width, _ptr(cu),
                              num_reqs, _ptr(out), S)
     return out
+
+
+# ---------------------------------------------------------------- O10
+def q_rope_quant(q_bf16, positions, cos_sin, w_bf16, softmax_scale, head_scale, interleave=False):
+    """q bf16 [T,64,128] (uint16), positions int64 [T], cos_sin fp32 [max_pos,64] (32 cosines then 32 sines),
+    w bf16 [T,64] -> (FP8 codes uint8 [T,64,128], bf16 weights uint16 [T,64])."""
+    lib = _load()
+    q = _c(q_bf16, np.uint16)
+    T = q.shape[0]
+    assert q.shape == (T, H, D)
+    pos = _c(positions, np.int64)
+    cs = _c(cos_sin, np.float32)
+    assert cs.ndim == 2 and cs.shape[1] == 64
+    w = _c(w_bf16, np.uint16)
+    assert w.shape == (T, H)
+    q8 = np.empty((T, H, D), dtype=np.uint8)
+    w_out = np.empty((T, H), dtype=np.uint16)
+    lib.orc_q_rope_quant(_ptr(q), _ptr(pos), T, _ptr(cs), cs.shape[0], int(bool(interleave)), _ptr(w),
+                         float(softmax_scale), float(head_scale), _ptr(q8), _ptr(w_out))
+    return q8, w_out

@@ -471,3 +471,56 @@ void orc_gather_prefill_k(const uint8_t* pool, int64_t num_blocks, int32_t block
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* O10 q preparation: RoPE, FP8 quantization and weight fold in one pass     */
+/* (P3 indexer steps ③ and ④: rotary position embedding on the first 64 of  */
+/* the 128 dims only, then one FP8 scale per 128 values of q, and the q     */
+/* scale multiplied into the head weights together with the softmax and    */
+/* head scales, weights * q_scale * softmax_scale * head_scale in that      */
+/* order; P3 pitfalls: the indexer's RoPE has its own interleave switch;    */
+/* P1 implementation breakdown: the fused q kernel writes the weights as    */
+/* bf16 directly, the fp32 result rounded once).                            */
+/* RoPE on frequency i (0..31) rotates the pair (a, b) = (i, i+32) when not */
+/* interleaved, (2i, 2i+1) when interleaved, by the angle whose cosine and  */
+/* sine are cos_sin[pos][i] and cos_sin[pos][32+i]:                         */
+/*   a' = a*cos - b*sin,  b' = b*cos + a*sin   (each op one fp32 rounding). */
+/* Quantization uses the k rule: scale = max(amax, 1e-4)/448, codes =       */
+/* E4M3(x/scale).  A position outside [0, max_pos) gives zero codes and a   */
+/* zero weight.                                                             */
+/* ------------------------------------------------------------------------ */
+void orc_q_rope_quant(const uint16_t* q, const int64_t* positions, int32_t T, const float* cos_sin, int64_t max_pos,
+                      int32_t interleave, const uint16_t* w, float softmax_scale, float head_scale, uint8_t* q8,
+                      uint16_t* w_out) {
+  int32_t t, h, i, d;
+  for (t = 0; t < T; t++) {
+    int64_t pos = positions[t];
+    for (h = 0; h < ORC_H; h++) {
+      const uint16_t* src = q + ((int64_t)t * ORC_H + h) * ORC_D;
+      uint8_t* dst = q8 + ((int64_t)t * ORC_H + h) * ORC_D;
+      float x[ORC_D], amax = 0.0f, scale, wf;
+      if (pos < 0 || pos >= max_pos) {
+        memset(dst, 0, ORC_D);
+        w_out[(int64_t)t * ORC_H + h] = 0;
+        continue;
+      }
+      for (d = 0; d < ORC_D; d++) x[d] = orc_bf16_to_f32(src[d]);
+      for (i = 0; i < 32; i++) {
+        int a = interleave ? 2 * i : i, b = interleave ? 2 * i + 1 : i + 32;
+        float c = cos_sin[pos * 64 + i], s = cos_sin[pos * 64 + 32 + i];
+        float xa = x[a], xb = x[b];
+        x[a] = xa * c - xb * s;
+        x[b] = xb * c + xa * s;
+      }
+      for (d = 0; d < ORC_D; d++)
+        if (fabsf(x[d]) > amax) amax = fabsf(x[d]);
+      scale = (amax > 1e-4f ? amax : 1e-4f) / 448.0f;
+      for (d = 0; d < ORC_D; d++) dst[d] = orc_e4m3_encode(x[d] / scale);
+      wf = orc_bf16_to_f32(w[(int64_t)t * ORC_H + h]);
+      wf = wf * scale;
+      wf = wf * softmax_scale;
+      wf = wf * head_scale;
+      w_out[(int64_t)t * ORC_H + h] = orc_bf16_rne(wf);
+    }
+  }
+}

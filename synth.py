@@ -123,6 +123,24 @@ def gather_case(seed, lens, block_size, span=None, extra_blocks=3):
                 block_stride=span * ROW, slot_mapping=slots_for(lens, bt, block_size), S=int(cu[-1]))
 
 
+def rope_cache(max_pos, base=10000.0):
+    """Rotary table [max_pos, 64] fp32: cos of the 32 frequencies base^(-2i/64) times the position, then their
+    sines (computed in fp64, rounded once)."""
+    inv = base ** (-np.arange(32, dtype=np.float64) * 2.0 / 64.0)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def q_prep_case(seed, T, max_pos=65536):
+    """Unrotated bf16 q [T,64,128] ~ N(0,1), positions ~ U{0..max_pos-1}, raw bf16 head weights ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(0, max_pos, size=T).astype(np.int64)
+    q = _bf16_bits(rng.standard_normal((T, H, D), dtype=np.float32))
+    w = _bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    return dict(q=q, positions=pos, w=w, cos_sin=rope_cache(max_pos), T=T,
+                softmax_scale=float(D) ** -0.5, head_scale=float(H) ** -0.5)
+
+
 # --------------------------------------------------------------------------- hierarchical sparse
 def draw_candidates(rng, maxb, num=64, distinct=60, dup=2):
     """Per row: `distinct` different ids from [0, maxb), `dup` repeats of those, one -1 and one id >= maxb,
