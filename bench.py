@@ -11,7 +11,8 @@ exactly to f16 and contracted on the f16 matrix cores, so its peak is the dense 
 measured on this device (register-only MFMA loops, a 4 GiB streaming read), the oracle's single-thread CPU
 rate on a bounded row sample, and the decode and hierarchical workloads (paged decode 64 x U{4096..65536};
 long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows + 1024 prefill rows)
-with their HBM roofline fractions, and the prefill K gather out of the paged cache (8192 and 131072 tokens).
+with their HBM roofline fractions, the prefill K gather out of the paged cache (8192 and 131072 tokens) and the q
+preparation (RoPE, FP8 quantization, weight fold) of the 2048-token chunk.
 Diagnostics go to stderr.
 
 `roofline.traffic` (HBM bytes per launch of the prefill logits kernel) comes from the committed counter
@@ -342,6 +343,31 @@ def bench_gather(steps, warmup, pool_bytes=512 << 20):
     return res
 
 
+# --------------------------------------------------------------------------- q preparation
+def bench_qprep(steps, warmup, T=2048, copies=16):
+    """q RoPE + FP8 quantization + weight fold for the prefill chunk's 2048 tokens.  16 copies of the bf16 q
+    (537 MB) rotate so that each call reads q from HBM."""
+    c = synth.q_prep_case(2, T, max_pos=8192)
+    qs = [dev(c["q"]) for _ in range(copies)]
+    pos, cs, w = dev(c["positions"]), dev(c["cos_sin"]), dev(c["w"])
+    q8 = torch.empty((T, 64, 128), dtype=torch.uint8, device="cuda")
+    wo = torch.empty((T, 64), dtype=torch.int16, device="cuda")
+    for i in range(warmup):
+        dsi.q_rope_quant(qs[i % copies], pos, cs, w, c["softmax_scale"], c["head_scale"], out=(q8, wo))
+    torch.cuda.synchronize()
+    tq = EventTimer()
+    queue_ahead(steps, 50)
+    for i in range(steps):
+        s = tq.start()
+        dsi.q_rope_quant(qs[i % copies], pos, cs, w, c["softmax_scale"], c["head_scale"], out=(q8, wo))
+        tq.stop(s)
+    ms = tq.mean_ms()
+    nbytes = T * (64 * (256 + 128 + 2 + 2) + 256 + 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(tokens=T, us=round(ms * 1e3, 2), algorithmic_bytes=nbytes, gbs=round(gbs, 1),
+                hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
 # --------------------------------------------------------------------------- hierarchical sparse
 def bench_sparse(steps, warmup):
     c = synth.workload(5)
@@ -445,6 +471,8 @@ def main():
         extra["sparse_w5"] = bench_sparse(args.steps, args.warmup)
         log("prefill K gather ...")
         extra["prefill_gather"] = bench_gather(args.steps, args.warmup)
+        log("q preparation ...")
+        extra["q_prep"] = bench_qprep(args.steps, args.warmup)
     log("cpu baseline ...")
     cpu = cpu_baseline(pf["c"], args.cpu_seconds)
     line = {

@@ -284,6 +284,36 @@ DSI_API int dsi_gather_prefill_k(const uint8_t* pool, int64_t num_blocks, int32_
                                  int32_t bt_width, const int32_t* cu_seq_lens, int32_t num_reqs, uint8_t* k_rows,
                                  int32_t S, hipStream_t stream);
 
+/*
+ * q preparation in one pass (P3 indexer steps ③ and ④, P3 pitfalls; P1
+ * implementation breakdown: the fused q kernel writes bf16 head weights, the
+ * fp32 result rounded once).  For token t and head h, with x the 128 bf16
+ * values of q widened to fp32 and p = positions[t]:
+ *   RoPE on dims 0..63 only: frequency i (0..31) rotates the pair (a, b) =
+ *     (i, i+32), or (2i, 2i+1) when interleave != 0, by c = cos_sin[p][i],
+ *     s = cos_sin[p][32+i]:  a' = a*c - b*s,  b' = b*c + a*s
+ *     (each product and sum one fp32 rounding, no fused multiply-add);
+ *   scale = max(amax, 1e-4)/448, q8[t][h][d] = E4M3FN(x[d]/scale) (IEEE
+ *     division, nearest even, saturating) — the k quantization rule;
+ *   w_out[t][h] = bf16(((w[t][h] * scale) * softmax_scale) * head_scale),
+ *     fp32 products, rounded to bf16 once (nearest even).
+ * A position outside [0, max_pos) gives zero codes and a zero weight.
+ *   q          bf16 [T][q_ld], head h at elements h*128 .. h*128+127;
+ *              16-byte aligned, q_ld a multiple of 8.
+ *   positions  int64 [T].
+ *   cos_sin    fp32 [max_pos][64]: the 32 cosines, then the 32 sines;
+ *              16-byte aligned.
+ *   w          bf16 [T][w_ld], the raw head weights.
+ *   q8         e4m3 [T][64][128] contiguous (8-byte aligned): the input of
+ *              the logits calls.  w_out bf16 [T][64] contiguous.
+ * Errors: EINVAL (nulls with T > 0, T < 0, q_ld < 8192, w_ld < 64,
+ * max_pos < 1); EALIGN.
+ */
+DSI_API int dsi_q_rope_quant(const uint16_t* q, int64_t q_ld, int32_t T, const int64_t* positions,
+                             const float* cos_sin, int64_t max_pos, int32_t interleave, const uint16_t* w,
+                             int64_t w_ld, float softmax_scale, float head_scale, uint8_t* q8, uint16_t* w_out,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _i32, _p,
                                                     _i64, _p]),
     "dsi_gather_prefill_k": (ctypes.c_int, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32, _p]),
+    "dsi_q_rope_quant": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i64, _i32, _p, _i64, ctypes.c_float,
+                                        ctypes.c_float, _p, _p, _p]),
 }
 
 ENTRY_POINTS = tuple(_SIGNATURES)
@@ -355,3 +357,33 @@ def gather_prefill_k(pool, block_size, block_table, cu_seq_lens, S=None, out=Non
                                           _rows(block_table, "block_table"), bt_width, _ptr(cu_seq_lens), num_reqs,
                                           _ptr(out), S, _stream(pool)), "gather_prefill_k")
     return out
+
+
+def q_rope_quant(q, positions, cos_sin, w, softmax_scale, head_scale, interleave=False, out=None):
+    """bf16 q [T,64,128] (or [T, q_ld] rows), int64 positions [T], fp32 cos_sin [max_pos,64], bf16 w [T, >=64]
+    -> (e4m3 q8 uint8 [T,64,128], bf16 weights [T,64] as int16 bit patterns)."""
+    dev = _dev(q, positions, cos_sin, w)
+    _need(q, _BF16, "q")
+    _need(positions, (torch.int64,), "positions", 1)
+    _need(cos_sin, (torch.float32,), "cos_sin", 2)
+    _need(w, _BF16, "w", 2)
+    _contig(positions, "positions")
+    _contig(cos_sin, "cos_sin")
+    T = q.shape[0]
+    q2 = q.reshape(T, -1) if q.dim() == 3 and q.is_contiguous() else q
+    q_ld = _rows(q2, "q")
+    if cos_sin.shape[1] != 64:
+        raise ValueError("cos_sin: need [max_pos, 64]")
+    if out is None:
+        out = (torch.empty((T, HEADS, HEAD_DIM), dtype=torch.uint8, device=dev),
+               torch.empty((T, HEADS), dtype=torch.int16, device=dev))
+    q8, w_out = out
+    _need(q8, (torch.uint8,), "q8")
+    _need(w_out, _BF16, "w_out")
+    _contig(q8, "q8")
+    _contig(w_out, "w_out")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_q_rope_quant(_ptr(q2), q_ld, T, _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
+                                      int(bool(interleave)), _ptr(w), _rows(w, "w"), float(softmax_scale),
+                                      float(head_scale), _ptr(q8), _ptr(w_out), _stream(q)), "q_rope_quant")
+    return q8, w_out

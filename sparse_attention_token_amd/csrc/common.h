@@ -73,6 +73,27 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (uint32_t)m;
 }
 
+// Four fp32 -> four E4M3FN codes (one dword, little-endian) on the hardware converter
+// (v_cvt_pk_fp8_f32): nearest even, sign kept for results that round to zero.  On every
+// fp32 input with |x| <= 464 it returns exactly what f32_to_e4m3 does (checked on the
+// device over all such bit patterns); callers keep |x| in that range.
+__device__ __forceinline__ uint32_t e4m3x4_hw(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// x / s rounded to nearest even, given y = RN(1/s): q = RN(x*y) is faithful, the remainder
+// x - q*s is exact in one fused multiply-add, and RN(q + remainder*y) is the correctly
+// rounded quotient whenever it is a normal number (Markstein's theorem; Handbook of
+// Floating-Point Arithmetic, division by fused multiply-add).  The sign is copied from x, so
+// a quotient that underflows keeps the sign an IEEE division gives it.  One IEEE division
+// per row (for y) replaces one per element.
+__device__ __forceinline__ float div_rn_by(float x, float s, float y) {
+  const float q = __fmul_rn(x, y);
+  const float r = __builtin_fmaf(-q, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+}
+
 // Four E4M3FN codes (one dword, little-endian) -> four f16 (two dwords), exact.
 __device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));

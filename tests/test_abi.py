@@ -167,6 +167,21 @@ def test_gather_validation():
     assert call(S=0, pool=None, out=None) == 0
 
 
+def test_q_rope_quant_validation():
+    f = dsi.lib().dsi_q_rope_quant
+
+    def call(q=A16, q_ld=8192, T=4, pos=A16, cs=A16, max_pos=16, w=A16, w_ld=64, q8=A16, wo=A16):
+        return f(q, q_ld, T, pos, cs, max_pos, 0, w, w_ld, 1.0, 1.0, q8, wo, None)
+
+    assert call(T=-1) == EINVAL and call(q_ld=8191) == EINVAL and call(w_ld=63) == EINVAL
+    assert call(max_pos=0) == EINVAL
+    for k in ("q", "pos", "cs", "w", "q8", "wo"):
+        assert call(**{k: None}) == EINVAL, k
+    assert call(q=A16 + 8) == EALIGN and call(q_ld=8196) == EALIGN and call(cs=A16 + 4) == EALIGN
+    assert call(pos=A16 + 4) == EALIGN and call(q8=A16 + 4) == EALIGN and call(wo=A16 + 1) == EALIGN
+    assert call(T=0, q=None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsi, "_lib", None)
     monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))

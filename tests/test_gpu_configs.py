@@ -199,3 +199,15 @@ def test_prefill_gather_full_size(L, bs):
     ref = oracle.gather_prefill_k(pool, c["num_blocks"], bs, c["block_stride"], c["block_table"], c["cu"], L)
     got = host(dsi.gather_prefill_k(dev(pool), bs, dev(c["block_table"]), dev(c["cu"]), S=L))
     assert np.array_equal(got, ref)
+
+
+def test_q_prep_full_chunk():
+    """The 2048-token prefill chunk's q (64 heads x 128 dims) rotated, quantized and folded; every code and
+    weight compared bit for bit with the oracle."""
+    c = synth.q_prep_case(2, 2048, max_pos=8192)
+    ref_q8, ref_w = oracle.q_rope_quant(c["q"], c["positions"], c["cos_sin"], c["w"], c["softmax_scale"],
+                                        c["head_scale"])
+    q8, w_out = dsi.q_rope_quant(dev(c["q"]), dev(c["positions"]), dev(c["cos_sin"]), dev(c["w"]),
+                                 c["softmax_scale"], c["head_scale"])
+    assert np.array_equal(host(q8), ref_q8)
+    assert np.array_equal(host(w_out), ref_w)

@@ -435,3 +435,25 @@ def test_gather_missing_pages_offsets_and_truncation():
     # no requests: every row is zero
     got, ref = _gather_both(c, pool, bs, bt, np.zeros(1, dtype=np.int32), 9)
     assert np.array_equal(got, ref) and not got.any()
+
+
+# ----------------------------------------------------------------------------- q RoPE + quant + weight fold
+@pytest.mark.parametrize("interleave", [False, True])
+def test_q_rope_quant_bit_exact_strided(interleave):
+    T, max_pos = 37, 4096
+    c = synth.q_prep_case(31 + interleave, T, max_pos=max_pos)
+    q, pos, w = c["q"].copy(), c["positions"].copy(), c["w"]
+    pos[3], pos[7] = -1, max_pos          # outside the table: zero rows
+    q[5, 9] = 0                           # an all-zero head row: scale 1e-4/448
+    q[6, 2] = synth._bf16_bits(synth._bf16_value(q[6, 2]) * np.float32(1e-30))  # tiny values
+    ref_q8, ref_w = oracle.q_rope_quant(q, pos, c["cos_sin"], w, c["softmax_scale"], c["head_scale"], interleave)
+    # q as a column slice of a wider projection output, w as a slice of [T, 192]
+    q_wide = np.zeros((T, 64 * 128 + 64), np.uint16)
+    q_wide[:, :8192] = q.reshape(T, -1)
+    w_wide = np.zeros((T, 192), np.uint16)
+    w_wide[:, 128:] = w
+    qt, wt = dev(q_wide), dev(w_wide)
+    q8, w_out = dsi.q_rope_quant(qt[:, :8192], dev(pos), dev(c["cos_sin"]), wt[:, 128:], c["softmax_scale"],
+                                 c["head_scale"], interleave=interleave)
+    assert np.array_equal(host(q8), ref_q8)
+    assert np.array_equal(host(w_out), ref_w)
