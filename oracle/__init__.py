@@ -52,6 +52,8 @@ def _load():
                                          _i64, _i32, _p, _i64]),
         "orc_topk_remap": (None, [_p, _i64, _i32, _i32, _p, _i64, _p, _i32, _p, _i64]),
         "orc_gather_prefill_k": (None, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32]),
+        "orc_topk_values": (None, [_p, _i64, _i32, _p, _i32, _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64]),
+        "orc_topk_merge": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i64]),
         "orc_q_rope_quant": (None, [_p, _p, _i32, _p, _i64, _i32, _p, ctypes.c_float, ctypes.c_float, _p, _p]),
     }
     for name, (res, args) in sig.items():
@@ -297,3 +299,34 @@ def q_rope_quant(q_bf16, positions, cos_sin, w_bf16, softmax_scale, head_scale, 
     lib.orc_q_rope_quant(_ptr(q), _ptr(pos), T, _ptr(cs), cs.shape[0], int(bool(interleave)), _ptr(w),
                          float(softmax_scale), float(head_scale), _ptr(q8), _ptr(w_out))
     return q8, w_out
+
+
+# ---------------------------------------------------------------- O11, O12
+def topk_values(logits, idx, starts=None, index_scale=1, index_offset=0, max_width=None):
+    """(values fp32, global indices int32) [rows, k] of one rank's local top-k selection `idx` (relative to
+    the row starts) over its fp32 logits [rows, >=max_width]."""
+    lib = _load()
+    x, ld = _rows(np.asarray(logits, dtype=np.float32), np.float32)
+    ix, ild = _rows(np.asarray(idx, dtype=np.int32), np.int32)
+    rows, k = ix.shape
+    st = None if starts is None else _c(starts, np.int32)
+    if max_width is None:
+        max_width = x.shape[1]
+    vals = np.empty((rows, k), dtype=np.float32)
+    g = np.empty((rows, k), dtype=np.int32)
+    lib.orc_topk_values(_ptr(x), ld, rows, _ptr(st), max_width, _ptr(ix), ild, k, index_scale, index_offset,
+                        _ptr(vals), k, _ptr(g), k)
+    return vals, g
+
+
+def topk_merge(vals, gidx, k):
+    """Candidate lists [num_lists, rows, k_in] (fp32 values, int32 global indices) -> int32 [rows, k]: the
+    indices of the k largest finite values with index >= 0, (value desc, index asc), then -1."""
+    lib = _load()
+    v = _c(vals, np.float32)
+    g = _c(gidx, np.int32)
+    assert v.shape == g.shape and v.ndim == 3
+    L, rows, k_in = v.shape
+    out = np.empty((rows, k), dtype=np.int32)
+    assert lib.orc_topk_merge(_ptr(v), _ptr(g), rows * k_in, k_in, L, rows, k_in, k, _ptr(out), k) == 0
+    return out

@@ -524,3 +524,68 @@ void orc_q_rope_quant(const uint16_t* q, const int64_t* positions, int32_t T, co
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* O11 one rank's top-k candidates under context parallelism (P3 pitfalls:  */
+/* with the context split across ranks, each rank keeps only its local      */
+/* top-k candidates, and those, not the score matrix, are exchanged).       */
+/* Entry j of row r: the rank-local selection p = idx[r][j] (relative to    */
+/* the row's start, as dsi_topk_select emits it) becomes the pair           */
+/*   value = logits[r][start + p],  global index = p*scale + offset;        */
+/* an empty slot (p < 0) or a column at or past max_width gives (-inf, -1). */
+/* ------------------------------------------------------------------------ */
+void orc_topk_values(const float* logits, int64_t ld, int32_t rows, const int32_t* starts, int32_t max_width,
+                     const int32_t* idx, int64_t idx_ld, int32_t k, int32_t index_scale, int32_t index_offset,
+                     float* vals, int64_t vals_ld, int32_t* gidx, int64_t gidx_ld) {
+  int32_t r, j;
+  for (r = 0; r < rows; r++) {
+    int32_t st = starts ? starts[r] : 0;
+    if (st < 0) st = 0;
+    for (j = 0; j < k; j++) {
+      int32_t p = idx[(int64_t)r * idx_ld + j];
+      float* v = vals + (int64_t)r * vals_ld + j;
+      int32_t* g = gidx + (int64_t)r * gidx_ld + j;
+      if (p < 0 || (int64_t)st + p >= max_width) {
+        *v = -INFINITY;
+        *g = -1;
+      } else {
+        *v = logits[(int64_t)r * ld + st + p];
+        *g = (int32_t)((int64_t)p * index_scale + index_offset);
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O12 merge of the ranks' candidate lists into the global top-k (P3        */
+/* pitfalls: the global top-k is chosen from the exchanged local            */
+/* candidates; it is exact because a token in the global top-k is also in   */
+/* the local top-k of the rank that holds it).  Row r of list l holds k_in  */
+/* (value, global index) pairs at l*list_stride + r*row_ld.  Pairs with a   */
+/* negative index or a non-finite value are ignored; the output is the      */
+/* indices of the k largest values, in the order (value desc, index asc),   */
+/* then -1.  Returns 0, or -1 if the scratch allocation fails.              */
+/* ------------------------------------------------------------------------ */
+int orc_topk_merge(const float* vals, const int32_t* gidx, int64_t list_stride, int64_t row_ld, int32_t num_lists,
+                   int32_t rows, int32_t k_in, int32_t k, int32_t* out, int64_t out_ld) {
+  int32_t r, l, j, n;
+  orc_vc* buf = (orc_vc*)malloc(sizeof(orc_vc) * (size_t)(num_lists * k_in > 0 ? num_lists * k_in : 1));
+  if (!buf) return -1;
+  for (r = 0; r < rows; r++) {
+    n = 0;
+    for (l = 0; l < num_lists; l++) {
+      for (j = 0; j < k_in; j++) {
+        int64_t a = (int64_t)l * list_stride + (int64_t)r * row_ld + j;
+        if (gidx[a] >= 0 && isfinite(vals[a])) {
+          buf[n].v = vals[a];
+          buf[n].c = gidx[a];
+          n++;
+        }
+      }
+    }
+    qsort(buf, (size_t)n, sizeof(orc_vc), cmp_vc);
+    for (j = 0; j < k; j++) out[(int64_t)r * out_ld + j] = j < n ? buf[j].c : -1;
+  }
+  free(buf);
+  return 0;
+}
