@@ -12,7 +12,8 @@ measured on this device (register-only MFMA loops, a 4 GiB streaming read), the 
 rate on a bounded row sample, and the decode and hierarchical workloads (paged decode 64 x U{4096..65536};
 long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows + 1024 prefill rows)
 with their HBM roofline fractions, the prefill K gather out of the paged cache (8192 and 131072 tokens) and the q
-preparation (RoPE, FP8 quantization, weight fold) of the 2048-token chunk.
+preparation (RoPE, FP8 quantization, weight fold) of the 2048-token chunk, and the context-parallel merge of 8 ranks'
+top-2048 lists for 64 decode rows.
 Diagnostics go to stderr.
 
 `roofline.traffic` (HBM bytes per launch of the prefill logits kernel) comes from the committed counter
@@ -368,6 +369,29 @@ def bench_qprep(steps, warmup, T=2048, copies=16):
                 hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
 
 
+# --------------------------------------------------------------------------- context-parallel merge
+def bench_merge(steps, warmup, rows=64, ranks=8):
+    """Merge of 8 ranks' local top-2048 candidate lists for the 64 rows of a decode step (what each rank
+    receives from the all-gather): global top-2048 per row."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    vals = torch.randn((ranks, rows, K), generator=g, device="cuda", dtype=torch.float32)
+    gidx = torch.arange(ranks * rows * K, dtype=torch.int32, device="cuda").view(ranks, rows, K)
+    out = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsi.topk_merge_workspace_bytes(rows, ranks, K), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        dsi.topk_merge(vals, gidx, k=K, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    tm = EventTimer()
+    queue_ahead(steps, 100)
+    for _ in range(steps):
+        s = tm.start()
+        dsi.topk_merge(vals, gidx, k=K, out=out, workspace=ws)
+        tm.stop(s)
+    ms = tm.mean_ms()
+    return dict(rows=rows, ranks=ranks, candidates_per_row=ranks * K, us=round(ms * 1e3, 2),
+                exchanged_bytes_per_rank=rows * K * 8)
+
+
 # --------------------------------------------------------------------------- hierarchical sparse
 def bench_sparse(steps, warmup):
     c = synth.workload(5)
@@ -473,6 +497,8 @@ def main():
         extra["prefill_gather"] = bench_gather(args.steps, args.warmup)
         log("q preparation ...")
         extra["q_prep"] = bench_qprep(args.steps, args.warmup)
+        log("context-parallel merge ...")
+        extra["cp_merge"] = bench_merge(args.steps, args.warmup)
     log("cpu baseline ...")
     cpu = cpu_baseline(pf["c"], args.cpu_seconds)
     line = {

@@ -314,6 +314,50 @@ DSI_API int dsi_q_rope_quant(const uint16_t* q, int64_t q_ld, int32_t T, const i
                              int64_t w_ld, float softmax_scale, float head_scale, uint8_t* q8, uint16_t* w_out,
                              hipStream_t stream);
 
+/*
+ * One rank's top-k candidates under context parallelism (P3 pitfalls: with a
+ * request's context split across ranks, each rank keeps only its local top-k
+ * candidates, and those, not the score matrix, are exchanged).  For row r and
+ * j < k, with p = idx[r][j] (a selection relative to the row's start, as
+ * dsi_topk_select emits it) and start = row_starts ? max(row_starts[r], 0) : 0:
+ *   vals[r][j] = logits[r][start + p],
+ *   gidx[r][j] = p*index_scale + index_offset   (int32, wrapping),
+ * and (-inf, -1) where p < 0 or start + p >= max_width.  The scale and offset
+ * map the rank's columns to positions in the whole context: 1 and the slice's
+ * first position for contiguous slices, R and the rank for round-robin ones.
+ *   logits fp32 [rows][ld], ld >= max_width; idx int32 [rows][idx_ld];
+ *   vals fp32 [rows][vals_ld]; gidx int32 [rows][gidx_ld]; lds >= k.
+ * Errors: EINVAL (nulls with rows, k > 0; negative sizes; lds too small);
+ * EUNSUPPORTED (rows > 65535); EALIGN (pointers not 4-byte aligned).
+ */
+DSI_API int dsi_topk_values(const float* logits, int64_t ld, int32_t rows, const int32_t* row_starts, int32_t max_width,
+                            const int32_t* idx, int64_t idx_ld, int32_t k, int32_t index_scale, int32_t index_offset,
+                            float* vals, int64_t vals_ld, int32_t* gidx, int64_t gidx_ld, hipStream_t stream);
+
+/* Workspace bytes dsi_topk_merge needs (0 for empty sizes). */
+DSI_API size_t dsi_topk_merge_workspace_bytes(int32_t rows, int32_t num_lists, int32_t k_in);
+
+/*
+ * Merge of the ranks' exchanged candidate lists into the global top-k (P3
+ * pitfalls: the global top-k is chosen from the local candidates; exact, as a
+ * token of the global top-k is in the local top-k of the rank holding it).
+ * Row r of list l holds k_in (value, global index) pairs at
+ * l*list_stride + r*row_ld in `vals` and `gidx` (an all-gather of every rank's
+ * dsi_topk_values output gives list_stride = rows*row_ld).  Pairs with a
+ * negative index or a non-finite value are ignored.  out[r][0 .. m) holds the
+ * global indices of the m = min(k, #valid) largest values, in no particular
+ * order (ties at the boundary broken either way), then -1.
+ *   out int32 [rows][out_ld], out_ld >= k; workspace of
+ *   dsi_topk_merge_workspace_bytes(rows, num_lists, k_in) bytes, 16-byte
+ *   aligned, used by this call only.
+ * Errors: EINVAL (nulls, rows < 0, num_lists < 1, k_in < 1, row_ld < k_in,
+ * out_ld < k); EUNSUPPORTED (k not in 1..2048, num_lists*k_in >= 2^31,
+ * rows > 65535); EWORKSPACE; EALIGN.
+ */
+DSI_API int dsi_topk_merge(const float* vals, const int32_t* gidx, int64_t list_stride, int64_t row_ld,
+                           int32_t num_lists, int32_t rows, int32_t k_in, int32_t k, int32_t* out, int64_t out_ld,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

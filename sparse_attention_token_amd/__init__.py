@@ -46,6 +46,9 @@ _SIGNATURES = {
     "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _i32, _p,
                                                     _i64, _p]),
     "dsi_gather_prefill_k": (ctypes.c_int, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32, _p]),
+    "dsi_topk_values": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64, _p]),
+    "dsi_topk_merge_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "dsi_topk_merge": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i64, _p, _sz, _p]),
     "dsi_q_rope_quant": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i64, _i32, _p, _i64, ctypes.c_float,
                                         ctypes.c_float, _p, _p, _p]),
 }
@@ -387,3 +390,50 @@ def q_rope_quant(q, positions, cos_sin, w, softmax_scale, head_scale, interleave
                                       int(bool(interleave)), _ptr(w), _rows(w, "w"), float(softmax_scale),
                                       float(head_scale), _ptr(q8), _ptr(w_out), _stream(q)), "q_rope_quant")
     return q8, w_out
+
+
+def topk_values(logits, idx, row_starts=None, index_scale=1, index_offset=0, max_width=None, out=None):
+    """One rank's local top-k selection -> (fp32 values, int32 global indices) [rows, k]."""
+    dev = _dev(logits, idx, row_starts)
+    _need(logits, (torch.float32,), "logits", 2)
+    _need(idx, _I32, "idx", 2)
+    rows, k = idx.shape
+    if max_width is None:
+        max_width = logits.shape[1]
+    if out is None:
+        out = (torch.empty((rows, k), dtype=torch.float32, device=dev),
+               torch.empty((rows, k), dtype=torch.int32, device=dev))
+    vals, gidx = out
+    with torch.cuda.device(dev):
+        _check(lib().dsi_topk_values(_ptr(logits), _rows(logits, "logits"), rows, _ptr(row_starts), max_width,
+                                     _ptr(idx), _rows(idx, "idx"), k, index_scale, index_offset, _ptr(vals),
+                                     _rows(vals, "vals"), _ptr(gidx), _rows(gidx, "gidx"), _stream(idx)),
+               "topk_values")
+    return vals, gidx
+
+
+def topk_merge_workspace_bytes(rows, num_lists, k_in):
+    return lib().dsi_topk_merge_workspace_bytes(rows, num_lists, k_in)
+
+
+def topk_merge(vals, gidx, k=MAX_TOPK, out=None, workspace=None):
+    """Exchanged candidate lists [num_lists, rows, k_in] (fp32 values, int32 global indices) -> int32 [rows, k]
+    global top-k indices, -1 padded."""
+    dev = _dev(vals, gidx, out, workspace)
+    _need(vals, (torch.float32,), "vals", 3)
+    _need(gidx, _I32, "gidx", 3)
+    if vals.shape != gidx.shape or vals.stride() != gidx.stride():
+        raise ValueError("vals and gidx must have the same shape and layout")
+    L, rows, k_in = vals.shape
+    if vals.stride(2) != 1:
+        raise ValueError("vals: candidate entries must be contiguous")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    need = topk_merge_workspace_bytes(rows, L, k_in)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsi_topk_merge(_ptr(vals), _ptr(gidx), vals.stride(0), vals.stride(1), L, rows, k_in, k,
+                                    _ptr(out), _rows(out, "out"), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(vals)), "topk_merge")
+    return out

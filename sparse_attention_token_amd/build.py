@@ -19,7 +19,7 @@ LIB_CEILING = os.path.join(HERE, "libdsi_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quant.hip", "prefill.hip", "gather_logits.hip", "topk.hip", "index.hip", "prefill_gather.hip", "q_prep.hip", "status.cpp"]
+SOURCES = ["quant.hip", "prefill.hip", "gather_logits.hip", "topk.hip", "index.hip", "prefill_gather.hip", "q_prep.hip", "cp_merge.hip", "status.cpp"]
 CEILING_SOURCES = ["ceiling.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",

@@ -182,6 +182,28 @@ def test_q_rope_quant_validation():
     assert call(T=0, q=None) == 0
 
 
+def test_cp_merge_validation():
+    L = dsi.lib()
+    f = L.dsi_topk_values
+    assert f(A16, 8, 2, None, 9, A16, 4, 4, 1, 0, A16, 4, A16, 4, None) == EINVAL  # ld < max_width
+    assert f(A16, 8, 2, None, 8, A16, 3, 4, 1, 0, A16, 4, A16, 4, None) == EINVAL  # idx_ld < k
+    assert f(None, 8, 2, None, 8, A16, 4, 4, 1, 0, A16, 4, A16, 4, None) == EINVAL
+    assert f(A16 + 2, 8, 2, None, 8, A16, 4, 4, 1, 0, A16, 4, A16, 4, None) == EALIGN
+    assert f(None, 8, 0, None, 8, None, 4, 4, 1, 0, None, 4, None, 4, None) == 0
+    need = L.dsi_topk_merge_workspace_bytes(4, 2, 64)
+    assert need >= 4 * 2 * 64 * 4 and L.dsi_topk_merge_workspace_bytes(0, 2, 64) == 0
+    m = L.dsi_topk_merge
+    assert m(A16, A16, 256, 64, 2, 4, 64, 0, A16, 64, A16, need, None) == EUNSUP      # k = 0
+    assert m(A16, A16, 256, 64, 2, 4, 64, 2049, A16, 4096, A16, need, None) == EUNSUP
+    assert m(A16, A16, 256, 63, 2, 4, 64, 16, A16, 64, A16, need, None) == EINVAL     # row_ld < k_in
+    assert m(A16, A16, 256, 64, 0, 4, 64, 16, A16, 64, A16, need, None) == EINVAL     # no lists
+    assert m(A16, A16, 256, 64, 2, 4, 64, 16, A16, 15, A16, need, None) == EINVAL     # out_ld < k
+    assert m(A16, A16, 256, 64, 2, 4, 64, 16, A16, 64, A16, need - 1, None) == EWS
+    assert m(A16, A16, 256, 64, 2, 4, 64, 16, A16, 64, A16 + 4, need, None) == EALIGN
+    assert m(None, A16, 256, 64, 2, 4, 64, 16, A16, 64, A16, need, None) == EINVAL
+    assert m(None, None, 256, 64, 2, 0, 64, 16, None, 64, None, 0, None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsi, "_lib", None)
     monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -457,3 +457,85 @@ def test_q_rope_quant_bit_exact_strided(interleave):
                                  c["head_scale"], interleave=interleave)
     assert np.array_equal(host(q8), ref_q8)
     assert np.array_equal(host(w_out), ref_w)
+
+
+# ----------------------------------------------------------------------------- context-parallel top-k
+def test_topk_values_bit_exact():
+    rng = np.random.default_rng(51)
+    rows, W, k = 5, 3000, 300
+    logits = rng.standard_normal((rows, W)).astype(np.float32)
+    starts = np.array([0, 100, 2999, 5, 1000], np.int32)
+    idx = rng.integers(-1, 2100, size=(rows, k)).astype(np.int32)  # some past max_width from their start
+    ref_v, ref_g = oracle.topk_values(logits, idx, starts=starts, index_scale=3, index_offset=7, max_width=2900)
+    v, g = dsi.topk_values(dev(logits), dev(idx), row_starts=dev(starts), index_scale=3, index_offset=7,
+                           max_width=2900)
+    assert np.array_equal(host(v), ref_v) and np.array_equal(host(g), ref_g)
+
+
+def _candidate_lists(rng, rows, W, R, k, kind):
+    """Oracle-made candidate lists of R contiguous slices of random rows."""
+    x = rng.standard_normal((rows, W)).astype(np.float32)
+    if kind == "ties":
+        x = (np.round(x * 2) / 2).astype(np.float32)
+    elif kind == "nonfinite":
+        m = rng.random((rows, W))
+        x[m < 0.05] = np.inf
+        x[(m >= 0.05) & (m < 0.1)] = np.nan
+    ends = rng.integers(W // 2, W + 1, size=rows).astype(np.int32)
+    ends[0] = 3  # fewer valid values than k
+    bounds = np.linspace(0, W, R + 1).astype(np.int32)
+    vals, gidx = [], []
+    for r in range(R):
+        lo, hi = int(bounds[r]), int(bounds[r + 1])
+        st = np.full(rows, lo, np.int32)
+        idx = oracle.topk_select(x, np.minimum(ends, hi).astype(np.int32), k, starts=st)
+        v, g = oracle.topk_values(x, idx, starts=st, index_offset=lo)
+        vals.append(v)
+        gidx.append(g)
+    return x, ends, np.stack(vals), np.stack(gidx)
+
+
+def _check_merge(got, ref, vals, gidx):
+    for r in range(got.shape[0]):
+        cand = {}
+        for v, g in zip(vals[:, r].ravel(), gidx[:, r].ravel()):
+            if g >= 0 and np.isfinite(v):
+                cand[int(g)] = v
+        sel, rsel = got[r][got[r] >= 0], ref[r][ref[r] >= 0]
+        assert sel.size == rsel.size and np.all(got[r][sel.size:] == -1), r
+        assert len(set(sel.tolist())) == sel.size and all(int(g) in cand for g in sel), r
+        assert np.array_equal(np.sort([cand[int(g)] for g in sel]), np.sort([cand[int(g)] for g in rsel])), r
+
+
+@pytest.mark.parametrize("R,W,k,kind", [(2, 600, 64, "plain"), (4, 5000, 512, "ties"), (8, 20000, 2048, "plain"),
+                                        (3, 3000, 700, "nonfinite"), (8, 131072, 2048, "ties")])
+def test_topk_merge_matches_oracle(R, W, k, kind):
+    rng = np.random.default_rng(R * 1000 + k)
+    rows = 6
+    x, ends, vals, gidx = _candidate_lists(rng, rows, W, R, k, kind)
+    ref = oracle.topk_merge(vals, gidx, k)
+    got = host(dsi.topk_merge(dev(vals), dev(gidx), k=k))
+    _check_merge(got, ref, vals, gidx)
+
+
+def test_topk_merge_of_local_topk_is_global_topk_on_gpu():
+    """The pages' exactness argument, on the device path alone: rank-local top-k over contiguous slices, their
+    candidates, the merge, against the top-k of the whole rows (compared as value multisets)."""
+    rng = np.random.default_rng(52)
+    rows, W, R, k = 16, 65536, 8, 2048
+    x = dev(rng.standard_normal((rows, W)).astype(np.float32))
+    ends = dev(rng.integers(3000, W + 1, size=rows).astype(np.int32))
+    full = host(dsi.topk_select(x, ends, k=k))
+    L = W // R
+    vals = torch.empty((R, rows, k), dtype=torch.float32, device="cuda")
+    gidx = torch.empty((R, rows, k), dtype=torch.int32, device="cuda")
+    for r in range(R):
+        st = torch.full((rows,), r * L, dtype=torch.int32, device="cuda")
+        en = torch.clamp(ends, max=(r + 1) * L)
+        idx = dsi.topk_select(x, en, k=k, row_starts=st)
+        dsi.topk_values(x, idx, row_starts=st, index_offset=r * L, out=(vals[r], gidx[r]))
+    merged = host(dsi.topk_merge(vals, gidx, k=k))
+    xh = host(x)
+    for r in range(rows):
+        a, b = full[r][full[r] >= 0], merged[r][merged[r] >= 0]
+        assert a.size == b.size and np.array_equal(np.sort(xh[r][a]), np.sort(xh[r][b])), r
