@@ -54,6 +54,11 @@ def _load():
         "orc_gather_prefill_k": (None, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32]),
         "orc_topk_values": (None, [_p, _i64, _i32, _p, _i32, _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64]),
         "orc_topk_merge": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i64]),
+        "orc_fp4_decode": (ctypes.c_float, [ctypes.c_uint8]),
+        "orc_fp4_encode": (ctypes.c_uint8, [ctypes.c_float]),
+        "orc_k_quant_and_cache_mxfp4": (None, [_p, _i64, _i64, _p, _p, _i32, _i64]),
+        "orc_sparse_mqa_logits_mxfp4": (None, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _p, _i64, _p,
+                                               _i32, _i64, _i32, _p, _i64]),
         "orc_q_rope_quant": (None, [_p, _p, _i32, _p, _i64, _i32, _p, ctypes.c_float, ctypes.c_float, _p, _p]),
     }
     for name, (res, args) in sig.items():
@@ -329,4 +334,52 @@ def topk_merge(vals, gidx, k):
     L, rows, k_in = v.shape
     out = np.empty((rows, k), dtype=np.int32)
     assert lib.orc_topk_merge(_ptr(v), _ptr(g), rows * k_in, k_in, L, rows, k_in, k, _ptr(out), k) == 0
+    return out
+
+
+# ---------------------------------------------------------------- O13, O14 (MXFP4 cache)
+ROW4 = 68
+
+
+def fp4_decode(codes):
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_fp4_decode(int(b)) for b in c.ravel()], dtype=np.float32).reshape(c.shape)
+
+
+def fp4_encode(x):
+    lib = _load()
+    x = np.asarray(x, dtype=np.float32)
+    return np.array([lib.orc_fp4_encode(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def k_quant_and_cache_mxfp4(k_bf16, slot_mapping, pool, block_size, block_stride):
+    """MXFP4-quantize bf16 k rows [n,128] (uint16 bits) into 68-byte rows of the uint8 pool in place."""
+    lib = _load()
+    k, k_ld = _rows(k_bf16, np.uint16)
+    assert k.shape[1] == D
+    slots = _c(slot_mapping, np.int64)
+    assert pool.dtype == np.uint8 and pool.flags["C_CONTIGUOUS"]
+    lib.orc_k_quant_and_cache_mxfp4(_ptr(k), k.shape[0], k_ld, _ptr(slots), _ptr(pool), block_size, block_stride)
+    return pool
+
+
+def sparse_mqa_logits_mxfp4(q, w, ks, ke, sparse_indices, end, sbk, k_src, block_table=None, row_to_req=None,
+                            block_size=0, block_stride=0, out_f32=False):
+    """As sparse_mqa_logits, on 68-byte MXFP4 key rows."""
+    lib = _load()
+    q = _c(q, np.uint8)
+    w = _c(w, np.uint16)
+    rows = q.shape[0]
+    si, si_ld = _rows(np.asarray(sparse_indices, dtype=np.int32), np.int32)
+    nsb = si.shape[1]
+    width = nsb * sbk
+    ks, ke, end = _c(ks, np.int32), _c(ke, np.int32), _c(end, np.int32)
+    k_src = _c(k_src, np.uint8)
+    bt, bt_ld = (None, 0) if block_table is None else _rows(np.asarray(block_table, dtype=np.int32), np.int32)
+    r2r = None if row_to_req is None else _c(row_to_req, np.int32)
+    out = np.empty((rows, width), dtype=np.float32 if out_f32 else np.uint16)
+    lib.orc_sparse_mqa_logits_mxfp4(_ptr(q), _ptr(w), rows, _ptr(ks), _ptr(ke), _ptr(si), si_ld, nsb, _ptr(end),
+                                    sbk, _ptr(k_src), _ptr(bt), bt_ld, _ptr(r2r), block_size, block_stride,
+                                    int(out_f32), _ptr(out), width)
     return out

@@ -145,16 +145,23 @@ static void decode_q_row(const uint8_t* q, const uint16_t* w, float qt[ORC_D][OR
   }
 }
 
-static float logit_one(float qt[ORC_D][ORC_H], const float wf[ORC_H], const uint8_t* krow) {
-  float kd[ORC_D], kscale, dot[ORC_H], acc = 0.0f;
+/* The logit of one query row against one decoded key vector kd[128]. */
+static float logit_kd(float qt[ORC_D][ORC_H], const float wf[ORC_H], const float kd[ORC_D]) {
+  float dot[ORC_H], acc = 0.0f;
   int h, d;
-  memcpy(&kscale, krow + ORC_D, 4);
-  for (d = 0; d < ORC_D; d++) kd[d] = orc_e4m3_decode(krow[d]) * kscale;
   for (h = 0; h < ORC_H; h++) dot[h] = 0.0f;
   for (d = 0; d < ORC_D; d++)
     for (h = 0; h < ORC_H; h++) dot[h] = dot[h] + qt[d][h] * kd[d];
   for (h = 0; h < ORC_H; h++) acc = acc + wf[h] * dot[h];
   return acc;
+}
+
+static float logit_one(float qt[ORC_D][ORC_H], const float wf[ORC_H], const uint8_t* krow) {
+  float kd[ORC_D], kscale;
+  int d;
+  memcpy(&kscale, krow + ORC_D, 4);
+  for (d = 0; d < ORC_D; d++) kd[d] = orc_e4m3_decode(krow[d]) * kscale;
+  return logit_kd(qt, wf, kd);
 }
 
 /* Prefill over gathered K rows (P3 prefill/decode table: prefill gathers the
@@ -588,4 +595,124 @@ int orc_topk_merge(const float* vals, const int32_t* gidx, int64_t list_stride, 
   }
   free(buf);
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O13 the MXFP4 indexer cache (P1 motivation and implementation: the V4.1  */
+/* sparse indexer runs on an MXFP4 indexer cache, checked at start-up, and  */
+/* scores FP8 q against FP4 k).  The pages name the format only; it is the  */
+/* OCP Microscaling format: FP4 E2M1 elements (sign, 2 exponent bits with   */
+/* bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no inf or */
+/* NaN) sharing one E8M0 scale 2^(E-127) per block of 32.  The row layout   */
+/* is a reading: 64 bytes of codes (element 2i in the low nibble of byte i, */
+/* 2i+1 in the high nibble), then the 4 scale bytes of dims 32j..32j+31:    */
+/* 68 bytes per token.                                                      */
+/* ------------------------------------------------------------------------ */
+#define ORC_ROW4 68
+
+float orc_fp4_decode(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+  return s ? -v : v;
+}
+
+/* Nearest FP4 code to a finite x, ties to the even code (mantissa bit 0),
+ * saturating at +-6; the sign is kept (a negative value that rounds to 0
+ * gives -0, code 8). */
+uint8_t orc_fp4_encode(float x) {
+  uint8_t sign = signbit(x) ? 8 : 0, best = 0;
+  double a = fabs((double)x), bd = INFINITY;
+  int c;
+  if (a >= 6.0) return sign | 7;
+  for (c = 0; c < 8; c++) {
+    double d = fabs(a - (double)orc_fp4_decode((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = (uint8_t)c;
+    }
+  }
+  return sign | best;
+}
+
+/* Shared exponent of one block of 32 (OCP MX conversion): floor(log2(amax))
+ * minus 2, the exponent of FP4's largest value, clamped to E8M0's range
+ * [-127, 127]; an all-zero block takes -127. */
+static int mx_shared_exp(const float* x) {
+  float amax = 0.0f;
+  int i, e, se;
+  for (i = 0; i < 32; i++)
+    if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+  if (amax == 0.0f) return -127;
+  (void)frexpf(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+  se = e - 1 - 2;
+  return se < -127 ? -127 : se > 127 ? 127 : se;
+}
+
+void orc_k_quant_and_cache_mxfp4(const uint16_t* k, int64_t n, int64_t k_ld, const int64_t* slot_mapping,
+                                 uint8_t* pool, int32_t block_size, int64_t block_stride) {
+  int64_t i;
+  int d, j;
+  for (i = 0; i < n; i++) {
+    int64_t slot = slot_mapping[i];
+    float x[ORC_D];
+    uint8_t* row;
+    if (slot < 0) continue;
+    row = pool + (slot / block_size) * block_stride + (slot % block_size) * ORC_ROW4;
+    for (d = 0; d < ORC_D; d++) x[d] = orc_bf16_to_f32(k[i * k_ld + d]);
+    memset(row, 0, 64);
+    for (j = 0; j < 4; j++) {
+      int se = mx_shared_exp(x + 32 * j);
+      row[64 + j] = (uint8_t)(se + 127);
+      for (d = 32 * j; d < 32 * j + 32; d++) {
+        uint8_t c = orc_fp4_encode(ldexpf(x[d], -se));
+        row[d / 2] |= (uint8_t)((d & 1) ? c << 4 : c);
+      }
+    }
+  }
+}
+
+/* Decoded key of an MXFP4 row: code value times its block's 2^(E-127). */
+static void decode_row_mxfp4(const uint8_t* krow, float kd[ORC_D]) {
+  int d;
+  for (d = 0; d < ORC_D; d++) {
+    uint8_t c = (d & 1) ? (uint8_t)(krow[d / 2] >> 4) : (uint8_t)(krow[d / 2] & 15);
+    kd[d] = ldexpf(orc_fp4_decode(c), (int)krow[64 + d / 32] - 127);
+  }
+}
+
+/* O14 sparse MQA logits on the MXFP4 cache: O7 with the key rows read as   */
+/* MXFP4 (68-byte rows, gathered [S][68] or paged), FP8 q as before.        */
+void orc_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, int32_t rows, const int32_t* row_ks,
+                                 const int32_t* row_ke, const int32_t* sparse_indices, int64_t si_ld,
+                                 int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
+                                 const uint8_t* k_src, const int32_t* block_table, int64_t bt_ld,
+                                 const int32_t* row_to_req, int32_t block_size, int64_t block_stride, int32_t out_f32,
+                                 void* out, int64_t ld) {
+  static float qt[ORC_D][ORC_H];
+  float wf[ORC_H], kd[ORC_D];
+  int32_t r, c, width = num_sparse_blocks * sparse_block_kv;
+  for (r = 0; r < rows; r++) {
+    int32_t ks = row_ks[r], ke = row_ke[r], e = end[r];
+    decode_q_row(q + (int64_t)r * ORC_H * ORC_D, w + (int64_t)r * ORC_H, qt, wf);
+    for (c = 0; c < width; c++) {
+      int32_t tok = sparse_indices[(int64_t)r * si_ld + c / sparse_block_kv] * sparse_block_kv + c % sparse_block_kv;
+      float v = -INFINITY;
+      if (c < e && tok >= ks && tok < ke) {
+        const uint8_t* krow;
+        if (block_table) {
+          int32_t req = row_to_req ? row_to_req[r] : r;
+          int32_t page = block_table[(int64_t)req * bt_ld + tok / block_size];
+          krow = k_src + (int64_t)page * block_stride + (int64_t)(tok % block_size) * ORC_ROW4;
+        } else {
+          krow = k_src + (int64_t)tok * ORC_ROW4;
+        }
+        decode_row_mxfp4(krow, kd);
+        v = logit_kd(qt, wf, kd);
+      }
+      if (out_f32)
+        ((float*)out)[(int64_t)r * ld + c] = v;
+      else
+        ((uint16_t*)out)[(int64_t)r * ld + c] = isfinite(v) ? orc_bf16_rne(v) : (uint16_t)0xFF80;
+    }
+  }
 }
