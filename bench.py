@@ -12,8 +12,8 @@ measured on this device (register-only MFMA loops, a 4 GiB streaming read), the 
 rate on a bounded row sample, and the decode and hierarchical workloads (paged decode 64 x U{4096..65536};
 long-context decode 16 x 2 rows x U{98304..131072}; hierarchical sparse 32 decode rows + 1024 prefill rows)
 with their HBM roofline fractions, the prefill K gather out of the paged cache (8192 and 131072 tokens) and the q
-preparation (RoPE, FP8 quantization, weight fold) of the 2048-token chunk, and the context-parallel merge of 8 ranks'
-top-2048 lists for 64 decode rows.
+preparation (RoPE, FP8 quantization, weight fold) of the 2048-token chunk, the context-parallel merge of 8 ranks'
+top-2048 lists for 64 decode rows, and the hierarchical workload again on the MXFP4 K cache.
 Diagnostics go to stderr.
 
 `roofline.traffic` (HBM bytes per launch of the prefill logits kernel) comes from the committed counter
@@ -393,17 +393,21 @@ def bench_merge(steps, warmup, rows=64, ranks=8):
 
 
 # --------------------------------------------------------------------------- hierarchical sparse
-def bench_sparse(steps, warmup):
-    c = synth.workload(5)
+def bench_sparse(steps, warmup, c, mxfp4=False):
+    """Workload 5, one step: expansion, sparse logits (decode rows from the paged pool, prefill rows from the
+    gathered chunk), bf16 top-k, remap and slot conversion.  mxfp4: the K cache in 68-byte MXFP4 rows."""
     sbk, cbs, nd, rows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
-    bs, stride, nb = c["block_size"], c["block_stride"], c["num_blocks"]
+    bs, nb = c["block_size"], c["num_blocks"]
+    row = 68 if mxfp4 else ROW
+    stride = bs * row
+    quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
+    logits_fn = dsi.sparse_mqa_logits_mxfp4 if mxfp4 else dsi.sparse_mqa_logits
     q, w, ks, ke, cand = dev(c["q"]), dev(c["w"]), dev(c["ks"]), dev(c["ke"]), dev(c["cand"])
     pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
-    dsi.k_quant_and_cache(dev(c["k_dec"]), dev(c["dec_slot_mapping"]), pool, bs, stride, nb)
+    quant(dev(c["k_dec"]), dev(c["dec_slot_mapping"]), pool, bs, stride, nb)
     Lp = c["Lp"]
-    pre = torch.zeros((Lp, ROW), dtype=torch.uint8, device="cuda")
-    dsi.k_quant_and_cache(dev(c["k_pre"]), torch.arange(Lp, dtype=torch.int64, device="cuda"), pre.view(-1), Lp,
-                          Lp * ROW, 1)
+    pre = torch.zeros((Lp, row), dtype=torch.uint8, device="cuda")
+    quant(dev(c["k_pre"]), torch.arange(Lp, dtype=torch.int64, device="cuda"), pre.view(-1), Lp, Lp * row, 1)
     bt, r2r = dev(c["block_table"]), dev(c["row_to_req"])
     nsb = cand.shape[1] * (cbs // sbk)
     width = nsb * sbk
@@ -420,9 +424,9 @@ def bench_sparse(steps, warmup):
         if timed:
             te.stop(s)
             s = tl.start()
-        dsi.sparse_mqa_logits(q[:nd], w[:nd], ks[:nd], ke[:nd], si[:nd], end[:nd], sbk, pool, block_table=bt,
-                              row_to_req=r2r, block_size=bs, block_stride_bytes=stride, num_k=nb, out=out[:nd])
-        dsi.sparse_mqa_logits(q[nd:], w[nd:], ks[nd:], ke[nd:], si[nd:], end[nd:], sbk, pre, out=out[nd:])
+        logits_fn(q[:nd], w[:nd], ks[:nd], ke[:nd], si[:nd], end[:nd], sbk, pool, block_table=bt, row_to_req=r2r,
+                  block_size=bs, block_stride_bytes=stride, num_k=nb, out=out[:nd])
+        logits_fn(q[nd:], w[nd:], ks[nd:], ke[nd:], si[nd:], end[nd:], sbk, pre.view(-1), num_k=Lp, out=out[nd:])
         if timed:
             tl.stop(s)
             s = tt.start()
@@ -449,11 +453,11 @@ def bench_sparse(steps, warmup):
     scored = int(host_end(end).sum())
     ms_l = tl.mean_ms()
     return dict(workload=f"hierarchical sparse: {nd} decode rows + {rows - nd} prefill rows, {nsb} sparse blocks "
-                         f"of {sbk}", rows=rows, ms_step=round(ms_step, 4), ms_expand=round(te.mean_ms(), 4),
+                         f"of {sbk}, {'MXFP4' if mxfp4 else 'FP8'} K cache ({row} B per token)", rows=rows, ms_step=round(ms_step, 4), ms_expand=round(te.mean_ms(), 4),
                 ms_logits=round(ms_l, 4), ms_topk=round(tt.mean_ms(), 4), ms_remap_slot=round(tr.mean_ms(), 4),
                 scored_pairs=scored, pairs_per_s=round(scored / (ms_step * 1e-3), 1),
                 logits_tflops=round(scored * FLOP_PER_PAIR / (ms_l * 1e-3) / 1e12, 1),
-                effective_gathered_gbs=round(scored * ROW / (ms_l * 1e-3) / 1e9, 1))
+                effective_gathered_gbs=round(scored * row / (ms_l * 1e-3) / 1e9, 1))
 
 
 def host_end(t):
@@ -492,7 +496,11 @@ def main():
             log(f"decode workload {n} ...")
             extra[f"decode_w{n}"] = bench_decode(n, args.steps, args.warmup)
         log("hierarchical sparse ...")
-        extra["sparse_w5"] = bench_sparse(args.steps, args.warmup)
+        c5 = synth.workload(5)
+        extra["sparse_w5"] = bench_sparse(args.steps, args.warmup, c5)
+        log("hierarchical sparse, MXFP4 cache ...")
+        extra["sparse_w5_mxfp4"] = bench_sparse(args.steps, args.warmup, c5, mxfp4=True)
+        del c5
         log("prefill K gather ...")
         extra["prefill_gather"] = bench_gather(args.steps, args.warmup)
         log("q preparation ...")

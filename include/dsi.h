@@ -358,6 +358,47 @@ DSI_API int dsi_topk_merge(const float* vals, const int32_t* gidx, int64_t list_
                            int32_t num_lists, int32_t rows, int32_t k_in, int32_t k, int32_t* out, int64_t out_ld,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The MXFP4 indexer cache (P1 motivation and implementation: the V4.1 sparse
+ * indexer reads an MXFP4 indexer cache, checked at start-up, and scores FP8 q
+ * against FP4 k).  The pages name the format only; it is the OCP
+ * Microscaling format — FP4 E2M1 elements (magnitudes 0, .5, 1, 1.5, 2, 3, 4,
+ * 6) sharing one E8M0 scale 2^(E-127) per 32 — in 68-byte rows: 64 bytes of
+ * codes (element 2i in the low nibble of byte i, 2i+1 in the high nibble),
+ * then the 4 scale bytes of dims 32j..32j+31.  Token i of a block sits at
+ * byte i*68 of the block.
+ *
+ * k quantization into that cache, fused with insertion (as
+ * dsi_k_quant_and_cache, same arguments; rows of 68 bytes).  Per block of 32:
+ * shared exponent se = floor(log2(amax)) - 2 clamped to [-127, 127] (-127
+ * for an all-zero block), scale byte se + 127, codes FP4(x * 2^-se) rounded
+ * to nearest even and saturated at +-6 (a value that rounds to zero keeps
+ * its sign).
+ * Errors: EINVAL (null with n > 0, n < 0, k_ld < 128, block_size < 1,
+ * num_blocks < 0, block_stride_bytes < block_size*68); EALIGN (k not 4-byte
+ * aligned or k_ld odd, pool or block_stride_bytes not multiples of 4).
+ */
+DSI_API int dsi_k_quant_and_cache_mxfp4(const uint16_t* k, int64_t n, int64_t k_ld, const int64_t* slot_mapping,
+                                        uint8_t* pool, int64_t num_blocks, int32_t block_size,
+                                        int64_t block_stride_bytes, hipStream_t stream);
+
+/*
+ * Sparse MQA logits on the MXFP4 cache: dsi_sparse_mqa_logits with every key
+ * row read as a 68-byte MXFP4 row (gathered rows [num_k][68] when block_table
+ * is NULL, else the paged pool).  The key's value is code * 2^(E-127) of its
+ * block; everything else (columns, masking, bf16 rounding, -inf) is as in
+ * dsi_sparse_mqa_logits.  Decoded values are exact in bf16 for block scales
+ * with E <= 252 (larger ones overflow, as they do in fp32).
+ * Errors: as dsi_sparse_mqa_logits, with block_stride_bytes >= block_size*68.
+ */
+DSI_API int dsi_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, int32_t rows, const int32_t* row_ks,
+                                        const int32_t* row_ke, const int32_t* sparse_indices, int64_t si_ld,
+                                        int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
+                                        const uint8_t* k_src, int64_t num_k, const int32_t* block_table,
+                                        int64_t bt_ld, int32_t bt_width, int32_t num_reqs, const int32_t* row_to_req,
+                                        int32_t block_size, int64_t block_stride_bytes, uint16_t* logits_bf16,
+                                        int64_t ld, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

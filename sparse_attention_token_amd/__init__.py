@@ -19,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsi.so")
 
 HEADS, HEAD_DIM, ROW_BYTES, MAX_TOPK = 64, 128, 132, 2048
+ROW_BYTES_MXFP4 = 68
 F32, BF16 = 0, 1
 
 
@@ -49,6 +50,9 @@ _SIGNATURES = {
     "dsi_topk_values": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64, _p]),
     "dsi_topk_merge_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "dsi_topk_merge": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i64, _p, _sz, _p]),
+    "dsi_k_quant_and_cache_mxfp4": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _i32, _i64, _p]),
+    "dsi_sparse_mqa_logits_mxfp4": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p,
+                                                   _i64, _i32, _i32, _p, _i32, _i64, _p, _i64, _p]),
     "dsi_q_rope_quant": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i64, _i32, _p, _i64, ctypes.c_float,
                                         ctypes.c_float, _p, _p, _p]),
 }
@@ -436,4 +440,64 @@ def topk_merge(vals, gidx, k=MAX_TOPK, out=None, workspace=None):
         _check(lib().dsi_topk_merge(_ptr(vals), _ptr(gidx), vals.stride(0), vals.stride(1), L, rows, k_in, k,
                                     _ptr(out), _rows(out, "out"), workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream(vals)), "topk_merge")
+    return out
+
+
+def k_quant_and_cache_mxfp4(k, slot_mapping, pool, block_size, block_stride_bytes=None, num_blocks=None):
+    """MXFP4-quantize bf16 k [n, >=128] into the 68-byte rows of `pool` at `slot_mapping` (int64)."""
+    dev = _dev(k, slot_mapping, pool)
+    _need(k, _BF16, "k")
+    _need(slot_mapping, (torch.int64,), "slot_mapping")
+    _need(pool, (torch.uint8,), "pool")
+    _contig(pool, "pool")
+    k_ld = _rows(k, "k")
+    if block_stride_bytes is None:
+        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * ROW_BYTES_MXFP4
+    if num_blocks is None:
+        num_blocks = pool.numel() // block_stride_bytes
+    with torch.cuda.device(dev):
+        _check(lib().dsi_k_quant_and_cache_mxfp4(_ptr(k), k.shape[0], k_ld, _ptr(slot_mapping), _ptr(pool),
+                                                 num_blocks, block_size, block_stride_bytes, _stream(k)),
+               "k_quant_and_cache_mxfp4")
+    return pool
+
+
+def sparse_mqa_logits_mxfp4(q, w, row_ks, row_ke, sparse_indices, end, sparse_block_kv, k_src, block_table=None,
+                            row_to_req=None, block_size=0, block_stride_bytes=None, num_k=None, bt_width=None,
+                            num_sparse_blocks=None, out=None):
+    """sparse_mqa_logits on 68-byte MXFP4 key rows (gathered [S,68] or a paged pool)."""
+    dev = _dev(q, w, row_ks, row_ke, sparse_indices, end, k_src, block_table, row_to_req, out)
+    _need(q, (torch.uint8,), "q", 3)
+    _need(w, _BF16, "w", 2)
+    for t, nm in ((q, "q"), (w, "w"), (row_ks, "row_ks"), (row_ke, "row_ke"), (end, "end"), (k_src, "k_src")):
+        _contig(t, nm)
+    rows = q.shape[0]
+    si_ld = _rows(sparse_indices, "sparse_indices")
+    if num_sparse_blocks is None:
+        num_sparse_blocks = sparse_indices.shape[1]
+    width = num_sparse_blocks * sparse_block_kv
+    bt_ld, num_reqs = 0, 0
+    if block_table is not None:
+        bt_ld = _rows(block_table, "block_table")
+        num_reqs = block_table.shape[0]
+        if bt_width is None:
+            bt_width = block_table.shape[1]
+        if block_stride_bytes is None:
+            block_stride_bytes = k_src.stride(0) if k_src.dim() > 1 else block_size * ROW_BYTES_MXFP4
+        if num_k is None:
+            num_k = k_src.numel() // block_stride_bytes
+    else:
+        bt_width, block_stride_bytes = 0, 0
+        if num_k is None:
+            num_k = k_src.numel() // ROW_BYTES_MXFP4
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.int16, device=dev)
+    _need(out, _BF16, "out")
+    ld = _rows(out, "out")
+    with torch.cuda.device(dev):
+        _check(lib().dsi_sparse_mqa_logits_mxfp4(_ptr(q), _ptr(w), rows, _ptr(row_ks), _ptr(row_ke),
+                                                 _ptr(sparse_indices), si_ld, num_sparse_blocks, _ptr(end),
+                                                 sparse_block_kv, _ptr(k_src), num_k, _ptr(block_table), bt_ld,
+                                                 bt_width, num_reqs, _ptr(row_to_req), block_size, block_stride_bytes,
+                                                 _ptr(out), ld, _stream(q)), "sparse_mqa_logits_mxfp4")
     return out

@@ -503,6 +503,247 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   }
 }
 
+// ------------------------------------------------------------------ sparse columns, MXFP4 cache
+// The same work split and DMA ring on 68-byte MXFP4 key rows (P1 motivation and
+// implementation: the V4.1 sparse indexer scores FP8 q against an MXFP4 k cache).  A key
+// lands in LDS as five 16-byte pieces at an 80-byte stride (bytes 0..63, then 52..67, so
+// the four scale bytes sit at 76..79; 20 dwords per key keep 16-byte reads by 8 consecutive
+// keys on distinct banks).  The block scales differ within one 16-dim MFMA step (each lane
+// half feeds its own 32-dim block), so they are applied while decoding: the hardware
+// converter turns each FP4 code times its block's 2^(E-127) into bf16, exactly, and q's
+// FP8 codes are decoded to bf16, exactly; the contraction runs on the bf16 matrix cores
+// with fp32 accumulation (products of 4- and 2-bit significands are exact).
+constexpr int kMxRow = 68;                          // bytes per MXFP4 key row
+constexpr int kMxLds = 80;                          // LDS bytes per key
+constexpr int kMxBuf = kDcChunk * kMxLds;           // 20480
+constexpr int kMxSlabsPerWave = kMxBuf / 1024 / 4;  // 5 DMA instructions per wavefront per chunk
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^(E-127) as an fp32 (E = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
+
+// Eight FP4 codes (one dword, element 2i in the low nibble of byte i) times `scale` -> bf16.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t x, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E4M3 codes (two dwords) -> bf16, exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// q[row] as bf16 A fragments (load_q32's layout).
+struct Q32b {
+  bf16x8 a[2][8];
+};
+
+__device__ __forceinline__ void load_q32_bf16(Q32b& f, const uint8_t* q_row, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint4 x = p[j];
+      f.a[hb][2 * j] = e4m3x8_to_bf16x8(x.x, x.y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_bf16x8(x.z, x.w);
+    }
+  }
+}
+
+// Raw B data of one key row for this lane (key l%32, lane half h = dims [64h, 64h+64)):
+// the half's 32 code bytes and the scales of its blocks 2h and 2h+1.
+struct MxRaw {
+  uint4 c0, c1;
+  float s0, s1;
+};
+
+__device__ __forceinline__ MxRaw load_mx_raw(const uint8_t* keys, int lane) {
+  const uint8_t* row = keys + (lane & 31) * kMxLds;
+  const int h = lane >> 5;
+  MxRaw r;
+  r.c0 = *reinterpret_cast<const uint4*>(row + 32 * h);
+  r.c1 = *reinterpret_cast<const uint4*>(row + 32 * h + 16);
+  const uint32_t sc = *reinterpret_cast<const uint32_t*>(row + 76);
+  r.s0 = e8m0_to_f32((sc >> (16 * h)) & 255u);
+  r.s1 = e8m0_to_f32((sc >> (16 * h + 8)) & 255u);
+  return r;
+}
+
+struct K32b {
+  bf16x8 b[8];
+};
+
+// Slices 2j and 2j+1 (dims 64h + 16j .. +16) of a raw row.
+__device__ __forceinline__ void decode_mx_pair(K32b& kb, const MxRaw& r, int j) {
+  const uint4& c = j < 2 ? r.c0 : r.c1;
+  const float sc = j < 2 ? r.s0 : r.s1;
+  const uint32_t w0 = (j & 1) ? c.z : c.x, w1 = (j & 1) ? c.w : c.y;
+  kb.b[2 * j] = fp4x8_to_bf16x8(w0, sc);
+  kb.b[2 * j + 1] = fp4x8_to_bf16x8(w1, sc);
+}
+
+// dc_phase on bf16 operands: MFMA i of the group, two head-sum FMAs of the previous group,
+// the next group's slices decoded as MFMAs 4j+3 retire their sources, then extra(i).
+template <bool kEpi, bool kNext, typename Extra>
+__device__ __forceinline__ void mx_phase(f32x16& x0, f32x16& x1, const Q32b& q, K32b& kb, const uint8_t* next,
+                                         int lane, const W32p& w, const f32x16& y0, const f32x16& y1,
+                                         float (&acc)[4], Extra&& extra) {
+  MxRaw raw;
+  if (kNext) raw = load_mx_raw(next, lane);
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int sl = i >> 1;
+    if ((i & 1) == 0)
+      x0 = mfma32_bf16(q.a[0][sl], kb.b[sl], i == 0 ? f32x16{} : x0);
+    else
+      x1 = mfma32_bf16(q.a[1][sl], kb.b[sl], i == 1 ? f32x16{} : x1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kEpi) {
+#pragma unroll
+      for (int e = 2 * i; e < 2 * i + 2; e++) {
+        if (e < 16)
+          acc[e & 3] = fmaf(w.get(0, e), y0[e], acc[e & 3]);
+        else
+          acc[e & 3] = fmaf(w.get(1, e - 16), y1[e - 16], acc[e & 3]);
+      }
+    }
+    if (kNext && (i & 3) == 3) decode_mx_pair(kb, raw, i >> 2);
+    extra(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__device__ __forceinline__ void mx_gather_piece(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
+                                                int lane, int i) {
+  const int slab = wave + 4 * i;
+  const int piece = slab * 64 + lane;
+  const int key = piece / 5, p = piece - key * 5;
+  const uint32_t off = key_off[key];
+  const uint8_t* a = off != kSpAbsent ? src + (int64_t)off * 4 + (p < 4 ? 16 * p : 52) : src;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(lds) : "memory");
+}
+
+__global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
+    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
+    const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
+    const int* __restrict__ end, int sbk, const uint8_t* __restrict__ k_src, int64_t num_k,
+    const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
+    const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
+    int64_t ld) {
+  constexpr int NB = 2;
+  constexpr int kKeysPerWave = kDcChunk / 4;
+  constexpr int kGroups = kKeysPerWave / 32;
+  constexpr int kStores = kKeysPerWave / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kMxBuf];
+  __shared__ uint32_t s_off[kSpKeys];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_src = num_k > 0;
+  const bool paged = block_table != nullptr;
+  const int sbk_shift = __builtin_ctz(sbk);
+  const int nch = (width + kDcChunk - 1) / kDcChunk;
+  const int kbase = wave * kKeysPerWave;
+
+  auto run = [&](int r, int c_first, int c_end) {
+    __syncthreads();  // the previous segment's buffers and offsets are no longer read
+    const int ks = row_ks[r], ke = row_ke[r], e = end[r];
+    const int req = paged ? (row_to_req ? row_to_req[r] : r) : 0;
+    const bool req_ok = !paged || (req >= 0 && req < num_reqs);
+    for (int t = tid; t < (c_end - c_first) * kDcChunk; t += 256) {
+      const int c = c_first * kDcChunk + t;
+      uint32_t off = kSpAbsent;
+      if (c < width && c < e) {
+        const int tok = sparse_indices[(int64_t)r * si_ld + (c >> sbk_shift)] * sbk + (c & (sbk - 1));
+        if (tok >= ks && tok < ke && tok >= 0) {
+          if (!paged) {
+            if (tok < num_k) off = (uint32_t)tok * (kMxRow / 4);
+          } else {
+            const int blk = tok / block_size;
+            if (req_ok && blk < bt_width) {
+              const int page = block_table[(int64_t)req * bt_ld + blk];
+              if (page >= 0 && page < num_k)
+                off = (uint32_t)(((int64_t)page * block_stride + (int64_t)(tok % block_size) * kMxRow) >> 2);
+            }
+          }
+        }
+      }
+      s_off[t] = off;
+    }
+    Q32b qf;
+    W32p wf;
+    load_q32_bf16(qf, q + (int64_t)r * kHeads * kDim, lane);
+    load_w32p(wf, w + (int64_t)r * kHeads, lane);
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)r * ld, (short)0, width * 2, 0x00020000);
+    __syncthreads();  // offsets visible
+
+    auto gather_piece = [&](int c, int i) {
+      if (has_src)
+        mx_gather_piece(s_buf[(c - c_first) % NB], s_off + (c - c_first) * kDcChunk, k_src, wave, lane, i);
+    };
+    auto score_chunk = [&](int c, const uint8_t* buf, int next) {
+      const uint32_t* coff = s_off + (c - c_first) * kDcChunk;
+#pragma unroll
+      for (int h = 0; h < kGroups / 2; h++) {
+        const uint8_t* keys = buf + (kbase + 64 * h) * kMxLds;
+        auto dma = [&](int i) {
+          if (h == 0 && i < kMxSlabsPerWave && next < c_end) gather_piece(next, i);
+        };
+        K32b kb;
+        const MxRaw r0 = load_mx_raw(keys, lane);
+#pragma unroll
+        for (int j = 0; j < 4; j++) decode_mx_pair(kb, r0, j);
+        f32x16 a0, a1, b0 = {}, b1 = {};
+        float acc[4];
+        mx_phase<false, true>(a0, a1, qf, kb, keys + 32 * kMxLds, lane, wf, b0, b1, acc, dma);
+        mx_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+        const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
+        const int key = kbase + 64 * h + lane;  // key within the chunk
+        const uint16_t o = coff[key] != kSpAbsent ? f32_to_bf16_rne(v) : (uint16_t)0xFF80u;
+        __builtin_amdgcn_raw_buffer_store_b16(o, out_rsrc, (c * kDcChunk + key) * 2, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+#pragma unroll
+    for (int i = 0; i < kMxSlabsPerWave; i++) gather_piece(c_first, i);
+    for (int cc = c_first; cc < c_end; cc++) {
+      if (has_src) wait_gather<NB, kStores>(min(cc - c_first, 1));
+      __syncthreads();
+      score_chunk(cc, s_buf[(cc - c_first) % NB], cc + 1);
+    }
+  };
+
+  const int64_t total = (int64_t)rows * nch;
+  int64_t g = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t g1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
+  while (g < g1) {  // uniform
+    const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
+    const int len = (int)min((int64_t)min(nch - lc, kSpJob), g1 - g);
+    run(r, lc, lc + len);
+    g += len;
+  }
+}
+
 }  // namespace
 }  // namespace dsi
 
@@ -576,6 +817,43 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
   const int64_t slots = 2 * (int64_t)cu_count();
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
   hipLaunchKernelGGL(sparse_logits_kernel, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
+                     si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
+                     block_size, block_stride_bytes, logits_bf16, ld);
+  return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+extern "C" int dsi_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, int32_t rows, const int32_t* row_ks,
+                                           const int32_t* row_ke, const int32_t* sparse_indices, int64_t si_ld,
+                                           int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
+                                           const uint8_t* k_src, int64_t num_k, const int32_t* block_table,
+                                           int64_t bt_ld, int32_t bt_width, int32_t num_reqs,
+                                           const int32_t* row_to_req, int32_t block_size, int64_t block_stride_bytes,
+                                           uint16_t* logits_bf16, int64_t ld, hipStream_t stream) {
+  using namespace dsi;
+  const int sbk = sparse_block_kv;
+  if (sbk < 8 || sbk > 128 || (sbk & (sbk - 1))) return DSI_EUNSUPPORTED;
+  if (rows < 0 || num_sparse_blocks < 1 || si_ld < num_sparse_blocks || num_k < 0) return DSI_EINVAL;
+  const int64_t width = (int64_t)num_sparse_blocks * sbk;
+  if (width > 0x7FFFFFFF || ld < width) return DSI_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (bt_width < 0 || bt_ld < bt_width || num_reqs < 0) return DSI_EINVAL;
+    if (block_size < 8 || (block_size % sbk) != 0 || (block_size % 8) != 0) return DSI_EUNSUPPORTED;
+    if (block_stride_bytes < (int64_t)block_size * kMxRow) return DSI_EINVAL;
+    if (block_stride_bytes & 15) return DSI_EALIGN;
+  }
+  if (rows == 0) return DSI_OK;
+  if (!q || !w || !row_ks || !row_ke || !sparse_indices || !end || !k_src || !logits_bf16) return DSI_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k_src) & 15) ||
+      (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits_bf16) & 1))
+    return DSI_EALIGN;
+  if (rows > 65535) return DSI_EUNSUPPORTED;
+  const int64_t src_bytes = paged ? num_k * block_stride_bytes : num_k * kMxRow;
+  if (src_bytes >= ((int64_t)1 << 34)) return DSI_EUNSUPPORTED;
+  const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
+  const int64_t slots = 2 * (int64_t)cu_count();
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
+  hipLaunchKernelGGL(sparse_logits_mx_kernel, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
                      si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
                      block_size, block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;

@@ -204,6 +204,25 @@ def test_cp_merge_validation():
     assert m(None, None, 256, 64, 2, 0, 64, 16, None, 64, None, 0, None) == 0
 
 
+def test_mxfp4_validation():
+    L = dsi.lib()
+    f = L.dsi_k_quant_and_cache_mxfp4
+    assert f(A16, 4, 128, A16, A16, 1, 64, 64 * 68 - 4, None) == EINVAL  # stride < 64 rows of 68
+    assert f(A16, 4, 127, A16, A16, 1, 64, 64 * 68, None) == EINVAL
+    assert f(A16 + 2, 4, 128, A16, A16, 1, 64, 64 * 68, None) == EALIGN
+    assert f(None, 0, 128, None, None, 1, 64, 64 * 68, None) == 0
+    g = L.dsi_sparse_mqa_logits_mxfp4
+
+    def call(sbk=16, nsb=4, si_ld=4, ld=64, bt=None, bs=0, stride=0, k_src=A16, q=A16):
+        return g(q, A16, 2, A16, A16, A16, si_ld, nsb, A16, sbk, k_src, 10, bt, 8, 8, 2, None, bs, stride, A16, ld,
+                 None)
+
+    assert call(sbk=12) == EUNSUP and call(si_ld=3) == EINVAL and call(ld=63) == EINVAL
+    assert call(bt=A16, bs=64, stride=64 * 68 - 16) == EINVAL
+    assert call(bt=A16, bs=64, stride=64 * 68 + 8) == EALIGN
+    assert call(bt=A16, bs=24) == EUNSUP and call(k_src=None) == EINVAL and call(q=A16 + 8) == EALIGN
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsi, "_lib", None)
     monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))

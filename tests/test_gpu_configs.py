@@ -211,3 +211,59 @@ def test_q_prep_full_chunk():
                                  c["softmax_scale"], c["head_scale"])
     assert np.array_equal(host(q8), ref_q8)
     assert np.array_equal(host(w_out), ref_w)
+
+
+def test_workload5_hierarchical_sparse_mxfp4():
+    """Workload 5 on the MXFP4 cache (68-byte rows; decode requests in 128-token pages, the prefill request
+    gathered): every row scored and selected on the device; k bytes and sampled rows against the oracle."""
+    c = synth.workload(5)
+    sbk, cbs, nd, rows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
+    bs, nb = c["block_size"], c["num_blocks"]
+    stride = bs * 68
+    ks, ke, cand = c["ks"], c["ke"], c["cand"]
+    si_ref, end_ref = oracle.expand_candidates(cand, ks, ke, cbs, sbk)
+    si_t, end_t = dev(si_ref), dev(end_ref)
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache_mxfp4(dev(c["k_dec"]), dev(c["dec_slot_mapping"]), pool, bs, stride, nb)
+    Lp = c["Lp"]
+    pre = torch.zeros(Lp * 68, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache_mxfp4(dev(c["k_pre"]), dev(np.arange(Lp, dtype=np.int64)), pre, Lp, Lp * 68, 1)
+    pre_ref = np.zeros(Lp * 68, np.uint8)
+    oracle.k_quant_and_cache_mxfp4(c["k_pre"], np.arange(Lp, dtype=np.int64), pre_ref, Lp, Lp * 68)
+    assert np.array_equal(host(pre), pre_ref), "prefill MXFP4 rows differ"
+    width = si_ref.shape[1] * sbk
+    out = torch.empty((rows, width), dtype=torch.int16, device="cuda")
+    q, w, ks_t, ke_t, bt = dev(c["q"]), dev(c["w"]), dev(ks), dev(ke), dev(c["block_table"])
+    dsi.sparse_mqa_logits_mxfp4(q[:nd], w[:nd], ks_t[:nd], ke_t[:nd], si_t[:nd], end_t[:nd], sbk, pool,
+                                block_table=bt, row_to_req=dev(c["row_to_req"]), block_size=bs,
+                                block_stride_bytes=stride, num_k=nb, out=out[:nd])
+    dsi.sparse_mqa_logits_mxfp4(q[nd:], w[nd:], ks_t[nd:], ke_t[nd:], si_t[nd:], end_t[nd:], sbk, pre,
+                                out=out[nd:])
+    col = host(dsi.topk_select(out, end_t, k=K))
+    got = host(out)
+    rng = np.random.default_rng(55)
+    starts = np.concatenate([[0], np.cumsum(c["dec_lens"])])
+    pool_h = None
+    for r in sorted(set([0, nd - 1, nd, rows - 1] + rng.integers(0, rows, 6).tolist())):
+        if r < nd:
+            pool_ref = np.zeros(nb * stride, np.uint8)
+            sl_map = c["dec_slot_mapping"][starts[r]:starts[r + 1]]
+            oracle.k_quant_and_cache_mxfp4(c["k_dec"][starts[r]:starts[r + 1]], sl_map, pool_ref, bs, stride)
+            pool_h = host(pool) if pool_h is None else pool_h
+            for p in np.unique(sl_map // bs):  # this request's pages hold the same bytes on both sides
+                a = int(p) * stride
+                assert np.array_equal(pool_h[a:a + stride], pool_ref[a:a + stride]), (r, p)
+            kw = dict(k_src=pool_ref, block_table=c["block_table"], row_to_req=c["row_to_req"][r:r + 1],
+                      block_size=bs, block_stride=stride)
+        else:
+            kw = dict(k_src=pre_ref)
+        sl = slice(r, r + 1)
+        ref_f32 = oracle.sparse_mqa_logits_mxfp4(c["q"][sl], c["w"][sl], ks[sl], ke[sl], si_ref[sl], end_ref[sl],
+                                                 sbk, out_f32=True, **kw)[0]
+        ref_bits = oracle.sparse_mqa_logits_mxfp4(c["q"][sl], c["w"][sl], ks[sl], ke[sl], si_ref[sl], end_ref[sl],
+                                                  sbk, **kw)[0]
+        valid = np.isfinite(ref_f32)
+        assert np.all(got[r][~valid] == 0xFF80)
+        assert_close(bf16_value(got[r][valid]), ref_f32[valid], tol_fn=tol_bf16, what=f"row {r} MXFP4 logits")
+        ref_col = oracle.topk_select(ref_bits[None, :], end_ref[sl], K, bf16=True)[0]
+        check_selection(col[r], ref_col, ref_f32, tol_fn=tol_bf16, end=int(end_ref[r]))

@@ -539,3 +539,125 @@ def test_topk_merge_of_local_topk_is_global_topk_on_gpu():
     for r in range(rows):
         a, b = full[r][full[r] >= 0], merged[r][merged[r] >= 0]
         assert a.size == b.size and np.array_equal(np.sort(xh[r][a]), np.sort(xh[r][b])), r
+
+
+# ----------------------------------------------------------------------------- MXFP4 cache
+ROW4 = 68
+
+
+def _mx_pool_oracle(k_bf16, slots, nb, bs, stride, fill=0xA5):
+    pool = np.full(nb * stride, fill, np.uint8)
+    oracle.k_quant_and_cache_mxfp4(k_bf16, slots, pool, bs, stride)
+    return pool
+
+
+def test_k_quant_mxfp4_every_bf16_value_bit_exact():
+    # each block of 32 holds 7.96875 (the largest bf16 below 8: shared exponent 0) and 31 sweep values, so
+    # every finite bf16 value up to that size is encoded at scale 1: ties, saturation, signs, subnormals
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    x = (bits << 16).view(np.float32)
+    vals = x[np.isfinite(x) & (np.abs(x) <= 7.96875)]
+    nblk = (vals.size + 30) // 31
+    flat = np.zeros(nblk * 31, np.float32)
+    flat[:vals.size] = vals
+    blocks = np.concatenate([np.full((nblk, 1), 7.96875, np.float32), flat.reshape(nblk, 31)], axis=1)
+    n = (nblk + 3) // 4
+    k = np.zeros((n * 4, 32), np.float32)
+    k[:nblk] = blocks
+    kb = synth._bf16_bits(k.reshape(n, 128))
+    slots = np.arange(n, dtype=np.int64)
+    ref = _mx_pool_oracle(kb, slots, 1, n, n * ROW4)
+    pool = torch.full((n * ROW4,), 0xA5, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache_mxfp4(dev(kb), dev(slots), pool, n, n * ROW4, 1)
+    assert np.array_equal(host(pool), ref)
+
+
+def test_k_quant_mxfp4_random_rows_packed_pool():
+    rng = np.random.default_rng(71)
+    n, bs = 1000, 64
+    kb = synth.draw_k(rng, n)
+    kb[0] = 0                                                                                  # zero row
+    kb[1] = synth._bf16_bits(rng.standard_normal(128).astype(np.float32) * np.float32(1e-38))  # subnormal-ish
+    kb[2] = synth._bf16_bits(rng.standard_normal(128).astype(np.float32) * np.float32(1e30))   # huge
+    kb[3, 40] = synth._bf16_bits(np.array([-7.5], np.float32))[0]                               # saturating block
+    stride = bs * ROW4 + 16
+    nb = (n + bs - 1) // bs + 2
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    slots[::9] = -1
+    ref = _mx_pool_oracle(kb, slots, nb, bs, stride)
+    pool = torch.full((nb * stride,), 0xA5, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache_mxfp4(dev(kb), dev(slots), pool, bs, stride, nb)
+    assert np.array_equal(host(pool), ref)
+
+
+def test_sparse_mxfp4_exact_integer_bit_exact():
+    """Keys on the FP4 grid with unit scales and q codes of small integers: every partial sum is exact, so
+    the device must match the oracle bit for bit (bf16 rounding of an exact value)."""
+    rng = np.random.default_rng(72)
+    S, T, sbk = 512, 8, 16
+    codes = rng.integers(0, 16, size=(S, 128)).astype(np.uint8)
+    codes[:, ::32] = 7  # +6 in each block: shared exponent 0
+    kb = synth._bf16_bits(oracle.fp4_decode(codes))
+    rows4 = _mx_pool_oracle(kb, np.arange(S, dtype=np.int64), 1, S, S * ROW4)
+    q = oracle.e4m3_encode(rng.integers(-8, 9, size=(T, 64, 128)).astype(np.float32))
+    w = synth._bf16_bits(np.float32(2.0) ** rng.integers(-6, 0, size=(T, 64)).astype(np.float32))
+    si = np.sort(rng.integers(0, S // sbk, size=(T, 12)), axis=1).astype(np.int32)
+    ks, ke = np.zeros(T, np.int32), np.full(T, S, np.int32)
+    end = np.full(T, 12 * sbk, np.int32)
+    ref = oracle.sparse_mqa_logits_mxfp4(q, w, ks, ke, si, end, sbk, rows4)
+    got = host(dsi.sparse_mqa_logits_mxfp4(dev(q), dev(w), dev(ks), dev(ke), dev(si), dev(end), sbk, dev(rows4)))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("sbk,ratio", [(128, 1), (16, 1), (8, 2)])
+def test_sparse_mxfp4_gathered_parity(sbk, ratio):
+    rng = np.random.default_rng(80 + sbk + ratio)
+    cbs, S, T, K = sbk * ratio, 3001, 12, 16
+    c = synth.prefill_case(50 + sbk, T=T, S=S, first_pos=S - T)
+    rows4 = _mx_pool_oracle(c["k"], np.arange(S, dtype=np.int64), 1, S, S * ROW4)
+    ks = np.zeros(T, np.int32)
+    ks[3] = sbk * 2
+    ke = c["ke"].copy()
+    ke[5] = 40
+    maxb = (np.maximum(ke - ks, 0) + cbs - 1) // cbs
+    cand = synth.draw_candidates(rng, maxb, num=K, distinct=min(12, int(maxb.min())), dup=2)
+    si, end = oracle.expand_candidates(cand, ks, ke, cbs, sbk)
+    ref_bits = oracle.sparse_mqa_logits_mxfp4(c["q"], c["w"], ks, ke, si, end, sbk, rows4)
+    ref_f32 = oracle.sparse_mqa_logits_mxfp4(c["q"], c["w"], ks, ke, si, end, sbk, rows4, out_f32=True)
+    got = host(dsi.sparse_mqa_logits_mxfp4(dev(c["q"]), dev(c["w"]), dev(ks), dev(ke), dev(si), dev(end), sbk,
+                                           dev(rows4)))
+    valid = np.isfinite(ref_f32)
+    assert np.array_equal(got[~valid], ref_bits[~valid])
+    assert_close(bf16_value(got[valid]), ref_f32[valid], tol_fn=tol_bf16, what="MXFP4 sparse logits")
+
+
+@pytest.mark.parametrize("sbk,bs", [(128, 128), (16, 64)])
+def test_sparse_mxfp4_paged_parity(sbk, bs):
+    rng = np.random.default_rng(sbk * 5 + bs)
+    lens = [700, 1, 129, 3000, 2048]
+    c = synth.decode_case(60 + sbk, B=len(lens), next_n=1, lmin=0, lmax=0, block_size=bs, lens=lens)
+    stride, nb = bs * ROW4 + 16, c["num_blocks"]
+    pool_np = _mx_pool_oracle(c["k"], c["slot_mapping"], nb, bs, stride)
+    rows = len(lens)
+    ks = np.zeros(rows, np.int32)
+    ke = np.array(lens, np.int32)
+    maxb = (np.maximum(ke - ks, 0) + sbk - 1) // sbk
+    cand = synth.draw_candidates(rng, maxb, num=8, distinct=6, dup=1)
+    si, end = oracle.expand_candidates(cand, ks, ke, sbk, sbk)
+    r2r = np.arange(rows, dtype=np.int32)
+    bt = c["block_table"].copy()
+    bt[3, 1] = -1  # a missing page scores -inf
+    # the oracle has no missing-page rule: it scores the intact table, and the missing page's tokens are
+    # masked to -inf afterwards, as the call documents
+    bt_ok = c["block_table"]
+    ref_f32 = oracle.sparse_mqa_logits_mxfp4(c["q"], c["w"], ks, ke, si, end, sbk, pool_np, block_table=bt_ok,
+                                             row_to_req=r2r, block_size=bs, block_stride=stride, out_f32=True)
+    got = host(dsi.sparse_mqa_logits_mxfp4(dev(c["q"]), dev(c["w"]), dev(ks), dev(ke), dev(si), dev(end), sbk,
+                                           dev(pool_np), block_table=dev(bt), row_to_req=dev(r2r), block_size=bs,
+                                           block_stride_bytes=stride, num_k=nb))
+    tok = si[3][np.arange(si.shape[1] * sbk) // sbk] * sbk + np.arange(si.shape[1] * sbk) % sbk
+    missing = (tok // bs) == 1
+    ref_f32[3, missing] = -np.inf
+    valid = np.isfinite(ref_f32)
+    assert np.all(got[~valid] == 0xFF80)
+    assert_close(bf16_value(got[valid]), ref_f32[valid], tol_fn=tol_bf16, what="MXFP4 sparse paged logits")
