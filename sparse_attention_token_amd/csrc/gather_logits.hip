@@ -381,8 +381,12 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
 // "absent" when the column scores -inf — so blocks, pages and invalid columns need no
 // special case later.  It then streams its chunks through the DMA ring and scores them as
 // the decode kernel scores one row (four wavefronts x 64 keys per chunk), rounding to bf16.
-constexpr int kSpJob = 4;                     // chunks per segment
-constexpr int kSpKeys = kSpJob * kDcChunk;    // columns per segment
+// Chunks per segment: longer segments pay the segment set-up (offsets, q decode) less often
+// (8 instead of 4 chunks: 205 -> 196 us on the hierarchical workload); the FP8 kernel's two
+// 36 KB buffers and 8 KB of offsets fill the 160 KB LDS at two workgroups per CU, the MXFP4
+// kernel's 20 KB buffers leave room for 16 (178 -> 165 us).
+constexpr int kSpJob = 8;
+constexpr int kMxJob = 16;
 constexpr uint32_t kSpAbsent = 0xFFFFFFFFu;   // source offsets are in 4-byte units
 
 // Piece i (0..8) of this wavefront's share of one chunk's gather (as dc_gather_piece, with
@@ -398,6 +402,7 @@ __device__ __forceinline__ void sp_gather_piece(uint8_t* buf, const uint32_t* ke
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(lds) : "memory");
 }
 
+template <int JOB>
 __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   constexpr int kGroups = kKeysPerWave / 32;
   constexpr int kStores = kKeysPerWave / 64;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kDcBuf];
-  __shared__ uint32_t s_off[kSpKeys];
+  __shared__ uint32_t s_off[JOB * kDcChunk];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   const int nch = (width + kDcChunk - 1) / kDcChunk;
   const int kbase = wave * kKeysPerWave;
 
-  // Score chunks [c_first, c_end) (at most kSpJob) of row r.
+  // Score chunks [c_first, c_end) (at most JOB) of row r.
   auto run = [&](int r, int c_first, int c_end) {
     __syncthreads();  // the previous segment's buffers and offsets are no longer read
     const int ks = row_ks[r], ke = row_ke[r], e = end[r];
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   const int64_t g1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
   while (g < g1) {  // uniform
     const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
-    const int len = (int)min((int64_t)min(nch - lc, kSpJob), g1 - g);
+    const int len = (int)min((int64_t)min(nch - lc, JOB), g1 - g);
     run(r, lc, lc + len);
     g += len;
   }
@@ -641,6 +646,7 @@ __device__ __forceinline__ void mx_gather_piece(uint8_t* buf, const uint32_t* ke
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(lds) : "memory");
 }
 
+template <int JOB>
 __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
   constexpr int kGroups = kKeysPerWave / 32;
   constexpr int kStores = kKeysPerWave / 64;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kMxBuf];
-  __shared__ uint32_t s_off[kSpKeys];
+  __shared__ uint32_t s_off[JOB * kDcChunk];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -738,7 +744,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
   const int64_t g1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
   while (g < g1) {  // uniform
     const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
-    const int len = (int)min((int64_t)min(nch - lc, kSpJob), g1 - g);
+    const int len = (int)min((int64_t)min(nch - lc, JOB), g1 - g);
     run(r, lc, lc + len);
     g += len;
   }
@@ -816,7 +822,7 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
   const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
   const int64_t slots = 2 * (int64_t)cu_count();
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
-  hipLaunchKernelGGL(sparse_logits_kernel, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
+  hipLaunchKernelGGL(sparse_logits_kernel<kSpJob>, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
                      si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
                      block_size, block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
@@ -853,7 +859,7 @@ extern "C" int dsi_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, 
   const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
   const int64_t slots = 2 * (int64_t)cu_count();
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
-  hipLaunchKernelGGL(sparse_logits_mx_kernel, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
+  hipLaunchKernelGGL(sparse_logits_mx_kernel<kMxJob>, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
                      si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
                      block_size, block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
