@@ -410,7 +410,8 @@ constexpr int reg_capacity() {
 // Bin search by wavefront 0 alone: lane l sums bins [l*B, l*B + B) of hist (B = nb / 64, or
 // bin l when nb < 64), a wavefront suffix sum gives each lane the count above its bins, and
 // the lane whose bins hold the `need`-th largest writes s_sel[0] = that bin, s_sel[1] = the
-// count strictly above it, s_sel[2] = the total.  Bins outside [lo, hi) count as empty.
+// count strictly above it, s_sel[3] = the count in it, s_sel[2] = the total.  Bins outside
+// [lo, hi) count as empty.
 // Call with all threads (after the histogram is complete); ends synchronised.
 template <int NB>
 __device__ __forceinline__ void find_bin_w0(const int* hist, int lo, int hi, int need, int* s_sel, int tid) {
@@ -447,17 +448,19 @@ __device__ __forceinline__ void find_bin_w0(const int* hist, int lo, int hi, int
     if (tid == 0) s_sel[2] = v;
     // the bin j with acc_j < need <= acc_j + h[j], acc_j = above + (bins above j): one
     // lane holds it, found without branches
-    int acc = above, sel = -1, sel_acc = 0;
+    int acc = above, sel = -1, sel_acc = 0, sel_cnt = 0;
 #pragma unroll
     for (int j = B - 1; j >= 0; j--) {
       const bool hit = acc < need && need <= acc + h[j];
       sel = hit ? tid * B + j : sel;
       sel_acc = hit ? acc : sel_acc;
+      sel_cnt = hit ? h[j] : sel_cnt;
       acc += h[j];
     }
     if (sel >= 0) {
       s_sel[0] = sel;
       s_sel[1] = sel_acc;
+      s_sel[3] = sel_cnt;
     }
   }
   __syncthreads();
@@ -613,8 +616,13 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
       constexpr int kWd[2] = {BF16 ? 5 : 11, 10};
       uint32_t prefix = b1 << kShift;
       int rem = need;
+      // When the bin a digit selects holds exactly the columns still needed, all of it is
+      // taken and the lower digits are skipped: the threshold becomes "every key from the
+      // bin's lowest key up" (prefix - 1 as a strict bound, nothing taken at equality).
+      bool whole = !BF16 && m == need;  // bf16 has one further digit: nothing to skip (measured)
 #pragma unroll
       for (int p = 0; p < kDigits; p++) {
+        if (whole) break;  // uniform: from LDS values read after a barrier
         const int sh = kSh[p], nb = 1 << kWd[p], hs = sh + kWd[p];
         for (int i = tid; i < nb; i += T) s_hist[i] = 0;
         __syncthreads();
@@ -629,6 +637,11 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
           find_bin_w0<1024>(s_hist, 0, nb, rem, s_sel, tid);
         prefix |= (uint32_t)s_sel[0] << sh;
         rem -= s_sel[1];
+        whole = !BF16 && s_sel[3] == rem;
+      }
+      if (whole) {
+        prefix -= 1;
+        rem = 0;
       }
       // prefix is the threshold key: boundary-bin keys above it are taken, and `rem` of
       // those equal to it
