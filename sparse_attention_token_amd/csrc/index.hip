@@ -14,6 +14,9 @@ namespace dsi {
 namespace {
 
 constexpr int kMaxSparse = 1024;  // num_candidates * ratio
+
+// log2(d) when d is a power of two, else -1.
+inline int pow2_shift(int d) { return d > 0 && (d & (d - 1)) == 0 ? __builtin_ctz((unsigned)d) : -1; }
 constexpr int kInt32Big = 0x7FFFFFFF;
 
 __device__ __forceinline__ int wrap_add(int a, int b) { return (int)((unsigned)a + (unsigned)b); }
@@ -82,36 +85,53 @@ __global__ __launch_bounds__(256) void expand_kernel(const int* __restrict__ can
   }
 }
 
-__global__ __launch_bounds__(256) void remap_kernel(const int* __restrict__ col, int64_t col_ld, int rows, int k,
+// Four entries per thread (one 16-byte load and store where the rows allow it), the
+// divisions by the block size as shifts when it is a power of two (shift >= 0).
+constexpr int kIdxPerThread = 4;
+
+__device__ __forceinline__ int div_by(int x, int d, int shift) { return shift >= 0 ? x >> shift : x / d; }
+__device__ __forceinline__ int mod_by(int x, int d, int shift) { return shift >= 0 ? x & (d - 1) : x % d; }
+
+template <typename F>
+__device__ __forceinline__ void map4(const int* in, int* out, int j0, int k, F&& f) {
+  if (j0 + kIdxPerThread <= k && !((reinterpret_cast<uintptr_t>(in + j0) | reinterpret_cast<uintptr_t>(out + j0)) & 15)) {
+    const int4 x = *reinterpret_cast<const int4*>(in + j0);
+    *reinterpret_cast<int4*>(out + j0) = make_int4(f(x.x), f(x.y), f(x.z), f(x.w));
+  } else {
+    for (int j = j0; j < min(j0 + kIdxPerThread, k); j++) out[j] = f(in[j]);
+  }
+}
+
+__global__ __launch_bounds__(256) void remap_kernel(const int* col, int64_t col_ld, int rows, int k,
                                                     const int* __restrict__ si, int64_t si_ld, int width,
-                                                    const int* __restrict__ row_ks, int sbk, int* out,
+                                                    const int* __restrict__ row_ks, int sbk, int sbk_shift, int* out,
                                                     int64_t out_ld) {
   const int r = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= k) return;
-  const int c = col[(int64_t)r * col_ld + j];
-  int v = -1;
-  if (c >= 0 && c < width) v = (si[(int64_t)r * si_ld + c / sbk] - row_ks[r] / sbk) * sbk + c % sbk;
-  out[(int64_t)r * out_ld + j] = v;
+  const int j0 = (blockIdx.x * 256 + threadIdx.x) * kIdxPerThread;
+  if (j0 >= k) return;
+  const int base = div_by(row_ks[r], sbk, row_ks[r] >= 0 ? sbk_shift : -1);
+  const int* sir = si + (int64_t)r * si_ld;
+  map4(col + (int64_t)r * col_ld, out + (int64_t)r * out_ld, j0, k, [&](int c) {
+    return c >= 0 && c < width ? (sir[div_by(c, sbk, sbk_shift)] - base) * sbk + mod_by(c, sbk, sbk_shift) : -1;
+  });
 }
 
 __global__ __launch_bounds__(256) void slot_kernel(const int* idx, int64_t idx_ld, int k,
                                                    const int* __restrict__ row_to_req,
                                                    const int* __restrict__ block_table, int64_t bt_ld, int bt_width,
-                                                   int num_reqs, int block_size, int block_span, int* out,
+                                                   int num_reqs, int block_size, int bs_shift, int block_span, int* out,
                                                    int64_t out_ld) {
   const int r = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= k) return;
-  const int p = idx[(int64_t)r * idx_ld + j];
-  int v = -1;
-  if (p >= 0) {
-    const int blk = p / block_size;
-    const int req = row_to_req ? row_to_req[r] : r;
-    if (blk < bt_width && req >= 0 && req < num_reqs)
-      v = block_table[(int64_t)req * bt_ld + blk] * block_span + p % block_size;
-  }
-  out[(int64_t)r * out_ld + j] = v;
+  const int j0 = (blockIdx.x * 256 + threadIdx.x) * kIdxPerThread;
+  if (j0 >= k) return;
+  const int req = row_to_req ? row_to_req[r] : r;
+  const bool req_ok = req >= 0 && req < num_reqs;
+  const int* btr = block_table + (int64_t)(req_ok ? req : 0) * bt_ld;
+  map4(idx + (int64_t)r * idx_ld, out + (int64_t)r * out_ld, j0, k, [&](int p) {
+    if (p < 0 || !req_ok) return -1;
+    const int blk = div_by(p, block_size, bs_shift);
+    return blk < bt_width ? btr[blk] * block_span + mod_by(p, block_size, bs_shift) : -1;
+  });
 }
 
 }  // namespace
@@ -151,8 +171,10 @@ extern "C" int dsi_topk_remap(const int32_t* col, int64_t col_ld, int32_t rows, 
   if (rows == 0 || k == 0) return DSI_OK;
   if (!col || !sparse_indices || !row_ks || !out) return DSI_EINVAL;
   if (rows > 65535) return DSI_EUNSUPPORTED;
-  hipLaunchKernelGGL(remap_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)rows), dim3(256), 0, stream, col,
-                     col_ld, rows, k, sparse_indices, si_ld, (int)width, row_ks, sparse_block_kv, out, out_ld);
+  const int per_block = 256 * kIdxPerThread;
+  hipLaunchKernelGGL(remap_kernel, dim3((unsigned)((k + per_block - 1) / per_block), (unsigned)rows), dim3(256), 0,
+                     stream, col, col_ld, rows, k, sparse_indices, si_ld, (int)width, row_ks, sparse_block_kv,
+                     pow2_shift(sparse_block_kv), out, out_ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
@@ -167,8 +189,9 @@ extern "C" int dsi_req_index_to_global_slot(const int32_t* idx, int64_t idx_ld, 
   if (rows == 0 || k == 0) return DSI_OK;
   if (!idx || !block_table || !out) return DSI_EINVAL;
   if (rows > 65535) return DSI_EUNSUPPORTED;
-  hipLaunchKernelGGL(slot_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)rows), dim3(256), 0, stream, idx,
-                     idx_ld, k, row_to_req, block_table, bt_ld, bt_width, num_reqs, block_size, block_span, out,
-                     out_ld);
+  const int per_block = 256 * kIdxPerThread;
+  hipLaunchKernelGGL(slot_kernel, dim3((unsigned)((k + per_block - 1) / per_block), (unsigned)rows), dim3(256), 0,
+                     stream, idx, idx_ld, k, row_to_req, block_table, bt_ld, bt_width, num_reqs, block_size,
+                     pow2_shift(block_size), block_span, out, out_ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
