@@ -45,6 +45,7 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E (published)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_logits_T2048_S8192_traffic.md")
 PREFILL_SOURCES = [os.path.join(ROOT, "sparse_attention_token_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
 FLOP_PER_PAIR = 2 * 64 * 128
+ALL_WORKLOADS = ["decode_w3", "decode_w4", "sparse_w5", "sparse_w5_mxfp4", "prefill_gather", "q_prep", "cp_merge"]
 
 
 def log(*a):
@@ -472,11 +473,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--workloads", default=None,
+                    help="comma-separated subset of the reported workloads (default: all): " + ",".join(ALL_WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the indexer path has no multi-GPU mode in this build "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
+    chosen = ALL_WORKLOADS if args.workloads is None else [w for w in args.workloads.split(",") if w]
+    unknown = [w for w in chosen if w not in ALL_WORKLOADS]
+    if unknown:
+        raise SystemExit(f"unknown workloads {unknown}; choose from {ALL_WORKLOADS}")
+    if args.only_headline:
+        chosen = []
     torch.cuda.set_device(0)
     dsi.lib()
 
@@ -491,20 +500,26 @@ def main():
     flops = pf["pairs"] * FLOP_PER_PAIR
     achieved = flops / (pf["ms_logits"] * 1e-3) / 1e12
     extra = {}
-    if not args.only_headline:
-        for n in (3, 4):
+    for n in (3, 4):
+        if f"decode_w{n}" in chosen:
             log(f"decode workload {n} ...")
             extra[f"decode_w{n}"] = bench_decode(n, args.steps, args.warmup)
-        log("hierarchical sparse ...")
+    if "sparse_w5" in chosen or "sparse_w5_mxfp4" in chosen:
         c5 = synth.workload(5)
-        extra["sparse_w5"] = bench_sparse(args.steps, args.warmup, c5)
-        log("hierarchical sparse, MXFP4 cache ...")
-        extra["sparse_w5_mxfp4"] = bench_sparse(args.steps, args.warmup, c5, mxfp4=True)
+        if "sparse_w5" in chosen:
+            log("hierarchical sparse ...")
+            extra["sparse_w5"] = bench_sparse(args.steps, args.warmup, c5)
+        if "sparse_w5_mxfp4" in chosen:
+            log("hierarchical sparse, MXFP4 cache ...")
+            extra["sparse_w5_mxfp4"] = bench_sparse(args.steps, args.warmup, c5, mxfp4=True)
         del c5
+    if "prefill_gather" in chosen:
         log("prefill K gather ...")
         extra["prefill_gather"] = bench_gather(args.steps, args.warmup)
+    if "q_prep" in chosen:
         log("q preparation ...")
         extra["q_prep"] = bench_qprep(args.steps, args.warmup)
+    if "cp_merge" in chosen:
         log("context-parallel merge ...")
         extra["cp_merge"] = bench_merge(args.steps, args.warmup)
     log("cpu baseline ...")
