@@ -264,23 +264,25 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   // Score chunk c: this wavefront's keys as kGroups / 2 pairs of 32-key groups, each pair
   // software-pipelined (dc_phase: the first group's MFMAs carry the second group's decode,
   // the second group's MFMAs the first group's head sum).  With two buffers the gather of
-  // chunk `next` (if any) is issued piece by piece between the first MFMAs, so that a busy
-  // vector-memory queue never holds up the matrix work; with more buffers it was issued
-  // whole right after the barrier.
+  // chunk `next` (if any) is issued whole before the first group: issuing it piece by piece
+  // between the first MFMAs (so that a busy vector-memory queue would not hold up the matrix
+  // work) measured slower — each DMA instruction then stalled the phase it sat in — in this
+  // kernel (65 -> 64 us) and more in the sparse ones (189 -> 176 us, 159 -> 150 us).
   auto score_chunk = [&](int c, const uint8_t* buf, int next) {
     const int64_t* seg = s_base + (c - c_first) * 16;
 #pragma unroll
     for (int h = 0; h < kGroups / 2; h++) {
       const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
-      auto dma = [&](int i) {
-        if (NB == 2 && h == 0 && i < kDcSlabsPerWave && has_pool && next < c_end)
+      if (NB == 2 && h == 0 && has_pool && next < c_end) {
+#pragma unroll
+        for (int i = 0; i < kDcSlabsPerWave; i++)
           dc_gather_piece(s_buf[(next - c_first) % NB], s_base + (next - c_first) * 16, pool, wave, lane, i);
-      };
+      }
       K32 kb;
       load_k32_raw(kb, keys, lane);
       f32x16 a0, a1, b0 = {}, b1 = {};
       float acc[4];
-      dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, dma);
+      dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, [](int) {});
       dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
       const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
       const int key = kbase + 64 * h + lane;  // key within the chunk
@@ -468,14 +470,15 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
 #pragma unroll
       for (int h = 0; h < kGroups / 2; h++) {
         const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
-        auto dma = [&](int i) {
-          if (h == 0 && i < kDcSlabsPerWave && next < c_end) gather_piece(next, i);
-        };
+        if (h == 0 && next < c_end) {
+#pragma unroll
+          for (int i = 0; i < kDcSlabsPerWave; i++) gather_piece(next, i);
+        }
         K32 kb;
         load_k32_raw(kb, keys, lane);
         f32x16 a0, a1, b0 = {}, b1 = {};
         float acc[4];
-        dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, dma);
+        dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, [](int) {});
         dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
         const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
         const int key = kbase + 64 * h + lane;  // key within the chunk
@@ -711,16 +714,17 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
 #pragma unroll
       for (int h = 0; h < kGroups / 2; h++) {
         const uint8_t* keys = buf + (kbase + 64 * h) * kMxLds;
-        auto dma = [&](int i) {
-          if (h == 0 && i < kMxSlabsPerWave && next < c_end) gather_piece(next, i);
-        };
+        if (h == 0 && next < c_end) {
+#pragma unroll
+          for (int i = 0; i < kMxSlabsPerWave; i++) gather_piece(next, i);
+        }
         K32b kb;
         const MxRaw r0 = load_mx_raw(keys, lane);
 #pragma unroll
         for (int j = 0; j < 4; j++) decode_mx_pair(kb, r0, j);
         f32x16 a0, a1, b0 = {}, b1 = {};
         float acc[4];
-        mx_phase<false, true>(a0, a1, qf, kb, keys + 32 * kMxLds, lane, wf, b0, b1, acc, dma);
+        mx_phase<false, true>(a0, a1, qf, kb, keys + 32 * kMxLds, lane, wf, b0, b1, acc, [](int) {});
         mx_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
         const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
         const int key = kbase + 64 * h + lane;  // key within the chunk
