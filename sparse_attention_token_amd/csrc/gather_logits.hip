@@ -50,37 +50,39 @@ constexpr int kDcSlabsPerWave = kDcBuf / 1024 / 4;  // 9 DMA instructions per wa
 constexpr int kDcJob = 8;                           // chunks per workgroup
 constexpr int kDcSegs = kDcJob * kDcChunk / 16;     // 16-token segments per job
 
-// Issue this wavefront's DMA pieces of one chunk.  Piece s of the chunk (16 bytes) is key
-// s/9, piece s%9; absent segments read the pool's first bytes (their keys score -inf).
-// The loads are issued as inline assembly (M0 = the LDS destination of the wavefront's
-// 1 KB, one wait state, global_load_lds_dwordx4), so the compiler does not treat them as
-// writes to the other buffer that the scoring of the current chunk has to wait for; the
-// kernel orders them itself with an explicit vmcnt wait and a barrier.  No other code in
-// the kernel uses M0.
-__device__ __forceinline__ void dc_gather(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
-                                          int lane) {
+// Issue this wavefront's NP DMA pieces of one chunk: slab i (1 KB of the chunk buffer) is
+// slab wave + 4i, lane l's 16 bytes are piece 64*slab + l, read from src_of(piece).  The
+// loads are issued as inline assembly (M0 = the LDS destination of the wavefront's 1 KB,
+// one wait state, global_load_lds_dwordx4), so the compiler does not treat them as writes
+// to the other buffer that the scoring of the current chunk has to wait for; the kernel
+// orders them itself with an explicit vmcnt wait and a barrier.  No other code in the
+// kernel uses M0.  Every source address (each needs an LDS read of its key's offset) is
+// computed before the first load is issued: the assembly statements are ordered memory
+// operations, so interleaving them with those reads cost one LDS round trip per load.
+template <int NP, typename SrcOf>
+__device__ __forceinline__ void dma_chunk(uint8_t* buf, int wave, int lane, SrcOf&& src_of) {
+  const uint8_t* src[NP];
 #pragma unroll
-  for (int i = 0; i < kDcSlabsPerWave; i++) {
-    const int slab = wave + 4 * i;
-    const int piece = slab * 64 + lane;
-    const int key = piece / 9, p = piece - key * 9;
-    const int64_t base = seg_base[key >> 4];
-    const uint8_t* src = base >= 0 ? pool + base + (key & 15) * kRow + (p < 8 ? 16 * p : 116) : pool;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+  for (int i = 0; i < NP; i++) src[i] = src_of((wave + 4 * i) * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < NP; i++) {
+    const uint32_t lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + (wave + 4 * i) * 1024));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[i]), "s"(lds)
+                 : "memory");
   }
 }
 
-// Piece i (0..8) of this wavefront's share of dc_gather.
-__device__ __forceinline__ void dc_gather_piece(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
-                                                int lane, int i) {
-  const int slab = wave + 4 * i;
-  const int piece = slab * 64 + lane;
-  const int key = piece / 9, p = piece - key * 9;
-  const int64_t base = seg_base[key >> 4];
-  const uint8_t* src = base >= 0 ? pool + base + (key & 15) * kRow + (p < 8 ? 16 * p : 116) : pool;
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+// This wavefront's share of one decode chunk: piece s (16 bytes) is key s/9, piece s%9 of
+// the key's 132-byte row (bytes 16p, or 116..131 for p = 8); absent segments read the
+// pool's first bytes (their keys score -inf).
+__device__ __forceinline__ void dc_gather(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
+                                          int lane) {
+  dma_chunk<kDcSlabsPerWave>(buf, wave, lane, [&](int piece) {
+    const int key = piece / 9, p = piece - key * 9;
+    const int64_t base = seg_base[key >> 4];
+    return base >= 0 ? pool + base + (key & 15) * kRow + (p < 8 ? 16 * p : 116) : pool;
+  });
 }
 
 // Wait until at most `n` of this wavefront's vector-memory operations are outstanding.
@@ -273,11 +275,8 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
 #pragma unroll
     for (int h = 0; h < kGroups / 2; h++) {
       const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
-      if (NB == 2 && h == 0 && has_pool && next < c_end) {
-#pragma unroll
-        for (int i = 0; i < kDcSlabsPerWave; i++)
-          dc_gather_piece(s_buf[(next - c_first) % NB], s_base + (next - c_first) * 16, pool, wave, lane, i);
-      }
+      if (NB == 2 && h == 0 && has_pool && next < c_end)
+        dc_gather(s_buf[(next - c_first) % NB], s_base + (next - c_first) * 16, pool, wave, lane);
       K32 kb;
       load_k32_raw(kb, keys, lane);
       f32x16 a0, a1, b0 = {}, b1 = {};
@@ -391,17 +390,14 @@ constexpr int kSpJob = 8;
 constexpr int kMxJob = 16;
 constexpr uint32_t kSpAbsent = 0xFFFFFFFFu;   // source offsets are in 4-byte units
 
-// Piece i (0..8) of this wavefront's share of one chunk's gather (as dc_gather_piece, with
-// one source offset per key).
-__device__ __forceinline__ void sp_gather_piece(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
-                                                int lane, int i) {
-  const int slab = wave + 4 * i;
-  const int piece = slab * 64 + lane;
-  const int key = piece / 9, p = piece - key * 9;
-  const uint32_t off = key_off[key];
-  const uint8_t* a = off != kSpAbsent ? src + (int64_t)off * 4 + (p < 8 ? 16 * p : 116) : src;
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(lds) : "memory");
+// This wavefront's share of one chunk's gather (as dc_gather, with one source offset per key).
+__device__ __forceinline__ void sp_gather(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
+                                          int lane) {
+  dma_chunk<kDcSlabsPerWave>(buf, wave, lane, [&](int piece) {
+    const int key = piece / 9, p = piece - key * 9;
+    const uint32_t off = key_off[key];
+    return off != kSpAbsent ? src + (int64_t)off * 4 + (p < 8 ? 16 * p : 116) : src;
+  });
 }
 
 template <int JOB>
@@ -461,19 +457,15 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
         __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)r * ld, (short)0, width * 2, 0x00020000);
     __syncthreads();  // offsets visible
 
-    auto gather_piece = [&](int c, int i) {
-      if (has_src)
-        sp_gather_piece(s_buf[(c - c_first) % NB], s_off + (c - c_first) * kDcChunk, k_src, wave, lane, i);
+    auto gather = [&](int c) {
+      if (has_src) sp_gather(s_buf[(c - c_first) % NB], s_off + (c - c_first) * kDcChunk, k_src, wave, lane);
     };
     auto score_chunk = [&](int c, const uint8_t* buf, int next) {
       const uint32_t* coff = s_off + (c - c_first) * kDcChunk;
 #pragma unroll
       for (int h = 0; h < kGroups / 2; h++) {
         const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
-        if (h == 0 && next < c_end) {
-#pragma unroll
-          for (int i = 0; i < kDcSlabsPerWave; i++) gather_piece(next, i);
-        }
+        if (h == 0 && next < c_end) gather(next);
         K32 kb;
         load_k32_raw(kb, keys, lane);
         f32x16 a0, a1, b0 = {}, b1 = {};
@@ -489,8 +481,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
       }
     };
 
-#pragma unroll
-    for (int i = 0; i < kDcSlabsPerWave; i++) gather_piece(c_first, i);
+    gather(c_first);
     for (int cc = c_first; cc < c_end; cc++) {
       // as in the decode kernel: after chunk cc's gather this wavefront issued the stores of
       // the chunk before it (when cc is not the segment's first)
@@ -638,15 +629,14 @@ __device__ __forceinline__ void mx_phase(f32x16& x0, f32x16& x1, const Q32b& q, 
   }
 }
 
-__device__ __forceinline__ void mx_gather_piece(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
-                                                int lane, int i) {
-  const int slab = wave + 4 * i;
-  const int piece = slab * 64 + lane;
-  const int key = piece / 5, p = piece - key * 5;
-  const uint32_t off = key_off[key];
-  const uint8_t* a = off != kSpAbsent ? src + (int64_t)off * 4 + (p < 4 ? 16 * p : 52) : src;
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + slab * 1024));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(lds) : "memory");
+// Five 16-byte pieces per 68-byte row: bytes 0..63 and 52..67.
+__device__ __forceinline__ void mx_gather(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
+                                          int lane) {
+  dma_chunk<kMxSlabsPerWave>(buf, wave, lane, [&](int piece) {
+    const int key = piece / 5, p = piece - key * 5;
+    const uint32_t off = key_off[key];
+    return off != kSpAbsent ? src + (int64_t)off * 4 + (p < 4 ? 16 * p : 52) : src;
+  });
 }
 
 template <int JOB>
@@ -705,19 +695,15 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
         __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)r * ld, (short)0, width * 2, 0x00020000);
     __syncthreads();  // offsets visible
 
-    auto gather_piece = [&](int c, int i) {
-      if (has_src)
-        mx_gather_piece(s_buf[(c - c_first) % NB], s_off + (c - c_first) * kDcChunk, k_src, wave, lane, i);
+    auto gather = [&](int c) {
+      if (has_src) mx_gather(s_buf[(c - c_first) % NB], s_off + (c - c_first) * kDcChunk, k_src, wave, lane);
     };
     auto score_chunk = [&](int c, const uint8_t* buf, int next) {
       const uint32_t* coff = s_off + (c - c_first) * kDcChunk;
 #pragma unroll
       for (int h = 0; h < kGroups / 2; h++) {
         const uint8_t* keys = buf + (kbase + 64 * h) * kMxLds;
-        if (h == 0 && next < c_end) {
-#pragma unroll
-          for (int i = 0; i < kMxSlabsPerWave; i++) gather_piece(next, i);
-        }
+        if (h == 0 && next < c_end) gather(next);
         K32b kb;
         const MxRaw r0 = load_mx_raw(keys, lane);
 #pragma unroll
@@ -734,8 +720,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
       }
     };
 
-#pragma unroll
-    for (int i = 0; i < kMxSlabsPerWave; i++) gather_piece(c_first, i);
+    gather(c_first);
     for (int cc = c_first; cc < c_end; cc++) {
       if (has_src) wait_gather<NB, kStores>(min(cc - c_first, 1));
       __syncthreads();
