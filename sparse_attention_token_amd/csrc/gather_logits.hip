@@ -385,9 +385,10 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
 // Chunks per segment: longer segments pay the segment set-up (offsets, q decode) less often
 // (8 instead of 4 chunks: 205 -> 196 us on the hierarchical workload); the FP8 kernel's two
 // 36 KB buffers and 8 KB of offsets fill the 160 KB LDS at two workgroups per CU, the MXFP4
-// kernel's 20 KB buffers leave room for 16 (178 -> 165 us).
+// kernel's 20 KB buffers leave room for 32, a whole 8192-column row (178 -> 165 us at 16,
+// 144 -> 138 us at 32).
 constexpr int kSpJob = 8;
-constexpr int kMxJob = 16;
+constexpr int kMxJob = 32;
 constexpr uint32_t kSpAbsent = 0xFFFFFFFFu;   // source offsets are in 4-byte units
 
 // This wavefront's share of one chunk's gather (as dc_gather, with one source offset per key).
