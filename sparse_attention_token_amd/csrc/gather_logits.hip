@@ -33,7 +33,7 @@ int cu_count() {
   return cached[dev];
 }
 // ------------------------------------------------------------------ paged decode
-// A workgroup (4 wavefronts) streams segments of up to 8 chunks of 256 keys of one request
+// A workgroup (4 wavefronts) streams segments of up to 16 chunks of 256 keys of one request
 // through a ring of LDS buffers: the DMA gathers of the next chunks are in flight while
 // one chunk is scored, and the request's q rows stay decoded in VGPRs for the segment.
 // Scoring decodes a 32-key group's FP8 codes under the previous group's MFMAs and sums
@@ -47,7 +47,8 @@ constexpr int kDcChunk = 256;                       // keys per LDS buffer
 constexpr int kDcRow = 144;                         // LDS bytes per key
 constexpr int kDcBuf = kDcChunk * kDcRow;           // 36864
 constexpr int kDcSlabsPerWave = kDcBuf / 1024 / 4;  // 9 DMA instructions per wavefront per chunk
-constexpr int kDcJob = 8;                           // chunks per workgroup
+constexpr int kDcJob = 16;                          // chunks per job (16 rather than 8: fewer set-ups,
+                                                    // 75.6 -> 71.7 us for 16 requests x 2 rows)
 constexpr int kDcSegs = kDcJob * kDcChunk / 16;     // 16-token segments per job
 
 // Issue this wavefront's NP DMA pieces of one chunk: slab i (1 KB of the chunk buffer) is
@@ -202,8 +203,8 @@ __device__ __forceinline__ float dc_head_sum(const W32p& w, const f32x16& y0, co
 
 // WPR = wavefronts per row (4, 2 or 1): each scores 256 / WPR keys of every chunk.  NB =
 // chunk buffers in LDS: NB - 1 gathers are in flight while one chunk is scored.
-// Work split.  persistent = 0: workgroup (x, y) takes chunks [8x, 8x + 8) of request y
-// (grid = (ceil(max_context_len / 2048), B)).  persistent = 1 (B <= kDcMaxReqs): the grid is
+// Work split.  persistent = 0: workgroup (x, y) takes chunks [kDcJob x, kDcJob (x + 1)) of request y
+// (grid = (ceil(max_context_len / (256 * kDcJob)), B)).  persistent = 1 (B <= kDcMaxReqs): the grid is
 // one-dimensional (two workgroups per CU) and workgroup i takes the i-th of gridDim.x equal
 // shares of all requests' chunks in request order, as segments of at most kDcJob chunks of
 // one request each, so that no CU idles while a few long jobs finish.
