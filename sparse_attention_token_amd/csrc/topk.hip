@@ -211,8 +211,8 @@ __device__ __forceinline__ void slice_range(int st, int en, int g, int G, int& a
 
 // The boundary bin b1 (top 11 key bits) is known, `above1` columns above it are written
 // to out[0, above1), and the m columns of bin b1 are in s_ckey/s_ccol (when m <= cap).
-// Resolves the remaining key bits (fp32: 11 then 10, bf16: 5) by histograms over the
-// candidates — or over the row when m > cap — and writes the k - above1 selected
+// Resolves the remaining key bits (fp32: three digits of 7, bf16: 5) by histograms over
+// the candidates — or over the row when m > cap — and writes the k - above1 selected
 // boundary-bin columns to out[above1, k).  Call with all threads.
 template <bool BF16, typename C>
 __device__ __forceinline__ void resolve_boundary(const uint8_t* row, int st, int en, int k, uint32_t b1, int above1,
@@ -224,9 +224,9 @@ __device__ __forceinline__ void resolve_boundary(const uint8_t* row, int st, int
   const int lane = tid & 63;
   int need = k - above1;
   constexpr int kLow = K::kTopShift;
-  const int nd = BF16 ? 1 : 2;
-  const int shifts[2] = {BF16 ? 0 : 10, 0};
-  const int widths[2] = {BF16 ? 5 : 11, 10};
+  const int nd = BF16 ? 1 : 3;
+  const int shifts[3] = {BF16 ? 0 : 14, 7, 0};
+  const int widths[3] = {BF16 ? 5 : 7, 7, 7};
   uint32_t prefix = b1 << kLow;  // known high bits of the threshold key
   const bool in_lds = m <= cap;
   for (int p = 0; p < nd; p++) {
@@ -609,11 +609,12 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
     const int m = s_cnt[3];
     const int need = k - above1;
     if (m <= kCap) {
-      // Further digits of the key (fp32: 11 then 10 bits; bf16: 5 bits) by histograms over
-      // the boundary bin's columns in LDS.
-      constexpr int kDigits = BF16 ? 1 : 2;
-      constexpr int kSh[2] = {BF16 ? 0 : 10, 0};
-      constexpr int kWd[2] = {BF16 ? 5 : 11, 10};
+      // Further digits of the key (fp32: three of 7 bits; bf16: 5 bits) by histograms over
+      // the boundary bin's columns in LDS.  Narrow digits keep each pass's fixed cost (clear
+      // the bins, search them) small: the candidates are a few hundred at most in practice.
+      constexpr int kDigits = BF16 ? 1 : 3;
+      constexpr int kSh[3] = {BF16 ? 0 : 14, 7, 0};
+      constexpr int kWd[3] = {BF16 ? 5 : 7, 7, 7};
       uint32_t prefix = b1 << kShift;
       int rem = need;
       // When the bin a digit selects holds exactly the columns still needed, all of it is
@@ -631,10 +632,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
           if ((key >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1);
         }
         __syncthreads();
-        if (p == 0)
-          find_bin_w0<(BF16 ? 32 : 2048)>(s_hist, 0, nb, rem, s_sel, tid);
-        else
-          find_bin_w0<1024>(s_hist, 0, nb, rem, s_sel, tid);
+        find_bin_w0<(BF16 ? 32 : 128)>(s_hist, 0, nb, rem, s_sel, tid);
         prefix |= (uint32_t)s_sel[0] << sh;
         rem -= s_sel[1];
         whole = !BF16 && s_sel[3] == rem;
