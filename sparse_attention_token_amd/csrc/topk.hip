@@ -737,40 +737,50 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
 
 // Step 2: one workgroup per row sums the slice histograms, finds the boundary bin b1 and
 // gives every slice the number of columns the slices before it hold above b1, at b1, and
-// valid (the offsets its writes start at).  grid = rows.
-__global__ __launch_bounds__(LongRows::kThreads) void topk_split_reduce_kernel(void* ws, int rows, int G, int k) {
-  using C = LongRows;
-  constexpr int kT = C::kThreads;
-  static_assert(C::kWaves >= kMaxSplit, "one wavefront per slice");
-  __shared__ int s_all[kMaxSplit][kHistBins];  // the slice histograms
-  __shared__ int s_hist[kHistBins];            // their sum
+// valid (the offsets its writes start at).  Thread t owns bins [8t, 8t + 8) of every slice
+// in registers; the per-slice counts are wavefront sums, then sums over the four
+// wavefronts.  grid = rows.
+using ReduceCfg = Cfg<256, 0, 1>;
+__global__ __launch_bounds__(ReduceCfg::kThreads) void topk_split_reduce_kernel(void* ws, int rows, int G, int k) {
+  using C = ReduceCfg;
+  constexpr int kT = C::kThreads, kB = kHistBins / kT;  // 8 bins per thread
+  static_assert(kB == 8, "two 16-byte loads per slice and thread");
+  __shared__ __attribute__((aligned(16))) int s_hist[kHistBins];
   __shared__ int s_wave[C::kWaves];
   __shared__ int s_sel[4];
-  __shared__ int s_slice[3][kMaxSplit];
+  __shared__ int s_part[C::kWaves][3][kMaxSplit];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const SplitWs w = split_ws(ws, rows, G);
   const int* hist = w.hist + (int64_t)r * G * kHistBins;
-  for (int i = tid; i < kHistBins; i += kT) {
-    int v[kMaxSplit], sum = 0;
+  int4 v[kMaxSplit][2];
 #pragma unroll
-    for (int j = 0; j < kMaxSplit; j++) v[j] = j < G ? hist[j * kHistBins + i] : 0;  // all loads in flight
-#pragma unroll
-    for (int j = 0; j < kMaxSplit; j++) {
-      s_all[j][i] = v[j];
-      sum += v[j];
-    }
-    s_hist[i] = sum;
+  for (int j = 0; j < kMaxSplit; j++) {  // all loads in flight
+    const int4* p = reinterpret_cast<const int4*>(hist + (int64_t)j * kHistBins + tid * kB);
+    v[j][0] = j < G ? p[0] : int4{0, 0, 0, 0};
+    v[j][1] = j < G ? p[1] : int4{0, 0, 0, 0};
   }
+  int4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; j++) {
+    s0.x += v[j][0].x, s0.y += v[j][0].y, s0.z += v[j][0].z, s0.w += v[j][0].w;
+    s1.x += v[j][1].x, s1.y += v[j][1].y, s1.z += v[j][1].z, s1.w += v[j][1].w;
+  }
+  reinterpret_cast<int4*>(s_hist + tid * kB)[0] = s0;
+  reinterpret_cast<int4*>(s_hist + tid * kB)[1] = s1;
   __syncthreads();
   select_bin<C, 1>(s_hist, kHistBins, k, s_wave, s_sel, tid);
   const uint32_t b1 = (uint32_t)s_sel[0];
-  if (wave < kMaxSplit) {  // wavefront j: columns of slice j above b1, at b1, valid
+  // this thread's bins of slice j above b1, at b1, valid
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; j++) {
+    const int h[kB] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w, v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
     int gt = 0, eq = 0, valid = 0;
-    for (int i = lane; i < kHistBins; i += 64) {
-      const int h = s_all[wave][i];
-      valid += h;
-      gt += (uint32_t)i > b1 ? h : 0;
-      eq += (uint32_t)i == b1 ? h : 0;
+#pragma unroll
+    for (int e = 0; e < kB; e++) {
+      const uint32_t bin = (uint32_t)(tid * kB + e);
+      valid += h[e];
+      gt += bin > b1 ? h[e] : 0;
+      eq += bin == b1 ? h[e] : 0;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -779,9 +789,9 @@ __global__ __launch_bounds__(LongRows::kThreads) void topk_split_reduce_kernel(v
       valid += __shfl_xor(valid, o);
     }
     if (lane == 0) {
-      s_slice[0][wave] = gt;
-      s_slice[1][wave] = eq;
-      s_slice[2][wave] = valid;
+      s_part[wave][0][j] = gt;
+      s_part[wave][1][j] = eq;
+      s_part[wave][2][j] = valid;
     }
   }
   __syncthreads();
@@ -789,7 +799,8 @@ __global__ __launch_bounds__(LongRows::kThreads) void topk_split_reduce_kernel(v
     int acc = 0;
     for (int j = 0; j < G; j++) {
       w.off[((int64_t)r * kMaxSplit + j) * 4 + tid] = acc;
-      acc += s_slice[tid][j];
+#pragma unroll
+      for (int q = 0; q < C::kWaves; q++) acc += s_part[q][tid][j];
     }
   }
   if (tid == 0) {
@@ -938,8 +949,8 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
     if (bf) {
       hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, workspace, rows, G);
-      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream, workspace,
-                         rows, G, k);
+      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(ReduceCfg::kThreads), 0, stream,
+                         workspace, rows, G, k);
       hipLaunchKernelGGL(topk_slice_select_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
       hipLaunchKernelGGL(topk_split_resolve_kernel<true>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
@@ -947,8 +958,8 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
     } else {
       hipLaunchKernelGGL(topk_slice_hist_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, workspace, rows, G);
-      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream, workspace,
-                         rows, G, k);
+      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(ReduceCfg::kThreads), 0, stream,
+                         workspace, rows, G, k);
       hipLaunchKernelGGL(topk_slice_select_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
       hipLaunchKernelGGL(topk_split_resolve_kernel<false>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
