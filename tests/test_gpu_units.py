@@ -192,17 +192,31 @@ def _rows_with_ties(rng, rows, width):
                                      (100, 7), (8193, 2048), (16384, 1000), (40000, 2048)])
 def test_topk_f32_same_input_exact_values(width, k):
     rng = np.random.default_rng(width + k)
-    rows = 6
+    rows = 8
     x = _rows_with_ties(rng, rows, width)
     x[1, 5] = np.nan
     x[1, 6] = np.inf
     x[2, 7] = -np.inf
     x[3, :] = 0.0
     x[3, ::2] = -0.0
+    # Adjacent floats 1 + i*2^-23 share every key bit but the lowest ones, so the last
+    # resolution digit decides the boundary.  Row 6: up to 5000 of them (a boundary bin
+    # larger than the in-LDS candidate list); row 7: 1000 of them under 1500 larger values
+    # (a boundary bin of 1000 columns resolved in LDS).
+    adj = lambda n: rng.permutation(np.float32(1.0) + np.arange(n, dtype=np.float32) * np.float32(2.0 ** -23))
+    n6 = min(width, 5000)
+    x[6, :n6] = adj(n6)
+    if width >= 2500:
+        x[7, :] = rng.uniform(-1.0, 0.5, width).astype(np.float32)
+        x[7, :1000] = adj(1000)
+        x[7, 1000:2500] = rng.uniform(2.0, 3.0, 1500).astype(np.float32)
+        x[7] = rng.permutation(x[7])
     starts = rng.integers(0, max(width // 4, 1), rows).astype(np.int32)
     ends = np.minimum(starts + rng.integers(0, width, rows), width).astype(np.int32)
     ends[0] = width
     starts[0] = 0
+    starts[6:] = 0
+    ends[6:] = width
     ref = oracle.topk_select(x, ends, k, starts=starts)
     got = host(dsi.topk_select(dev(x), dev(ends), k=k, row_starts=dev(starts)))
     for r in range(rows):
