@@ -60,6 +60,7 @@ def _load():
         "orc_sparse_mqa_logits_mxfp4": (None, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _p, _i64, _p,
                                                _i32, _i64, _i32, _p, _i64]),
         "orc_q_rope_quant": (None, [_p, _p, _i32, _p, _i64, _i32, _p, ctypes.c_float, ctypes.c_float, _p, _p]),
+        "orc_mqa_logits_paged_mxfp4": (None, [_p, _p, _i32, _i32, _p, _p, _i32, _i64, _p, _i64, _i32, _p, _i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -382,4 +383,20 @@ def sparse_mqa_logits_mxfp4(q, w, ks, ke, sparse_indices, end, sbk, k_src, block
     lib.orc_sparse_mqa_logits_mxfp4(_ptr(q), _ptr(w), rows, _ptr(ks), _ptr(ke), _ptr(si), si_ld, nsb, _ptr(end),
                                     sbk, _ptr(k_src), _ptr(bt), bt_ld, _ptr(r2r), block_size, block_stride,
                                     int(out_f32), _ptr(out), width)
+    return out
+
+# ---------------------------------------------------------------- O15
+def mqa_logits_paged_mxfp4(q, w, next_n, context_lens, pool, block_size, block_stride, block_table, width):
+    """Decode rows straight from a paged pool of 68-byte MXFP4 rows -> fp32 [B*next_n, width]."""
+    lib = _load()
+    q = _c(q, np.uint8)
+    w = _c(w, np.uint16)
+    cl = _c(context_lens, np.int32)
+    B = cl.shape[0]
+    assert q.shape == (B * next_n, H, D) and w.shape == (B * next_n, H)
+    bt, bt_ld = _rows(block_table, np.int32)
+    assert pool.dtype == np.uint8 and pool.flags["C_CONTIGUOUS"]
+    out = np.empty((B * next_n, width), dtype=np.float32)
+    lib.orc_mqa_logits_paged_mxfp4(_ptr(q), _ptr(w), B, next_n, _ptr(cl), _ptr(pool), block_size, block_stride,
+                                   _ptr(bt), bt_ld, width, _ptr(out), width)
     return out

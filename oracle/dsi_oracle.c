@@ -716,3 +716,36 @@ void orc_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, int32_t ro
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* O15 paged decode on the MXFP4 cache: O2's decode rows with every key row  */
+/* read as a 68-byte MXFP4 row (P1 motivation and implementation: the V4.1   */
+/* indexer cache holds MXFP4 keys; decode reads the paged cache directly, P3 */
+/* prefill/decode table).  Token s of request b lives at                     */
+/* pool + bt[b][s / bs] * block_stride + (s % bs) * 68; a key's value is its  */
+/* code times its block's 2^(E-127), and no per-token scale follows.         */
+void orc_mqa_logits_paged_mxfp4(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                const int32_t* context_lens, const uint8_t* pool, int32_t block_size,
+                                int64_t block_stride, const int32_t* block_table, int64_t bt_ld, int32_t width,
+                                float* logits, int64_t ld) {
+  static float qt[ORC_D][ORC_H];
+  float wf[ORC_H], kd[ORC_D];
+  int32_t b, i, s;
+  for (b = 0; b < B; b++) {
+    for (i = 0; i < next_n; i++) {
+      int64_t r = (int64_t)b * next_n + i;
+      int32_t ke = context_lens[b] - next_n + i + 1;
+      decode_q_row(q + r * ORC_H * ORC_D, w + r * ORC_H, qt, wf);
+      for (s = 0; s < width; s++) {
+        float* o = logits + r * ld + s;
+        if (s < ke) {
+          int32_t page = block_table[(int64_t)b * bt_ld + s / block_size];
+          decode_row_mxfp4(pool + (int64_t)page * block_stride + (int64_t)(s % block_size) * ORC_ROW4, kd);
+          *o = logit_kd(qt, wf, kd);
+        } else {
+          *o = -INFINITY;
+        }
+      }
+    }
+  }
+}

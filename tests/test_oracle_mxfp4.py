@@ -159,3 +159,71 @@ def test_logits_against_fp64_paged():
             terms = wd[r][:, None] * qd[r] * kd[tok][None, :]
             exact = terms.sum()
             assert abs(got[r, c] - exact) <= 2.0 ** -20 * np.abs(terms).sum() + 1e-30, (r, c)
+
+
+def _paged_mx_pool(rng, k, bs, extra_pages=3, pad=16):
+    """k rows [S, 128] (bf16 bits) MXFP4-quantized into a pool of permuted pages (stride bs*68 + pad)."""
+    S = k.shape[0]
+    npg = (S + bs - 1) // bs
+    nb = npg + extra_pages
+    perm = rng.permutation(nb)[:npg].astype(np.int32)
+    stride = bs * 68 + pad
+    pool = np.full(nb * stride, 0x5A, np.uint8)
+    s = np.arange(S)
+    oracle.k_quant_and_cache_mxfp4(k, perm[s // bs].astype(np.int64) * bs + s % bs, pool, bs, stride)
+    return pool, perm, stride
+
+
+def test_paged_decode_against_fp64():
+    """O15 on ragged requests with two next-n rows each, permuted pages and padded page strides: every scored
+    cell equals the fp64 sum of w*q*k over the independently decoded key (within fp32 accumulation), the
+    row's last visible token is L - next_n + i, and everything past it (up to the output width) is -inf."""
+    rng = np.random.default_rng(65)
+    bs, next_n = 16, 2
+    lens = np.array([37, 1, 70], np.int32)
+    width = 80
+    S = int(lens.max())
+    k = synth.draw_k(rng, S)
+    pool, perm, stride = _paged_mx_pool(rng, k, bs)
+    B = lens.shape[0]
+    bt = np.tile(perm, (B, 1))
+    qf = synth.draw_q(rng, B * next_n)
+    q, w = synth.finish_q(rng, qf)
+    got = oracle.mqa_logits_paged_mxfp4(q, w, next_n, lens, pool, bs, stride, bt, width)
+    rows = np.stack([pool[perm[s // bs] * stride + (s % bs) * 68:][:68] for s in range(S)])
+    kd = _decode_mx(rows)
+    qd = oracle.e4m3_decode(q).astype(np.float64)
+    wd = synth._bf16_value(w).astype(np.float64)
+    for b in range(B):
+        for i in range(next_n):
+            r = b * next_n + i
+            ke = int(lens[b]) - next_n + i + 1
+            assert np.all(got[r, max(ke, 0):] == -np.inf)
+            for s in range(max(ke, 0)):
+                terms = wd[r][:, None] * qd[r] * kd[s][None, :]
+                assert abs(got[r, s] - terms.sum()) <= 2.0 ** -20 * np.abs(terms).sum() + 1e-30, (r, s)
+
+
+def test_paged_decode_equals_fp8_path_on_keys_both_formats_hold():
+    """Keys whose values are FP4 codes times 2^-2 in every 32-block (scale byte 125) are E4M3 values too:
+    O15 on the MXFP4 pool and O2's paged decode on the FP8 pool (scale 1) give bit-identical logits."""
+    rng = np.random.default_rng(66)
+    bs, S = 32, 96
+    codes = rng.integers(0, 16, size=(S, 128)).astype(np.uint8)
+    codes[:, ::32] = 7  # every block reaches 6 * 2^-2, so its shared exponent is -2
+    kvals = oracle.fp4_decode(codes) * np.float32(2.0 ** -2)
+    kb = synth._bf16_bits(kvals)
+    pool4, perm, stride4 = _paged_mx_pool(rng, kb, bs)
+    stride8 = bs * 132
+    pool8 = np.zeros(len(pool4) // stride4 * stride8, np.uint8)
+    for s in range(S):
+        row = pool8[perm[s // bs] * stride8 + (s % bs) * 132:][:132]
+        row[:128] = oracle.e4m3_encode(kvals[s])
+        row[128:] = np.ones(1, np.float32).view(np.uint8)
+    lens = np.array([S, 50], np.int32)
+    bt = np.tile(perm, (2, 1))
+    q, w = synth.finish_q(rng, synth.draw_q(rng, 2))
+    a = oracle.mqa_logits_paged(q, w, 1, lens, pool8, bs, stride8, bt, S)
+    b = oracle.mqa_logits_paged_mxfp4(q, w, 1, lens, pool4, bs, stride4, bt, S)
+    assert np.array_equal(a, b)
+    assert np.isinf(b[1, 50:]).all() and np.isfinite(b[0]).all()
