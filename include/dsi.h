@@ -399,6 +399,27 @@ DSI_API int dsi_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, int
                                         int32_t block_size, int64_t block_stride_bytes, uint16_t* logits_bf16,
                                         int64_t ld, hipStream_t stream);
 
+/*
+ * Paged decode logits on the MXFP4 cache (P1 motivation and implementation:
+ * the V4.1 indexer cache holds MXFP4 keys; P3 prefill/decode table: decode
+ * reads the paged cache directly): dsi_paged_mqa_logits_decode with token s
+ * read as a 68-byte MXFP4 row (dsi_k_quant_and_cache_mxfp4's layout) at
+ *   pool + block_table[b*bt_ld + s/block_size]*block_stride_bytes
+ *        + (s % block_size)*68,
+ * whose value is code * 2^(E-127) of its 32-dim block; no per-token scale
+ * follows.  Rows, ranges, -inf for absent pages and every other rule are those
+ * of dsi_paged_mqa_logits_decode.  The codes are decoded exactly to bf16 and
+ * contracted on the bf16 matrix cores with fp32 accumulation.
+ * Errors: as dsi_paged_mqa_logits_decode, with block_stride_bytes >=
+ * block_size*68 (and a multiple of 16).
+ */
+DSI_API int dsi_paged_mqa_logits_decode_mxfp4(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                              const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                              int32_t block_size, int64_t block_stride_bytes,
+                                              const int32_t* block_table, int64_t bt_ld, int32_t bt_width,
+                                              int32_t max_context_len, float* logits, int64_t ld,
+                                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,8 @@ _SIGNATURES = {
     "dsi_mqa_logits_prefill": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _p, _p, _p, _i64, _p]),
     "dsi_paged_mqa_logits_decode": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i64, _i32, _i64, _p, _i64, _i32,
                                                    _i32, _p, _i64, _p]),
+    "dsi_paged_mqa_logits_decode_mxfp4": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i64, _i32, _i64, _p, _i64,
+                                                         _i32, _i32, _p, _i64, _p]),
     "dsi_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "dsi_topk_select": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _i32, _p, _i64, _p, _sz, _p]),
     "dsi_expand_candidates": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _p, _i64, _i32, _i32, _p, _i64, _p,
@@ -169,8 +171,9 @@ def mqa_logits_prefill(q, w, k_rows, row_ks, row_ke, out=None):
 
 
 def paged_mqa_logits_decode(q, w, context_lens, pool, block_size, block_table, max_context_len, next_n=1,
-                            out=None, block_stride_bytes=None, num_blocks=None, bt_width=None):
-    """Decode logits straight from the paged pool; fp32 out [B*next_n, >=max_context_len]."""
+                            out=None, block_stride_bytes=None, num_blocks=None, bt_width=None, mxfp4=False):
+    """Decode logits straight from the paged pool; fp32 out [B*next_n, >=max_context_len].
+    mxfp4=True reads 68-byte MXFP4 rows (dsi_paged_mqa_logits_decode_mxfp4) instead of 132-byte FP8 rows."""
     dev = _dev(q, w, context_lens, pool, block_table, out)
     _need(q, (torch.uint8,), "q", 3)
     _need(w, _BF16, "w", 2)
@@ -180,7 +183,7 @@ def paged_mqa_logits_decode(q, w, context_lens, pool, block_size, block_table, m
         _contig(t, nm)
     B = context_lens.shape[0]
     if block_stride_bytes is None:
-        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * ROW_BYTES
+        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * (ROW_BYTES_MXFP4 if mxfp4 else ROW_BYTES)
     if num_blocks is None:
         num_blocks = pool.numel() // block_stride_bytes
     bt_ld = _rows(block_table, "block_table")
@@ -190,11 +193,11 @@ def paged_mqa_logits_decode(q, w, context_lens, pool, block_size, block_table, m
         out = torch.empty((B * next_n, max_context_len), dtype=torch.float32, device=dev)
     _need(out, (torch.float32,), "out")
     ld = _rows(out, "out")
+    fn = lib().dsi_paged_mqa_logits_decode_mxfp4 if mxfp4 else lib().dsi_paged_mqa_logits_decode
     with torch.cuda.device(dev):
-        _check(lib().dsi_paged_mqa_logits_decode(_ptr(q), _ptr(w), B, next_n, _ptr(context_lens), _ptr(pool),
-                                                 num_blocks, block_size, block_stride_bytes, _ptr(block_table), bt_ld,
-                                                 bt_width, max_context_len, _ptr(out), ld, _stream(q)),
-               "paged_mqa_logits_decode")
+        _check(fn(_ptr(q), _ptr(w), B, next_n, _ptr(context_lens), _ptr(pool), num_blocks, block_size,
+                  block_stride_bytes, _ptr(block_table), bt_ld, bt_width, max_context_len, _ptr(out), ld, _stream(q)),
+               "paged_mqa_logits_decode_mxfp4" if mxfp4 else "paged_mqa_logits_decode")
     return out
 
 

@@ -201,6 +201,144 @@ __device__ __forceinline__ float dc_head_sum(const W32p& w, const f32x16& y0, co
   return dc_acc_sum(acc);
 }
 
+// ------------------------------------------------------------------ MXFP4 key rows
+// A 68-byte MXFP4 row lands in LDS as five 16-byte pieces at an 80-byte stride (bytes
+// 0..63, then 52..67, so the four scale bytes sit at 76..79; 20 dwords per key keep
+// 16-byte reads by 8 consecutive keys on distinct banks).  The block scales differ within
+// one 16-dim MFMA step (each lane half feeds its own 32-dim block), so they are applied
+// while decoding: the hardware converter turns each FP4 code times its block's 2^(E-127)
+// into bf16, exactly, and q's FP8 codes are decoded to bf16, exactly; the contraction runs
+// on the bf16 matrix cores with fp32 accumulation (products of 4- and 2-bit significands
+// are exact).
+constexpr int kMxRow = 68;                          // bytes per MXFP4 key row
+constexpr int kMxLds = 80;                          // LDS bytes per key
+constexpr int kMxBuf = kDcChunk * kMxLds;           // 20480
+constexpr int kMxSlabsPerWave = kMxBuf / 1024 / 4;  // 5 DMA instructions per wavefront per chunk
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^(E-127) as an fp32 (E = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
+
+// Eight FP4 codes (one dword, element 2i in the low nibble of byte i) times `scale` -> bf16.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t x, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E4M3 codes (two dwords) -> bf16, exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// q[row] as bf16 A fragments (load_q32's layout).
+struct Q32b {
+  bf16x8 a[2][8];
+};
+
+__device__ __forceinline__ void load_q32_bf16(Q32b& f, const uint8_t* q_row, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint4 x = p[j];
+      f.a[hb][2 * j] = e4m3x8_to_bf16x8(x.x, x.y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_bf16x8(x.z, x.w);
+    }
+  }
+}
+
+// Raw B data of one key row for this lane (key l%32, lane half h = dims [64h, 64h+64)):
+// the half's 32 code bytes and the scales of its blocks 2h and 2h+1.
+struct MxRaw {
+  uint4 c0, c1;
+  float s0, s1;
+};
+
+__device__ __forceinline__ MxRaw load_mx_raw(const uint8_t* keys, int lane) {
+  const uint8_t* row = keys + (lane & 31) * kMxLds;
+  const int h = lane >> 5;
+  MxRaw r;
+  r.c0 = *reinterpret_cast<const uint4*>(row + 32 * h);
+  r.c1 = *reinterpret_cast<const uint4*>(row + 32 * h + 16);
+  const uint32_t sc = *reinterpret_cast<const uint32_t*>(row + 76);
+  r.s0 = e8m0_to_f32((sc >> (16 * h)) & 255u);
+  r.s1 = e8m0_to_f32((sc >> (16 * h + 8)) & 255u);
+  return r;
+}
+
+struct K32b {
+  bf16x8 b[8];
+};
+
+// Slices 2j and 2j+1 (dims 64h + 16j .. +16) of a raw row.
+__device__ __forceinline__ void decode_mx_pair(K32b& kb, const MxRaw& r, int j) {
+  const uint4& c = j < 2 ? r.c0 : r.c1;
+  const float sc = j < 2 ? r.s0 : r.s1;
+  const uint32_t w0 = (j & 1) ? c.z : c.x, w1 = (j & 1) ? c.w : c.y;
+  kb.b[2 * j] = fp4x8_to_bf16x8(w0, sc);
+  kb.b[2 * j + 1] = fp4x8_to_bf16x8(w1, sc);
+}
+
+// dc_phase on bf16 operands: MFMA i of the group, two head-sum FMAs of the previous group,
+// the next group's slices decoded as MFMAs 4j+3 retire their sources, then extra(i).
+template <bool kEpi, bool kNext, typename Extra>
+__device__ __forceinline__ void mx_phase(f32x16& x0, f32x16& x1, const Q32b& q, K32b& kb, const uint8_t* next,
+                                         int lane, const W32p& w, const f32x16& y0, const f32x16& y1,
+                                         float (&acc)[4], Extra&& extra) {
+  MxRaw raw;
+  if (kNext) raw = load_mx_raw(next, lane);
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int sl = i >> 1;
+    if ((i & 1) == 0)
+      x0 = mfma32_bf16(q.a[0][sl], kb.b[sl], i == 0 ? f32x16{} : x0);
+    else
+      x1 = mfma32_bf16(q.a[1][sl], kb.b[sl], i == 1 ? f32x16{} : x1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kEpi) {
+#pragma unroll
+      for (int e = 2 * i; e < 2 * i + 2; e++) {
+        if (e < 16)
+          acc[e & 3] = fmaf(w.get(0, e), y0[e], acc[e & 3]);
+        else
+          acc[e & 3] = fmaf(w.get(1, e - 16), y1[e - 16], acc[e & 3]);
+      }
+    }
+    if (kNext && (i & 3) == 3) decode_mx_pair(kb, raw, i >> 2);
+    extra(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// This wavefront's share of one decode chunk of MXFP4 rows (as dc_gather): piece s is key
+// s/5, piece s%5 of its 68-byte row (bytes 16p, or 52..67 for p = 4).
+__device__ __forceinline__ void dc_gather_mx(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
+                                             int lane) {
+  dma_chunk<kMxSlabsPerWave>(buf, wave, lane, [&](int piece) {
+    const int key = piece / 5, p = piece - key * 5;
+    const int64_t base = seg_base[key >> 4];
+    return base >= 0 ? pool + base + (key & 15) * kMxRow + (p < 4 ? 16 * p : 52) : pool;
+  });
+}
+
+// ------------------------------------------------------------------ paged decode kernel
 // WPR = wavefronts per row (4, 2 or 1): each scores 256 / WPR keys of every chunk.  NB =
 // chunk buffers in LDS: NB - 1 gathers are in flight while one chunk is scored.
 // Work split.  persistent = 0: workgroup (x, y) takes chunks [kDcJob x, kDcJob (x + 1)) of request y
@@ -210,16 +348,21 @@ __device__ __forceinline__ float dc_head_sum(const W32p& w, const f32x16& y0, co
 // one request each, so that no CU idles while a few long jobs finish.
 constexpr int kDcMaxReqs = 1024;
 
-template <int WPR, int NB>
+// MX selects the cache format: false = 132-byte FP8 rows (f16 matrix cores, per-key fp32
+// scale), true = 68-byte MXFP4 rows (bf16 matrix cores, block scales applied in decoding).
+template <int WPR, int NB, bool MX>
 __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int B, int next_n,
     const int* __restrict__ context_lens, const uint8_t* __restrict__ pool, int64_t num_blocks, int block_size,
     int64_t block_stride, const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int max_ctx,
     float* __restrict__ logits, int64_t ld, int persistent) {
+  static_assert(!MX || NB == 2, "the MXFP4 ring's waits assume two buffers");
   constexpr int kKeysPerWave = kDcChunk / WPR;
   constexpr int kGroups = kKeysPerWave / 32;
   constexpr int kStores = kKeysPerWave / 64;
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kDcBuf];
+  constexpr int kRowBytes = MX ? kMxRow : kRow;  // bytes per key in the pool
+  constexpr int kLdsRow = MX ? kMxLds : kDcRow;  // bytes per key in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][MX ? kMxBuf : kDcBuf];
   __shared__ int64_t s_base[kDcSegs];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -241,7 +384,8 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
       const int blk = s / block_size;
       if (blk < bt_width) {
         const int page = block_table[(int64_t)b * bt_ld + blk];
-        if (page >= 0 && page < num_blocks) base = (int64_t)page * block_stride + (int64_t)(s % block_size) * kRow;
+        if (page >= 0 && page < num_blocks)
+          base = (int64_t)page * block_stride + (int64_t)(s % block_size) * kRowBytes;
       }
     }
     s_base[sg] = base;
@@ -252,9 +396,12 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   const int kbase = (wave % WPR) * kKeysPerWave;
   const bool active = row < next_n;  // 3 rows: the fourth wavefront only gathers
   const int rr = min(row, next_n - 1);
-  Q32 qf;
+  std::conditional_t<MX, Q32b, Q32> qf;
   W32p wf;
-  load_q32(qf, q + ((int64_t)b * next_n + rr) * kHeads * kDim, lane);
+  if constexpr (MX)
+    load_q32_bf16(qf, q + ((int64_t)b * next_n + rr) * kHeads * kDim, lane);
+  else
+    load_q32(qf, q + ((int64_t)b * next_n + rr) * kHeads * kDim, lane);
   load_w32p(wf, w + ((int64_t)b * next_n + rr) * kHeads, lane);
   const int ke = active ? min(L - next_n + rr + 1, max_ctx) : 0;
   const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -262,7 +409,11 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   __syncthreads();  // segment bases visible
 
   auto gather = [&](int c) {  // chunk c into its buffer
-    if (has_pool) dc_gather(s_buf[(c - c_first) % NB], s_base + (c - c_first) * 16, pool, wave, lane);
+    if (!has_pool) return;
+    if constexpr (MX)
+      dc_gather_mx(s_buf[(c - c_first) % NB], s_base + (c - c_first) * 16, pool, wave, lane);
+    else
+      dc_gather(s_buf[(c - c_first) % NB], s_base + (c - c_first) * 16, pool, wave, lane);
   };
   // Score chunk c: this wavefront's keys as kGroups / 2 pairs of 32-key groups, each pair
   // software-pipelined (dc_phase: the first group's MFMAs carry the second group's decode,
@@ -275,18 +426,27 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
     const int64_t* seg = s_base + (c - c_first) * 16;
 #pragma unroll
     for (int h = 0; h < kGroups / 2; h++) {
-      const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
-      if (NB == 2 && h == 0 && has_pool && next < c_end)
-        dc_gather(s_buf[(next - c_first) % NB], s_base + (next - c_first) * 16, pool, wave, lane);
-      K32 kb;
-      load_k32_raw(kb, keys, lane);
+      const uint8_t* keys = buf + (kbase + 64 * h) * kLdsRow;
+      if (NB == 2 && h == 0 && next < c_end) gather(next);
       f32x16 a0, a1, b0 = {}, b1 = {};
       float acc[4];
-      dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, [](int) {});
-      dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+      float scale = 1.0f;  // MXFP4: the block scales are in the decoded values
+      if constexpr (MX) {
+        K32b kb;
+        const MxRaw r0 = load_mx_raw(keys, lane);
+#pragma unroll
+        for (int j = 0; j < 4; j++) decode_mx_pair(kb, r0, j);
+        mx_phase<false, true>(a0, a1, qf, kb, keys + 32 * kLdsRow, lane, wf, b0, b1, acc, [](int) {});
+        mx_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+      } else {
+        K32 kb;
+        load_k32_raw(kb, keys, lane);
+        dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kLdsRow, lane, wf, b0, b1, acc, [](int) {});
+        dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+        scale = *reinterpret_cast<const float*>(buf + (kbase + 64 * h + lane) * kLdsRow + 140);
+      }
       const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
       const int key = kbase + 64 * h + lane;  // key within the chunk
-      const float scale = *reinterpret_cast<const float*>(buf + key * kDcRow + 140);
       const float out = seg[key >> 4] >= 0 ? v * scale : -INFINITY;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_rsrc, (c * kDcChunk + key) * 4, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -506,131 +666,8 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
 
 // ------------------------------------------------------------------ sparse columns, MXFP4 cache
 // The same work split and DMA ring on 68-byte MXFP4 key rows (P1 motivation and
-// implementation: the V4.1 sparse indexer scores FP8 q against an MXFP4 k cache).  A key
-// lands in LDS as five 16-byte pieces at an 80-byte stride (bytes 0..63, then 52..67, so
-// the four scale bytes sit at 76..79; 20 dwords per key keep 16-byte reads by 8 consecutive
-// keys on distinct banks).  The block scales differ within one 16-dim MFMA step (each lane
-// half feeds its own 32-dim block), so they are applied while decoding: the hardware
-// converter turns each FP4 code times its block's 2^(E-127) into bf16, exactly, and q's
-// FP8 codes are decoded to bf16, exactly; the contraction runs on the bf16 matrix cores
-// with fp32 accumulation (products of 4- and 2-bit significands are exact).
-constexpr int kMxRow = 68;                          // bytes per MXFP4 key row
-constexpr int kMxLds = 80;                          // LDS bytes per key
-constexpr int kMxBuf = kDcChunk * kMxLds;           // 20480
-constexpr int kMxSlabsPerWave = kMxBuf / 1024 / 4;  // 5 DMA instructions per wavefront per chunk
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// 2^(E-127) as an fp32 (E = 0 gives the subnormal 2^-127).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
-
-// Eight FP4 codes (one dword, element 2i in the low nibble of byte i) times `scale` -> bf16.
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t x, float scale) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// Eight E4M3 codes (two dwords) -> bf16, exact.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// q[row] as bf16 A fragments (load_q32's layout).
-struct Q32b {
-  bf16x8 a[2][8];
-};
-
-__device__ __forceinline__ void load_q32_bf16(Q32b& f, const uint8_t* q_row, int lane) {
-  const int m = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int hb = 0; hb < 2; hb++) {
-    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint4 x = p[j];
-      f.a[hb][2 * j] = e4m3x8_to_bf16x8(x.x, x.y);
-      f.a[hb][2 * j + 1] = e4m3x8_to_bf16x8(x.z, x.w);
-    }
-  }
-}
-
-// Raw B data of one key row for this lane (key l%32, lane half h = dims [64h, 64h+64)):
-// the half's 32 code bytes and the scales of its blocks 2h and 2h+1.
-struct MxRaw {
-  uint4 c0, c1;
-  float s0, s1;
-};
-
-__device__ __forceinline__ MxRaw load_mx_raw(const uint8_t* keys, int lane) {
-  const uint8_t* row = keys + (lane & 31) * kMxLds;
-  const int h = lane >> 5;
-  MxRaw r;
-  r.c0 = *reinterpret_cast<const uint4*>(row + 32 * h);
-  r.c1 = *reinterpret_cast<const uint4*>(row + 32 * h + 16);
-  const uint32_t sc = *reinterpret_cast<const uint32_t*>(row + 76);
-  r.s0 = e8m0_to_f32((sc >> (16 * h)) & 255u);
-  r.s1 = e8m0_to_f32((sc >> (16 * h + 8)) & 255u);
-  return r;
-}
-
-struct K32b {
-  bf16x8 b[8];
-};
-
-// Slices 2j and 2j+1 (dims 64h + 16j .. +16) of a raw row.
-__device__ __forceinline__ void decode_mx_pair(K32b& kb, const MxRaw& r, int j) {
-  const uint4& c = j < 2 ? r.c0 : r.c1;
-  const float sc = j < 2 ? r.s0 : r.s1;
-  const uint32_t w0 = (j & 1) ? c.z : c.x, w1 = (j & 1) ? c.w : c.y;
-  kb.b[2 * j] = fp4x8_to_bf16x8(w0, sc);
-  kb.b[2 * j + 1] = fp4x8_to_bf16x8(w1, sc);
-}
-
-// dc_phase on bf16 operands: MFMA i of the group, two head-sum FMAs of the previous group,
-// the next group's slices decoded as MFMAs 4j+3 retire their sources, then extra(i).
-template <bool kEpi, bool kNext, typename Extra>
-__device__ __forceinline__ void mx_phase(f32x16& x0, f32x16& x1, const Q32b& q, K32b& kb, const uint8_t* next,
-                                         int lane, const W32p& w, const f32x16& y0, const f32x16& y1,
-                                         float (&acc)[4], Extra&& extra) {
-  MxRaw raw;
-  if (kNext) raw = load_mx_raw(next, lane);
-#pragma unroll
-  for (int j = 0; j < 4; j++) acc[j] = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int sl = i >> 1;
-    if ((i & 1) == 0)
-      x0 = mfma32_bf16(q.a[0][sl], kb.b[sl], i == 0 ? f32x16{} : x0);
-    else
-      x1 = mfma32_bf16(q.a[1][sl], kb.b[sl], i == 1 ? f32x16{} : x1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kEpi) {
-#pragma unroll
-      for (int e = 2 * i; e < 2 * i + 2; e++) {
-        if (e < 16)
-          acc[e & 3] = fmaf(w.get(0, e), y0[e], acc[e & 3]);
-        else
-          acc[e & 3] = fmaf(w.get(1, e - 16), y1[e - 16], acc[e & 3]);
-      }
-    }
-    if (kNext && (i & 3) == 3) decode_mx_pair(kb, raw, i >> 2);
-    extra(i);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
+// implementation: the V4.1 sparse indexer scores FP8 q against an MXFP4 k cache), with the
+// MXFP4 key format below.
 // Five 16-byte pieces per 68-byte row: bytes 0..63 and 52..67.
 __device__ __forceinline__ void mx_gather(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
                                           int lane) {
@@ -744,16 +781,19 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
 }  // namespace
 }  // namespace dsi
 
-extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
-                                           const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
-                                           int32_t block_size, int64_t block_stride_bytes,
-                                           const int32_t* block_table, int64_t bt_ld, int32_t bt_width,
-                                           int32_t max_context_len, float* logits, int64_t ld, hipStream_t stream) {
-  using namespace dsi;
+namespace dsi {
+namespace {
+
+// Checks and launch shared by both cache formats (row_bytes: 132 FP8, 68 MXFP4).
+template <bool MX>
+int paged_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
+                 const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                 const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits,
+                 int64_t ld, hipStream_t stream) {
   if (B < 0 || max_context_len < 0 || ld < max_context_len || num_blocks < 0 || bt_width < 0 || bt_ld < bt_width)
     return DSI_EINVAL;
   if (next_n < 1 || next_n > 4 || block_size < 16 || (block_size % 16) != 0) return DSI_EUNSUPPORTED;
-  if (block_stride_bytes < (int64_t)block_size * kRow) return DSI_EINVAL;
+  if (block_stride_bytes < (int64_t)block_size * (MX ? kMxRow : kRow)) return DSI_EINVAL;
   if (B == 0 || max_context_len == 0) return DSI_OK;
   if (!q || !w || !context_lens || !pool || !block_table || !logits) return DSI_EINVAL;
   if (B > 65535) return DSI_EUNSUPPORTED;
@@ -774,11 +814,33 @@ extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, 
   }
   const int wpr = next_n == 1 ? 4 : next_n == 2 ? 2 : 1;
   constexpr int kNB = 2;
-  auto k = wpr == 4 ? paged_decode_kernel<4, kNB> : wpr == 2 ? paged_decode_kernel<2, kNB>
-                                                             : paged_decode_kernel<1, kNB>;
+  auto k = wpr == 4 ? paged_decode_kernel<4, kNB, MX> : wpr == 2 ? paged_decode_kernel<2, kNB, MX>
+                                                                 : paged_decode_kernel<1, kNB, MX>;
   hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, q, w, B, next_n, context_lens, pool, num_blocks, block_size,
                      block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld, (int)persistent);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+}  // namespace
+}  // namespace dsi
+
+extern "C" int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                           const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                           int32_t block_size, int64_t block_stride_bytes,
+                                           const int32_t* block_table, int64_t bt_ld, int32_t bt_width,
+                                           int32_t max_context_len, float* logits, int64_t ld, hipStream_t stream) {
+  return dsi::paged_decode<false>(q, w, B, next_n, context_lens, pool, num_blocks, block_size, block_stride_bytes,
+                                  block_table, bt_ld, bt_width, max_context_len, logits, ld, stream);
+}
+
+extern "C" int dsi_paged_mqa_logits_decode_mxfp4(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                                 const int32_t* context_lens, const uint8_t* pool,
+                                                 int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                                                 const int32_t* block_table, int64_t bt_ld, int32_t bt_width,
+                                                 int32_t max_context_len, float* logits, int64_t ld,
+                                                 hipStream_t stream) {
+  return dsi::paged_decode<true>(q, w, B, next_n, context_lens, pool, num_blocks, block_size, block_stride_bytes,
+                                 block_table, bt_ld, bt_width, max_context_len, logits, ld, stream);
 }
 
 extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_t rows, const int32_t* row_ks,

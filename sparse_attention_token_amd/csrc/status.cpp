@@ -20,4 +20,4 @@ extern "C" const char* dsi_status_string(int status) {
   }
 }
 
-extern "C" int dsi_abi_version(void) { return 6; }
+extern "C" int dsi_abi_version(void) { return 7; }

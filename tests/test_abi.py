@@ -223,6 +223,25 @@ def test_mxfp4_validation():
     assert call(bt=A16, bs=24) == EUNSUP and call(k_src=None) == EINVAL and call(q=A16 + 8) == EALIGN
 
 
+def test_decode_mxfp4_validation():
+    """The MXFP4 paged decode takes the FP8 decode's checks, with 68-byte rows in the page stride."""
+    L = dsi.lib()
+
+    def call(**kw):
+        a = dict(q=A16, w=A16, B=2, next_n=1, cl=A16, pool=A16, nb=10, bs=64, stride=64 * 68, bt=A16, bt_ld=4,
+                 bt_w=4, maxc=256, out=A16, ld=256)
+        a.update(kw)
+        return L.dsi_paged_mqa_logits_decode_mxfp4(a["q"], a["w"], a["B"], a["next_n"], a["cl"], a["pool"], a["nb"],
+                                                   a["bs"], a["stride"], a["bt"], a["bt_ld"], a["bt_w"], a["maxc"],
+                                                   a["out"], a["ld"], None)
+    assert call(next_n=0) == EUNSUP and call(next_n=5) == EUNSUP and call(bs=24) == EUNSUP
+    assert call(ld=255) == EINVAL and call(B=-1) == EINVAL and call(bt_ld=3) == EINVAL
+    assert call(stride=64 * 68 - 16) == EINVAL  # a page must hold block_size rows of 68 bytes
+    assert call(pool=None) == EINVAL and call(out=None) == EINVAL
+    assert call(stride=64 * 68 + 4) == EALIGN and call(q=A16 + 4) == EALIGN and call(w=A16 + 2) == EALIGN
+    assert call(B=0) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsi, "_lib", None)
     monkeypatch.setattr(dsi, "LIB_PATH", str(tmp_path / "missing.so"))

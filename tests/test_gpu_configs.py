@@ -66,17 +66,22 @@ def test_workload2_prefill_chunk():
     _prefill_workload(2, sample)
 
 
-def _decode_workload(n, n_sample):
+def _decode_workload(n, n_sample, mxfp4=False):
     c = synth.workload(n)
-    bs, stride, nb = c["block_size"], c["block_stride"], c["num_blocks"]
+    bs, nb = c["block_size"], c["num_blocks"]
+    row = 68 if mxfp4 else ROW
+    stride = bs * row if mxfp4 else c["block_stride"]
+    quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
+    quant_ref = oracle.k_quant_and_cache_mxfp4 if mxfp4 else oracle.k_quant_and_cache
+    logits_ref = oracle.mqa_logits_paged_mxfp4 if mxfp4 else oracle.mqa_logits_paged
     nn, B = c["next_n"], c["B"]
     lens = c["context_lens"]
     maxc = int(lens.max())
     pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
-    dsi.k_quant_and_cache(dev(c["k"]), dev(c["slot_mapping"]), pool, bs, stride, nb)
+    quant(dev(c["k"]), dev(c["slot_mapping"]), pool, bs, stride, nb)
     bt = dev(c["block_table"])
     logits = dsi.paged_mqa_logits_decode(dev(c["q"]), dev(c["w"]), dev(lens), pool, bs, bt, maxc, next_n=nn,
-                                         block_stride_bytes=stride, num_blocks=nb)
+                                         block_stride_bytes=stride, num_blocks=nb, mxfp4=mxfp4)
     ends = np.repeat(lens, nn) - nn + np.tile(np.arange(nn), B) + 1
     idx_t = dsi.topk_select(logits, dev(ends.astype(np.int32)), k=K)
     row_to_req = np.repeat(np.arange(B, dtype=np.int32), nn)
@@ -93,13 +98,13 @@ def _decode_workload(n, n_sample):
         # oracle: quantize this request's tokens into its own pool, compare the bytes, then score its rows
         pool_ref = np.zeros(nb * stride, np.uint8)
         sl = c["slot_mapping"][starts[b]:starts[b + 1]]
-        oracle.k_quant_and_cache(c["k"][starts[b]:starts[b + 1]], sl, pool_ref, bs, stride)
-        toks = (c["block_table"][b, np.arange(L) // bs].astype(np.int64) * stride + (np.arange(L) % bs) * ROW)
-        rowbytes = toks[:, None] + np.arange(ROW)[None, :]
+        quant_ref(c["k"][starts[b]:starts[b + 1]], sl, pool_ref, bs, stride)
+        toks = (c["block_table"][b, np.arange(L) // bs].astype(np.int64) * stride + (np.arange(L) % bs) * row)
+        rowbytes = toks[:, None] + np.arange(row)[None, :]
         assert np.array_equal(pool_gpu[rowbytes], pool_ref[rowbytes]), f"request {b}: k rows differ"
         rr = slice(b * nn, (b + 1) * nn)
-        ref = oracle.mqa_logits_paged(c["q"][rr], c["w"][rr], nn, lens[b:b + 1], pool_ref, bs, stride,
-                                      c["block_table"][b:b + 1], maxc)
+        ref = logits_ref(c["q"][rr], c["w"][rr], nn, lens[b:b + 1], pool_ref, bs, stride, c["block_table"][b:b + 1],
+                         maxc)
         for i in range(nn):
             r = b * nn + i
             valid = np.isfinite(ref[i])
@@ -121,6 +126,15 @@ def test_workload3_paged_decode():
 
 def test_workload4_long_context_decode():
     _decode_workload(4, 3)
+
+
+def test_workload3_paged_decode_mxfp4():
+    """Workload 3 on the MXFP4 cache: quantize into 68-byte rows, score, select, convert to slots."""
+    _decode_workload(3, 3, mxfp4=True)
+
+
+def test_workload4_long_context_decode_mxfp4():
+    _decode_workload(4, 2, mxfp4=True)
 
 
 def test_workload5_hierarchical_sparse():

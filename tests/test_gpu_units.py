@@ -675,3 +675,45 @@ def test_sparse_mxfp4_paged_parity(sbk, bs):
     valid = np.isfinite(ref_f32)
     assert np.all(got[~valid] == 0xFF80)
     assert_close(bf16_value(got[valid]), ref_f32[valid], tol_fn=tol_bf16, what="MXFP4 sparse paged logits")
+
+
+# ----------------------------------------------------------------------------- paged decode on the MXFP4 cache
+@pytest.mark.parametrize("next_n,bs,extra,long", [(1, 64, 0, False), (2, 64, 16, False), (3, 16, 0, False),
+                                                   (4, 32, 32, False), (1, 64, 16, True), (2, 16, 0, True)])
+def test_decode_mxfp4_parity_ragged(next_n, bs, extra, long):
+    """As test_decode_parity_ragged, on 68-byte MXFP4 rows (padded page strides, jobs spanning many chunks)."""
+    lens = [4099, 2048 * 8 + 1, 2048 * 3 + 257, 9000] if long else [1, 15, 16, 17, 300, 1000 + next_n, 2049]
+    c = synth.decode_case(80 + next_n, B=len(lens), next_n=next_n, lmin=0, lmax=0, block_size=bs, lens=lens)
+    stride = bs * ROW4 + extra
+    nb = c["num_blocks"]
+    pool_np = _mx_pool_oracle(c["k"], c["slot_mapping"], nb, bs, stride)
+    width = max(lens) + 3
+    ref = oracle.mqa_logits_paged_mxfp4(c["q"], c["w"], next_n, c["context_lens"], pool_np, bs, stride,
+                                        c["block_table"], width)
+    ld = width + 5
+    out = torch.full((len(lens) * next_n, ld), -3.5, dtype=torch.float32, device="cuda")
+    dsi.paged_mqa_logits_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(pool_np), bs,
+                                dev(c["block_table"]), width, next_n=next_n, out=out[:, :width],
+                                block_stride_bytes=stride, num_blocks=nb, mxfp4=True)
+    got = host(out)
+    valid = np.isfinite(ref)
+    assert_close(got[:, :width][valid], ref[valid], what="MXFP4 decode logits")
+    assert np.all(got[:, :width][~valid] == -3.5) and np.all(got[:, width:] == -3.5)
+
+
+def test_decode_mxfp4_bad_page_ids_score_minus_inf():
+    c = synth.decode_case(21, B=2, next_n=1, lmin=0, lmax=0, block_size=16, lens=[64, 64])
+    bs, stride, nb = 16, 16 * ROW4, c["num_blocks"]
+    pool_np = _mx_pool_oracle(c["k"], c["slot_mapping"], nb, bs, stride)
+    bt = c["block_table"].copy()
+    bt[0, 1] = nb + 100  # out of range page
+    bt[1, 2] = -7
+    got = host(dsi.paged_mqa_logits_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(pool_np), bs,
+                                           dev(bt), 64, block_stride_bytes=stride, num_blocks=nb, mxfp4=True))
+    assert np.all(np.isneginf(got[0, 16:32])) and np.all(np.isneginf(got[1, 32:48]))
+    ref = oracle.mqa_logits_paged_mxfp4(c["q"], c["w"], 1, c["context_lens"], pool_np, bs, stride,
+                                        c["block_table"], 64)
+    keep = np.ones((2, 64), bool)
+    keep[0, 16:32] = False
+    keep[1, 32:48] = False
+    assert_close(got[keep], ref[keep], what="MXFP4 decode logits")
