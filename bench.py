@@ -39,13 +39,15 @@ from sparse_attention_token_amd import ceiling  # noqa: E402
 import synth  # noqa: E402
 
 ROW, K = 132, 2048
+ROW_MXFP4 = 68  # MXFP4 cache row: 64 bytes of FP4 codes + 4 E8M0 block scales
 F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA (published)
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E (published)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_logits_T2048_S8192_traffic.md")
 PREFILL_SOURCES = [os.path.join(ROOT, "sparse_attention_token_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
 FLOP_PER_PAIR = 2 * 64 * 128
-ALL_WORKLOADS = ["decode_w3", "decode_w4", "sparse_w5", "sparse_w5_mxfp4", "prefill_gather", "q_prep", "cp_merge"]
+ALL_WORKLOADS = ["decode_w3", "decode_w4", "decode_w3_mxfp4", "decode_w4_mxfp4", "sparse_w5", "sparse_w5_mxfp4",
+                 "prefill_gather", "q_prep", "cp_merge"]
 
 
 def log(*a):
@@ -235,9 +237,14 @@ def cpu_baseline(c, max_seconds):
 
 
 # --------------------------------------------------------------------------- paged decode
-def bench_decode(n, steps, warmup, copies=4):
+def bench_decode(n, steps, warmup, copies=4, mxfp4=False):
+    """Decode workload n: logits straight from the paged cache (132-byte FP8 rows, or 68-byte MXFP4 rows),
+    top-2048, slot conversion."""
     c = synth.workload(n)
-    bs, stride, nb, nn, B = c["block_size"], c["block_stride"], c["num_blocks"], c["next_n"], c["B"]
+    bs, nb, nn, B = c["block_size"], c["num_blocks"], c["next_n"], c["B"]
+    row = ROW_MXFP4 if mxfp4 else ROW
+    stride = bs * row if mxfp4 else c["block_stride"]
+    quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
     lens = c["context_lens"]
     maxc = int(lens.max())
     sumL = int(lens.sum())
@@ -255,7 +262,7 @@ def bench_decode(n, steps, warmup, copies=4):
         sl = (bt[np.repeat(np.arange(B), lens), np.concatenate([np.arange(L) for L in lens]) // bs].astype(np.int64)
               * bs + np.concatenate([np.arange(L) for L in lens]) % bs)
         pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
-        dsi.k_quant_and_cache(k_t, dev(sl), pool, bs, stride, nb)
+        quant(k_t, dev(sl), pool, bs, stride, nb)
         pools.append(pool)
         tables.append(dev(bt))
     del k_t, slot_t
@@ -270,7 +277,7 @@ def bench_decode(n, steps, warmup, copies=4):
         p, bt = pools[i % copies], tables[i % copies]
         s = tl.start() if timed else None
         dsi.paged_mqa_logits_decode(q, w, cl, p, bs, bt, maxc, next_n=nn, out=logits, block_stride_bytes=stride,
-                                    num_blocks=nb)
+                                    num_blocks=nb, mxfp4=mxfp4)
         if timed:
             tl.stop(s)
             s = tt.start()
@@ -296,10 +303,11 @@ def bench_decode(n, steps, warmup, copies=4):
     ms_l, ms_t, ms_s = tl.mean_ms(), tt.mean_ms(), ts.mean_ms()
     V = int(ends_np.sum())
     nblk = int(sum((int(L) + bs - 1) // bs for L in lens))
-    bytes_logits = ROW * sumL + 4 * nblk + rows * (64 * 128 + 64 * 2) + 4 * V
+    bytes_logits = row * sumL + 4 * nblk + rows * (64 * 128 + 64 * 2) + 4 * V
     bytes_topk = 4 * V + rows * K * 4
     gbs = (bytes_logits + bytes_topk) / ((ms_l + ms_t) * 1e-3) / 1e9
-    return dict(workload=f"paged decode {B} x next_n {nn}, lengths U{{{int(lens.min())}..{int(lens.max())}}}",
+    cache = ", MXFP4 cache (68 B per token)" if mxfp4 else ""
+    return dict(workload=f"paged decode {B} x next_n {nn}, lengths U{{{int(lens.min())}..{int(lens.max())}}}{cache}",
                 rows=rows, sum_tokens=sumL, ms_step=round(ms_step, 4), ms_logits=round(ms_l, 4),
                 ms_topk=round(ms_t, 4), ms_slot=round(ms_s, 4),
                 logits_gbs=round(bytes_logits / (ms_l * 1e-3) / 1e9, 1),
@@ -399,7 +407,7 @@ def bench_sparse(steps, warmup, c, mxfp4=False):
     gathered chunk), bf16 top-k, remap and slot conversion.  mxfp4: the K cache in 68-byte MXFP4 rows."""
     sbk, cbs, nd, rows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
     bs, nb = c["block_size"], c["num_blocks"]
-    row = 68 if mxfp4 else ROW
+    row = ROW_MXFP4 if mxfp4 else ROW
     stride = bs * row
     quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
     logits_fn = dsi.sparse_mqa_logits_mxfp4 if mxfp4 else dsi.sparse_mqa_logits
@@ -504,6 +512,10 @@ def main():
         if f"decode_w{n}" in chosen:
             log(f"decode workload {n} ...")
             extra[f"decode_w{n}"] = bench_decode(n, args.steps, args.warmup)
+    for n in (3, 4):
+        if f"decode_w{n}_mxfp4" in chosen:
+            log(f"decode workload {n}, MXFP4 cache ...")
+            extra[f"decode_w{n}_mxfp4"] = bench_decode(n, args.steps, args.warmup, mxfp4=True)
     if "sparse_w5" in chosen or "sparse_w5_mxfp4" in chosen:
         c5 = synth.workload(5)
         if "sparse_w5" in chosen:
