@@ -2,7 +2,8 @@
 into a HIP graph once and replayed (page "V4.1 indexer uses sparse MQA logits": the path is exercised under
 CUDA-graph capture, with the expansion and schedule reused by later layers).
 
-The decode step (k insert, paged logits, split top-k with its workspace, slot conversion) and the hierarchical
+The decode step (k insert, paged logits, split top-k with its workspace, slot conversion; on the FP8 and on the
+MXFP4 cache) and the hierarchical
 step (expansion, sparse logits, bf16 top-k, remap) are captured, then replayed several times with eager work and
 synchronisation between the replays; every replay must reproduce the eager outputs (selections compared by their value multisets, since the order of the output and
 the choice among tied values are free).
@@ -19,9 +20,12 @@ pytestmark = pytest.mark.gpu
 K = 2048
 
 
-def test_decode_step_graph_replays():
+@pytest.mark.parametrize("mxfp4", [False, True])
+def test_decode_step_graph_replays(mxfp4):
     c = synth.decode_case(90, B=8, next_n=1, lmin=3000, lmax=40000, block_size=64)
-    bs, stride, nb = c["block_size"], c["block_stride"], c["num_blocks"]
+    bs, nb = c["block_size"], c["num_blocks"]
+    stride = bs * 68 if mxfp4 else c["block_stride"]
+    quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
     lens = c["context_lens"]
     maxc = int(lens.max())
     pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
@@ -35,9 +39,9 @@ def test_decode_step_graph_replays():
     assert dsi.topk_workspace_bytes(8, maxc, K) > 0  # the split path with its workspace is in the graph
 
     def step():
-        dsi.k_quant_and_cache(k_t, slots_t, pool, bs, stride, nb)
+        quant(k_t, slots_t, pool, bs, stride, nb)
         dsi.paged_mqa_logits_decode(q, w, cl, pool, bs, bt, maxc, out=logits, block_stride_bytes=stride,
-                                    num_blocks=nb)
+                                    num_blocks=nb, mxfp4=mxfp4)
         dsi.topk_select(logits, ends, k=K, out=idx, workspace=ws)
         dsi.req_index_to_global_slot(idx, bt, bs, bs, out=slots)
 
