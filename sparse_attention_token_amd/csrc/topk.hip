@@ -399,6 +399,8 @@ struct RegCfg {
   static constexpr int kCopies = 1;
   static constexpr int kBinsPerThread = kHistBins / THREADS;
 };
+using RegTiny = RegCfg<256, 4>;    // fp32 rows up to 4096 columns, bf16 rows up to 8192 (fewer VGPRs: more rows
+                                   // per CU, e.g. 1056 bf16 rows of 8192 in one round instead of two)
 using RegSmall = RegCfg<256, 8>;   // fp32 rows up to 8192 columns, bf16 rows up to 16384
 using RegMid = RegCfg<256, 16>;    // fp32 rows up to 16384 columns
 
@@ -535,7 +537,26 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   const int nvec = (en - c0) / E;
   const int c1 = c0 + nvec * E;
   const uint4* vec = reinterpret_cast<const uint4*>(row + (size_t)c0 * K::kElemBytes);
-  uint32_t kk[N + 2];  // keys; 0 (an ignored bin) for slots outside the row
+  // Keys; 0 (an ignored bin) for slots outside the row.  bf16 keys are 16 bits: two share a
+  // register (key j in half j & 1 of kk[j / 2]), which saves a third of the kernel's VGPRs.
+  constexpr int kPack = BF16 ? 2 : 1;
+  uint32_t kk[(N + 2) / kPack];
+  auto key_at = [&](int j) -> uint32_t {
+    if constexpr (BF16)
+      return (j & 1) ? (kk[j >> 1] >> 16) : (kk[j >> 1] & 0xFFFFu);
+    else
+      return kk[j];
+  };
+  auto set_key = [&](int j, uint32_t v) {  // called for j in increasing order
+    if constexpr (BF16) {
+      if (j & 1)
+        kk[j >> 1] |= v << 16;
+      else
+        kk[j >> 1] = v;
+    } else {
+      kk[j] = v;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < V; i++) {
     const int vi = i * T + tid;
@@ -545,16 +566,16 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
     for (int e = 0; e < E; e++) {
       uint32_t key;
       K::key(K::elem(x, e), key);
-      kk[i * E + e] = vi < nvec ? key : 0u;
+      set_key(i * E + e, vi < nvec ? key : 0u);
     }
   }
   const bool ha = tid < c0 - st, ta = tid < en - c1;
   {
     uint32_t key;
     K::key(ha ? K::load1(row, st + tid) : 0u, key);
-    kk[N] = ha ? key : 0u;
+    set_key(N, ha ? key : 0u);
     K::key(ta ? K::load1(row, c1 + tid) : 0u, key);
-    kk[N + 1] = ta ? key : 0u;
+    set_key(N + 1, ta ? key : 0u);
   }
   // column of kk[j] relative to st
   const int col_base = c0 - st + tid * E;
@@ -565,10 +586,10 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   for (int i = 0; i < V; i++) {
     const bool in = i * T + tid < nvec;
 #pragma unroll
-    for (int e = 0; e < E; e++) atomicAdd(&s_hist[in ? kk[i * E + e] >> kShift : kHistBins + lane], 1);
+    for (int e = 0; e < E; e++) atomicAdd(&s_hist[in ? key_at(i * E + e) >> kShift : kHistBins + lane], 1);
   }
-  atomicAdd(&s_hist[ha ? kk[N] >> kShift : kHistBins + lane], 1);
-  atomicAdd(&s_hist[ta ? kk[N + 1] >> kShift : kHistBins + lane], 1);
+  atomicAdd(&s_hist[ha ? key_at(N) >> kShift : kHistBins + lane], 1);
+  atomicAdd(&s_hist[ta ? key_at(N + 1) >> kShift : kHistBins + lane], 1);
   launder(kk);  // the bins are recomputed where needed rather than kept, one register per key
   __syncthreads();
   find_bin_w0<kHistBins>(s_hist, kLoBin, kHiBin, k, s_sel, tid);
@@ -583,7 +604,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   int ngt = 0, neq = 0;
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
-    const uint32_t d = kk[j] >> kShift;
+    const uint32_t d = key_at(j) >> kShift;
     ngt += (d - lo_w - 1u) < span_w ? 1 : 0;
     neq += d == b1 ? 1 : 0;
   }
@@ -592,13 +613,13 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   launder(kk);
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
-    const uint32_t d = kk[j] >> kShift;
+    const uint32_t d = key_at(j) >> kShift;
     const bool gt = (d - lo_w - 1u) < span_w;
     const bool eq = d == b1;
     const int col = column(j);
     s_out[gt ? pg : DSI_MAX_TOPK + lane] = col;
     const int cs = (eq && pe < kCap) ? pe : kCap + lane;
-    s_ckey[cs] = kk[j];
+    s_ckey[cs] = key_at(j);
     s_ccol[cs] = col;
     pg += gt ? 1 : 0;
     pe += eq ? 1 : 0;
@@ -972,7 +993,9 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
   hipLaunchKernelGGL((topk_reg_kernel<B, CFG>), grid, dim3(CFG::kThreads), 0, stream, src, row_bytes, row_starts, \
                      row_ends, max_width, k, out, out_ld)
   if (!bf) {
-    if (max_width <= reg_capacity<false, RegSmall>())
+    if (max_width <= reg_capacity<false, RegTiny>())
+      DSI_TOPK_REG(false, RegTiny);
+    else if (max_width <= reg_capacity<false, RegSmall>())
       DSI_TOPK_REG(false, RegSmall);
     else if (max_width <= reg_capacity<false, RegMid>())
       DSI_TOPK_REG(false, RegMid);
@@ -980,7 +1003,9 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
       hipLaunchKernelGGL((topk_kernel<false, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, k, out, out_ld);
   } else {
-    if (max_width <= reg_capacity<true, RegSmall>())
+    if (max_width <= reg_capacity<true, RegTiny>())
+      DSI_TOPK_REG(true, RegTiny);
+    else if (max_width <= reg_capacity<true, RegSmall>())
       DSI_TOPK_REG(true, RegSmall);
     else
       hipLaunchKernelGGL((topk_kernel<true, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
