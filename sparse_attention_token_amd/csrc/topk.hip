@@ -402,7 +402,7 @@ struct RegCfg {
 using RegTiny = RegCfg<256, 4>;    // fp32 rows up to 4096 columns, bf16 rows up to 8192 (fewer VGPRs: more rows
                                    // per CU, e.g. 1056 bf16 rows of 8192 in one round instead of two)
 using RegSmall = RegCfg<256, 8>;   // fp32 rows up to 8192 columns, bf16 rows up to 16384
-using RegMid = RegCfg<256, 16>;    // fp32 rows up to 16384 columns
+using RegMid = RegCfg<512, 8>;     // fp32 rows up to 16384 columns (512 threads: half the per-row latency of 256 x 64 keys)
 
 template <bool BF16, typename C>
 constexpr int reg_capacity() {
