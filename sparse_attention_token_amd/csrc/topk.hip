@@ -15,12 +15,12 @@
 //     those candidates, digit by digit (by passes over the row when the boundary bin
 //     outgrows LDS).  Output slots are reserved per wavefront (ballot + popcount, one LDS
 //     atomic);
-//   * few long rows are split between up to 16 workgroups per row, in four launches that
-//     communicate through the caller's workspace: per-slice histograms; per row, their
-//     sum, the boundary bin and each slice's output offsets; every slice writes its
-//     columns above the boundary bin from its offset (no atomics across workgroups) and
-//     appends its boundary-bin columns to a per-row candidate list; one workgroup per row
-//     resolves the candidates as above.
+//   * few long rows are split between up to 16 workgroups per row, in three launches that
+//     communicate through the caller's workspace: per-slice histograms; then every slice
+//     sums its row's histograms, finds the boundary bin and its own output offsets from the
+//     slices before it, writes its columns above the boundary bin from its offset (no
+//     atomics across workgroups) and appends its boundary-bin columns to a per-row
+//     candidate list; one workgroup per row resolves the candidates as above.
 #include <algorithm>
 
 #include "common.h"
@@ -697,14 +697,12 @@ using SliceCfg = Cfg<512, 0, 1>;
 struct SplitWs {
   int* hist;      // [rows][G][2048]
   int* meta;      // [rows][4]: b1, above1, total, m
-  int* off;       // [rows][kMaxSplit][4]: columns of the earlier slices above b1, at b1, valid
   uint32_t* key;  // [rows][kSplitCap]
   int* col;       // [rows][kSplitCap]
 };
 
 __host__ __device__ inline size_t split_ws_bytes(int rows, int G) {
-  return (size_t)rows * G * kHistBins * 4 + (size_t)rows * 16 + (size_t)rows * kMaxSplit * 16 +
-         (size_t)rows * kSplitCap * 8;
+  return (size_t)rows * G * kHistBins * 4 + (size_t)rows * 16 + (size_t)rows * kSplitCap * 8;
 }
 
 __device__ __forceinline__ SplitWs split_ws(void* ws, int rows, int G) {
@@ -714,8 +712,6 @@ __device__ __forceinline__ SplitWs split_ws(void* ws, int rows, int G) {
   p += (size_t)rows * G * kHistBins * 4;
   w.meta = reinterpret_cast<int*>(p);
   p += (size_t)rows * 16;
-  w.off = reinterpret_cast<int*>(p);
-  p += (size_t)rows * kMaxSplit * 16;
   w.key = reinterpret_cast<uint32_t*>(p);
   p += (size_t)rows * kSplitCap * 4;
   w.col = reinterpret_cast<int*>(p);
@@ -756,106 +752,83 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
   }
 }
 
-// Step 2: one workgroup per row sums the slice histograms, finds the boundary bin b1 and
-// gives every slice the number of columns the slices before it hold above b1, at b1, and
-// valid (the offsets its writes start at).  Thread t owns bins [8t, 8t + 8) of every slice
-// in registers; the per-slice counts are wavefront sums, then sums over the four
-// wavefronts.  grid = rows.
-using ReduceCfg = Cfg<256, 0, 1>;
-__global__ __launch_bounds__(ReduceCfg::kThreads) void topk_split_reduce_kernel(void* ws, int rows, int G, int k) {
-  using C = ReduceCfg;
-  constexpr int kT = C::kThreads, kB = kHistBins / kT;  // 8 bins per thread
-  static_assert(kB == 8, "two 16-byte loads per slice and thread");
-  __shared__ __attribute__((aligned(16))) int s_hist[kHistBins];
-  __shared__ int s_wave[C::kWaves];
-  __shared__ int s_sel[4];
-  __shared__ int s_part[C::kWaves][3][kMaxSplit];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const SplitWs w = split_ws(ws, rows, G);
-  const int* hist = w.hist + (int64_t)r * G * kHistBins;
-  int4 v[kMaxSplit][2];
-#pragma unroll
-  for (int j = 0; j < kMaxSplit; j++) {  // all loads in flight
-    const int4* p = reinterpret_cast<const int4*>(hist + (int64_t)j * kHistBins + tid * kB);
-    v[j][0] = j < G ? p[0] : int4{0, 0, 0, 0};
-    v[j][1] = j < G ? p[1] : int4{0, 0, 0, 0};
-  }
-  int4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < kMaxSplit; j++) {
-    s0.x += v[j][0].x, s0.y += v[j][0].y, s0.z += v[j][0].z, s0.w += v[j][0].w;
-    s1.x += v[j][1].x, s1.y += v[j][1].y, s1.z += v[j][1].z, s1.w += v[j][1].w;
-  }
-  reinterpret_cast<int4*>(s_hist + tid * kB)[0] = s0;
-  reinterpret_cast<int4*>(s_hist + tid * kB)[1] = s1;
-  __syncthreads();
-  select_bin<C, 1>(s_hist, kHistBins, k, s_wave, s_sel, tid);
-  const uint32_t b1 = (uint32_t)s_sel[0];
-  // this thread's bins of slice j above b1, at b1, valid
-#pragma unroll
-  for (int j = 0; j < kMaxSplit; j++) {
-    const int h[kB] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w, v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
-    int gt = 0, eq = 0, valid = 0;
-#pragma unroll
-    for (int e = 0; e < kB; e++) {
-      const uint32_t bin = (uint32_t)(tid * kB + e);
-      valid += h[e];
-      gt += bin > b1 ? h[e] : 0;
-      eq += bin == b1 ? h[e] : 0;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      gt += __shfl_xor(gt, o);
-      eq += __shfl_xor(eq, o);
-      valid += __shfl_xor(valid, o);
-    }
-    if (lane == 0) {
-      s_part[wave][0][j] = gt;
-      s_part[wave][1][j] = eq;
-      s_part[wave][2][j] = valid;
-    }
-  }
-  __syncthreads();
-  if (tid < 3) {  // exclusive prefix over the slices
-    int acc = 0;
-    for (int j = 0; j < G; j++) {
-      w.off[((int64_t)r * kMaxSplit + j) * 4 + tid] = acc;
-#pragma unroll
-      for (int q = 0; q < C::kWaves; q++) acc += s_part[q][tid][j];
-    }
-  }
-  if (tid == 0) {
-    int* meta = w.meta + (int64_t)r * 4;
-    meta[0] = (int)b1;
-    meta[1] = s_sel[1];
-    meta[2] = s_sel[2];
-    meta[3] = s_hist[b1];
-  }
-}
-
-// Step 3: every slice writes its columns above the boundary bin from its offset (or, when
-// every valid value is selected, all its valid columns, and the last slice the -1
-// padding); its boundary-bin columns go to the row's candidate list from its offset.
-// grid = (G, rows).
+// Step 2: every slice sums its row's slice histograms (thread t owns bins [4t, 4t + 4) of every
+// slice, from L2), finds the boundary bin b1, and takes its offsets from the slices before it:
+// the columns they hold above b1, at b1, and valid.  It then writes its columns above the
+// boundary bin from its offset (or, when every valid value is selected, all its valid columns,
+// and the last slice the -1 padding); its boundary-bin columns go to the row's candidate list
+// from its offset.  Slice 0 leaves {b1, above1, total, m} for step 3.  grid = (G, rows).
 template <bool BF16>
 __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
     const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
     const int* __restrict__ row_ends, int max_width, int k, int* __restrict__ out, int64_t out_ld, void* ws, int rows,
     int G) {
   using K = Keys<BF16>;
-  constexpr int kT = SliceCfg::kThreads;
+  using C = SliceCfg;
+  constexpr int kT = C::kThreads;
+  static_assert(C::kBinsPerThread == 4, "one int4 of bins per thread and slice");
+  __shared__ __attribute__((aligned(16))) int s_hist[kHistBins];
+  __shared__ int s_wave[C::kWaves];
+  __shared__ int s_sel[4];
+  __shared__ int s_red[3][C::kWaves];
   __shared__ int s_cnt[2];
-  const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const SplitWs w = split_ws(ws, rows, G);
-  const int* meta = w.meta + (int64_t)r * 4;
-  const int* off = w.off + ((int64_t)r * kMaxSplit + g) * 4;
-  const uint32_t b1 = (uint32_t)meta[0];
-  const int total = meta[2];
-  const bool all = total <= k;
-  const int out_base = all ? off[2] : off[0];
-  const int cand_base = off[1];
+  const int* hist = w.hist + (int64_t)r * G * kHistBins;
+  int4 hv[kMaxSplit];
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; j++)  // all loads in flight
+    hv[j] = j < G ? reinterpret_cast<const int4*>(hist + (int64_t)j * kHistBins)[tid] : int4{0, 0, 0, 0};
+  int4 sum = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; j++) sum.x += hv[j].x, sum.y += hv[j].y, sum.z += hv[j].z, sum.w += hv[j].w;
+  reinterpret_cast<int4*>(s_hist)[tid] = sum;
   if (tid < 2) s_cnt[tid] = 0;
+  if (tid < 2) s_sel[tid] = 0;  // stays 0 (an in-range bin) when every valid value is selected
   __syncthreads();
+  select_bin<C, 1>(s_hist, kHistBins, k, s_wave, s_sel, tid);
+  const uint32_t b1 = (uint32_t)s_sel[0];
+  const int total = s_sel[2];
+  const bool all = total <= k;
+  // columns of the slices before this one: above b1, at b1, valid
+  int gt = 0, eq = 0, valid = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; j++) {
+    if (j < g) {
+      const int h[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t bin = (uint32_t)(4 * tid + e);
+        valid += h[e];
+        gt += bin > b1 ? h[e] : 0;
+        eq += bin == b1 ? h[e] : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt += __shfl_xor(gt, o);
+    eq += __shfl_xor(eq, o);
+    valid += __shfl_xor(valid, o);
+  }
+  if (lane == 0) {
+    s_red[0][wave] = gt;
+    s_red[1][wave] = eq;
+    s_red[2][wave] = valid;
+  }
+  __syncthreads();
+  int sgt = 0, seq = 0, svalid = 0;
+#pragma unroll
+  for (int q = 0; q < C::kWaves; q++) sgt += s_red[0][q], seq += s_red[1][q], svalid += s_red[2][q];
+  const int out_base = all ? svalid : sgt;
+  const int cand_base = seq;
+  if (g == 0 && tid == 0) {
+    int* meta = w.meta + (int64_t)r * 4;
+    meta[0] = (int)b1;
+    meta[1] = s_sel[1];
+    meta[2] = total;
+    meta[3] = s_hist[b1];
+  }
   const int st = row_starts ? max(row_starts[r], 0) : 0;
   const int en = max(min(row_ends[r], max_width), st);
   int a, b;
@@ -892,7 +865,7 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
     for (int j = total + tid; j < k; j += kT) orow[j] = -1;
 }
 
-// Step 4: one workgroup per row resolves the boundary bin from the candidate list.
+// Step 3: one workgroup per row resolves the boundary bin from the candidate list.
 template <bool BF16>
 __global__ __launch_bounds__(LongRows::kThreads) void topk_split_resolve_kernel(
     const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
@@ -970,8 +943,6 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
     if (bf) {
       hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, workspace, rows, G);
-      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(ReduceCfg::kThreads), 0, stream,
-                         workspace, rows, G, k);
       hipLaunchKernelGGL(topk_slice_select_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
       hipLaunchKernelGGL(topk_split_resolve_kernel<true>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
@@ -979,8 +950,6 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
     } else {
       hipLaunchKernelGGL(topk_slice_hist_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, workspace, rows, G);
-      hipLaunchKernelGGL(topk_split_reduce_kernel, dim3((unsigned)rows), dim3(ReduceCfg::kThreads), 0, stream,
-                         workspace, rows, G, k);
       hipLaunchKernelGGL(topk_slice_select_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
       hipLaunchKernelGGL(topk_split_resolve_kernel<false>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
