@@ -468,6 +468,65 @@ __device__ __forceinline__ void find_bin_w0(const int* hist, int lo, int hi, int
   __syncthreads();
 }
 
+// find_bin_w0 for the 2048-bin first digit, spread over all WAVES wavefronts: wavefront q
+// owns bins [q*B*64, (q+1)*B*64) (B = 2048 / (64 * WAVES) per lane), the wavefronts' totals
+// meet in s_part, and the one holding the `need`-th largest writes s_sel as find_bin_w0 does.
+// Call with all threads (after the histogram is complete); ends synchronised.
+template <int WAVES>
+__device__ __forceinline__ void find_bin_all(const int* hist, int lo, int hi, int need, int* s_part, int* s_sel,
+                                             int tid) {
+  constexpr int B = kHistBins / (64 * WAVES);
+  static_assert(B >= 4 && B % 4 == 0, "whole int4 reads per lane");
+  const int lane = tid & 63, wave = tid >> 6;
+  const int first = tid * B;  // this lane's first bin (bins ascend with tid)
+  int h[B], local = 0;
+#pragma unroll
+  for (int j = 0; j < B; j += 4) {
+    const int4 x = *reinterpret_cast<const int4*>(hist + first + j);
+    h[j] = x.x;
+    h[j + 1] = x.y;
+    h[j + 2] = x.z;
+    h[j + 3] = x.w;
+  }
+#pragma unroll
+  for (int j = 0; j < B; j++) {
+    const int bin = first + j;
+    h[j] = (bin >= lo && bin < hi) ? h[j] : 0;
+    local += h[j];
+  }
+  int v = local;  // suffix sum over the wavefront's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_down(v, off);
+    if (lane + off < 64) v += y;
+  }
+  if (lane == 0) s_part[wave] = v;  // the wavefront's total
+  __syncthreads();
+  int above_w = 0, total = 0;
+#pragma unroll
+  for (int q = 0; q < WAVES; q++) {
+    const int t = s_part[q];
+    total += t;
+    above_w += q > wave ? t : 0;
+  }
+  if (tid == 0) s_sel[2] = total;
+  int acc = above_w + v - local, sel = -1, sel_acc = 0, sel_cnt = 0;
+#pragma unroll
+  for (int j = B - 1; j >= 0; j--) {
+    const bool hit = acc < need && need <= acc + h[j];
+    sel = hit ? first + j : sel;
+    sel_acc = hit ? acc : sel_acc;
+    sel_cnt = hit ? h[j] : sel_cnt;
+    acc += h[j];
+  }
+  if (sel >= 0) {
+    s_sel[0] = sel;
+    s_sel[1] = sel_acc;
+    s_sel[3] = sel_cnt;
+  }
+  __syncthreads();
+}
+
 // Makes the compiler treat the values as redefined here, so that predicates computed from
 // them in an earlier unrolled loop are recomputed rather than kept alive (as one 64-bit
 // lane mask each) until a later loop.
@@ -592,7 +651,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   atomicAdd(&s_hist[ta ? key_at(N + 1) >> kShift : kHistBins + lane], 1);
   launder(kk);  // the bins are recomputed where needed rather than kept, one register per key
   __syncthreads();
-  find_bin_w0<kHistBins>(s_hist, kLoBin, kHiBin, k, s_sel, tid);
+  find_bin_all<C::kWaves>(s_hist, kLoBin, kHiBin, k, s_wave, s_sel, tid);
   const int total = s_sel[2];
   const bool all = total <= k;  // every finite value is selected
   const uint32_t b1 = all ? 0xFFFFFFFFu : (uint32_t)s_sel[0];
