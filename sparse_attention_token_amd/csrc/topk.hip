@@ -80,50 +80,73 @@ struct Keys {
 
 // Visit every column of [st, en) once, in batches: f(n, active[], column[], raw[]) with
 // n = 2 (the unaligned head and tail, fewer than 16 bytes each, element loads) and then
-// n = 16 per round of 16-byte loads (K::kUnroll per thread in flight).  Every lane of the workgroup makes the same calls (active = false for
-// padding), so f may use wavefront ballots.
-template <bool BF16, int THREADS, typename F>
-__device__ __forceinline__ void scan_row(const uint8_t* row, int st, int en, int tid, F&& f) {
+// n = 16 per round of 16-byte loads (K::kUnroll per thread in flight).  Every lane of the workgroup makes the same
+// calls (active = false for padding), so f may use wavefront ballots.  Constructing the reader issues the head, the
+// tail and the first round's loads, so a kernel can put them in flight before other work and visit the row later.
+template <bool BF16, int THREADS>
+struct RowReader {
   using K = Keys<BF16>;
-  constexpr int E = K::kPerVec;
-  constexpr int kUnroll = K::kUnroll;
-  constexpr int N = kUnroll * E;
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + (uintptr_t)st * K::kElemBytes;
-  int c0 = st + (int)(((16 - (addr & 15)) & 15) / K::kElemBytes);
-  if (c0 > en) c0 = en;
-  const int nvec = (en - c0) / E;
-  const int c1 = c0 + nvec * E;
-  {
+  static constexpr int E = K::kPerVec;
+  static constexpr int kUnroll = K::kUnroll;
+  static constexpr int N = kUnroll * E;
+  const uint4* vec;
+  int c0, c1, nvec, st, tid;
+  bool hact[2];
+  uint32_t hraw[2];
+  uint4 v[kUnroll];
+
+  __device__ __forceinline__ RowReader(const uint8_t* row, int st_, int en, int tid_) : st(st_), tid(tid_) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + (uintptr_t)st * K::kElemBytes;
+    c0 = st + (int)(((16 - (addr & 15)) & 15) / K::kElemBytes);
+    if (c0 > en) c0 = en;
+    nvec = (en - c0) / E;
+    c1 = c0 + nvec * E;
+    vec = reinterpret_cast<const uint4*>(row + (size_t)c0 * K::kElemBytes);
+    load(0);
     const int nh = c0 - st, nt = en - c1;
-    const bool act[2] = {tid < nh, tid < nt};
-    const int col[2] = {st + tid, c1 + tid};
-    const uint32_t raw[2] = {act[0] ? K::load1(row, col[0]) : 0u, act[1] ? K::load1(row, col[1]) : 0u};
-    f(act, col, raw);
+    hact[0] = tid < nh;
+    hact[1] = tid < nt;
+    hraw[0] = hact[0] ? K::load1(row, st + tid) : 0u;
+    hraw[1] = hact[1] ? K::load1(row, c1 + tid) : 0u;
   }
-  const uint4* vec = reinterpret_cast<const uint4*>(row + (size_t)c0 * K::kElemBytes);
-  for (int base = 0; base < nvec; base += THREADS * kUnroll) {
-    uint4 v[kUnroll];
+  __device__ __forceinline__ void load(int base) {
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
       const int vi = base + u * THREADS + tid;
       if (vi < nvec) v[u] = vec[vi];
     }
-    bool act[N];
-    int col[N];
-    uint32_t raw[N];
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      const int vi = base + u * THREADS + tid;
-      const bool a = vi < nvec;
-#pragma unroll
-      for (int e = 0; e < E; e++) {
-        act[u * E + e] = a;
-        col[u * E + e] = c0 + vi * E + e;
-        raw[u * E + e] = a ? K::elem(v[u], e) : 0u;
-      }
-    }
-    f(act, col, raw);
   }
+  template <typename F>
+  __device__ __forceinline__ void run(F&& f) {
+    {
+      const int col[2] = {st + tid, c1 + tid};
+      f(hact, col, hraw);
+    }
+    for (int base = 0; base < nvec; base += THREADS * kUnroll) {
+      if (base) load(base);
+      bool act[N];
+      int col[N];
+      uint32_t raw[N];
+#pragma unroll
+      for (int u = 0; u < kUnroll; u++) {
+        const int vi = base + u * THREADS + tid;
+        const bool a = vi < nvec;
+#pragma unroll
+        for (int e = 0; e < E; e++) {
+          act[u * E + e] = a;
+          col[u * E + e] = c0 + vi * E + e;
+          raw[u * E + e] = a ? K::elem(v[u], e) : 0u;
+        }
+      }
+      f(act, col, raw);
+    }
+  }
+};
+
+template <bool BF16, int THREADS, typename F>
+__device__ __forceinline__ void scan_row(const uint8_t* row, int st, int en, int tid, F&& f) {
+  RowReader<BF16, THREADS> rd(row, st, en, tid);
+  rd.run(f);
 }
 
 // Reserve consecutive slots for the set predicates of a batch, one LDS atomic per
@@ -777,7 +800,20 @@ __device__ __forceinline__ SplitWs split_ws(void* ws, int rows, int G) {
   return w;
 }
 
-// Step 1: the 11-bit histogram of each slice.  grid = (G, rows).
+// Slice workgroups are numbered so that the G slices of a row run on one XCD (workgroups go to the eight XCDs in
+// turn by linear id; row r's resolve workgroup, number r, lands on the same one): the row's slice histograms then
+// meet in that XCD's L2 rather than being fetched into all eight.  Grid: 8 * ceil(rows / 8) * G workgroups; false
+// for the padding.
+__device__ __forceinline__ bool split_coords(int G, int rows, int& r, int& g) {
+  const int x = (int)blockIdx.x & 7, q = (int)blockIdx.x >> 3;
+  g = q % G;
+  r = (q / G) * 8 + x;
+  return r < rows;
+}
+
+__host__ inline unsigned split_grid(int rows, int G) { return (unsigned)(8 * ((rows + 7) / 8) * G); }
+
+// Step 1: the 11-bit histogram of each slice.
 template <bool BF16>
 __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
     const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
@@ -785,15 +821,17 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
   using K = Keys<BF16>;
   constexpr int kC = SliceCfg::kCopies;
   __shared__ int s_hist[kHistBins * kC];
-  const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  int r, g;
+  if (!split_coords(G, rows, r, g)) return;
   const int st = row_starts ? max(row_starts[r], 0) : 0;
   const int en = max(min(row_ends[r], max_width), st);
   int a, b;
   slice_range(st, en, g, G, a, b);
+  RowReader<BF16, SliceCfg::kThreads> rd(logits + (int64_t)r * row_bytes, a, b, tid);
   for (int i = tid; i < kHistBins * kC; i += SliceCfg::kThreads) s_hist[i] = 0;
   __syncthreads();
-  scan_row<BF16, SliceCfg::kThreads>(logits + (int64_t)r * row_bytes, a, b, tid,
-                                     [&](const auto& act, const auto&, const auto& raw) {
+  rd.run([&](const auto& act, const auto&, const auto& raw) {
     constexpr int n = sizeof(act) / sizeof(act[0]);
 #pragma unroll
     for (int i = 0; i < n; i++) {
@@ -816,7 +854,8 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
 // the columns they hold above b1, at b1, and valid.  It then writes its columns above the
 // boundary bin from its offset (or, when every valid value is selected, all its valid columns,
 // and the last slice the -1 padding); its boundary-bin columns go to the row's candidate list
-// from its offset.  Slice 0 leaves {b1, above1, total, m} for step 3.  grid = (G, rows).
+// from its offset.  Slice 0 leaves {b1, above1, total, m} for step 3.  The slice's first loads are issued before
+// the histograms are read.
 template <bool BF16>
 __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
     const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
@@ -831,7 +870,14 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
   __shared__ int s_sel[4];
   __shared__ int s_red[3][C::kWaves];
   __shared__ int s_cnt[2];
-  const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int r, g;
+  if (!split_coords(G, rows, r, g)) return;
+  const int st = row_starts ? max(row_starts[r], 0) : 0;
+  const int en = max(min(row_ends[r], max_width), st);
+  int a, b;
+  slice_range(st, en, g, G, a, b);
+  RowReader<BF16, kT> rd(logits + (int64_t)r * row_bytes, a, b, tid);
   const SplitWs w = split_ws(ws, rows, G);
   const int* hist = w.hist + (int64_t)r * G * kHistBins;
   int4 hv[kMaxSplit];
@@ -888,14 +934,10 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
     meta[2] = total;
     meta[3] = s_hist[b1];
   }
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
-  int a, b;
-  slice_range(st, en, g, G, a, b);
   int* orow = out + (int64_t)r * out_ld;
   uint32_t* ckey = w.key + (int64_t)r * kSplitCap;
   int* ccol = w.col + (int64_t)r * kSplitCap;
-  scan_row<BF16, kT>(logits + (int64_t)r * row_bytes, a, b, tid, [&](const auto& act, const auto& col, const auto& raw) {
+  rd.run([&](const auto& act, const auto& col, const auto& raw) {
     constexpr int n = sizeof(act) / sizeof(act[0]);
     bool gt[n], eq[n];
     uint32_t keys[n];
@@ -998,7 +1040,7 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
   const int G = split_count(rows, max_width);
   const bool bf = dtype == DSI_BF16;
   if (G > 1) {
-    const dim3 grid((unsigned)G, (unsigned)rows);
+    const dim3 grid(split_grid(rows, G));
     if (bf) {
       hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
                          row_starts, row_ends, max_width, workspace, rows, G);
