@@ -234,7 +234,7 @@ __device__ __forceinline__ void slice_range(int st, int en, int g, int G, int& a
 
 // The boundary bin b1 (top 11 key bits) is known, `above1` columns above it are written
 // to out[0, above1), and the m columns of bin b1 are in s_ckey/s_ccol (when m <= cap).
-// Resolves the remaining key bits (fp32: three digits of 7, bf16: 5) by histograms over
+// Resolves the remaining key bits (fp32: digits of 10 and 11 bits, bf16: 5) by histograms over
 // the candidates — or over the row when m > cap — and writes the k - above1 selected
 // boundary-bin columns to out[above1, k).  Call with all threads.
 template <bool BF16, typename C>
@@ -247,9 +247,9 @@ __device__ __forceinline__ void resolve_boundary(const uint8_t* row, int st, int
   const int lane = tid & 63;
   int need = k - above1;
   constexpr int kLow = K::kTopShift;
-  const int nd = BF16 ? 1 : 3;
-  const int shifts[3] = {BF16 ? 0 : 14, 7, 0};
-  const int widths[3] = {BF16 ? 5 : 7, 7, 7};
+  const int nd = BF16 ? 1 : 2;
+  const int shifts[2] = {BF16 ? 0 : 11, 0};
+  const int widths[2] = {BF16 ? 5 : 10, 11};
   uint32_t prefix = b1 << kLow;  // known high bits of the threshold key
   const bool in_lds = m <= cap;
   for (int p = 0; p < nd; p++) {
