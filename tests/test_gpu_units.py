@@ -243,12 +243,13 @@ def test_topk_bf16_exact_values(width):
         assert np.array_equal(np.sort(f[r, got[r][got[r] >= 0]]), np.sort(f[r, ref[r][ref[r] >= 0]]))
 
 
-@pytest.mark.parametrize("bf16", [False, True])
-def test_topk_split_long_rows(bf16):
+@pytest.mark.parametrize("bf16,rows", [(False, 8), (True, 8), (False, 13)])
+def test_topk_split_long_rows(bf16, rows):
     """Few long rows are split between workgroups; cover the take-all, all-invalid, heavy-tie
-    (boundary bin larger than the candidate list) and ordinary rows."""
+    (boundary bin larger than the candidate list) and ordinary rows, and a row count that leaves
+    some of the workgroup numbers (a row's slices share one XCD) without a row."""
     rng = np.random.default_rng(21 + bf16)
-    rows, width = 8, 50000
+    width = 50000
     x = (rng.standard_normal((rows, width)) * 40).astype(np.float32)
     x[1, 1000:] = -np.inf           # 1000 valid: take all, pad with -1
     x[2, :] = np.nan                # nothing valid
@@ -257,6 +258,8 @@ def test_topk_split_long_rows(bf16):
     x[5] = np.round(x[5] / 8) * 8   # many ties
     ends = np.array([width, width, width, width, width, 30001, 20000, 49999], np.int32)
     starts = np.array([0, 0, 0, 0, 3, 17, 0, 12345], np.int32)
+    ends = np.concatenate([ends, rng.integers(20000, width + 1, rows - 8)]).astype(np.int32)
+    starts = np.concatenate([starts, rng.integers(0, 5000, rows - 8)]).astype(np.int32)
     if bf16:
         bits = synth._bf16_bits(x)
         vals = bf16_value(bits)
