@@ -83,11 +83,12 @@ struct Keys {
 // n = 16 per round of 16-byte loads (K::kUnroll per thread in flight).  Every lane of the workgroup makes the same
 // calls (active = false for padding), so f may use wavefront ballots.  Constructing the reader issues the head, the
 // tail and the first round's loads, so a kernel can put them in flight before other work and visit the row later.
-template <bool BF16, int THREADS>
+// Each round's loads are issued before the previous round is visited.  UNROLL: 16-byte loads per thread and round.
+template <bool BF16, int THREADS, int UNROLL = Keys<BF16>::kUnroll>
 struct RowReader {
   using K = Keys<BF16>;
   static constexpr int E = K::kPerVec;
-  static constexpr int kUnroll = K::kUnroll;
+  static constexpr int kUnroll = UNROLL;
   static constexpr int N = kUnroll * E;
   const uint4* vec;
   int c0, c1, nvec, st, tid;
@@ -123,7 +124,10 @@ struct RowReader {
       f(hact, col, hraw);
     }
     for (int base = 0; base < nvec; base += THREADS * kUnroll) {
-      if (base) load(base);
+      uint4 cur[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; u++) cur[u] = v[u];
+      if (base + THREADS * kUnroll < nvec) load(base + THREADS * kUnroll);
       bool act[N];
       int col[N];
       uint32_t raw[N];
@@ -135,7 +139,7 @@ struct RowReader {
         for (int e = 0; e < E; e++) {
           act[u * E + e] = a;
           col[u * E + e] = c0 + vi * E + e;
-          raw[u * E + e] = a ? K::elem(v[u], e) : 0u;
+          raw[u * E + e] = a ? K::elem(cur[u], e) : 0u;
         }
       }
       f(act, col, raw);
@@ -877,7 +881,8 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
   const int en = max(min(row_ends[r], max_width), st);
   int a, b;
   slice_range(st, en, g, G, a, b);
-  RowReader<BF16, kT> rd(logits + (int64_t)r * row_bytes, a, b, tid);
+  constexpr int kU = 2;  // 8 fp32 values per thread and round: fewer live ballot masks (measured 27.3 -> 26.0 us)
+  RowReader<BF16, kT, kU> rd(logits + (int64_t)r * row_bytes, a, b, tid);
   const SplitWs w = split_ws(ws, rows, G);
   const int* hist = w.hist + (int64_t)r * G * kHistBins;
   int4 hv[kMaxSplit];
