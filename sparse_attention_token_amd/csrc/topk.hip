@@ -80,10 +80,11 @@ struct Keys {
 
 // Visit every column of [st, en) once, in batches: f(n, active[], column[], raw[]) with
 // n = 2 (the unaligned head and tail, fewer than 16 bytes each, element loads) and then
-// n = 16 per round of 16-byte loads (K::kUnroll per thread in flight).  Every lane of the workgroup makes the same
-// calls (active = false for padding), so f may use wavefront ballots.  Constructing the reader issues the head, the
-// tail and the first round's loads, so a kernel can put them in flight before other work and visit the row later.
-// Each round's loads are issued before the previous round is visited.  UNROLL: 16-byte loads per thread and round.
+// n = UNROLL x (values per 16 bytes) per round of 16-byte loads (UNROLL per thread and round; 16 fp32 or bf16 values
+// by default).  Every lane of the workgroup makes the same calls (active = false for padding), so f may use
+// wavefront ballots.  Constructing the reader issues the head, the tail and the first round's loads, so a kernel can
+// put them in flight before other work and visit the row later; the next round's loads are issued before a round is
+// visited.
 template <bool BF16, int THREADS, int UNROLL = Keys<BF16>::kUnroll>
 struct RowReader {
   using K = Keys<BF16>;
