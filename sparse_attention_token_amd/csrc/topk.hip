@@ -779,7 +779,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
 // ---------------------------------------------------------------- long rows split G ways
 // Workspace: per (row, slice) an 11-bit histogram; per row {b1, above1, total, m}; per row
 // up to kSplitCap boundary-bin candidates (key, column).
-using SliceCfg = Cfg<512, 0, 1>;
+using SliceCfg = Cfg<512, 0, 2>;  // two histogram copies in the slice step (measured 26.0 -> 25.6 us)
 
 struct SplitWs {
   int* hist;      // [rows][G][2048]
