@@ -211,29 +211,125 @@ def bench_prefill(steps, warmup):
     return dict(c=c, pairs=pairs, ms_step=ms_step, ms_logits=ms_logits, ms_topk=ms_topk, T=T, S=S)
 
 
-def cpu_baseline(c, max_seconds):
-    """The oracle as it is, single thread, on a bounded sample of the same workload: the chunk's k rows
-    quantized, then logits and top-2048 for evenly spaced query rows until the time budget is used."""
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _decode_bytes(L, nn, bs):
+    """Algorithmic bytes of one request's decode logits + top-k (the GPU figure's formula): its K once, its block
+    table, q and weights per row, the logits written and read back, the index rows written."""
+    V = sum(L - nn + i + 1 for i in range(nn))
+    return ROW * L + 4 * ((L + bs - 1) // bs) + nn * (64 * 128 + 64 * 2) + 8 * V + nn * K * 4
+
+
+def cpu_baselines(c2, budget_s):
+    """The oracle as it is (single thread, never tuned) on a bounded sample of each workload, the whole chain
+    the GPU runs: k quantization, logits, top-k and slot conversion (or expansion, sparse logits, top-k, remap
+    and slots).  Rows or requests are taken in a seeded random order until each workload's share of the time
+    budget is spent.  Returns the headline object (workload 2) with every workload under `per_config`."""
     import oracle
-    T, S = c["T"], c["S"]
+    per = {}
+    share = budget_s / 5.0
+
+    # workloads 1 and 2: quantize the whole history, then logits + top-2048 per query row
+    def dense(c, seconds):
+        T, S = c["T"], c["S"]
+        t0 = time.perf_counter()
+        rows = np.zeros((S, ROW), np.uint8)
+        oracle.k_quant_and_cache(c["k"], np.arange(S), rows.reshape(-1), S, S * ROW)
+        done, pairs = 0, 0
+        for t in np.random.default_rng(0).permutation(T):
+            sl = slice(int(t), int(t) + 1)
+            lg = oracle.mqa_logits_gathered(c["q"][sl], c["w"][sl], rows, c["ks"][sl], c["ke"][sl])
+            oracle.topk_select(lg, c["ke"][sl], K, starts=c["ks"][sl])
+            pairs += int(c["ke"][t] - c["ks"][t])
+            done += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        dt = time.perf_counter() - t0
+        return dict(value=pairs / dt, unit="pairs/s", seconds=round(dt, 2),
+                    sample=f"{done} of {T} query rows (all {S} k rows quantized first)")
+
+    per["1_tiny_dense"] = dense(synth.workload(1), share)
+    per["2_prefill_chunk"] = dense(c2, 2 * share)
+
+    # workloads 3 and 4: per request, its k rows quantized into a pool of its own pages, paged logits for its
+    # next-n rows, top-2048 and slot conversion
+    for n, name in ((3, "3_paged_decode"), (4, "4_long_context_decode")):
+        c = synth.workload(n)
+        nn, bs = c["next_n"], c["block_size"]
+        lens = c["context_lens"]
+        starts = np.concatenate([[0], np.cumsum(lens)])
+        t0 = time.perf_counter()
+        done, pairs, nbytes = 0, 0, 0
+        for b in np.random.default_rng(n).permutation(c["B"]):
+            L = int(lens[b])
+            nblk = (L + bs - 1) // bs
+            pool = np.zeros(nblk * bs * ROW, np.uint8)
+            bt = np.arange(nblk, dtype=np.int32)[None, :]
+            oracle.k_quant_and_cache(c["k"][starts[b]:starts[b + 1]], np.arange(L), pool, bs, bs * ROW)
+            rr = slice(b * nn, (b + 1) * nn)
+            lg = oracle.mqa_logits_paged(c["q"][rr], c["w"][rr], nn, lens[b:b + 1], pool, bs, bs * ROW, bt, L)
+            ends = np.array([L - nn + i + 1 for i in range(nn)], np.int32)
+            idx = oracle.topk_select(lg, ends, K)
+            oracle.req_index_to_global_slot(idx, bt, bs, bs, row_to_req=np.zeros(nn, np.int32))
+            pairs += int(ends.sum())
+            nbytes += _decode_bytes(L, nn, bs)
+            done += 1
+            if time.perf_counter() - t0 > share:
+                break
+        dt = time.perf_counter() - t0
+        per[name] = dict(value=pairs / dt, unit="pairs/s", gbs_equivalent=round(nbytes / dt / 1e9, 4),
+                         rows_per_s=round(done * nn / dt, 2), seconds=round(dt, 2),
+                         sample=f"{done} of {c['B']} requests ({done * nn} rows), each quantized, scored, selected "
+                                f"and converted to slots")
+
+    # workload 5: expansion of every row, then per sampled row sparse logits (bf16), top-2048, remap (+ slots)
+    c = synth.workload(5)
+    sbk, cbs, nd, nrows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
+    bs = c["block_size"]
     t0 = time.perf_counter()
-    rows = np.zeros((S, ROW), np.uint8)
-    oracle.k_quant_and_cache(c["k"], np.arange(S), rows.reshape(-1), S, S * ROW)
-    order = np.random.default_rng(0).permutation(T)
-    done_rows, pairs = 0, 0
-    for t in order:
-        sl = slice(int(t), int(t) + 1)
-        lg = oracle.mqa_logits_gathered(c["q"][sl], c["w"][sl], rows, c["ks"][sl], c["ke"][sl])
-        oracle.topk_select(lg, c["ke"][sl], K, starts=c["ks"][sl])
-        pairs += int(c["ke"][t] - c["ks"][t])
-        done_rows += 1
-        if time.perf_counter() - t0 > max_seconds:
+    si, end = oracle.expand_candidates(c["cand"], c["ks"], c["ke"], cbs, sbk)
+    pre = np.zeros((c["Lp"], ROW), np.uint8)
+    oracle.k_quant_and_cache(c["k_pre"], np.arange(c["Lp"]), pre.reshape(-1), c["Lp"], c["Lp"] * ROW)
+    dstarts = np.concatenate([[0], np.cumsum(c["dec_lens"])])
+    done, scored = 0, 0
+    for r in np.random.default_rng(5).permutation(nrows):
+        sl = slice(int(r), int(r) + 1)
+        if r < nd:
+            L = int(c["dec_lens"][r])
+            nblk = (L + bs - 1) // bs
+            pool = np.zeros(nblk * bs * ROW, np.uint8)
+            oracle.k_quant_and_cache(c["k_dec"][dstarts[r]:dstarts[r + 1]], np.arange(L), pool, bs, bs * ROW)
+            bt = np.arange(nblk, dtype=np.int32)[None, :]
+            kw = dict(k_src=pool, block_table=bt, row_to_req=np.zeros(1, np.int32), block_size=bs,
+                      block_stride=bs * ROW)
+        else:
+            kw = dict(k_src=pre)
+        lg = oracle.sparse_mqa_logits(c["q"][sl], c["w"][sl], c["ks"][sl], c["ke"][sl], si[sl], end[sl], sbk, **kw)
+        col = oracle.topk_select(lg, end[sl], K, bf16=True)
+        pos = oracle.topk_remap(col, si[sl], c["ks"][sl], sbk)
+        if r < nd:
+            oracle.req_index_to_global_slot(pos, kw["block_table"], bs, bs, row_to_req=np.zeros(1, np.int32))
+        scored += int(end[r])
+        done += 1
+        if time.perf_counter() - t0 > share:
             break
     dt = time.perf_counter() - t0
-    return dict(value=pairs / dt, unit="pairs/s", cores=1, kind="oracle",
-                sample=f"{done_rows} of {T} query rows of the prefill chunk (plus quantizing all {S} k rows), "
-                       f"{dt:.1f} s, 1 thread, host {platform.processor() or platform.machine()} "
-                       f"with {os.cpu_count()} cores")
+    per["5_hierarchical_sparse"] = dict(value=scored / dt, unit="scored pairs/s", seconds=round(dt, 2),
+                                        sample=f"expansion of all {nrows} rows, the 131K-token prefill history "
+                                               f"quantized, then {done} rows scored, selected and remapped")
+    head = per["2_prefill_chunk"]
+    return dict(value=head["value"], unit="pairs/s", cores=1, kind="oracle",
+                sample=f"prefill chunk: {head['sample']}, {head['seconds']} s; one thread on a host "
+                       f"{host_cpu_model()} with {os.cpu_count()} logical CPUs",
+                per_config=per)
 
 
 # --------------------------------------------------------------------------- paged decode
@@ -473,12 +569,29 @@ def host_end(t):
     return t.cpu().numpy().astype(np.int64)
 
 
+def bars(achieved_tflops, extra):
+    """The stated targets and where this run stands against each (met or not, said plainly)."""
+    fp8 = achieved_tflops / FP8_PEAK_TFLOPS
+    out = {"prefill_logits_vs_fp8_peak": {
+        "target": 0.5, "achieved": round(fp8, 4), "met": fp8 >= 0.5,
+        "note": "the FP8 x FP8 contraction runs on the f16 matrix cores (codes decoded exactly to f16): gfx950's "
+                "FP8-operand MFMAs truncate inside one instruction by more than the 1e-3 (1 + |ref|) logit "
+                "tolerance; the f16 peak is half the FP8 peak, so 0.5 of FP8 is 1.0 of f16, unreachable on this "
+                "path"}}
+    for n in (3, 4):
+        w = extra.get(f"decode_w{n}")
+        if w:
+            out[f"decode_w{n}_logits_topk_vs_hbm"] = {"target": 0.6, "achieved": w["hbm_frac"],
+                                                      "met": w["hbm_frac"] >= 0.6}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--workloads", default=None,
@@ -535,7 +648,7 @@ def main():
         log("context-parallel merge ...")
         extra["cp_merge"] = bench_merge(args.steps, args.warmup)
     log("cpu baseline ...")
-    cpu = cpu_baseline(pf["c"], args.cpu_seconds)
+    cpu = cpu_baselines(pf["c"], args.cpu_seconds)
     line = {
         "metric": "indexer q.k pairs/s (prefill chunk: k insert + dense FP8 logits + top-2048)",
         "value": round(value, 1),
@@ -559,6 +672,11 @@ def main():
                      "frac_of_fp8_peak": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "measured_ceiling": ceil},
         "cpu_baseline": cpu,
+        "bars": bars(achieved, extra),
+        "pages_cost_context": {
+            "indexer": "64 heads x 128 dims, FP8 q and k", "main_mla": "128 heads x 576 dims, bf16",
+            "indexer_cache_bytes_per_token": 132, "main_mla_cache_bytes_per_token": 1152,
+            "source": "DeepSeek V3.2 DSA inference flow page, the scorer cost table"},
         "workloads": extra,
     }
     print(json.dumps(line), flush=True)

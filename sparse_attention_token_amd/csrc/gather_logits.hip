@@ -53,13 +53,15 @@ constexpr int kDcSegs = kDcJob * kDcChunk / 16;     // 16-token segments per job
 
 // Issue this wavefront's NP DMA pieces of one chunk: slab i (1 KB of the chunk buffer) is
 // slab wave + 4i, lane l's 16 bytes are piece 64*slab + l, read from src_of(piece).  The
-// loads are issued as inline assembly (M0 = the LDS destination of the wavefront's 1 KB,
-// one wait state, global_load_lds_dwordx4), so the compiler does not treat them as writes
-// to the other buffer that the scoring of the current chunk has to wait for; the kernel
-// orders them itself with an explicit vmcnt wait and a barrier.  No other code in the
-// kernel uses M0.  Every source address (each needs an LDS read of its key's offset) is
-// computed before the first load is issued: the assembly statements are ordered memory
-// operations, so interleaving them with those reads cost one LDS round trip per load.
+// loads are issued as inline assembly (one wait state, then global_load_lds_dwordx4), so the
+// compiler does not treat them as writes to the other buffer that the scoring of the current
+// chunk has to wait for; the kernel orders them itself with an explicit vmcnt wait and a
+// barrier.  The LDS destination of the wavefront's 1 KB goes in M0 through the operand
+// constraint "{m0}": the compiler writes M0 itself and knows the statement reads it (M0 is a
+// reserved register, so naming it as a clobber would not protect a value the compiler keeps
+// there).  Every source address (each needs an LDS read of its key's offset) is computed
+// before the first load is issued: the assembly statements are ordered memory operations,
+// so interleaving them with those reads cost one LDS round trip per load.
 template <int NP, typename SrcOf>
 __device__ __forceinline__ void dma_chunk(uint8_t* buf, int wave, int lane, SrcOf&& src_of) {
   const uint8_t* src[NP];
@@ -69,8 +71,7 @@ __device__ __forceinline__ void dma_chunk(uint8_t* buf, int wave, int lane, SrcO
   for (int i = 0; i < NP; i++) {
     const uint32_t lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + (wave + 4 * i) * 1024));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[i]), "s"(lds)
-                 : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[i]), "{m0}"(lds) : "memory");
   }
 }
 

@@ -1,8 +1,10 @@
 """Shared helpers for the GPU parity tests: device transfer, the tolerance rules and the top-k comparison.
 
 Tolerances (the indexer's stated bar): fp32 logits |gpu - ref| <= 1e-3 (1 + |ref|); bf16 sparse logits add
-half a bf16 ulp, 2^-8 |ref|, for the one rounding the path performs; a top-k selection is accepted when it
-has the oracle's size and every selected/non-selected pair is ordered correctly up to those tolerances.
+half a bf16 ulp, 2^-8 |ref|, for the one rounding the path performs.  A top-k selection is accepted when it
+has the oracle's size and every swap is within one tolerance: for a selected g and a non-selected valid x,
+ref[x] - ref[g] <= 1e-3 (1 + max(|ref[x]|, |ref[g]|)).  On bf16 rows each side's half ulp is added, since two
+logits that differ by up to one bf16 ulp can round to the same value and tie.
 """
 import numpy as np
 import torch
@@ -47,10 +49,23 @@ def assert_close(gpu, ref, tol_fn=tol_f32, what="logits"):
                              f"gpu={gpu[bad][:5]} ref={ref[bad][:5]}")
 
 
-def check_selection(gpu_idx, ref_idx, ref_vals, tol_fn=tol_f32, start=0, end=None):
+def swap_tolerance(x, g, rule="f32"):
+    """Largest ref[x] - ref[g] allowed when g is selected and x is not (element-wise).  rule: "f32" (one logit
+    tolerance), "bf16" (plus each side's half ulp) or "exact" (identical inputs: no swap across a difference)."""
+    x, g = np.abs(np.asarray(x, np.float64)), np.abs(np.asarray(g, np.float64))
+    if rule == "exact":
+        return 0.0 * (x + g)
+    t = 1e-3 * (1.0 + np.maximum(x, g))
+    if rule == "bf16":
+        return t + 2.0 ** -8 * (x + g)
+    assert rule == "f32", rule
+    return t
+
+
+def check_selection(gpu_idx, ref_idx, ref_vals, rule="f32", start=0, end=None):
     """One row.  gpu_idx/ref_idx: int32 [k] positions relative to `start` (-1 = empty); ref_vals: the oracle's
-    values of the row (absolute columns).  Same size, no duplicates, valid positions, and
-    max over non-selected valid x of (ref[x] - tol) <= min over selected g of (ref[g] + tol)."""
+    values of the row (absolute columns).  Same size, no duplicates, valid positions, and every swap within
+    swap_tolerance(rule)."""
     end = ref_vals.shape[0] if end is None else end
     g = gpu_idx[gpu_idx >= 0]
     o = ref_idx[ref_idx >= 0]
@@ -68,10 +83,23 @@ def check_selection(gpu_idx, ref_idx, ref_vals, tol_fn=tol_f32, start=0, end=Non
         assert finite.sum() == 0
         return
     rest = finite & ~sel
-    if rest.any():
-        hi_rest = np.max(row[rest] - tol_fn(row[rest]))
-        lo_sel = np.min(row[g] + tol_fn(row[g]))
-        assert hi_rest <= lo_sel, f"selection misses a larger value: {hi_rest} > {lo_sel}"
+    if not rest.any():
+        return
+    rv, sv = row[rest], row[g]
+    lo = sv.min()
+    hi = rv.max()
+    if hi <= lo:
+        return
+    # only pairs ordered the wrong way need a check: non-selected above the smallest selected value, and
+    # selected below the largest non-selected value
+    xs = rv[rv > lo]
+    gs = sv[sv < hi]
+    diff = xs[:, None] - gs[None, :]
+    ok = diff <= swap_tolerance(xs[:, None], gs[None, :], rule)
+    if not ok.all():
+        i, j = np.argwhere(~ok)[0]
+        raise AssertionError(f"selection misses a larger value: non-selected {xs[i]} vs selected {gs[j]} "
+                             f"(difference {diff[i, j]}, allowed {swap_tolerance(xs[i], gs[j], rule)})")
 
 
 def gathered_rows_oracle(k_bf16):

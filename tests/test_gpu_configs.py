@@ -195,7 +195,7 @@ def test_workload5_hierarchical_sparse():
         assert np.all(got[r][~valid] == 0xFF80)
         assert_close(bf16_value(got[r][valid]), ref_f32[valid], tol_fn=tol_bf16, what=f"row {r} sparse logits")
         ref_col = oracle.topk_select(ref_bits[None, :], end_ref[sl], K, bf16=True)[0]
-        check_selection(col[r], ref_col, ref_f32, tol_fn=tol_bf16, end=int(end_ref[r]))
+        check_selection(col[r], ref_col, ref_f32, rule="bf16", end=int(end_ref[r]))
         if r < nd:
             p = pos[r]
             exp = np.where(p >= 0, c["block_table"][r, np.maximum(p, 0) // bs] * bs + np.maximum(p, 0) % bs, -1)
@@ -280,4 +280,4 @@ def test_workload5_hierarchical_sparse_mxfp4():
         assert np.all(got[r][~valid] == 0xFF80)
         assert_close(bf16_value(got[r][valid]), ref_f32[valid], tol_fn=tol_bf16, what=f"row {r} MXFP4 logits")
         ref_col = oracle.topk_select(ref_bits[None, :], end_ref[sl], K, bf16=True)[0]
-        check_selection(col[r], ref_col, ref_f32, tol_fn=tol_bf16, end=int(end_ref[r]))
+        check_selection(col[r], ref_col, ref_f32, rule="bf16", end=int(end_ref[r]))

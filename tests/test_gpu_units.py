@@ -220,7 +220,7 @@ def test_topk_f32_same_input_exact_values(width, k):
     ref = oracle.topk_select(x, ends, k, starts=starts)
     got = host(dsi.topk_select(dev(x), dev(ends), k=k, row_starts=dev(starts)))
     for r in range(rows):
-        check_selection(got[r], ref[r], x[r], tol_fn=lambda v: 0.0 * v, start=starts[r], end=ends[r])
+        check_selection(got[r], ref[r], x[r], rule="exact", start=starts[r], end=ends[r])
         g = got[r][got[r] >= 0] + starts[r]
         o = ref[r][ref[r] >= 0] + starts[r]
         assert np.array_equal(np.sort(x[r, g]), np.sort(x[r, o]))
@@ -239,7 +239,7 @@ def test_topk_bf16_exact_values(width):
     got = host(dsi.topk_select(dev(bits), dev(ends), k=2048))
     f = bf16_value(bits)
     for r in range(9):
-        check_selection(got[r], ref[r], f[r], tol_fn=lambda v: 0.0 * v, end=ends[r])
+        check_selection(got[r], ref[r], f[r], rule="exact", end=ends[r])
         assert np.array_equal(np.sort(f[r, got[r][got[r] >= 0]]), np.sort(f[r, ref[r][ref[r] >= 0]]))
 
 
@@ -270,7 +270,7 @@ def test_topk_split_long_rows(bf16, rows):
         ref = oracle.topk_select(x, ends, 2048, starts=starts)
         got = host(dsi.topk_select(dev(x), dev(ends), k=2048, row_starts=dev(starts)))
     for r in range(rows):
-        check_selection(got[r], ref[r], vals[r], tol_fn=lambda v: 0.0 * v, start=starts[r], end=ends[r])
+        check_selection(got[r], ref[r], vals[r], rule="exact", start=starts[r], end=ends[r])
         g = got[r][got[r] >= 0] + starts[r]
         o = ref[r][ref[r] >= 0] + starts[r]
         assert np.array_equal(np.sort(vals[r, g]), np.sort(vals[r, o]))
@@ -289,7 +289,7 @@ def test_topk_strided_rows_and_out():
     assert np.all(got[:, :10] == -9) and np.all(got[:, 2058:] == -9)
     ref = oracle.topk_select(x, ends, 2048)
     for r in range(4):
-        check_selection(got[r, 10:2058], ref[r], x[r], tol_fn=lambda v: 0.0 * v)
+        check_selection(got[r, 10:2058], ref[r], x[r], rule="exact")
 
 
 # ----------------------------------------------------------------------------- expansion / remap / slot
