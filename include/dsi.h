@@ -33,7 +33,9 @@
  *     touches no memory outside the buffers described by its arguments, and
  *     the affected outputs are as documented per call.
  *   - Calls that overlap on one stream are ordered; the library holds no
- *     global state, so calls on different streams are independent.
+ *     global state, so calls on different streams are independent — with one
+ *     exception: dsi_topk_select_noalloc works in a device array the library
+ *     keeps per GPU.
  */
 #ifndef DSI_H
 #define DSI_H
@@ -166,6 +168,26 @@ DSI_API size_t dsi_topk_workspace_bytes(int32_t rows, int32_t max_width, int32_t
 DSI_API int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, int32_t rows, const int32_t* row_starts,
                     const int32_t* row_ends, int32_t max_width, int32_t k, int32_t* out, int64_t out_ld,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the device array dsi_topk_select_noalloc works in (one per GPU). */
+#define DSI_TOPK_NOALLOC_MAX_BYTES (16u << 20)
+
+/*
+ * dsi_topk_select for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that forbid allocation): the same selection, rules
+ * and errors, with the workspace taken from a device array of
+ * DSI_TOPK_NOALLOC_MAX_BYTES that the library holds on each GPU it runs on until
+ * the process ends.  The call itself allocates and frees nothing; on its first
+ * call on a GPU it looks up that GPU's array (a symbol-address query).  Every
+ * call on one GPU works in the same array and leaves its contents behind, so
+ * calls that overlap on one GPU (on different streams, or captured graphs
+ * replayed concurrently) race and give undefined results; calls ordered on one
+ * stream are safe.  Sizes whose workspace (dsi_topk_workspace_bytes) exceeds the
+ * array return DSI_EWORKSPACE before any HIP call.
+ */
+DSI_API int dsi_topk_select_noalloc(const void* logits, int32_t dtype, int64_t ld, int32_t rows,
+                                    const int32_t* row_starts, const int32_t* row_ends, int32_t max_width,
+                                    int32_t k, int32_t* out, int64_t out_ld, hipStream_t stream);
 
 /*
  * Candidate expansion of the hierarchical indexer (P1 key source snippets:

@@ -41,6 +41,7 @@ _SIGNATURES = {
                                                          _i32, _i32, _p, _i64, _p]),
     "dsi_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "dsi_topk_select": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _i32, _p, _i64, _p, _sz, _p]),
+    "dsi_topk_select_noalloc": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _i32, _p, _i64, _p]),
     "dsi_expand_candidates": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _p, _i64, _i32, _i32, _p, _i64, _p,
                                              _i64, _p]),
     "dsi_sparse_mqa_logits": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p, _i64,
@@ -231,6 +232,26 @@ def topk_select(logits, row_ends, k=MAX_TOPK, row_starts=None, max_width=None, o
     with torch.cuda.device(dev):
         _check(lib().dsi_topk_select(_ptr(logits), dtype, ld, rows, _ptr(row_starts), _ptr(row_ends), max_width, k,
                                      _ptr(out), out_ld, ws_ptr, ws_bytes, _stream(logits)), "topk_select")
+    return out
+
+
+def topk_select_noalloc(logits, row_ends, out, k=MAX_TOPK, row_starts=None, max_width=None):
+    """topk_select with no workspace argument and no allocation: the library's per-GPU scratch array is used
+    (calls that overlap on one GPU race).  `out` int32 [rows, >=k] is required."""
+    dev = _dev(logits, row_ends, row_starts, out)
+    if logits.dtype == torch.float32:
+        dtype = F32
+    elif logits.dtype in _BF16:
+        dtype = BF16
+    else:
+        raise TypeError(f"logits: unsupported dtype {logits.dtype}")
+    _need(out, _I32, "out")
+    if max_width is None:
+        max_width = logits.shape[1]
+    with torch.cuda.device(dev):
+        _check(lib().dsi_topk_select_noalloc(_ptr(logits), dtype, _rows(logits, "logits"), logits.shape[0],
+                                             _ptr(row_starts), _ptr(row_ends), max_width, k, _ptr(out),
+                                             _rows(out, "out"), _stream(logits)), "topk_select_noalloc")
     return out
 
 

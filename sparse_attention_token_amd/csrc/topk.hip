@@ -22,6 +22,7 @@
 //     atomics across workgroups) and appends its boundary-bin columns to a per-row
 //     candidate list; one workgroup per row resolves the candidates as above.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -1025,11 +1026,12 @@ extern "C" size_t dsi_topk_workspace_bytes(int32_t rows, int32_t max_width, int3
   return G > 1 ? split_ws_bytes(rows, G) : 0;
 }
 
-extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, int32_t rows,
-                               const int32_t* row_starts, const int32_t* row_ends, int32_t max_width, int32_t k,
-                               int32_t* out, int64_t out_ld, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
-  using namespace dsi;
+namespace dsi {
+namespace {
+
+int topk_select_impl(const void* logits, int32_t dtype, int64_t ld, int32_t rows, const int32_t* row_starts,
+                     const int32_t* row_ends, int32_t max_width, int32_t k, int32_t* out, int64_t out_ld,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != DSI_F32 && dtype != DSI_BF16) return DSI_EUNSUPPORTED;
   if (k < 1 || k > DSI_MAX_TOPK) return DSI_EUNSUPPORTED;
   if (rows < 0 || max_width < 0 || ld < max_width || out_ld < k) return DSI_EINVAL;
@@ -1089,4 +1091,61 @@ extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, in
   }
 #undef DSI_TOPK_REG
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// The workspace of dsi_topk_select_noalloc: one file-scope device array per GPU, held for the
+// process's lifetime.  In host code `scratch` names a host-side stand-in, not device memory, so
+// the kernels get the array's device address, looked up once per device (with that device
+// current) and kept in s_scratch.
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) uint8_t scratch[DSI_TOPK_NOALLOC_MAX_BYTES];
+std::mutex s_scratch_mu;
+void* s_scratch[kMaxDevices];
+
+// The device address of this stream's GPU's array (looked up on first use).
+int scratch_for(hipStream_t stream, void** ptr) {
+  int dev = -1, cur = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess) return DSI_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return DSI_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(s_scratch_mu);
+  if (!s_scratch[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DSI_ELAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return DSI_ELAUNCH;
+    if (e != hipSuccess || !p) return DSI_ELAUNCH;
+    s_scratch[dev] = p;
+  }
+  *ptr = s_scratch[dev];
+  return DSI_OK;
+}
+
+}  // namespace
+}  // namespace dsi
+
+extern "C" int dsi_topk_select(const void* logits, int32_t dtype, int64_t ld, int32_t rows,
+                               const int32_t* row_starts, const int32_t* row_ends, int32_t max_width, int32_t k,
+                               int32_t* out, int64_t out_ld, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return dsi::topk_select_impl(logits, dtype, ld, rows, row_starts, row_ends, max_width, k, out, out_ld, workspace,
+                               workspace_bytes, stream);
+}
+
+extern "C" int dsi_topk_select_noalloc(const void* logits, int32_t dtype, int64_t ld, int32_t rows,
+                                       const int32_t* row_starts, const int32_t* row_ends, int32_t max_width,
+                                       int32_t k, int32_t* out, int64_t out_ld, hipStream_t stream) {
+  using namespace dsi;
+  if (dtype != DSI_F32 && dtype != DSI_BF16) return DSI_EUNSUPPORTED;
+  if (k < 1 || k > DSI_MAX_TOPK) return DSI_EUNSUPPORTED;
+  if (rows < 0 || max_width < 0 || ld < max_width || out_ld < k) return DSI_EINVAL;
+  const size_t need = dsi_topk_workspace_bytes(rows, max_width, k);
+  if (need > (size_t)DSI_TOPK_NOALLOC_MAX_BYTES) return DSI_EWORKSPACE;  // before any HIP call
+  void* ws = nullptr;
+  if (need) {
+    const int st = scratch_for(stream, &ws);
+    if (st != DSI_OK) return st;
+  }
+  return topk_select_impl(logits, dtype, ld, rows, row_starts, row_ends, max_width, k, out, out_ld, ws,
+                          need ? (size_t)DSI_TOPK_NOALLOC_MAX_BYTES : 0, stream);
 }
