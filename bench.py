@@ -366,22 +366,27 @@ def bench_decode(n, steps, warmup, copies=4, mxfp4=False):
     logits = torch.empty((rows, maxc), dtype=torch.float32, device="cuda")
     idx = torch.empty((rows, K), dtype=torch.int32, device="cuda")
     slots = torch.empty((rows, K), dtype=torch.int32, device="cuda")
-    ws = torch.empty(max(dsi.topk_workspace_bytes(rows, maxc, K), 16), dtype=torch.uint8, device="cuda")
-    tl, tt, ts = EventTimer(), EventTimer(), EventTimer()
+    ws = torch.empty(max(dsi.paged_mqa_topk_decode_workspace_bytes(B, nn, maxc, K), 16), dtype=torch.uint8,
+                     device="cuda")
+    ws_sep = torch.empty(max(dsi.topk_workspace_bytes(rows, maxc, K), 16), dtype=torch.uint8, device="cuda")
+    tlt, ts = EventTimer(), EventTimer()
+
+    def decode_topk(i):
+        dsi.paged_mqa_topk_decode(q, w, cl, pools[i % copies], bs, tables[i % copies], maxc, next_n=nn, k=K,
+                                  logits=logits, out=idx, workspace=ws, block_stride_bytes=stride, num_blocks=nb,
+                                  mxfp4=mxfp4)
+
+    def logits_only(i):
+        dsi.paged_mqa_logits_decode(q, w, cl, pools[i % copies], bs, tables[i % copies], maxc, next_n=nn,
+                                    out=logits, block_stride_bytes=stride, num_blocks=nb, mxfp4=mxfp4)
 
     def step(i, timed):
-        p, bt = pools[i % copies], tables[i % copies]
-        s = tl.start() if timed else None
-        dsi.paged_mqa_logits_decode(q, w, cl, p, bs, bt, maxc, next_n=nn, out=logits, block_stride_bytes=stride,
-                                    num_blocks=nb, mxfp4=mxfp4)
+        s = tlt.start() if timed else None
+        decode_topk(i)
         if timed:
-            tl.stop(s)
-            s = tt.start()
-        dsi.topk_select(logits, ends, k=K, out=idx, workspace=ws)
-        if timed:
-            tt.stop(s)
+            tlt.stop(s)
             s = ts.start()
-        dsi.req_index_to_global_slot(idx, bt, bs, bs, row_to_req=r2r, out=slots)
+        dsi.req_index_to_global_slot(idx, tables[i % copies], bs, bs, row_to_req=r2r, out=slots)
         if timed:
             ts.stop(s)
 
@@ -396,20 +401,38 @@ def bench_decode(n, steps, warmup, copies=4, mxfp4=False):
     b.record()
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / steps
-    ms_l, ms_t, ms_s = tl.mean_ms(), tt.mean_ms(), ts.mean_ms()
+    ms_lt, ms_s = tlt.mean_ms(), ts.mean_ms()
+    # breakdown: the logits kernel alone, and the two separate calls (logits, then dsi_topk_select)
+    tl, tsep = EventTimer(), EventTimer()
+    queue_ahead(steps)
+    for i in range(steps):
+        s = tl.start()
+        logits_only(i)
+        tl.stop(s)
+    ms_l = tl.mean_ms()
+    queue_ahead(steps)
+    for i in range(steps):
+        s = tsep.start()
+        logits_only(i)
+        dsi.topk_select(logits, ends, k=K, out=idx, workspace=ws_sep)
+        tsep.stop(s)
+    ms_sep = tsep.mean_ms()
     V = int(ends_np.sum())
     nblk = int(sum((int(L) + bs - 1) // bs for L in lens))
     bytes_logits = row * sumL + 4 * nblk + rows * (64 * 128 + 64 * 2) + 4 * V
     bytes_topk = 4 * V + rows * K * 4
-    gbs = (bytes_logits + bytes_topk) / ((ms_l + ms_t) * 1e-3) / 1e9
+    gbs = (bytes_logits + bytes_topk) / (ms_lt * 1e-3) / 1e9
     cache = ", MXFP4 cache (68 B per token)" if mxfp4 else ""
     return dict(workload=f"paged decode {B} x next_n {nn}, lengths U{{{int(lens.min())}..{int(lens.max())}}}{cache}",
-                rows=rows, sum_tokens=sumL, ms_step=round(ms_step, 4), ms_logits=round(ms_l, 4),
-                ms_topk=round(ms_t, 4), ms_slot=round(ms_s, 4),
+                rows=rows, sum_tokens=sumL, ms_step=round(ms_step, 4), ms_logits_topk=round(ms_lt, 4),
+                ms_logits=round(ms_l, 4), ms_topk=round(ms_lt - ms_l, 4), ms_slot=round(ms_s, 4),
+                ms_separate_calls=round(ms_sep, 4),
                 logits_gbs=round(bytes_logits / (ms_l * 1e-3) / 1e9, 1),
                 logits_topk_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
-                rows_per_s=round(rows / ((ms_l + ms_t) * 1e-3), 1),
-                algorithmic_bytes=bytes_logits + bytes_topk)
+                rows_per_s=round(rows / (ms_lt * 1e-3), 1),
+                algorithmic_bytes=bytes_logits + bytes_topk,
+                timing="ms_logits_topk: dsi_paged_mqa_topk_decode (one call); ms_logits: the logits call alone; "
+                       "ms_topk: their difference; ms_separate_calls: the logits call then dsi_topk_select")
 
 
 # --------------------------------------------------------------------------- prefill K gather

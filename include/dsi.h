@@ -142,6 +142,48 @@ DSI_API int dsi_paged_mqa_logits_decode(const uint8_t* q, const uint16_t* w, int
                                 int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits, int64_t ld,
                                 hipStream_t stream);
 
+/* Workspace bytes dsi_paged_mqa_topk_decode(_mxfp4) needs for these sizes (0 = none). */
+DSI_API size_t dsi_paged_mqa_topk_decode_workspace_bytes(int32_t B, int32_t next_n, int32_t max_context_len,
+                                                         int32_t k);
+
+/*
+ * The decode indexer step in one call: the logits of dsi_paged_mqa_logits_decode
+ * (same arguments, same `logits` output), then their top-k into the index table
+ * main attention reads (P3 data flow 2 and the prefill/decode table: decode scores
+ * the paged cache directly, then keeps the k best positions per query row).  Row
+ * b*next_n+i selects from its own columns [0, min(L - next_n + i + 1,
+ * max_context_len)) with the rules of dsi_topk_select: out[r][0 .. m) holds the
+ * positions of m = min(k, finite values) largest logits in any order, then -1.
+ * With one row per request and rows long enough to be split (more than 16384
+ * columns, fewer than 512 rows), the decode kernel also counts the top-k's
+ * first-digit histograms while it writes the logits, which saves the top-k one
+ * launch and one read of the logits.
+ *   out int32 [B*next_n][out_ld], out_ld >= k; workspace of
+ *   dsi_paged_mqa_topk_decode_workspace_bytes(B, next_n, max_context_len, k)
+ *   bytes, 16-byte aligned, used by this call only.
+ * Errors: those of dsi_paged_mqa_logits_decode; EUNSUPPORTED (k not in 1..2048);
+ * EINVAL (out_ld < k, out NULL); EWORKSPACE; EALIGN (out, workspace).
+ */
+DSI_API int dsi_paged_mqa_topk_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                      const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                      int32_t block_size, int64_t block_stride_bytes, const int32_t* block_table,
+                                      int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits,
+                                      int64_t ld, int32_t k, int32_t* out, int64_t out_ld, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsi_paged_mqa_topk_decode on the MXFP4 cache: the logits of
+ * dsi_paged_mqa_logits_decode_mxfp4 (68-byte rows), then the same top-k.
+ * Errors: as dsi_paged_mqa_topk_decode, with the MXFP4 row stride rules.
+ */
+DSI_API int dsi_paged_mqa_topk_decode_mxfp4(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                            const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                            int32_t block_size, int64_t block_stride_bytes,
+                                            const int32_t* block_table, int64_t bt_ld, int32_t bt_width,
+                                            int32_t max_context_len, float* logits, int64_t ld, int32_t k,
+                                            int32_t* out, int64_t out_ld, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
 /*
  * Workspace bytes dsi_topk_select needs for these sizes (0 = none; pass any
  * pointer or NULL then).

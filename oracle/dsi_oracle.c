@@ -169,7 +169,7 @@ static float logit_one(float qt[ORC_D][ORC_H], const float wf[ORC_H], const uint
  * [0, S) gets -inf. */
 void orc_mqa_logits_gathered(const uint8_t* q, const uint16_t* w, int32_t rows, const uint8_t* k_rows, int32_t S,
                              const int32_t* ks, const int32_t* ke, float* logits, int64_t ld) {
-  static float qt[ORC_D][ORC_H];
+  float qt[ORC_D][ORC_H]; /* 32 KB on the caller's stack: concurrent calls from several threads stay independent */
   float wf[ORC_H];
   int32_t t, s;
   for (t = 0; t < rows; t++) {
@@ -193,7 +193,7 @@ void orc_mqa_logits_gathered(const uint8_t* q, const uint16_t* w, int32_t rows, 
 void orc_mqa_logits_paged(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
                           const uint8_t* pool, int32_t block_size, int64_t block_stride, const int32_t* block_table,
                           int64_t bt_ld, int32_t width, float* logits, int64_t ld) {
-  static float qt[ORC_D][ORC_H];
+  float qt[ORC_D][ORC_H]; /* 32 KB on the caller's stack: concurrent calls from several threads stay independent */
   float wf[ORC_H];
   int32_t b, i, s;
   for (b = 0; b < B; b++) {
@@ -402,7 +402,7 @@ void orc_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_t rows, co
                            int32_t num_sparse_blocks, const int32_t* end, int32_t sparse_block_kv,
                            const uint8_t* k_src, const int32_t* block_table, int64_t bt_ld, const int32_t* row_to_req,
                            int32_t block_size, int64_t block_stride, int32_t out_f32, void* out, int64_t ld) {
-  static float qt[ORC_D][ORC_H];
+  float qt[ORC_D][ORC_H]; /* 32 KB on the caller's stack: concurrent calls from several threads stay independent */
   float wf[ORC_H];
   int32_t r, c, width = num_sparse_blocks * sparse_block_kv;
   for (r = 0; r < rows; r++) {
@@ -688,7 +688,7 @@ void orc_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, int32_t ro
                                  const uint8_t* k_src, const int32_t* block_table, int64_t bt_ld,
                                  const int32_t* row_to_req, int32_t block_size, int64_t block_stride, int32_t out_f32,
                                  void* out, int64_t ld) {
-  static float qt[ORC_D][ORC_H];
+  float qt[ORC_D][ORC_H]; /* 32 KB on the caller's stack: concurrent calls from several threads stay independent */
   float wf[ORC_H], kd[ORC_D];
   int32_t r, c, width = num_sparse_blocks * sparse_block_kv;
   for (r = 0; r < rows; r++) {
@@ -728,7 +728,7 @@ void orc_mqa_logits_paged_mxfp4(const uint8_t* q, const uint16_t* w, int32_t B, 
                                 const int32_t* context_lens, const uint8_t* pool, int32_t block_size,
                                 int64_t block_stride, const int32_t* block_table, int64_t bt_ld, int32_t width,
                                 float* logits, int64_t ld) {
-  static float qt[ORC_D][ORC_H];
+  float qt[ORC_D][ORC_H]; /* 32 KB on the caller's stack: concurrent calls from several threads stay independent */
   float wf[ORC_H], kd[ORC_D];
   int32_t b, i, s;
   for (b = 0; b < B; b++) {

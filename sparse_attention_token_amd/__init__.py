@@ -40,6 +40,11 @@ _SIGNATURES = {
     "dsi_paged_mqa_logits_decode_mxfp4": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i64, _i32, _i64, _p, _i64,
                                                          _i32, _i32, _p, _i64, _p]),
     "dsi_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "dsi_paged_mqa_topk_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "dsi_paged_mqa_topk_decode": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i64, _i32, _i64, _p, _i64, _i32, _i32,
+                                                 _p, _i64, _i32, _p, _i64, _p, _sz, _p]),
+    "dsi_paged_mqa_topk_decode_mxfp4": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i64, _i32, _i64, _p, _i64, _i32,
+                                                       _i32, _p, _i64, _i32, _p, _i64, _p, _sz, _p]),
     "dsi_topk_select": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _i32, _p, _i64, _p, _sz, _p]),
     "dsi_topk_select_noalloc": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _i32, _p, _i64, _p]),
     "dsi_expand_candidates": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _p, _i64, _i32, _i32, _p, _i64, _p,
@@ -200,6 +205,51 @@ def paged_mqa_logits_decode(q, w, context_lens, pool, block_size, block_table, m
                   block_stride_bytes, _ptr(block_table), bt_ld, bt_width, max_context_len, _ptr(out), ld, _stream(q)),
                "paged_mqa_logits_decode_mxfp4" if mxfp4 else "paged_mqa_logits_decode")
     return out
+
+
+def paged_mqa_topk_decode_workspace_bytes(B, next_n, max_context_len, k=MAX_TOPK):
+    return lib().dsi_paged_mqa_topk_decode_workspace_bytes(B, next_n, max_context_len, k)
+
+
+def paged_mqa_topk_decode(q, w, context_lens, pool, block_size, block_table, max_context_len, next_n=1, k=MAX_TOPK,
+                          logits=None, out=None, workspace=None, block_stride_bytes=None, num_blocks=None,
+                          bt_width=None, mxfp4=False):
+    """The decode step in one call: logits straight from the paged pool (fp32 [B*next_n, >=max_context_len]) and
+    their top-k (int32 [B*next_n, k], request-local positions, -1 padded).  Returns (logits, out)."""
+    dev = _dev(q, w, context_lens, pool, block_table, logits, out, workspace)
+    _need(q, (torch.uint8,), "q", 3)
+    _need(w, _BF16, "w", 2)
+    _need(context_lens, _I32, "context_lens")
+    _need(block_table, _I32, "block_table")
+    for t, nm in ((q, "q"), (w, "w"), (context_lens, "context_lens"), (pool, "pool")):
+        _contig(t, nm)
+    B = context_lens.shape[0]
+    if block_stride_bytes is None:
+        block_stride_bytes = pool.stride(0) if pool.dim() > 1 else block_size * (ROW_BYTES_MXFP4 if mxfp4 else ROW_BYTES)
+    if num_blocks is None:
+        num_blocks = pool.numel() // block_stride_bytes
+    bt_ld = _rows(block_table, "block_table")
+    if bt_width is None:
+        bt_width = block_table.shape[1]
+    if logits is None:
+        logits = torch.empty((B * next_n, max_context_len), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B * next_n, k), dtype=torch.int32, device=dev)
+    _need(logits, (torch.float32,), "logits")
+    _need(out, _I32, "out")
+    need = paged_mqa_topk_decode_workspace_bytes(B, next_n, max_context_len, k)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    fn = lib().dsi_paged_mqa_topk_decode_mxfp4 if mxfp4 else lib().dsi_paged_mqa_topk_decode
+    with torch.cuda.device(dev):
+        _check(fn(_ptr(q), _ptr(w), B, next_n, _ptr(context_lens), _ptr(pool), num_blocks, block_size,
+                  block_stride_bytes, _ptr(block_table), bt_ld, bt_width, max_context_len, _ptr(logits),
+                  _rows(logits, "logits"), k, _ptr(out), _rows(out, "out"), ws_ptr, ws_bytes, _stream(q)),
+               "paged_mqa_topk_decode_mxfp4" if mxfp4 else "paged_mqa_topk_decode")
+    return logits, out
 
 
 def topk_workspace_bytes(rows, max_width, k):

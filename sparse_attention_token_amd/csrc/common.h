@@ -102,6 +102,32 @@ __device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
   return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 2^(E-127) as an fp32 (E = 0 gives the subnormal 2^-127): an MXFP4 block's E8M0 scale.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
+
+// Eight FP4 E2M1 codes (one dword, element 2i in the low nibble of byte i) times `scale` -> bf16 on the
+// hardware converter (v_cvt_scalef32_pk_bf16_fp4): exact for every code and every scale 2^(E-127) with E <= 252
+// (checked on the device over all of them).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t x, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E4M3 codes (two dwords) -> bf16, exact (v_cvt_scalef32_pk_bf16_fp8 at scale 1).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Eight codes (two dwords) -> one f16x8 operand.
 __device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t x0, uint32_t x1) {
   const uint2 a = e4m3x4_to_f16x4(x0), b = e4m3x4_to_f16x4(x1);

@@ -14,6 +14,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "topk_split.h"
 
 namespace dsi {
 namespace {
@@ -216,32 +217,8 @@ constexpr int kMxLds = 80;                          // LDS bytes per key
 constexpr int kMxBuf = kDcChunk * kMxLds;           // 20480
 constexpr int kMxSlabsPerWave = kMxBuf / 1024 / 4;  // 5 DMA instructions per wavefront per chunk
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// 2^(E-127) as an fp32 (E = 0 gives the subnormal 2^-127).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
-
-// Eight FP4 codes (one dword, element 2i in the low nibble of byte i) times `scale` -> bf16.
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t x, float scale) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// Eight E4M3 codes (two dwords) -> bf16, exact.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t x0, uint32_t x1) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // q[row] as bf16 A fragments (load_q32's layout).
@@ -351,13 +328,23 @@ constexpr int kDcMaxReqs = 1024;
 
 // MX selects the cache format: false = 132-byte FP8 rows (f16 matrix cores, per-key fp32
 // scale), true = 68-byte MXFP4 rows (bf16 matrix cores, block scales applied in decoding).
-template <int WPR, int NB, bool MX>
+// HIST (persistent, one row per request): the kernel also counts the first-digit histogram of
+// the top-k's split path (topk_split.h) for every request it scores, in LDS as bin pairs, and
+// writes it to slot blockIdx.x + b when it leaves request b.  The workgroups taking a
+// request's chunks are consecutive and every share is non-empty, so the request's slots are
+// consecutive too and no two (workgroup, request) pairs share one: the workgroup holding the
+// request's first chunk records the first slot (and clears the request's counters), the one
+// holding its last chunk the last slot.  A share is at most 255 chunks (the host sizes the
+// grid), so a slot's bin counts fit in 16 bits.
+template <int WPR, int NB, bool MX, bool HIST>
 __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int B, int next_n,
     const int* __restrict__ context_lens, const uint8_t* __restrict__ pool, int64_t num_blocks, int block_size,
     int64_t block_stride, const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int max_ctx,
-    float* __restrict__ logits, int64_t ld, int persistent) {
+    float* __restrict__ logits, int64_t ld, int persistent, void* ws, int64_t num_slots) {
   static_assert(!MX || NB == 2, "the MXFP4 ring's waits assume two buffers");
+  static_assert(!HIST || WPR == 4, "histograms are counted for one row per request");
+  if constexpr (HIST) persistent = 1;  // a compile-time fact here: the per-request grid's code is dropped
   constexpr int kKeysPerWave = kDcChunk / WPR;
   constexpr int kGroups = kKeysPerWave / 32;
   constexpr int kStores = kKeysPerWave / 64;
@@ -365,17 +352,32 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   constexpr int kLdsRow = MX ? kMxLds : kDcRow;  // bytes per key in LDS
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][MX ? kMxBuf : kDcBuf];
   __shared__ int64_t s_base[kDcSegs];
+  __shared__ uint32_t s_hist[HIST ? kSlotWords : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool has_pool = num_blocks > 0;
   auto chunks_of = [&](int L) { return (min(max(L, 0), max_ctx) + kDcChunk - 1) / kDcChunk; };
+  if constexpr (HIST)
+    for (int j = tid; j < kSlotWords; j += 256) s_hist[j] = 0u;  // ordered before use by run()'s first barrier
 
   // Score chunks [c_first, c_end) (at most kDcJob) of request b.
   auto run = [&](int b, int c_first, int c_end) {
   const int L = context_lens[b];
   const int Lc = min(L, max_ctx);  // the last row of the request sees [0, L)
   __syncthreads();  // the previous segment's buffers and segment bases are no longer read
+  if constexpr (HIST) {
+    if (tid == 0) {
+      int* meta = split_ws(ws, B, num_slots).meta + (int64_t)b * kMetaInts;
+      const int slot = (int)blockIdx.x + b;
+      if (c_first == 0) {
+        meta[kMetaFirst] = slot;
+        meta[kMetaCntGt] = 0;
+        meta[kMetaCntEq] = 0;
+      }
+      if (c_end == chunks_of(L)) meta[kMetaLast] = slot;
+    }
+  }
 
   // Segment bases of the whole job (-1: absent).
   for (int sg = tid; sg < kDcSegs; sg += 256) {
@@ -450,6 +452,12 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
       const int key = kbase + 64 * h + lane;  // key within the chunk
       const float out = seg[key >> 4] >= 0 ? v * scale : -INFINITY;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_rsrc, (c * kDcChunk + key) * 4, 0, 0);
+      if constexpr (HIST) {  // every column inside the row's range; non-finite values fall in bins the top-k ignores
+        if (c * kDcChunk + key < ke) {
+          const uint32_t bin = f32_first_bin(out);
+          atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1u) << 4));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -480,7 +488,8 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   };  // run
 
   // Persistent: every wavefront finds this workgroup's share from all requests' chunk counts
-  // (lane l holds requests l, l + 64, ...; a running prefix over them), then walks it.
+  // (lane l holds requests l, l + 64, ...; a running prefix over them), then walks it.  With fewer
+  // chunks than workgroups, only the first `total` take one chunk each: no share is empty.
   int b = B, start = 0, g0 = 0, g1 = 0;  // the request holding chunk g0 and its first global chunk
   if (persistent) {
     const int nblk = (B + 63) / 64;  // uniform
@@ -493,8 +502,10 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
       total += v;
     }
-    g0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
-    g1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+    const int nwg = min((int)gridDim.x, total);
+    if ((int)blockIdx.x >= nwg) return;  // uniform: no share
+    g0 = (int)((int64_t)blockIdx.x * total / nwg);
+    g1 = (int)((int64_t)(blockIdx.x + 1) * total / nwg);
     int carry = 0;
     for (int i = 0; i < nblk && b == B; i++) {
       const int r = i * 64 + lane;
@@ -521,10 +532,28 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   b = __builtin_amdgcn_readfirstlane(b);
   int lc = __builtin_amdgcn_readfirstlane(g0 - start);
   int remaining = g1 - g0;
+  int counted = -1;  // HIST: the request whose counts s_hist holds
+  // HIST: write request rb's counts to its slot and clear them (each word by the thread that owns it)
+  auto flush = [&](int rb) {
+    __syncthreads();  // every lane's counts are in
+    uint32_t* dst = split_ws(ws, B, num_slots).slots + ((int64_t)blockIdx.x + rb) * kSlotWords;
+    for (int j = tid; j < kSlotWords; j += 256) {
+      dst[j] = s_hist[j];
+      s_hist[j] = 0u;
+    }
+  };
   while (remaining > 0 && b < B) {  // uniform
     const int cb = __builtin_amdgcn_readfirstlane(chunks_of(context_lens[b]));
     const int len = min(remaining, min(cb - lc, kDcJob));
-    if (len > 0) run(b, lc, lc + len);
+    if (len > 0) {
+      if constexpr (HIST) {
+        if (counted != b) {
+          if (counted >= 0) flush(counted);
+          counted = b;
+        }
+      }
+      run(b, lc, lc + len);
+    }
     remaining -= max(len, 0);
     lc += max(len, 0);
     if (lc >= cb) {
@@ -533,6 +562,8 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
       lc = 0;
     }
   }
+  if constexpr (HIST)
+    if (counted >= 0) flush(counted);
 }
 
 // ------------------------------------------------------------------ sparse columns
@@ -785,12 +816,12 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
 namespace dsi {
 namespace {
 
-// Checks and launch shared by both cache formats (row_bytes: 132 FP8, 68 MXFP4).
+// Checks shared by both cache formats and by the fused top-k calls.
 template <bool MX>
-int paged_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
-                 const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
-                 const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits,
-                 int64_t ld, hipStream_t stream) {
+int paged_decode_check(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
+                       const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                       const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t max_context_len,
+                       float* logits, int64_t ld) {
   if (B < 0 || max_context_len < 0 || ld < max_context_len || num_blocks < 0 || bt_width < 0 || bt_ld < bt_width)
     return DSI_EINVAL;
   if (next_n < 1 || next_n > 4 || block_size < 16 || (block_size % 16) != 0) return DSI_EUNSUPPORTED;
@@ -801,25 +832,121 @@ int paged_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(pool) & 15) ||
       (block_stride_bytes & 15) || (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits) & 3))
     return DSI_EALIGN;
+  return DSI_OK;
+}
+
+// Persistent shares pay off where scoring a chunk is cheap (one row per request: the tail of
+// unequal jobs dominated); with two or more rows per request the per-request grid measured
+// faster.
+bool dc_persistent(int B, int next_n) { return B <= kDcMaxReqs && next_n == 1; }
+
+// Persistent grid: two workgroups per CU, and enough that no share exceeds 255 chunks (the
+// histogram slots count in 16 bits).
+int64_t dc_grid(int B, int64_t max_chunks) {
+  const int64_t all = max_chunks * B;
+  return std::max<int64_t>(1, std::max(std::min<int64_t>(2 * (int64_t)cu_count(), all), (all + 254) / 255));
+}
+
+// Slots the fused call provides: an upper bound of the persistent grid for any device of up to
+// 512 CUs, plus one per request (a workgroup's slots are blockIdx.x + request).
+int64_t dc_num_slots(int B, int64_t max_chunks) {
+  return std::max<int64_t>(1024, (max_chunks * B + 254) / 255) + B;
+}
+
+// The fused call counts the histograms in the decode kernel when the top-k takes the split path
+// and the decode kernel the persistent one.
+bool dc_fused(int B, int next_n, int max_ctx) {
+  return dc_persistent(B, next_n) && split_groups_f32(B * next_n, max_ctx) > 1;
+}
+
+template <bool MX, bool HIST>
+int launch_paged_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
+                        const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                        const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t max_context_len,
+                        float* logits, int64_t ld, void* ws, int64_t num_slots, hipStream_t stream) {
   const int64_t max_chunks = (max_context_len + kDcChunk - 1) / kDcChunk;
-  // Persistent shares pay off where scoring a chunk is cheap (one row per request: the
-  // tail of unequal jobs dominated); with two or more rows per request the per-request
-  // grid measured faster.
-  const bool persistent = B <= kDcMaxReqs && next_n == 1;
+  const bool persistent = dc_persistent(B, next_n);
   dim3 grid;
-  if (persistent) {  // two workgroups per CU, each an equal share of the chunks
-    const int64_t slots = 2 * (int64_t)cu_count();
-    grid = dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, max_chunks * B)));
+  if (persistent) {
+    int64_t g = dc_grid(B, max_chunks);
+    if (HIST) g = std::min<int64_t>(g, num_slots - B);  // the slots bound the grid (never below the 255-chunk floor)
+    grid = dim3((unsigned)g);
   } else {
     grid = dim3((unsigned)((max_chunks + kDcJob - 1) / kDcJob), (unsigned)B);
   }
   const int wpr = next_n == 1 ? 4 : next_n == 2 ? 2 : 1;
   constexpr int kNB = 2;
-  auto k = wpr == 4 ? paged_decode_kernel<4, kNB, MX> : wpr == 2 ? paged_decode_kernel<2, kNB, MX>
-                                                                 : paged_decode_kernel<1, kNB, MX>;
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, q, w, B, next_n, context_lens, pool, num_blocks, block_size,
-                     block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld, (int)persistent);
+  if constexpr (HIST) {
+    hipLaunchKernelGGL((paged_decode_kernel<4, kNB, MX, true>), grid, dim3(256), 0, stream, q, w, B, next_n,
+                       context_lens, pool, num_blocks, block_size, block_stride_bytes, block_table, bt_ld, bt_width,
+                       max_context_len, logits, ld, 1, ws, num_slots);
+  } else {
+    auto k = wpr == 4 ? paged_decode_kernel<4, kNB, MX, false>
+             : wpr == 2 ? paged_decode_kernel<2, kNB, MX, false> : paged_decode_kernel<1, kNB, MX, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                       block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld,
+                       (int)persistent, nullptr, (int64_t)0);
+  }
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+template <bool MX>
+int paged_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
+                 const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                 const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits,
+                 int64_t ld, hipStream_t stream) {
+  const int st = paged_decode_check<MX>(q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                                        block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld);
+  if (st != DSI_OK || B == 0 || max_context_len == 0) return st;
+  return launch_paged_decode<MX, false>(q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                                        block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld,
+                                        nullptr, 0, stream);
+}
+
+size_t paged_topk_ws_bytes(int32_t B, int32_t next_n, int32_t max_context_len, int32_t k) {
+  if (B <= 0 || next_n < 1 || max_context_len <= 0) return 0;
+  if (dc_fused(B, next_n, max_context_len))
+    return split_ws_bytes((int64_t)B * next_n, dc_num_slots(B, (max_context_len + kDcChunk - 1) / kDcChunk));
+  return dsi_topk_workspace_bytes(B * next_n, max_context_len, k);
+}
+
+// Decode logits and their top-k in one call: the decode kernel counts the split top-k's
+// histograms while it writes the logits (when both take those paths), else the plain decode
+// kernel and the top-k of dsi_topk_select, with the rows' ranges taken from the lengths.
+template <bool MX>
+int paged_topk_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n, const int32_t* context_lens,
+                      const uint8_t* pool, int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                      const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t max_context_len,
+                      float* logits, int64_t ld, int32_t k, int32_t* out, int64_t out_ld, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  const int st = paged_decode_check<MX>(q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                                        block_stride_bytes, block_table, bt_ld, bt_width, max_context_len, logits, ld);
+  if (st != DSI_OK) return st;
+  if (k < 1 || k > DSI_MAX_TOPK) return DSI_EUNSUPPORTED;
+  if (out_ld < k) return DSI_EINVAL;
+  const size_t need = paged_topk_ws_bytes(B, next_n, max_context_len, k);
+  if (ws_bytes < need || (need && !ws)) return DSI_EWORKSPACE;
+  if (B == 0) return DSI_OK;
+  if (!out || !context_lens) return DSI_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(out) & 3) || (reinterpret_cast<uintptr_t>(ws) & 15)) return DSI_EALIGN;
+  const int rows = B * next_n;
+  const RowRange range{nullptr, nullptr, context_lens, next_n, max_context_len};
+  if (dc_fused(B, next_n, max_context_len)) {
+    const int64_t slots = dc_num_slots(B, (max_context_len + kDcChunk - 1) / kDcChunk);
+    const int r = launch_paged_decode<MX, true>(q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                                                block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
+                                                logits, ld, ws, slots, stream);
+    if (r != DSI_OK) return r;
+    return launch_split_select(logits, ld, rows, range, k, out, out_ld, ws, slots,
+                               split_groups_f32(rows, max_context_len), stream);
+  }
+  if (max_context_len > 0) {
+    const int r = launch_paged_decode<MX, false>(q, w, B, next_n, context_lens, pool, num_blocks, block_size,
+                                                 block_stride_bytes, block_table, bt_ld, bt_width, max_context_len,
+                                                 logits, ld, nullptr, 0, stream);
+    if (r != DSI_OK) return r;
+  }
+  return topk_dispatch(logits, false, ld, rows, range, max_context_len, k, out, out_ld, ws, stream);
 }
 
 }  // namespace
@@ -842,6 +969,34 @@ extern "C" int dsi_paged_mqa_logits_decode_mxfp4(const uint8_t* q, const uint16_
                                                  hipStream_t stream) {
   return dsi::paged_decode<true>(q, w, B, next_n, context_lens, pool, num_blocks, block_size, block_stride_bytes,
                                  block_table, bt_ld, bt_width, max_context_len, logits, ld, stream);
+}
+
+extern "C" size_t dsi_paged_mqa_topk_decode_workspace_bytes(int32_t B, int32_t next_n, int32_t max_context_len,
+                                                            int32_t k) {
+  return dsi::paged_topk_ws_bytes(B, next_n, max_context_len, k);
+}
+
+extern "C" int dsi_paged_mqa_topk_decode(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                         const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                         int32_t block_size, int64_t block_stride_bytes, const int32_t* block_table,
+                                         int64_t bt_ld, int32_t bt_width, int32_t max_context_len, float* logits,
+                                         int64_t ld, int32_t k, int32_t* out, int64_t out_ld, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  return dsi::paged_topk_decode<false>(q, w, B, next_n, context_lens, pool, num_blocks, block_size, block_stride_bytes,
+                                       block_table, bt_ld, bt_width, max_context_len, logits, ld, k, out, out_ld,
+                                       workspace, workspace_bytes, stream);
+}
+
+extern "C" int dsi_paged_mqa_topk_decode_mxfp4(const uint8_t* q, const uint16_t* w, int32_t B, int32_t next_n,
+                                               const int32_t* context_lens, const uint8_t* pool, int64_t num_blocks,
+                                               int32_t block_size, int64_t block_stride_bytes,
+                                               const int32_t* block_table, int64_t bt_ld, int32_t bt_width,
+                                               int32_t max_context_len, float* logits, int64_t ld, int32_t k,
+                                               int32_t* out, int64_t out_ld, void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream) {
+  return dsi::paged_topk_decode<true>(q, w, B, next_n, context_lens, pool, num_blocks, block_size, block_stride_bytes,
+                                      block_table, bt_ld, bt_width, max_context_len, logits, ld, k, out, out_ld,
+                                      workspace, workspace_bytes, stream);
 }
 
 extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_t rows, const int32_t* row_ks,

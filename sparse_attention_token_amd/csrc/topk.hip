@@ -15,29 +15,31 @@
 //     those candidates, digit by digit (by passes over the row when the boundary bin
 //     outgrows LDS).  Output slots are reserved per wavefront (ballot + popcount, one LDS
 //     atomic);
-//   * few long rows are split between up to 16 workgroups per row, in three launches that
+//   * few long rows are split between workgroups of 8192 columns, in three launches that
 //     communicate through the caller's workspace: per-slice histograms; then every slice
-//     sums its row's histograms, finds the boundary bin and its own output offsets from the
-//     slices before it, writes its columns above the boundary bin from its offset (no
-//     atomics across workgroups) and appends its boundary-bin columns to a per-row
-//     candidate list; one workgroup per row resolves the candidates as above.
+//     sums its row's histograms, finds the boundary bin, writes its columns above it at
+//     positions reserved by one atomic per workgroup and appends its boundary-bin columns to
+//     a per-row candidate list; one workgroup per row resolves the candidates as above.  The
+//     paged decode kernel can count the histograms while it writes the logits, which leaves
+//     two launches (topk_split.h).
 #include <algorithm>
 #include <mutex>
 
 #include "common.h"
+#include "topk_split.h"
 
 namespace dsi {
 namespace {
 
-constexpr int kHistBins = 2048;
+constexpr int kHistBins = kSplitBins;
 constexpr int kShortRow = 16384;  // rows up to this width are held in registers, one workgroup per row
-constexpr int kSplitCap = 12288;  // boundary-bin candidates kept per row when rows are split
-constexpr int kMaxSplit = 16;     // workgroups per row at most
 
 // Workgroup size and the number of boundary-bin candidates kept in LDS.
 // Histograms may keep kCopies lane-interleaved copies of every bin (bin b, copy lane %
-// kCopies at b * kCopies + copy); select_bin sums the copies.  Measured on the indexer
-// workloads, one copy is fastest (more copies cost occupancy and buy nothing).
+// kCopies at b * kCopies + copy); select_bin sums the copies.  One copy where the histogram
+// shares LDS with much else (more copies cost occupancy); two in the split path's slice
+// step, where lanes alternate between them so that neighbouring lanes with equal bins do not
+// collide (measured faster there).
 template <int THREADS, int CAP, int COPIES>
 struct Cfg {
   static constexpr int kThreads = THREADS;
@@ -233,9 +235,9 @@ __device__ __forceinline__ void select_bin(const int* hist, int nb, int need, in
 
 // Columns [a, b) of slice g of G of a row's range [st, en): contiguous, nearly equal.
 __device__ __forceinline__ void slice_range(int st, int en, int g, int G, int& a, int& b) {
-  const int w = (en - st + G - 1) / G;
-  a = min(st + g * w, en);
-  b = min(a + w, en);
+  const int64_t w = ((int64_t)en - st + G - 1) / G;
+  a = (int)min((int64_t)st + g * w, (int64_t)en);
+  b = (int)min((int64_t)a + w, (int64_t)en);
 }
 
 // The boundary bin b1 (top 11 key bits) is known, `above1` columns above it are written
@@ -327,8 +329,7 @@ __device__ __forceinline__ void resolve_boundary(const uint8_t* row, int st, int
 // ---------------------------------------------------------------- one workgroup per row
 template <bool BF16, typename C>
 __global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __restrict__ logits, int64_t row_bytes,
-                                                          const int* __restrict__ row_starts,
-                                                          const int* __restrict__ row_ends, int max_width, int k,
+                                                          RowRange range, int k,
                                                           int* __restrict__ out, int64_t out_ld) {
   using K = Keys<BF16>;
   __shared__ int s_hist[kHistBins * C::kCopies];
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(C::kThreads) void topk_kernel(const uint8_t* __rest
   __shared__ int s_cnt[4];  // 0: written above the boundary, 1: candidates, 2/3: written from candidates
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
+  int st, en;
+  range.get(r, st, en);
   const uint8_t* row = logits + (int64_t)r * row_bytes;
   int* orow = out + (int64_t)r * out_ld;
 
@@ -590,8 +591,7 @@ __device__ __forceinline__ void reserve2(int a, int b, int* ca, int* cb, int lan
 
 template <bool BF16, typename C>
 __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __restrict__ logits, int64_t row_bytes,
-                                                              const int* __restrict__ row_starts,
-                                                              const int* __restrict__ row_ends, int max_width, int k,
+                                                              RowRange range, int k,
                                                               int* __restrict__ out, int64_t out_ld) {
   using K = Keys<BF16>;
   constexpr int T = C::kThreads, E = K::kPerVec, V = C::kVpt, N = V * E;
@@ -610,8 +610,8 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   __shared__ int s_cnt[4];  // 0: written, 3: boundary bin; 1/2: resolution
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
+  int st, en;
+  range.get(r, st, en);
   const uint8_t* row = logits + (int64_t)r * row_bytes;
   int* orow = out + (int64_t)r * out_ld;
 
@@ -777,39 +777,34 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   for (int j = tid; j < k; j += T) orow[j] = j < n ? s_out[j] : -1;
 }
 
-// ---------------------------------------------------------------- long rows split G ways
-// Workspace: per (row, slice) an 11-bit histogram; per row {b1, above1, total, m}; per row
-// up to kSplitCap boundary-bin candidates (key, column).
-using SliceCfg = Cfg<512, 0, 2>;  // two histogram copies in the slice step (measured 26.0 -> 25.6 us)
+// ---------------------------------------------------------------- long rows split between workgroups
+// Few long rows (decode): each row is cut into G slices of at most 8192 fp32 (16384 bf16)
+// columns, one 512-thread workgroup per slice, in up to three launches that communicate through
+// the caller's workspace (layout in topk_split.h):
+//   1. topk_slice_hist_kernel: each slice's first-digit histogram into its slot — skipped when
+//      the paged decode kernel has counted the row's slots while writing its logits;
+//   2. topk_split_select_kernel: every slice holds its columns in registers as keys, sums its
+//      row's slots (the row's histogram, 4 bins per thread), finds the boundary bin b1, and
+//      writes its columns above b1 (every valid column when the row has at most k) at output
+//      positions reserved by one device-scope atomic per workgroup; its boundary-bin columns go
+//      to the row's candidate list the same way;
+//   3. topk_split_resolve_kernel: one workgroup per row resolves the boundary bin from the
+//      candidates (or from the row, when it holds more than the list) and pads with -1.
+// No workgroup waits for another within a launch: the output order is any order, so the only
+// shared state is two counters per row.
+constexpr int kSplitThreads = 512;
+constexpr int kSplitVecs = 4;  // 16-byte vectors per thread: 16 fp32 or 32 bf16 columns
+using SliceCfg = Cfg<kSplitThreads, 0, 2>;  // two histogram copies in the slice step (measured 26.0 -> 25.6 us)
 
-struct SplitWs {
-  int* hist;      // [rows][G][2048]
-  int* meta;      // [rows][4]: b1, above1, total, m
-  uint32_t* key;  // [rows][kSplitCap]
-  int* col;       // [rows][kSplitCap]
-};
-
-__host__ __device__ inline size_t split_ws_bytes(int rows, int G) {
-  return (size_t)rows * G * kHistBins * 4 + (size_t)rows * 16 + (size_t)rows * kSplitCap * 8;
+template <bool BF16>
+constexpr int split_slice_cap() {
+  return kSplitThreads * kSplitVecs * Keys<BF16>::kPerVec;
 }
-
-__device__ __forceinline__ SplitWs split_ws(void* ws, int rows, int G) {
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  SplitWs w;
-  w.hist = reinterpret_cast<int*>(p);
-  p += (size_t)rows * G * kHistBins * 4;
-  w.meta = reinterpret_cast<int*>(p);
-  p += (size_t)rows * 16;
-  w.key = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * kSplitCap * 4;
-  w.col = reinterpret_cast<int*>(p);
-  return w;
-}
+static_assert(split_slice_cap<true>() < 65536, "slot halves count at most 65535 columns");
 
 // Slice workgroups are numbered so that the G slices of a row run on one XCD (workgroups go to the eight XCDs in
-// turn by linear id; row r's resolve workgroup, number r, lands on the same one): the row's slice histograms then
-// meet in that XCD's L2 rather than being fetched into all eight.  Grid: 8 * ceil(rows / 8) * G workgroups; false
-// for the padding.
+// turn by linear id; row r's resolve workgroup, number r, lands on the same one): the row's slots and candidates
+// then meet in that XCD's L2.  Grid: 8 * ceil(rows / 8) * G workgroups; false for the padding.
 __device__ __forceinline__ bool split_coords(int G, int rows, int& r, int& g) {
   const int x = (int)blockIdx.x & 7, q = (int)blockIdx.x >> 3;
   g = q % G;
@@ -819,23 +814,24 @@ __device__ __forceinline__ bool split_coords(int G, int rows, int& r, int& g) {
 
 __host__ inline unsigned split_grid(int rows, int G) { return (unsigned)(8 * ((rows + 7) / 8) * G); }
 
-// Step 1: the 11-bit histogram of each slice.
+// Step 1: the first-digit histogram of each slice into slot r*G + g; slice 0 records the row's slot range and
+// clears its counters.
 template <bool BF16>
-__global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
-    const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
-    const int* __restrict__ row_ends, int max_width, void* ws, int rows, int G) {
+__global__ __launch_bounds__(kSplitThreads) void topk_slice_hist_kernel(const uint8_t* __restrict__ logits,
+                                                                       int64_t row_bytes, RowRange range, void* ws,
+                                                                       int rows, int G) {
   using K = Keys<BF16>;
   constexpr int kC = SliceCfg::kCopies;
   __shared__ int s_hist[kHistBins * kC];
   const int tid = threadIdx.x, lane = tid & 63;
   int r, g;
   if (!split_coords(G, rows, r, g)) return;
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
+  int st, en;
+  range.get(r, st, en);
   int a, b;
   slice_range(st, en, g, G, a, b);
-  RowReader<BF16, SliceCfg::kThreads> rd(logits + (int64_t)r * row_bytes, a, b, tid);
-  for (int i = tid; i < kHistBins * kC; i += SliceCfg::kThreads) s_hist[i] = 0;
+  RowReader<BF16, kSplitThreads> rd(logits + (int64_t)r * row_bytes, a, b, tid);
+  for (int i = tid; i < kHistBins * kC; i += kSplitThreads) s_hist[i] = 0;
   __syncthreads();
   rd.run([&](const auto& act, const auto&, const auto& raw) {
     constexpr int n = sizeof(act) / sizeof(act[0]);
@@ -846,139 +842,201 @@ __global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_hist_kernel(
     }
   });
   __syncthreads();
-  int* dst = split_ws(ws, rows, G).hist + ((int64_t)r * G + g) * kHistBins;
-  for (int i = tid; i < kHistBins; i += SliceCfg::kThreads) {
-    int h = 0;
+  const int64_t slots = (int64_t)rows * G;
+  const SplitWs w = split_ws(ws, rows, slots);
+  uint32_t* dst = w.slots + ((int64_t)r * G + g) * kSlotWords;
+  for (int j = tid; j < kSlotWords; j += kSplitThreads) {
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int c = 0; c < kC; c++) h += s_hist[i * kC + c];
-    dst[i] = h;
+    for (int c = 0; c < kC; c++) lo += s_hist[(2 * j) * kC + c], hi += s_hist[(2 * j + 1) * kC + c];
+    dst[j] = lo | (hi << 16);
+  }
+  if (g == 0 && tid == 0) {
+    int* meta = w.meta + (int64_t)r * kMetaInts;
+    meta[kMetaFirst] = r * G;
+    meta[kMetaLast] = r * G + G - 1;
+    meta[kMetaCntGt] = 0;
+    meta[kMetaCntEq] = 0;
   }
 }
 
-// Step 2: every slice sums its row's slice histograms (thread t owns bins [4t, 4t + 4) of every
-// slice, from L2), finds the boundary bin b1, and takes its offsets from the slices before it:
-// the columns they hold above b1, at b1, and valid.  It then writes its columns above the
-// boundary bin from its offset (or, when every valid value is selected, all its valid columns,
-// and the last slice the -1 padding); its boundary-bin columns go to the row's candidate list
-// from its offset.  Slice 0 leaves {b1, above1, total, m} for step 3.  The slice's first loads are issued before
-// the histograms are read.
+// Step 2.  Keys in registers as in topk_reg_kernel (invalid columns and empty slots get key 0, a bin no finite
+// value reaches); per-thread counts, one workgroup prefix sum of both counts packed in a word (a slice's counts
+// stay below 2^16), one atomic per count per workgroup.
 template <bool BF16>
-__global__ __launch_bounds__(SliceCfg::kThreads) void topk_slice_select_kernel(
-    const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
-    const int* __restrict__ row_ends, int max_width, int k, int* __restrict__ out, int64_t out_ld, void* ws, int rows,
-    int G) {
+__global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
+    const uint8_t* __restrict__ logits, int64_t row_bytes, RowRange range, int k, int* __restrict__ out,
+    int64_t out_ld, void* ws, int rows, int64_t num_slots, int G) {
   using K = Keys<BF16>;
-  using C = SliceCfg;
-  constexpr int kT = C::kThreads;
-  static_assert(C::kBinsPerThread == 4, "one int4 of bins per thread and slice");
+  constexpr int T = kSplitThreads, E = K::kPerVec, V = kSplitVecs, N = V * E, W = T / 64;
+  constexpr int kShift = K::kTopShift;
+  constexpr uint32_t kLoBin = 4, kHiBin = kHistBins - 4;  // finite values have bins in [kLoBin, kHiBin)
   __shared__ __attribute__((aligned(16))) int s_hist[kHistBins];
-  __shared__ int s_wave[C::kWaves];
   __shared__ int s_sel[4];
-  __shared__ int s_red[3][C::kWaves];
-  __shared__ int s_cnt[2];
+  __shared__ int s_part[W];
+  __shared__ int s_wsum[W];
+  __shared__ int s_base[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int r, g;
   if (!split_coords(G, rows, r, g)) return;
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
+  int st, en;
+  range.get(r, st, en);
   int a, b;
   slice_range(st, en, g, G, a, b);
-  constexpr int kU = 2;  // 8 fp32 values per thread and round: fewer live ballot masks (measured 27.3 -> 26.0 us)
-  RowReader<BF16, kT, kU> rd(logits + (int64_t)r * row_bytes, a, b, tid);
-  const SplitWs w = split_ws(ws, rows, G);
-  const int* hist = w.hist + (int64_t)r * G * kHistBins;
-  int4 hv[kMaxSplit];
+  if (a >= b) return;  // uniform; an empty row is padded by the resolve step alone
+
+  // this slice's keys: head [a, c0) and tail [c1, b) one element per thread, nvec aligned vectors between
+  const uint8_t* row = logits + (int64_t)r * row_bytes;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + (uintptr_t)a * K::kElemBytes;
+  const int c0 = min(a + (int)(((16 - (addr & 15)) & 15) / K::kElemBytes), b);
+  const int nvec = (b - c0) / E;
+  const int c1 = c0 + nvec * E;
+  const uint4* vec = reinterpret_cast<const uint4*>(row + (size_t)c0 * K::kElemBytes);
+  constexpr int kPack = BF16 ? 2 : 1;
+  uint32_t kk[(N + 2) / kPack];
+  auto key_at = [&](int j) -> uint32_t {
+    if constexpr (BF16)
+      return (j & 1) ? (kk[j >> 1] >> 16) : (kk[j >> 1] & 0xFFFFu);
+    else
+      return kk[j];
+  };
+  auto set_key = [&](int j, uint32_t v) {
+    if constexpr (BF16) {
+      if (j & 1)
+        kk[j >> 1] |= v << 16;
+      else
+        kk[j >> 1] = v;
+    } else {
+      kk[j] = v;
+    }
+  };
+  uint4 x[V];
 #pragma unroll
-  for (int j = 0; j < kMaxSplit; j++)  // all loads in flight
-    hv[j] = j < G ? reinterpret_cast<const int4*>(hist + (int64_t)j * kHistBins)[tid] : int4{0, 0, 0, 0};
-  int4 sum = {0, 0, 0, 0};
+  for (int i = 0; i < V; i++) {
+    const int vi = i * T + tid;
+    x[i] = vi < nvec ? vec[vi] : uint4{0u, 0u, 0u, 0u};
+  }
+  const bool ha = tid < c0 - a, ta = tid < b - c1;
+  const uint32_t hraw = ha ? K::load1(row, a + tid) : 0u, traw = ta ? K::load1(row, c1 + tid) : 0u;
+
+  // the row's histogram: the sum of its slots; thread t owns bins 4t .. 4t+3 (two words of every slot)
+  const SplitWs w = split_ws(ws, rows, num_slots);
+  int* meta = w.meta + (int64_t)r * kMetaInts;
+  const int s_lo = max(meta[kMetaFirst], 0);
+  const int s_hi = (int)min((int64_t)meta[kMetaLast], num_slots - 1);
+  uint32_t h[4] = {0u, 0u, 0u, 0u};
+  {
+    const uint2* sp = reinterpret_cast<const uint2*>(w.slots) + tid;
+    int s = s_lo;
+    for (; s + 4 <= s_hi + 1; s += 4) {  // four slots' loads in flight
+      uint2 y[4];
 #pragma unroll
-  for (int j = 0; j < kMaxSplit; j++) sum.x += hv[j].x, sum.y += hv[j].y, sum.z += hv[j].z, sum.w += hv[j].w;
-  reinterpret_cast<int4*>(s_hist)[tid] = sum;
-  if (tid < 2) s_cnt[tid] = 0;
-  if (tid < 2) s_sel[tid] = 0;  // stays 0 (an in-range bin) when every valid value is selected
+      for (int u = 0; u < 4; u++) y[u] = sp[(int64_t)(s + u) * (kSlotWords / 2)];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        h[0] += y[u].x & 0xFFFFu, h[1] += y[u].x >> 16, h[2] += y[u].y & 0xFFFFu, h[3] += y[u].y >> 16;
+      }
+    }
+    for (; s <= s_hi; s++) {
+      const uint2 y = sp[(int64_t)s * (kSlotWords / 2)];
+      h[0] += y.x & 0xFFFFu, h[1] += y.x >> 16, h[2] += y.y & 0xFFFFu, h[3] += y.y >> 16;
+    }
+  }
+  reinterpret_cast<int4*>(s_hist)[tid] = int4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+  if (tid < 4) s_sel[tid] = 0;  // stays 0 when the row has at most k values (no bin is selected)
   __syncthreads();
-  select_bin<C, 1>(s_hist, kHistBins, k, s_wave, s_sel, tid);
-  const uint32_t b1 = (uint32_t)s_sel[0];
+  find_bin_all<W>(s_hist, kLoBin, kHiBin, k, s_part, s_sel, tid);
   const int total = s_sel[2];
-  const bool all = total <= k;
-  // columns of the slices before this one: above b1, at b1, valid
-  int gt = 0, eq = 0, valid = 0;
+  const bool all = total <= k;  // every finite value is selected
+  const uint32_t b1 = all ? 0xFFFFFFFFu : (uint32_t)s_sel[0];
+  const int above1 = all ? total : s_sel[1];
+  const int m = all ? 0 : s_sel[3];
+  const bool collect = !all && m <= kSplitCap;
+  // written: bins in (lo_w, kHiBin)
+  const uint32_t lo_w = all ? kLoBin - 1 : b1;
+  const uint32_t span_w = kHiBin - lo_w - 1;
+
 #pragma unroll
-  for (int j = 0; j < kMaxSplit; j++) {
-    if (j < g) {
-      const int h[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+  for (int i = 0; i < V; i++) {
+    const bool in = i * T + tid < nvec;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const uint32_t bin = (uint32_t)(4 * tid + e);
-        valid += h[e];
-        gt += bin > b1 ? h[e] : 0;
-        eq += bin == b1 ? h[e] : 0;
-      }
+    for (int e = 0; e < E; e++) {
+      uint32_t key;
+      const bool ok = K::key(K::elem(x[i], e), key);
+      set_key(i * E + e, in && ok ? key : 0u);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    gt += __shfl_xor(gt, o);
-    eq += __shfl_xor(eq, o);
-    valid += __shfl_xor(valid, o);
+  {
+    uint32_t key;
+    const bool hok = K::key(hraw, key);
+    set_key(N, ha && hok ? key : 0u);
+    const uint32_t hk = key;
+    (void)hk;
+    const bool tok = K::key(traw, key);
+    set_key(N + 1, ta && tok ? key : 0u);
   }
-  if (lane == 0) {
-    s_red[0][wave] = gt;
-    s_red[1][wave] = eq;
-    s_red[2][wave] = valid;
+  // column of kk[j]
+  auto column = [&](int j) { return j < N ? c0 + tid * E + (j / E) * T * E + (j % E) : (j == N ? a + tid : c1 + tid); };
+
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int j = 0; j < N + 2; j++) {
+    const uint32_t d = key_at(j) >> kShift;
+    ngt += (d - lo_w - 1u) < span_w ? 1 : 0;
+    neq += (collect && d == b1) ? 1 : 0;
+  }
+  // workgroup exclusive prefix of both counts, packed (gt << 16 | eq)
+  const int packed = (ngt << 16) | neq;
+  int incl = packed;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, wg_total = 0;
+#pragma unroll
+  for (int q = 0; q < W; q++) {
+    const int t = s_wsum[q];
+    before += q < wave ? t : 0;
+    wg_total += t;
+  }
+  if (tid == 0) {
+    s_base[0] = (wg_total >> 16) ? atomicAdd(&meta[kMetaCntGt], wg_total >> 16) : 0;
+    s_base[1] = (wg_total & 0xFFFF) ? atomicAdd(&meta[kMetaCntEq], wg_total & 0xFFFF) : 0;
+    if (g == 0) {
+      meta[kMetaB1] = (int)b1;
+      meta[kMetaAbove] = above1;
+      meta[kMetaTotal] = total;
+      meta[kMetaM] = m;
+    }
   }
   __syncthreads();
-  int sgt = 0, seq = 0, svalid = 0;
-#pragma unroll
-  for (int q = 0; q < C::kWaves; q++) sgt += s_red[0][q], seq += s_red[1][q], svalid += s_red[2][q];
-  const int out_base = all ? svalid : sgt;
-  const int cand_base = seq;
-  if (g == 0 && tid == 0) {
-    int* meta = w.meta + (int64_t)r * 4;
-    meta[0] = (int)b1;
-    meta[1] = s_sel[1];
-    meta[2] = total;
-    meta[3] = s_hist[b1];
-  }
+  const int excl = before + incl - packed;
+  int pg = s_base[0] + (excl >> 16);
+  int pe = s_base[1] + (excl & 0xFFFF);
   int* orow = out + (int64_t)r * out_ld;
-  uint32_t* ckey = w.key + (int64_t)r * kSplitCap;
-  int* ccol = w.col + (int64_t)r * kSplitCap;
-  rd.run([&](const auto& act, const auto& col, const auto& raw) {
-    constexpr int n = sizeof(act) / sizeof(act[0]);
-    bool gt[n], eq[n];
-    uint32_t keys[n];
-    int pos[n], slot[n];
+  uint32_t* cand = w.cand + (int64_t)r * kSplitCap * 2;
 #pragma unroll
-    for (int i = 0; i < n; i++) {
-      uint32_t key = 0;
-      const bool valid = act[i] && K::key(raw[i], key);
-      const uint32_t d = key >> K::kTopShift;
-      gt[i] = valid && (all || d > b1);
-      eq[i] = valid && !all && d == b1;
-      keys[i] = key;
-    }
-    reserve_batch(gt, &s_cnt[0], lane, pos);
-    reserve_batch(eq, &s_cnt[1], lane, slot);
-#pragma unroll
-    for (int i = 0; i < n; i++) {
-      if (gt[i] && out_base + pos[i] < k) orow[out_base + pos[i]] = col[i] - st;
-      if (eq[i] && cand_base + slot[i] < kSplitCap) {
-        ckey[cand_base + slot[i]] = keys[i];
-        ccol[cand_base + slot[i]] = col[i];
-      }
-    }
-  });
-  if (all && g == G - 1)
-    for (int j = total + tid; j < k; j += kT) orow[j] = -1;
+  for (int j = 0; j < N + 2; j++) {
+    const uint32_t key = key_at(j);
+    const uint32_t d = key >> kShift;
+    const bool gt = (d - lo_w - 1u) < span_w;
+    const bool eq = collect && d == b1;
+    const int col = column(j);
+    if (gt && pg < k) orow[pg] = col - st;
+    if (eq && pe < kSplitCap) *reinterpret_cast<uint2*>(cand + 2 * pe) = uint2{key, (uint32_t)col};
+    pg += gt ? 1 : 0;
+    pe += eq ? 1 : 0;
+  }
 }
 
-// Step 3: one workgroup per row resolves the boundary bin from the candidate list.
+// Step 3: one workgroup per row resolves the boundary bin.
 template <bool BF16>
 __global__ __launch_bounds__(LongRows::kThreads) void topk_split_resolve_kernel(
-    const uint8_t* __restrict__ logits, int64_t row_bytes, const int* __restrict__ row_starts,
-    const int* __restrict__ row_ends, int max_width, int k, int* __restrict__ out, int64_t out_ld, void* ws, int rows,
-    int G) {
+    const uint8_t* __restrict__ logits, int64_t row_bytes, RowRange range, int k, int* __restrict__ out,
+    int64_t out_ld, void* ws, int rows, int64_t num_slots) {
   using C = LongRows;
   static_assert(kSplitCap <= C::kCap, "the candidate list must fit in LDS");
   __shared__ int s_hist[kHistBins * C::kCopies];
@@ -988,45 +1046,125 @@ __global__ __launch_bounds__(LongRows::kThreads) void topk_split_resolve_kernel(
   __shared__ int s_sel[4];
   __shared__ int s_cnt[4];
   const int r = blockIdx.x, tid = threadIdx.x;
-  const SplitWs w = split_ws(ws, rows, G);
-  const int* meta = w.meta + (int64_t)r * 4;
-  const uint32_t b1 = (uint32_t)meta[0];
-  const int above1 = meta[1], total = meta[2], m = meta[3];
-  if (total <= k) return;  // uniform: the slices wrote everything
+  int st, en;
+  range.get(r, st, en);
+  int* orow = out + (int64_t)r * out_ld;
+  if (en <= st) {  // uniform: an empty row
+    for (int j = tid; j < k; j += C::kThreads) orow[j] = -1;
+    return;
+  }
+  const SplitWs w = split_ws(ws, rows, num_slots);
+  const int* meta = w.meta + (int64_t)r * kMetaInts;
+  const uint32_t b1 = (uint32_t)meta[kMetaB1];
+  const int above1 = meta[kMetaAbove], total = meta[kMetaTotal], m = meta[kMetaM];
+  if (total <= k) {  // uniform: the slices wrote every valid column
+    for (int j = max(total, 0) + tid; j < k; j += C::kThreads) orow[j] = -1;
+    return;
+  }
+  const uint32_t* cand = w.cand + (int64_t)r * kSplitCap * 2;
+  if (m <= kSplitCap && m == k - above1) {  // the whole boundary bin is taken
+    for (int i = tid; i < m; i += C::kThreads) orow[above1 + i] = (int)cand[2 * i + 1] - st;
+    return;
+  }
   if (m <= kSplitCap)
     for (int i = tid; i < m; i += C::kThreads) {
-      s_ckey[i] = w.key[(int64_t)r * kSplitCap + i];
-      s_ccol[i] = w.col[(int64_t)r * kSplitCap + i];
+      const uint2 c = reinterpret_cast<const uint2*>(cand)[i];
+      s_ckey[i] = c.x;
+      s_ccol[i] = (int)c.y;
     }
   if (tid < 4) s_cnt[tid] = 0;
   __syncthreads();
-  const int st = row_starts ? max(row_starts[r], 0) : 0;
-  const int en = max(min(row_ends[r], max_width), st);
   resolve_boundary<BF16, C>(logits + (int64_t)r * row_bytes, st, en, k, b1, above1, m, kSplitCap, s_ckey, s_ccol,
-                            s_hist, s_wave, s_sel, s_cnt, out + (int64_t)r * out_ld, tid);
+                            s_hist, s_wave, s_sel, s_cnt, orow, tid);
 }
 
 // Workgroups per row: split long rows when there are too few rows to fill the CUs.
-inline int split_count(int rows, int max_width) {
+inline int split_count(int rows, int max_width, bool bf16) {
   if (max_width <= kShortRow || rows >= 512) return 1;
-  int g = (512 + rows - 1) / rows;
-  g = std::min(g, kMaxSplit);
-  g = std::min(g, (max_width + 8191) / 8192);  // at least ~8K columns per slice
-  return std::max(g, 1);
+  const int cap = bf16 ? split_slice_cap<true>() : split_slice_cap<false>();
+  return (int)(((int64_t)max_width + cap - 1) / cap);
+}
+
+template <bool BF16>
+int launch_select_resolve(const uint8_t* src, int64_t row_bytes, int rows, const RowRange& range, int k, int* out,
+                          int64_t out_ld, void* ws, int64_t num_slots, int G, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_split_select_kernel<BF16>, dim3(split_grid(rows, G)), dim3(kSplitThreads), 0, stream, src,
+                     row_bytes, range, k, out, out_ld, ws, rows, num_slots, G);
+  hipLaunchKernelGGL(topk_split_resolve_kernel<BF16>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream, src,
+                     row_bytes, range, k, out, out_ld, ws, rows, num_slots);
+  return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
 }  // namespace
+}  // namespace dsi
+
+namespace dsi {
+
+int split_groups_f32(int rows, int max_width) { return split_count(rows, max_width, false); }
+
+int launch_split_select(const float* logits, int64_t ld, int rows, const RowRange& range, int k, int* out,
+                        int64_t out_ld, void* ws, int64_t num_slots, int G, hipStream_t stream) {
+  return launch_select_resolve<false>(reinterpret_cast<const uint8_t*>(logits), ld * 4, rows, range, k, out, out_ld,
+                                      ws, num_slots, G, stream);
+}
+
 }  // namespace dsi
 
 extern "C" size_t dsi_topk_workspace_bytes(int32_t rows, int32_t max_width, int32_t k) {
   using namespace dsi;
   (void)k;
   if (rows <= 0 || max_width <= 0) return 0;
-  const int G = split_count(rows, max_width);
-  return G > 1 ? split_ws_bytes(rows, G) : 0;
+  // the larger of the fp32 and bf16 split sizes (the dtype is not an argument)
+  const int G = std::max(split_count(rows, max_width, false), split_count(rows, max_width, true));
+  return G > 1 ? split_ws_bytes(rows, (int64_t)rows * G) : 0;
 }
 
 namespace dsi {
+
+int topk_dispatch(const void* logits, bool bf, int64_t ld, int rows, const RowRange& range, int max_width, int k,
+                  int* out, int64_t out_ld, void* workspace, hipStream_t stream) {
+  const int64_t row_bytes = ld * (bf ? 2 : 4);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(logits);
+  const int G = split_count(rows, max_width, bf);
+  if (G > 1) {
+    const int64_t slots = (int64_t)rows * G;
+    const dim3 grid(split_grid(rows, G));
+    if (bf) {
+      hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(kSplitThreads), 0, stream, src, row_bytes, range,
+                         workspace, rows, G);
+      return launch_select_resolve<true>(src, row_bytes, rows, range, k, out, out_ld, workspace, slots, G, stream);
+    }
+    hipLaunchKernelGGL(topk_slice_hist_kernel<false>, grid, dim3(kSplitThreads), 0, stream, src, row_bytes, range,
+                       workspace, rows, G);
+    return launch_select_resolve<false>(src, row_bytes, rows, range, k, out, out_ld, workspace, slots, G, stream);
+  }
+  const dim3 grid((unsigned)rows);
+#define DSI_TOPK_REG(B, CFG)                                                                                        \
+  hipLaunchKernelGGL((topk_reg_kernel<B, CFG>), grid, dim3(CFG::kThreads), 0, stream, src, row_bytes, range, k, out, \
+                     out_ld)
+  if (!bf) {
+    if (max_width <= reg_capacity<false, RegTiny>())
+      DSI_TOPK_REG(false, RegTiny);
+    else if (max_width <= reg_capacity<false, RegSmall>())
+      DSI_TOPK_REG(false, RegSmall);
+    else if (max_width <= reg_capacity<false, RegMid>())
+      DSI_TOPK_REG(false, RegMid);
+    else
+      hipLaunchKernelGGL((topk_kernel<false, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
+                         range, k, out, out_ld);
+  } else {
+    if (max_width <= reg_capacity<true, RegTiny>())
+      DSI_TOPK_REG(true, RegTiny);
+    else if (max_width <= reg_capacity<true, RegSmall>())
+      DSI_TOPK_REG(true, RegSmall);
+    else
+      hipLaunchKernelGGL((topk_kernel<true, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
+                         range, k, out, out_ld);
+  }
+#undef DSI_TOPK_REG
+  return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
 namespace {
 
 int topk_select_impl(const void* logits, int32_t dtype, int64_t ld, int32_t rows, const int32_t* row_starts,
@@ -1043,54 +1181,8 @@ int topk_select_impl(const void* logits, int32_t dtype, int64_t ld, int32_t rows
   if (dtype == DSI_BF16 && (reinterpret_cast<uintptr_t>(logits) & 1)) return DSI_EALIGN;
   if ((reinterpret_cast<uintptr_t>(out) & 3) || (reinterpret_cast<uintptr_t>(workspace) & 15)) return DSI_EALIGN;
   if (rows > 65535) return DSI_EUNSUPPORTED;
-  const int64_t row_bytes = ld * (dtype == DSI_F32 ? 4 : 2);
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(logits);
-  const int G = split_count(rows, max_width);
-  const bool bf = dtype == DSI_BF16;
-  if (G > 1) {
-    const dim3 grid(split_grid(rows, G));
-    if (bf) {
-      hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
-                         row_starts, row_ends, max_width, workspace, rows, G);
-      hipLaunchKernelGGL(topk_slice_select_kernel<true>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
-                         row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
-      hipLaunchKernelGGL(topk_split_resolve_kernel<true>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
-                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
-    } else {
-      hipLaunchKernelGGL(topk_slice_hist_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
-                         row_starts, row_ends, max_width, workspace, rows, G);
-      hipLaunchKernelGGL(topk_slice_select_kernel<false>, grid, dim3(SliceCfg::kThreads), 0, stream, src, row_bytes,
-                         row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
-      hipLaunchKernelGGL(topk_split_resolve_kernel<false>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream,
-                         src, row_bytes, row_starts, row_ends, max_width, k, out, out_ld, workspace, rows, G);
-    }
-    return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
-  }
-  const dim3 grid((unsigned)rows);
-#define DSI_TOPK_REG(B, CFG)                                                                                        \
-  hipLaunchKernelGGL((topk_reg_kernel<B, CFG>), grid, dim3(CFG::kThreads), 0, stream, src, row_bytes, row_starts, \
-                     row_ends, max_width, k, out, out_ld)
-  if (!bf) {
-    if (max_width <= reg_capacity<false, RegTiny>())
-      DSI_TOPK_REG(false, RegTiny);
-    else if (max_width <= reg_capacity<false, RegSmall>())
-      DSI_TOPK_REG(false, RegSmall);
-    else if (max_width <= reg_capacity<false, RegMid>())
-      DSI_TOPK_REG(false, RegMid);
-    else
-      hipLaunchKernelGGL((topk_kernel<false, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
-                         row_starts, row_ends, max_width, k, out, out_ld);
-  } else {
-    if (max_width <= reg_capacity<true, RegTiny>())
-      DSI_TOPK_REG(true, RegTiny);
-    else if (max_width <= reg_capacity<true, RegSmall>())
-      DSI_TOPK_REG(true, RegSmall);
-    else
-      hipLaunchKernelGGL((topk_kernel<true, LongRows>), grid, dim3(LongRows::kThreads), 0, stream, src, row_bytes,
-                         row_starts, row_ends, max_width, k, out, out_ld);
-  }
-#undef DSI_TOPK_REG
-  return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+  return topk_dispatch(logits, dtype == DSI_BF16, ld, rows, RowRange{row_starts, row_ends, nullptr, 1, max_width},
+                       max_width, k, out, out_ld, workspace, stream);
 }
 
 // ---------------------------------------------------------------- no-allocation variant

@@ -6,6 +6,9 @@ has the oracle's size and every swap is within one tolerance: for a selected g a
 ref[x] - ref[g] <= 1e-3 (1 + max(|ref[x]|, |ref[g]|)).  On bf16 rows each side's half ulp is added, since two
 logits that differ by up to one bf16 ulp can round to the same value and tie.
 """
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
@@ -114,3 +117,12 @@ def paged_pool_oracle(k_bf16, slot_mapping, num_blocks, block_size, block_stride
     pool = np.zeros(num_blocks * block_stride, np.uint8)
     oracle.k_quant_and_cache(k_bf16, slot_mapping, pool, block_size, block_stride)
     return pool
+
+
+def parallel(fn, items, workers=None):
+    """fn(item) for every item on host threads, re-raising the first failure.  The oracle's C calls release the
+    interpreter lock, so its single-threaded instances run side by side (at most 16, the host share of one GPU)."""
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(fn, it) for it in items]:
+            f.result()

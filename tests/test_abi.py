@@ -264,3 +264,41 @@ def test_ceiling_library_exports_and_validation():
     assert L.dsic_stream_read(A16 + 4, 32, 1, A16, None) == EALIGN
     assert L.dsic_copy(A16, A16 + 8, 32, 1, None) == EALIGN
     assert L.dsic_copy(None, A16, 32, 1, None) == EINVAL
+
+
+def test_probe_library_exports_and_validation():
+    from sparse_attention_token_amd import probe
+    src = open(os.path.join(ROOT, "include", "dsi_probe.h")).read()
+    names = sorted(set(re.findall(r"DSI_PROBE_API\s+[\w\s\*]*?\b(dsip_\w+)\s*\(", src)))
+    assert names == sorted(probe.ENTRY_POINTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True, text=True).stdout
+    assert sorted(set(re.findall(r" T (dsip_\w+)", out))) == names
+    L = probe.lib()
+    assert L.dsip_e4m3_encode_changes(0, 0, A16, 4, A16, A16, None) == EINVAL  # n < 1
+    assert L.dsip_e4m3_encode_changes(0xFFFFFFF0, 32, A16, 4, A16, A16, None) == EINVAL  # past 2^32
+    assert L.dsip_e4m3_encode_changes(0, 16, None, 4, A16, A16, None) == EINVAL
+    assert L.dsip_e4m3_decode_all(None, A16, None) == EINVAL
+    assert L.dsip_fp4_decode_all(None, None) == EINVAL
+
+
+def test_decode_topk_call_validation():
+    L = dsi.lib()
+
+    def call(**kw):
+        a = dict(q=A16, w=A16, B=2, next_n=1, cl=A16, pool=A16, nb=10, bs=64, stride=64 * 132, bt=A16, bt_ld=4,
+                 bt_w=4, maxc=256, logits=A16, ld=256, k=2048, out=A16, out_ld=2048, ws=A16, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.dsi_paged_mqa_topk_decode(a["q"], a["w"], a["B"], a["next_n"], a["cl"], a["pool"], a["nb"], a["bs"],
+                                           a["stride"], a["bt"], a["bt_ld"], a["bt_w"], a["maxc"], a["logits"],
+                                           a["ld"], a["k"], a["out"], a["out_ld"], a["ws"], a["ws_bytes"], None)
+    assert call(k=0) == EUNSUP and call(k=2049) == EUNSUP
+    assert call(out_ld=100, k=128) == EINVAL
+    assert call(ld=255) == EINVAL
+    assert call(next_n=5) == EUNSUP
+    assert call(out=None) == EINVAL
+    assert call(out=A16 + 2) == EALIGN
+    assert call(B=8, maxc=40000, ld=40000, ws_bytes=16) == EWS  # the split path needs a workspace
+    assert call(B=0) == 0
+    assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 1, 40000, 2048) > L.dsi_topk_workspace_bytes(8, 40000, 2048)
+    assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 2, 40000, 2048) == L.dsi_topk_workspace_bytes(16, 40000, 2048)
+    assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 1, 4000, 2048) == 0

@@ -14,6 +14,7 @@ from parity_util import (ROW, assert_close, bf16_value, check_selection, dev, ga
                          paged_pool_oracle, tol_bf16)
 
 pytestmark = pytest.mark.gpu
+K = 2048
 
 
 # ----------------------------------------------------------------------------- k quant + cache insert
@@ -720,3 +721,98 @@ def test_decode_mxfp4_bad_page_ids_score_minus_inf():
     keep[0, 16:32] = False
     keep[1, 32:48] = False
     assert_close(got[keep], ref[keep], what="MXFP4 decode logits")
+
+
+# ----------------------------------------------------------------------------- decode logits + top-k in one call
+def _fused_decode_case(seed, lens, next_n, maxc, mxfp4, bad_page_req=None):
+    c = synth.decode_case(seed, B=len(lens), next_n=next_n, lmin=0, lmax=0, block_size=64, lens=lens)
+    bs, nb = c["block_size"], c["num_blocks"]
+    row = 68 if mxfp4 else ROW
+    stride = bs * row
+    quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
+    quant_ref = oracle.k_quant_and_cache_mxfp4 if mxfp4 else oracle.k_quant_and_cache
+    logits_ref = oracle.mqa_logits_paged_mxfp4 if mxfp4 else oracle.mqa_logits_paged
+    pool_ref = np.zeros(nb * stride, np.uint8)
+    quant_ref(c["k"], c["slot_mapping"], pool_ref, bs, stride)
+    bt = c["block_table"].copy()
+    if bad_page_req is not None:  # one page id out of the pool: its 64 tokens score -inf and are never selected
+        bt[bad_page_req, 1] = nb + 5
+    B = len(lens)
+    ref = logits_ref(c["q"], c["w"], next_n, c["context_lens"], pool_ref, bs, stride,
+                     np.where(bt < nb, bt, 0).astype(np.int32), maxc)
+    if bad_page_req is not None:
+        for i in range(next_n):
+            ref[bad_page_req * next_n + i, 64:128] = -np.inf
+    ends = np.minimum(np.maximum(np.repeat(c["context_lens"], next_n) - next_n + np.tile(np.arange(next_n), B) + 1, 0),
+                      maxc).astype(np.int32)
+    return c, pool_ref, bt, ref, ends, stride
+
+
+@pytest.mark.parametrize("mxfp4", [False, True])
+@pytest.mark.parametrize("next_n,lens,maxc", [
+    (1, [0, 1, 100, 2047, 2048, 2049, 17000, 40000, 33333, 5000], 36000),  # split top-k, histograms in the decode kernel
+    (2, [2, 100, 2049, 2050, 20000, 30000], 30000),                        # next-n rows: the top-k counts its own
+])
+def test_decode_topk_call_short_and_long_rows(mxfp4, next_n, lens, maxc):
+    """dsi_paged_mqa_topk_decode: short rows (the -1 rule) mixed with rows long enough for the split top-k, a
+    context longer than max_context_len (clipped) and a page id outside the pool; logits, selection and slot
+    conversion of every row against the oracle, and the selection against the two separate calls."""
+    bad = 7 if next_n == 1 else 4  # a long request
+    c, pool_ref, bt, ref, ends, stride = _fused_decode_case(41 + next_n, lens, next_n, maxc, mxfp4, bad_page_req=bad)
+    bs, nb, B = 64, c["num_blocks"], len(lens)
+    rows = B * next_n
+    pool = dev(pool_ref)
+    q, w, cl, bt_t = dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(bt)
+    logits = torch.full((rows, maxc + 16), 7.0, dtype=torch.float32, device="cuda")
+    ws_bytes = dsi.paged_mqa_topk_decode_workspace_bytes(B, next_n, maxc)
+    ws = torch.full((max(ws_bytes, 16),), 0xA5, dtype=torch.uint8, device="cuda")  # no state carried in the workspace
+    _, idx_t = dsi.paged_mqa_topk_decode(q, w, cl, pool, bs, bt_t, maxc, next_n=next_n, logits=logits, workspace=ws,
+                                         block_stride_bytes=stride, num_blocks=nb, mxfp4=mxfp4)
+    r2r = np.repeat(np.arange(B, dtype=np.int32), next_n)
+    slots = host(dsi.req_index_to_global_slot(idx_t, bt_t, bs, bs, row_to_req=dev(r2r)))
+    got, idx = host(logits), host(idx_t)
+    for r in range(rows):
+        e = int(ends[r])
+        valid = np.isfinite(ref[r])
+        lost = max(0, min(e, 128) - 64) if r // next_n == bad else 0  # tokens 64..127 of the missing page
+        assert valid.sum() == e - lost
+        assert_close(got[r][:maxc][valid], ref[r][valid], what=f"row {r} logits")
+        assert np.all(np.isneginf(got[r][:e][~valid[:e]]))
+        assert np.all(got[r][e:] == 7.0), "columns past the row's range are not written"
+        ref_idx = oracle.topk_select(ref[r:r + 1], ends[r:r + 1], K)[0]
+        check_selection(idx[r], ref_idx, ref[r], end=e)
+        n_valid = int(min(K, valid.sum()))
+        assert np.all(idx[r][:n_valid] >= 0) and np.all(idx[r][n_valid:] == -1)
+    exp = oracle.req_index_to_global_slot(idx, bt, bs, bs, row_to_req=r2r)
+    sel_pages = np.where(idx >= 0, np.take_along_axis(np.repeat(bt, next_n, axis=0), np.maximum(idx, 0) // bs, 1), 0)
+    assert np.all(sel_pages < nb), "a position on the missing page was selected"
+    assert np.array_equal(slots, exp)
+    # the same logits and selections as the two separate calls
+    logits2 = dsi.paged_mqa_logits_decode(q, w, cl, pool, bs, bt_t, maxc, next_n=next_n, block_stride_bytes=stride,
+                                          num_blocks=nb, mxfp4=mxfp4)
+    idx2 = host(dsi.topk_select(logits2, dev(ends), k=K))
+    g2 = host(logits2)
+    for r in range(rows):
+        e = int(ends[r])
+        assert np.array_equal(g2[r][:e], got[r][:e])
+        a, b = idx[r][idx[r] >= 0], idx2[r][idx2[r] >= 0]
+        assert np.array_equal(np.sort(got[r][a]), np.sort(got[r][b]))
+
+
+def test_decode_topk_call_ties_and_heavy_boundary():
+    """Every key of a long row equal (one logit value over 40000 columns): the boundary bin holds more columns
+    than the candidate list, so the split top-k resolves it by passes over the row; any 2048 of the tied
+    columns are correct."""
+    lens = [40000, 30000, 3000]
+    c = synth.decode_case(44, B=3, next_n=1, lmin=0, lmax=0, block_size=64, lens=lens)
+    k = np.tile(c["k"][:1], (c["k"].shape[0], 1))  # one k row everywhere: every logit of a row is the same
+    bs, nb, stride = 64, c["num_blocks"], 64 * ROW
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    dsi.k_quant_and_cache(dev(k), dev(c["slot_mapping"]), pool, bs, stride, nb)
+    logits, idx_t = dsi.paged_mqa_topk_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), pool, bs,
+                                              dev(c["block_table"]), 40000)
+    idx, got = host(idx_t), host(logits)
+    for r, L in enumerate(lens):
+        sel = idx[r][idx[r] >= 0]
+        assert sel.size == min(K, L) and np.unique(sel).size == sel.size and sel.max() < L
+        assert np.all(got[r][sel] == got[r][0]) and np.all(got[r][:L] == got[r][0])
