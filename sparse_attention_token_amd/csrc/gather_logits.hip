@@ -374,6 +374,7 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
         meta[kMetaFirst] = slot;
         meta[kMetaCntGt] = 0;
         meta[kMetaCntEq] = 0;
+        meta[kMetaDone] = 0;
       }
       if (c_end == chunks_of(L)) meta[kMetaLast] = slot;
     }

@@ -857,33 +857,64 @@ __global__ __launch_bounds__(kSplitThreads) void topk_slice_hist_kernel(const ui
     meta[kMetaLast] = r * G + G - 1;
     meta[kMetaCntGt] = 0;
     meta[kMetaCntEq] = 0;
+    meta[kMetaDone] = 0;
   }
 }
 
-// Step 2.  Keys in registers as in topk_reg_kernel (invalid columns and empty slots get key 0, a bin no finite
-// value reaches); per-thread counts, one workgroup prefix sum of both counts packed in a word (a slice's counts
-// stay below 2^16), one atomic per count per workgroup.
+// Step 2 (the last).  Keys in registers as in topk_reg_kernel (invalid columns and empty slots get key 0, a bin no
+// finite value reaches); per-thread counts, one workgroup prefix sum of both counts packed in a word (a slice's
+// counts stay below 2^16), one atomic per count per workgroup.  Then the boundary bin: every slice appends its
+// candidates to the row's list with device-scope atomic stores, waits until they have completed, and counts itself
+// done with a device-scope atomic add; the slice that finds itself last (its add returns the count of all the
+// others) reads every candidate back with device-scope atomic loads and resolves them in registers by 7-bit digits.
+// No workgroup waits for another, and no fence writes the caches back: only the candidates and the counters, all
+// accessed with device-scope atomics, cross workgroups.
+constexpr int kCandPerThread = kSplitCap / kSplitThreads;  // 24: the resolving slice holds every candidate
+static_assert(kCandPerThread * kSplitThreads == kSplitCap, "candidates divide over the threads");
+using SplitCfg = Cfg<kSplitThreads, 0, 1>;  // the passes over the row when the boundary bin outgrows the list
+
+// The boundary bin by passes over the row (heavy ties: more columns than the candidate list holds), out of line so
+// that its registers do not burden the common path.
+template <bool BF16>
+__device__ __attribute__((noinline)) void split_resolve_by_row(const uint8_t* row, int st, int en, int k, uint32_t b1,
+                                                               int above1, int m, int* s_hist, int* s_part, int* s_sel,
+                                                               int* s_cnt, int* orow, int tid) {
+  resolve_boundary<BF16, SplitCfg>(row, st, en, k, b1, above1, m, 0, nullptr, nullptr, s_hist, s_part, s_sel, s_cnt,
+                                   orow, tid);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
     const uint8_t* __restrict__ logits, int64_t row_bytes, RowRange range, int k, int* __restrict__ out,
-    int64_t out_ld, void* ws, int rows, int64_t num_slots, int G) {
+    int64_t out_ld, void* ws, int rows, int64_t num_slots, int G, int slots_per_row) {
   using K = Keys<BF16>;
   constexpr int T = kSplitThreads, E = K::kPerVec, V = kSplitVecs, N = V * E, W = T / 64;
   constexpr int kShift = K::kTopShift;
   constexpr uint32_t kLoBin = 4, kHiBin = kHistBins - 4;  // finite values have bins in [kLoBin, kHiBin)
+  constexpr int kSlotBatch = 16;                          // slot loads in flight per thread
   __shared__ __attribute__((aligned(16))) int s_hist[kHistBins];
   __shared__ int s_sel[4];
   __shared__ int s_part[W];
   __shared__ int s_wsum[W];
   __shared__ int s_base[2];
+  __shared__ int s_cnt[4];
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int r, g;
   if (!split_coords(G, rows, r, g)) return;
   int st, en;
   range.get(r, st, en);
+  int* orow = out + (int64_t)r * out_ld;
+  if (en <= st) {  // an empty row: slice 0 pads it
+    if (g == 0)
+      for (int j = tid; j < k; j += T) orow[j] = -1;
+    return;
+  }
   int a, b;
   slice_range(st, en, g, G, a, b);
-  if (a >= b) return;  // uniform; an empty row is padded by the resolve step alone
+  if (a >= b) return;  // uniform: a slice past the row's end
+  const int64_t wid = ((int64_t)en - st + G - 1) / G;
+  const int nslices = (int)(((int64_t)en - st + wid - 1) / wid);  // the row's slices that reach the end
 
   // this slice's keys: head [a, c0) and tail [c1, b) one element per thread, nvec aligned vectors between
   const uint8_t* row = logits + (int64_t)r * row_bytes;
@@ -919,31 +950,33 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
   const bool ha = tid < c0 - a, ta = tid < b - c1;
   const uint32_t hraw = ha ? K::load1(row, a + tid) : 0u, traw = ta ? K::load1(row, c1 + tid) : 0u;
 
-  // the row's histogram: the sum of its slots; thread t owns bins 4t .. 4t+3 (two words of every slot)
+  // the row's histogram: the sum of its slots; thread t owns bins 4t .. 4t+3 (two words of every slot); a batch of
+  // slots' loads is issued before any is summed
   const SplitWs w = split_ws(ws, rows, num_slots);
   int* meta = w.meta + (int64_t)r * kMetaInts;
-  const int s_lo = max(meta[kMetaFirst], 0);
-  const int s_hi = (int)min((int64_t)meta[kMetaLast], num_slots - 1);
+  // slots_per_row > 0: row r's slots are r*slots_per_row onwards (known without a load); else its metadata says
+  const int s_lo = slots_per_row ? r * slots_per_row : max(meta[kMetaFirst], 0);
+  const int s_hi = (int)min(slots_per_row ? (int64_t)r * slots_per_row + slots_per_row - 1 : (int64_t)meta[kMetaLast],
+                            num_slots - 1);
   uint32_t h[4] = {0u, 0u, 0u, 0u};
   {
     const uint2* sp = reinterpret_cast<const uint2*>(w.slots) + tid;
-    int s = s_lo;
-    for (; s + 4 <= s_hi + 1; s += 4) {  // four slots' loads in flight
-      uint2 y[4];
+    for (int s0 = s_lo; s0 <= s_hi; s0 += kSlotBatch) {
+      uint2 y[kSlotBatch];
 #pragma unroll
-      for (int u = 0; u < 4; u++) y[u] = sp[(int64_t)(s + u) * (kSlotWords / 2)];
+      for (int u = 0; u < kSlotBatch; u++)
+        y[u] = s0 + u <= s_hi ? sp[(int64_t)(s0 + u) * (kSlotWords / 2)] : uint2{0u, 0u};
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
+      for (int u = 0; u < kSlotBatch; u++) {
         h[0] += y[u].x & 0xFFFFu, h[1] += y[u].x >> 16, h[2] += y[u].y & 0xFFFFu, h[3] += y[u].y >> 16;
       }
     }
-    for (; s <= s_hi; s++) {
-      const uint2 y = sp[(int64_t)s * (kSlotWords / 2)];
-      h[0] += y.x & 0xFFFFu, h[1] += y.x >> 16, h[2] += y.y & 0xFFFFu, h[3] += y.y >> 16;
-    }
   }
   reinterpret_cast<int4*>(s_hist)[tid] = int4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
-  if (tid < 4) s_sel[tid] = 0;  // stays 0 when the row has at most k values (no bin is selected)
+  if (tid < 4) {
+    s_sel[tid] = 0;  // stays 0 when the row has at most k values (no bin is selected)
+    s_cnt[tid] = 0;
+  }
   __syncthreads();
   find_bin_all<W>(s_hist, kLoBin, kHiBin, k, s_part, s_sel, tid);
   const int total = s_sel[2];
@@ -970,8 +1003,6 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
     uint32_t key;
     const bool hok = K::key(hraw, key);
     set_key(N, ha && hok ? key : 0u);
-    const uint32_t hk = key;
-    (void)hk;
     const bool tok = K::key(traw, key);
     set_key(N + 1, ta && tok ? key : 0u);
   }
@@ -1005,19 +1036,14 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
   if (tid == 0) {
     s_base[0] = (wg_total >> 16) ? atomicAdd(&meta[kMetaCntGt], wg_total >> 16) : 0;
     s_base[1] = (wg_total & 0xFFFF) ? atomicAdd(&meta[kMetaCntEq], wg_total & 0xFFFF) : 0;
-    if (g == 0) {
-      meta[kMetaB1] = (int)b1;
-      meta[kMetaAbove] = above1;
-      meta[kMetaTotal] = total;
-      meta[kMetaM] = m;
-    }
   }
   __syncthreads();
   const int excl = before + incl - packed;
   int pg = s_base[0] + (excl >> 16);
   int pe = s_base[1] + (excl & 0xFFFF);
-  int* orow = out + (int64_t)r * out_ld;
-  uint32_t* cand = w.cand + (int64_t)r * kSplitCap * 2;
+  unsigned long long* cand = w.cand + (int64_t)r * kSplitCap;
+  // Candidates go to the row's list as device-scope atomic stores (written through to the point where every XCD
+  // sees them); the wait below covers their completion before the slice counts itself done.
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
     const uint32_t key = key_at(j);
@@ -1026,56 +1052,85 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
     const bool eq = collect && d == b1;
     const int col = column(j);
     if (gt && pg < k) orow[pg] = col - st;
-    if (eq && pe < kSplitCap) *reinterpret_cast<uint2*>(cand + 2 * pe) = uint2{key, (uint32_t)col};
+    if (eq && pe < kSplitCap)
+      __hip_atomic_store(cand + pe, ((unsigned long long)(uint32_t)col << 32) | key, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     pg += gt ? 1 : 0;
     pe += eq ? 1 : 0;
+    __builtin_amdgcn_sched_barrier(0);  // one element at a time: no lane masks kept for later elements
   }
-}
-
-// Step 3: one workgroup per row resolves the boundary bin.
-template <bool BF16>
-__global__ __launch_bounds__(LongRows::kThreads) void topk_split_resolve_kernel(
-    const uint8_t* __restrict__ logits, int64_t row_bytes, RowRange range, int k, int* __restrict__ out,
-    int64_t out_ld, void* ws, int rows, int64_t num_slots) {
-  using C = LongRows;
-  static_assert(kSplitCap <= C::kCap, "the candidate list must fit in LDS");
-  __shared__ int s_hist[kHistBins * C::kCopies];
-  __shared__ uint32_t s_ckey[kSplitCap];
-  __shared__ int s_ccol[kSplitCap];
-  __shared__ int s_wave[C::kWaves];
-  __shared__ int s_sel[4];
-  __shared__ int s_cnt[4];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  int st, en;
-  range.get(r, st, en);
-  int* orow = out + (int64_t)r * out_ld;
-  if (en <= st) {  // uniform: an empty row
-    for (int j = tid; j < k; j += C::kThreads) orow[j] = -1;
+  if (all) {  // uniform: nothing to resolve; slice 0 pads the row
+    if (g == 0)
+      for (int j = total + tid; j < k; j += T) orow[j] = -1;
     return;
   }
-  const SplitWs w = split_ws(ws, rows, num_slots);
-  const int* meta = w.meta + (int64_t)r * kMetaInts;
-  const uint32_t b1 = (uint32_t)meta[kMetaB1];
-  const int above1 = meta[kMetaAbove], total = meta[kMetaTotal], m = meta[kMetaM];
-  if (total <= k) {  // uniform: the slices wrote every valid column
-    for (int j = max(total, 0) + tid; j < k; j += C::kThreads) orow[j] = -1;
-    return;
-  }
-  const uint32_t* cand = w.cand + (int64_t)r * kSplitCap * 2;
-  if (m <= kSplitCap && m == k - above1) {  // the whole boundary bin is taken
-    for (int i = tid; i < m; i += C::kThreads) orow[above1 + i] = (int)cand[2 * i + 1] - st;
-    return;
-  }
-  if (m <= kSplitCap)
-    for (int i = tid; i < m; i += C::kThreads) {
-      const uint2 c = reinterpret_cast<const uint2*>(cand)[i];
-      s_ckey[i] = c.x;
-      s_ccol[i] = (int)c.y;
-    }
-  if (tid < 4) s_cnt[tid] = 0;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's candidate stores have completed
   __syncthreads();
-  resolve_boundary<BF16, C>(logits + (int64_t)r * row_bytes, st, en, k, b1, above1, m, kSplitCap, s_ckey, s_ccol,
-                            s_hist, s_wave, s_sel, s_cnt, orow, tid);
+  if (tid == 0) s_last = atomicAdd(&meta[kMetaDone], 1) == nslices - 1;
+  __syncthreads();
+  if (!s_last) return;  // uniform
+
+  // The row's last slice: the boundary bin b1 holds m columns, need = k - above1 of them are selected.
+  const int need = k - above1;
+  if (!collect) {  // more than the list holds (heavy ties): passes over the row
+    split_resolve_by_row<BF16>(row, st, en, k, b1, above1, m, s_hist, s_part, s_sel, s_cnt, orow, tid);
+    return;
+  }
+  uint32_t ck[kCandPerThread];
+  int cc[kCandPerThread];
+  const int nj = (m + T - 1) / T;  // uniform: rounds of candidates that hold any
+#pragma unroll
+  for (int j = 0; j < kCandPerThread; j++) {
+    const int i = tid + j * T;
+    unsigned long long v = 0;
+    if (j < nj && i < m) v = __hip_atomic_load(cand + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ck[j] = (uint32_t)v;  // key 0 (an unused entry) never matches a prefix in bin b1 >= 4
+    cc[j] = (int)(v >> 32);
+  }
+  // Further digits of the key (fp32: three of 7 bits; bf16: 5 bits), each by a histogram over the candidates; when
+  // the bin a digit selects holds exactly the columns still needed, all of it is taken and the lower digits are
+  // skipped ("every key from the bin's lowest up": prefix - 1 as a strict bound, nothing taken at equality).
+  constexpr int kDigits = BF16 ? 1 : 3;
+  constexpr int kSh[3] = {BF16 ? 0 : 14, 7, 0};
+  constexpr int kWd[3] = {BF16 ? 5 : 7, 7, 7};
+  uint32_t prefix = b1 << kShift;
+  int rem = need;
+  bool whole = !BF16 && m == need;
+#pragma unroll
+  for (int p = 0; p < kDigits; p++) {
+    if (whole) break;  // uniform
+    const int sh = kSh[p], nb = 1 << kWd[p], hs = sh + kWd[p];
+    __syncthreads();  // the previous digit's bins are no longer read
+    for (int i = tid; i < nb; i += T) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCandPerThread; j++) {
+      if (j < nj && (ck[j] >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(ck[j] >> sh) & (nb - 1)], 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    find_bin_w0<(BF16 ? 32 : 128)>(s_hist, 0, nb, rem, s_sel, tid);
+    prefix |= (uint32_t)s_sel[0] << sh;
+    rem -= s_sel[1];
+    whole = !BF16 && s_sel[3] == rem;
+  }
+  if (whole) {
+    prefix -= 1;
+    rem = 0;
+  }
+  const int n_above_tau = need - rem;
+#pragma unroll
+  for (int j = 0; j < kCandPerThread; j++) {
+    const uint32_t key = ck[j];
+    if (j >= nj || (key >> kShift) != b1) continue;  // unused entries (j >= nj: uniform)
+    if (key > prefix) {
+      orow[above1 + atomicAdd(&s_cnt[1], 1)] = cc[j] - st;
+    } else if (key == prefix) {
+      const int t = atomicAdd(&s_cnt[2], 1);
+      if (t < rem) orow[above1 + n_above_tau + t] = cc[j] - st;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Workgroups per row: split long rows when there are too few rows to fill the CUs.
@@ -1087,11 +1142,9 @@ inline int split_count(int rows, int max_width, bool bf16) {
 
 template <bool BF16>
 int launch_select_resolve(const uint8_t* src, int64_t row_bytes, int rows, const RowRange& range, int k, int* out,
-                          int64_t out_ld, void* ws, int64_t num_slots, int G, hipStream_t stream) {
+                          int64_t out_ld, void* ws, int64_t num_slots, int G, int slots_per_row, hipStream_t stream) {
   hipLaunchKernelGGL(topk_split_select_kernel<BF16>, dim3(split_grid(rows, G)), dim3(kSplitThreads), 0, stream, src,
-                     row_bytes, range, k, out, out_ld, ws, rows, num_slots, G);
-  hipLaunchKernelGGL(topk_split_resolve_kernel<BF16>, dim3((unsigned)rows), dim3(LongRows::kThreads), 0, stream, src,
-                     row_bytes, range, k, out, out_ld, ws, rows, num_slots);
+                     row_bytes, range, k, out, out_ld, ws, rows, num_slots, G, slots_per_row);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
@@ -1105,7 +1158,7 @@ int split_groups_f32(int rows, int max_width) { return split_count(rows, max_wid
 int launch_split_select(const float* logits, int64_t ld, int rows, const RowRange& range, int k, int* out,
                         int64_t out_ld, void* ws, int64_t num_slots, int G, hipStream_t stream) {
   return launch_select_resolve<false>(reinterpret_cast<const uint8_t*>(logits), ld * 4, rows, range, k, out, out_ld,
-                                      ws, num_slots, G, stream);
+                                      ws, num_slots, G, 0, stream);
 }
 
 }  // namespace dsi
@@ -1132,11 +1185,11 @@ int topk_dispatch(const void* logits, bool bf, int64_t ld, int rows, const RowRa
     if (bf) {
       hipLaunchKernelGGL(topk_slice_hist_kernel<true>, grid, dim3(kSplitThreads), 0, stream, src, row_bytes, range,
                          workspace, rows, G);
-      return launch_select_resolve<true>(src, row_bytes, rows, range, k, out, out_ld, workspace, slots, G, stream);
+      return launch_select_resolve<true>(src, row_bytes, rows, range, k, out, out_ld, workspace, slots, G, G, stream);
     }
     hipLaunchKernelGGL(topk_slice_hist_kernel<false>, grid, dim3(kSplitThreads), 0, stream, src, row_bytes, range,
                        workspace, rows, G);
-    return launch_select_resolve<false>(src, row_bytes, rows, range, k, out, out_ld, workspace, slots, G, stream);
+    return launch_select_resolve<false>(src, row_bytes, rows, range, k, out, out_ld, workspace, slots, G, G, stream);
   }
   const dim3 grid((unsigned)rows);
 #define DSI_TOPK_REG(B, CFG)                                                                                        \

@@ -11,11 +11,12 @@
 // Workspace, from its start (16-byte aligned):
 //   slots  uint32 [num_slots][1024]: slot s holds bins 2j (low half) and 2j+1 (high half) of
 //          word j; a part never exceeds 65535 columns, so the halves never carry;
-//   meta   int32  [rows][8]: 0 first slot, 1 last slot, 2 boundary bin b1, 3 count above it,
-//          4 finite values in the row, 5 count in the boundary bin, 6 columns written so far,
-//          7 boundary-bin candidates collected so far (6 and 7: device-scope atomic counters,
-//          zeroed by the writer of the row's first slot);
-//   cand   uint32 [rows][kSplitCap][2]: the row's boundary-bin (key, column) pairs.
+//   meta   int32  [rows][8]: 0 first slot, 1 last slot, 2 columns written so far, 3 boundary-bin
+//          candidates collected so far, 4 slices done (2..4: device-scope atomic counters, zeroed
+//          by the writer of the row's first slot);
+//   cand   uint64 [rows][kSplitCap]: the row's boundary-bin candidates, key in the low word and
+//          column in the high word, written and read only with device-scope atomics (the row's
+//          last slice to finish reads every slice's candidates at the point of coherence).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,12 +31,12 @@ constexpr int kSlotBytes = kSlotWords * 4;
 constexpr int kSplitCap = 12288;          // boundary-bin candidates kept per row
 constexpr int kMetaInts = 8;
 
-enum SplitMeta { kMetaFirst = 0, kMetaLast, kMetaB1, kMetaAbove, kMetaTotal, kMetaM, kMetaCntGt, kMetaCntEq };
+enum SplitMeta { kMetaFirst = 0, kMetaLast, kMetaCntGt, kMetaCntEq, kMetaDone };
 
 struct SplitWs {
   uint32_t* slots;
   int* meta;
-  uint32_t* cand;
+  unsigned long long* cand;
 };
 
 __host__ __device__ inline size_t split_ws_bytes(int64_t rows, int64_t num_slots) {
@@ -49,7 +50,7 @@ __host__ __device__ inline SplitWs split_ws(void* ws, int64_t rows, int64_t num_
   p += (size_t)num_slots * kSlotBytes;
   w.meta = reinterpret_cast<int*>(p);
   p += (size_t)rows * kMetaInts * 4;
-  w.cand = reinterpret_cast<uint32_t*>(p);
+  w.cand = reinterpret_cast<unsigned long long*>(p);
   return w;
 }
 
@@ -88,8 +89,8 @@ __device__ __forceinline__ uint32_t f32_first_bin(float x) {
 int topk_dispatch(const void* logits, bool bf16, int64_t ld, int rows, const RowRange& range, int max_width, int k,
                   int* out, int64_t out_ld, void* workspace, hipStream_t stream);
 
-// Selection over slots already written (by the paged decode kernel): the select and resolve
-// launches of the split path, on `stream`.  Rows are fp32.  G = workgroups per row.
+// Selection over slots already written (by the paged decode kernel): the split path's selection
+// launch, on `stream`.  Rows are fp32.  G = workgroups per row.
 int launch_split_select(const float* logits, int64_t ld, int rows, const RowRange& range, int k, int* out,
                         int64_t out_ld, void* ws, int64_t num_slots, int G, hipStream_t stream);
 
