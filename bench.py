@@ -522,8 +522,10 @@ def bench_merge(steps, warmup, rows=64, ranks=8):
 
 # --------------------------------------------------------------------------- hierarchical sparse
 def bench_sparse(steps, warmup, c, mxfp4=False):
-    """Workload 5, one step: expansion, sparse logits (decode rows from the paged pool, prefill rows from the
-    gathered chunk), bf16 top-k, remap and slot conversion.  mxfp4: the K cache in 68-byte MXFP4 rows."""
+    """Workload 5, one step: expansion and the columns' schedule (both once per step, shared by every layer), sparse
+    logits from the schedule (decode rows from the paged pool, prefill rows from the gathered chunk), bf16 top-k,
+    remap and slot conversion.  mxfp4: the K cache in 68-byte MXFP4 rows.  The one-shot logits call (no schedule)
+    is timed beside it."""
     sbk, cbs, nd, rows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
     bs, nb = c["block_size"], c["num_blocks"]
     row = ROW_MXFP4 if mxfp4 else ROW
@@ -541,6 +543,7 @@ def bench_sparse(steps, warmup, c, mxfp4=False):
     width = nsb * sbk
     si = torch.empty((rows, nsb), dtype=torch.int32, device="cuda")
     end = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    sched = torch.empty((rows, nsb), dtype=torch.int64, device="cuda")
     out = torch.empty((rows, width), dtype=torch.int16, device="cuda")
     col = torch.empty((rows, K), dtype=torch.int32, device="cuda")
     slots = torch.empty((nd, K), dtype=torch.int32, device="cuda")
@@ -549,12 +552,15 @@ def bench_sparse(steps, warmup, c, mxfp4=False):
     def step(timed):
         s = te.start() if timed else None
         dsi.expand_candidates(cand, ks, ke, cbs, sbk, out=(si, end))
+        dsi.sparse_schedule(ks[:nd], ke[:nd], si[:nd], end[:nd], sbk, pool, block_table=bt, row_to_req=r2r,
+                            block_size=bs, block_stride_bytes=stride, num_k=nb, mxfp4=mxfp4, out=sched[:nd])
+        dsi.sparse_schedule(ks[nd:], ke[nd:], si[nd:], end[nd:], sbk, pre.view(-1), num_k=Lp, mxfp4=mxfp4,
+                            out=sched[nd:])
         if timed:
             te.stop(s)
             s = tl.start()
-        logits_fn(q[:nd], w[:nd], ks[:nd], ke[:nd], si[:nd], end[:nd], sbk, pool, block_table=bt, row_to_req=r2r,
-                  block_size=bs, block_stride_bytes=stride, num_k=nb, out=out[:nd])
-        logits_fn(q[nd:], w[nd:], ks[nd:], ke[nd:], si[nd:], end[nd:], sbk, pre.view(-1), num_k=Lp, out=out[nd:])
+        dsi.sparse_mqa_logits_scheduled(q[:nd], w[:nd], sched[:nd], sbk, pool, out=out[:nd], mxfp4=mxfp4)
+        dsi.sparse_mqa_logits_scheduled(q[nd:], w[nd:], sched[nd:], sbk, pre.view(-1), out=out[nd:], mxfp4=mxfp4)
         if timed:
             tl.stop(s)
             s = tt.start()
@@ -580,12 +586,26 @@ def bench_sparse(steps, warmup, c, mxfp4=False):
     ms_step = a.elapsed_time(b) / steps
     scored = int(host_end(end).sum())
     ms_l = tl.mean_ms()
+    # the one-shot logits calls (columns' sources worked out inside the kernel), for comparison
+    t1 = EventTimer()
+    queue_ahead(steps)
+    for _ in range(steps):
+        s = t1.start()
+        logits_fn(q[:nd], w[:nd], ks[:nd], ke[:nd], si[:nd], end[:nd], sbk, pool, block_table=bt, row_to_req=r2r,
+                  block_size=bs, block_stride_bytes=stride, num_k=nb, out=out[:nd])
+        logits_fn(q[nd:], w[nd:], ks[nd:], ke[nd:], si[nd:], end[nd:], sbk, pre.view(-1), num_k=Lp, out=out[nd:])
+        t1.stop(s)
+    ms_once = t1.mean_ms()
     return dict(workload=f"hierarchical sparse: {nd} decode rows + {rows - nd} prefill rows, {nsb} sparse blocks "
-                         f"of {sbk}, {'MXFP4' if mxfp4 else 'FP8'} K cache ({row} B per token)", rows=rows, ms_step=round(ms_step, 4), ms_expand=round(te.mean_ms(), 4),
-                ms_logits=round(ms_l, 4), ms_topk=round(tt.mean_ms(), 4), ms_remap_slot=round(tr.mean_ms(), 4),
-                scored_pairs=scored, pairs_per_s=round(scored / (ms_step * 1e-3), 1),
+                         f"of {sbk}, {'MXFP4' if mxfp4 else 'FP8'} K cache ({row} B per token)", rows=rows,
+                ms_step=round(ms_step, 4), ms_expand_schedule=round(te.mean_ms(), 4), ms_logits=round(ms_l, 4),
+                ms_logits_one_shot=round(ms_once, 4), ms_topk=round(tt.mean_ms(), 4),
+                ms_remap_slot=round(tr.mean_ms(), 4), scored_pairs=scored,
+                pairs_per_s=round(scored / (ms_step * 1e-3), 1),
                 logits_tflops=round(scored * FLOP_PER_PAIR / (ms_l * 1e-3) / 1e12, 1),
-                effective_gathered_gbs=round(scored * row / (ms_l * 1e-3) / 1e9, 1))
+                effective_gathered_gbs=round(scored * row / (ms_l * 1e-3) / 1e9, 1),
+                timing="expansion and schedule once per step (shared by every layer); ms_logits: the scheduled "
+                       "logits calls of one layer; ms_logits_one_shot: the calls without a schedule")
 
 
 def host_end(t):

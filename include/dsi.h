@@ -286,6 +286,55 @@ DSI_API int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_t r
                           int64_t block_stride_bytes, uint16_t* logits_bf16, int64_t ld, hipStream_t stream);
 
 /*
+ * The per-step schedule of the sparse columns (P1 key source snippets and
+ * implementation breakdown: the row metadata of the sparse logits is computed
+ * once per step and reused by every later consumer layer, as the expansion is;
+ * the layers share the block tables and differ only in their K).  For row r
+ * and sparse block j (tokens tok0 + o, o < sparse_block_kv, tok0 =
+ * sparse_indices[r][j]*sparse_block_kv) one 8-byte entry: the byte offset of
+ * the block's first token's row in the K source divided by 4, and the range
+ * [lo, hi) of o whose columns dsi_sparse_mqa_logits would score (c < end[r],
+ * row_ks[r] <= tok < row_ke[r], tok >= 0, the row inside the source as that
+ * call checks it), packed base | lo << 32 | hi << 40; 0xFFFFFFFF with
+ * lo = hi = 0 when none.  row_bytes: 132 (FP8 rows, for
+ * dsi_sparse_mqa_logits_scheduled) or 68 (MXFP4 rows, for its _mxfp4 form).
+ * Every other argument is that of dsi_sparse_mqa_logits(_mxfp4), with the same
+ * checks and errors.
+ *   schedule uint64 [rows][num_sparse_blocks] (dsi_sparse_schedule_bytes),
+ *   8-byte aligned.
+ */
+DSI_API size_t dsi_sparse_schedule_bytes(int32_t rows, int32_t num_sparse_blocks);
+DSI_API int dsi_sparse_schedule(int32_t rows, const int32_t* row_ks, const int32_t* row_ke,
+                                const int32_t* sparse_indices, int64_t si_ld, int32_t num_sparse_blocks,
+                                const int32_t* end, int32_t sparse_block_kv, int32_t row_bytes, int64_t num_k,
+                                const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t num_reqs,
+                                const int32_t* row_to_req, int32_t block_size, int64_t block_stride_bytes,
+                                uint64_t* schedule, hipStream_t stream);
+
+/*
+ * dsi_sparse_mqa_logits with the columns' sources taken from a schedule
+ * (dsi_sparse_schedule with row_bytes 132): the same bf16 logits, -inf where
+ * the schedule has no valid column.  k_src is the K source (gathered rows or
+ * paged pool, as the schedule was built for) of k_src_bytes bytes; a column
+ * whose row would extend past k_src_bytes scores -inf, so a schedule cannot
+ * lead outside the source.  One schedule serves every layer of a step.
+ * Errors: EINVAL (nulls, rows < 0, num_sparse_blocks < 1, ld too small,
+ * k_src_bytes < 0); EUNSUPPORTED (sparse_block_kv not a power of two in
+ * 8..128, rows > 65535, k_src_bytes >= 2^34); EALIGN (q, k_src 16-byte, w,
+ * schedule 8-byte aligned).
+ */
+DSI_API int dsi_sparse_mqa_logits_scheduled(const uint8_t* q, const uint16_t* w, int32_t rows,
+                                            const uint64_t* schedule, int32_t num_sparse_blocks,
+                                            int32_t sparse_block_kv, const uint8_t* k_src, int64_t k_src_bytes,
+                                            uint16_t* logits_bf16, int64_t ld, hipStream_t stream);
+
+/* dsi_sparse_mqa_logits_scheduled on MXFP4 rows (schedule built with row_bytes 68). */
+DSI_API int dsi_sparse_mqa_logits_scheduled_mxfp4(const uint8_t* q, const uint16_t* w, int32_t rows,
+                                                  const uint64_t* schedule, int32_t num_sparse_blocks,
+                                                  int32_t sparse_block_kv, const uint8_t* k_src, int64_t k_src_bytes,
+                                                  uint16_t* logits_bf16, int64_t ld, hipStream_t stream);
+
+/*
  * Sparse column -> request-local position (P1 implementation breakdown: the
  * compressed-space top-k is mapped back to context positions):
  *   out[r][j] = (sparse_indices[r][c/sbk] - floor(row_ks[r]/sbk))*sbk + c%sbk

@@ -52,6 +52,11 @@ _SIGNATURES = {
     "dsi_sparse_mqa_logits": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p, _i64,
                                              _i32, _i32, _p, _i32, _i64, _p, _i64, _p]),
     "dsi_topk_remap": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i64, _i32, _p, _i32, _p, _i64, _p]),
+    "dsi_sparse_schedule_bytes": (_sz, [_i32, _i32]),
+    "dsi_sparse_schedule": (ctypes.c_int, [_i32, _p, _p, _p, _i64, _i32, _p, _i32, _i32, _i64, _p, _i64, _i32, _i32,
+                                           _p, _i32, _i64, _p, _p]),
+    "dsi_sparse_mqa_logits_scheduled": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _i32, _p, _i64, _p, _i64, _p]),
+    "dsi_sparse_mqa_logits_scheduled_mxfp4": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _i32, _p, _i64, _p, _i64, _p]),
     "dsi_req_index_to_global_slot": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _i32, _p,
                                                     _i64, _p]),
     "dsi_gather_prefill_k": (ctypes.c_int, [_p, _i64, _i32, _i64, _p, _i64, _i32, _p, _i32, _p, _i32, _p]),
@@ -367,6 +372,67 @@ def sparse_mqa_logits(q, w, row_ks, row_ke, sparse_indices, end, sparse_block_kv
                                            si_ld, num_sparse_blocks, _ptr(end), sparse_block_kv, _ptr(k_src), num_k,
                                            _ptr(block_table), bt_ld, bt_width, num_reqs, _ptr(row_to_req), block_size,
                                            block_stride_bytes, _ptr(out), ld, _stream(q)), "sparse_mqa_logits")
+    return out
+
+
+def sparse_schedule(row_ks, row_ke, sparse_indices, end, sparse_block_kv, k_src, block_table=None, row_to_req=None,
+                    block_size=0, block_stride_bytes=None, num_k=None, bt_width=None, num_sparse_blocks=None,
+                    mxfp4=False, out=None):
+    """The per-step schedule of the sparse columns (one uint64 per row and sparse block, as int64 here): built once
+    per step, then passed to sparse_mqa_logits_scheduled for every layer."""
+    dev = _dev(row_ks, row_ke, sparse_indices, end, k_src, block_table, row_to_req, out)
+    row_bytes = ROW_BYTES_MXFP4 if mxfp4 else ROW_BYTES
+    rows = row_ks.shape[0]
+    si_ld = _rows(sparse_indices, "sparse_indices")
+    if num_sparse_blocks is None:
+        num_sparse_blocks = sparse_indices.shape[1]
+    bt_ld, num_reqs = 0, 0
+    if block_table is not None:
+        bt_ld = _rows(block_table, "block_table")
+        num_reqs = block_table.shape[0]
+        if bt_width is None:
+            bt_width = block_table.shape[1]
+        if block_stride_bytes is None:
+            block_stride_bytes = k_src.stride(0) if k_src.dim() > 1 else block_size * row_bytes
+        if num_k is None:
+            num_k = k_src.numel() // block_stride_bytes
+    else:
+        bt_width, block_stride_bytes = 0, 0
+        if num_k is None:
+            num_k = k_src.numel() // row_bytes
+    if out is None:
+        out = torch.empty((rows, num_sparse_blocks), dtype=torch.int64, device=dev)
+    _need(out, (torch.int64,), "schedule")
+    _contig(out, "schedule")
+    for t, nm in ((row_ks, "row_ks"), (row_ke, "row_ke"), (end, "end")):
+        _contig(t, nm)
+    with torch.cuda.device(dev):
+        _check(lib().dsi_sparse_schedule(rows, _ptr(row_ks), _ptr(row_ke), _ptr(sparse_indices), si_ld,
+                                         num_sparse_blocks, _ptr(end), sparse_block_kv, row_bytes, num_k,
+                                         _ptr(block_table), bt_ld, bt_width, num_reqs, _ptr(row_to_req), block_size,
+                                         block_stride_bytes, _ptr(out), _stream(row_ks)), "sparse_schedule")
+    return out
+
+
+def sparse_mqa_logits_scheduled(q, w, schedule, sparse_block_kv, k_src, out=None, mxfp4=False):
+    """bf16 logits on the candidate columns with the columns' sources from a schedule (sparse_schedule); k_src is any
+    K source of the layout the schedule was built for."""
+    dev = _dev(q, w, schedule, k_src, out)
+    _need(q, (torch.uint8,), "q", 3)
+    _need(w, _BF16, "w", 2)
+    _need(schedule, (torch.int64,), "schedule", 2)
+    for t, nm in ((q, "q"), (w, "w"), (schedule, "schedule"), (k_src, "k_src")):
+        _contig(t, nm)
+    rows, nsb = schedule.shape
+    width = nsb * sparse_block_kv
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.int16, device=dev)
+    _need(out, _BF16, "out")
+    fn = lib().dsi_sparse_mqa_logits_scheduled_mxfp4 if mxfp4 else lib().dsi_sparse_mqa_logits_scheduled
+    with torch.cuda.device(dev):
+        _check(fn(_ptr(q), _ptr(w), rows, _ptr(schedule), nsb, sparse_block_kv, _ptr(k_src),
+                  k_src.numel() * k_src.element_size(), _ptr(out), _rows(out, "out"), _stream(q)),
+               "sparse_mqa_logits_scheduled_mxfp4" if mxfp4 else "sparse_mqa_logits_scheduled")
     return out
 
 

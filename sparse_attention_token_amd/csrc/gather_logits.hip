@@ -595,14 +595,70 @@ __device__ __forceinline__ void sp_gather(uint8_t* buf, const uint32_t* key_off,
   });
 }
 
-template <int JOB>
+// Source offsets (4-byte units, kSpAbsent for columns that score -inf) of columns [c0, c0 + n) of row r into s_off,
+// for key rows of ROWB bytes.  With a schedule (one entry per sparse block: the block's base offset, and the first
+// and one-past-last valid column within it; dsi_sparse_schedule), one entry serves all the block's columns and every
+// offset is bounded by the source's size; without one, every column follows its token through sparse_indices and,
+// when paged, the block table.
+template <int ROWB, bool SCHED>
+__device__ __forceinline__ void fill_offsets(uint32_t* s_off, int r, int c0, int n, int tid, int width, int sbk,
+                                             int sbk_shift, const unsigned long long* sched, int nsb, int64_t src_bytes,
+                                             const int* row_ks, const int* row_ke, const int* end,
+                                             const int* sparse_indices, int64_t si_ld, int64_t num_k,
+                                             const int* block_table, int64_t bt_ld, int bt_width, int num_reqs,
+                                             const int* row_to_req, int block_size, int64_t block_stride) {
+  if constexpr (SCHED) {
+    const unsigned long long* srow = sched + (int64_t)r * nsb;
+    for (int t = tid; t < n; t += 256) {
+      const int c = c0 + t;
+      uint32_t off = kSpAbsent;
+      if (c < width) {
+        const unsigned long long e = srow[c >> sbk_shift];
+        const uint32_t base = (uint32_t)e, lo = (uint32_t)(e >> 32) & 0xFFu, hi = (uint32_t)(e >> 40) & 0xFFu;
+        const uint32_t o = (uint32_t)(c & (sbk - 1));
+        if (base != kSpAbsent && o >= lo && o < hi) {
+          const uint32_t x = base + o * (ROWB / 4);
+          if ((uint64_t)x * 4 + ROWB <= (uint64_t)src_bytes) off = x;
+        }
+      }
+      s_off[t] = off;
+    }
+    return;
+  }
+  const bool paged = block_table != nullptr;
+  const int ks = row_ks[r], ke = row_ke[r], e = end[r];
+  const int req = paged ? (row_to_req ? row_to_req[r] : r) : 0;
+  const bool req_ok = !paged || (req >= 0 && req < num_reqs);
+  for (int t = tid; t < n; t += 256) {
+    const int c = c0 + t;
+    uint32_t off = kSpAbsent;
+    if (c < width && c < e) {
+      const int tok = sparse_indices[(int64_t)r * si_ld + (c >> sbk_shift)] * sbk + (c & (sbk - 1));
+      if (tok >= ks && tok < ke && tok >= 0) {
+        if (!paged) {
+          if (tok < num_k) off = (uint32_t)tok * (ROWB / 4);
+        } else {
+          const int blk = tok / block_size;
+          if (req_ok && blk < bt_width) {
+            const int page = block_table[(int64_t)req * bt_ld + blk];
+            if (page >= 0 && page < num_k)
+              off = (uint32_t)(((int64_t)page * block_stride + (int64_t)(tok % block_size) * ROWB) >> 2);
+          }
+        }
+      }
+    }
+    s_off[t] = off;
+  }
+}
+
+template <int JOB, bool SCHED>
 __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
     const int* __restrict__ end, int sbk, const uint8_t* __restrict__ k_src, int64_t num_k,
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
     const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
-    int64_t ld) {
+    int64_t ld, const unsigned long long* __restrict__ sched, int64_t src_bytes) {
   constexpr int NB = 2;
   constexpr int kKeysPerWave = kDcChunk / 4;
   constexpr int kGroups = kKeysPerWave / 32;
@@ -613,7 +669,6 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool has_src = num_k > 0;
-  const bool paged = block_table != nullptr;
   const int sbk_shift = __builtin_ctz(sbk);
   const int nch = (width + kDcChunk - 1) / kDcChunk;
   const int kbase = wave * kKeysPerWave;
@@ -621,29 +676,9 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   // Score chunks [c_first, c_end) (at most JOB) of row r.
   auto run = [&](int r, int c_first, int c_end) {
     __syncthreads();  // the previous segment's buffers and offsets are no longer read
-    const int ks = row_ks[r], ke = row_ke[r], e = end[r];
-    const int req = paged ? (row_to_req ? row_to_req[r] : r) : 0;
-    const bool req_ok = !paged || (req >= 0 && req < num_reqs);
-    for (int t = tid; t < (c_end - c_first) * kDcChunk; t += 256) {
-      const int c = c_first * kDcChunk + t;
-      uint32_t off = kSpAbsent;
-      if (c < width && c < e) {
-        const int tok = sparse_indices[(int64_t)r * si_ld + (c >> sbk_shift)] * sbk + (c & (sbk - 1));
-        if (tok >= ks && tok < ke && tok >= 0) {
-          if (!paged) {
-            if (tok < num_k) off = (uint32_t)tok * (kRow / 4);
-          } else {
-            const int blk = tok / block_size;
-            if (req_ok && blk < bt_width) {
-              const int page = block_table[(int64_t)req * bt_ld + blk];
-              if (page >= 0 && page < num_k)
-                off = (uint32_t)(((int64_t)page * block_stride + (int64_t)(tok % block_size) * kRow) >> 2);
-            }
-          }
-        }
-      }
-      s_off[t] = off;
-    }
+    fill_offsets<kRow, SCHED>(s_off, r, c_first * kDcChunk, (c_end - c_first) * kDcChunk, tid, width, sbk, sbk_shift, sched,
+                       width >> sbk_shift, src_bytes, row_ks, row_ke, end, sparse_indices, si_ld, num_k, block_table,
+                       bt_ld, bt_width, num_reqs, row_to_req, block_size, block_stride);
     Q32 qf;
     W32p wf;
     load_q32(qf, q + (int64_t)r * kHeads * kDim, lane);
@@ -711,14 +746,14 @@ __device__ __forceinline__ void mx_gather(uint8_t* buf, const uint32_t* key_off,
   });
 }
 
-template <int JOB>
+template <int JOB, bool SCHED>
 __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
     const int* __restrict__ end, int sbk, const uint8_t* __restrict__ k_src, int64_t num_k,
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
     const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
-    int64_t ld) {
+    int64_t ld, const unsigned long long* __restrict__ sched, int64_t src_bytes) {
   constexpr int NB = 2;
   constexpr int kKeysPerWave = kDcChunk / 4;
   constexpr int kGroups = kKeysPerWave / 32;
@@ -729,36 +764,15 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool has_src = num_k > 0;
-  const bool paged = block_table != nullptr;
   const int sbk_shift = __builtin_ctz(sbk);
   const int nch = (width + kDcChunk - 1) / kDcChunk;
   const int kbase = wave * kKeysPerWave;
 
   auto run = [&](int r, int c_first, int c_end) {
     __syncthreads();  // the previous segment's buffers and offsets are no longer read
-    const int ks = row_ks[r], ke = row_ke[r], e = end[r];
-    const int req = paged ? (row_to_req ? row_to_req[r] : r) : 0;
-    const bool req_ok = !paged || (req >= 0 && req < num_reqs);
-    for (int t = tid; t < (c_end - c_first) * kDcChunk; t += 256) {
-      const int c = c_first * kDcChunk + t;
-      uint32_t off = kSpAbsent;
-      if (c < width && c < e) {
-        const int tok = sparse_indices[(int64_t)r * si_ld + (c >> sbk_shift)] * sbk + (c & (sbk - 1));
-        if (tok >= ks && tok < ke && tok >= 0) {
-          if (!paged) {
-            if (tok < num_k) off = (uint32_t)tok * (kMxRow / 4);
-          } else {
-            const int blk = tok / block_size;
-            if (req_ok && blk < bt_width) {
-              const int page = block_table[(int64_t)req * bt_ld + blk];
-              if (page >= 0 && page < num_k)
-                off = (uint32_t)(((int64_t)page * block_stride + (int64_t)(tok % block_size) * kMxRow) >> 2);
-            }
-          }
-        }
-      }
-      s_off[t] = off;
-    }
+    fill_offsets<kMxRow, SCHED>(s_off, r, c_first * kDcChunk, (c_end - c_first) * kDcChunk, tid, width, sbk, sbk_shift,
+                         sched, width >> sbk_shift, src_bytes, row_ks, row_ke, end, sparse_indices, si_ld, num_k,
+                         block_table, bt_ld, bt_width, num_reqs, row_to_req, block_size, block_stride);
     Q32b qf;
     W32p wf;
     load_q32_bf16(qf, q + (int64_t)r * kHeads * kDim, lane);
@@ -809,6 +823,40 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
     run(r, lc, lc + len);
     g += len;
   }
+}
+
+// ------------------------------------------------------------------ per-step schedule of the sparse columns
+// One entry per (row, sparse block j): tokens tok0 + o, o < sbk, with tok0 = sparse_indices[r][j]*sbk, lie in one
+// page (the page size is a multiple of sbk) or in one run of gathered rows, so column j*sbk + o reads
+// base + o*ROWB/4 (4-byte units).  Its columns are valid for o in [lo, hi): c < end, ks <= tok < ke, tok >= 0, and
+// the token's row is in the source (gathered: tok < num_k; paged: the request, block index and page id are in
+// range).  An entry packs base | lo << 32 | hi << 40, or kSpAbsent with lo = hi = 0 when no column is valid.
+__global__ __launch_bounds__(256) void sparse_schedule_kernel(
+    int rows, const int* __restrict__ row_ks, const int* __restrict__ row_ke, const int* __restrict__ sparse_indices,
+    int64_t si_ld, int nsb, const int* __restrict__ end, int sbk, int row_bytes, int64_t num_k,
+    const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs, const int* __restrict__ row_to_req,
+    int block_size, int64_t block_stride, unsigned long long* __restrict__ sched) {
+  const int r = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows || j >= nsb) return;
+  const int64_t tok0 = (int64_t)sparse_indices[(int64_t)r * si_ld + j] * sbk;
+  const int64_t lo = std::min<int64_t>(std::max<int64_t>(std::max(row_ks[r], 0) - tok0, 0), sbk);
+  int64_t hi = std::min<int64_t>((int64_t)row_ke[r] - tok0, (int64_t)end[r] - (int64_t)j * sbk);
+  hi = std::max<int64_t>(std::min<int64_t>(hi, sbk), 0);
+  int64_t base = -1;
+  if (block_table == nullptr) {
+    hi = std::max<int64_t>(std::min<int64_t>(hi, num_k - tok0), 0);
+    if (lo < hi) base = tok0 * row_bytes;
+  } else if (lo < hi) {  // then tok0 >= 0
+    const int req = row_to_req ? row_to_req[r] : r;
+    const int64_t blk = tok0 / block_size;
+    if (req >= 0 && req < num_reqs && blk < bt_width) {
+      const int page = block_table[(int64_t)req * bt_ld + blk];
+      if (page >= 0 && page < num_k) base = (int64_t)page * block_stride + (tok0 % block_size) * row_bytes;
+    }
+  }
+  sched[(int64_t)r * nsb + j] = (base >= 0 && lo < hi)
+                                    ? ((uint64_t)(base >> 2) | ((uint64_t)lo << 32) | ((uint64_t)hi << 40))
+                                    : (uint64_t)kSpAbsent;
 }
 
 }  // namespace
@@ -1032,9 +1080,9 @@ extern "C" int dsi_sparse_mqa_logits(const uint8_t* q, const uint16_t* w, int32_
   const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
   const int64_t slots = 2 * (int64_t)cu_count();
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
-  hipLaunchKernelGGL(sparse_logits_kernel<kSpJob>, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
+  hipLaunchKernelGGL((sparse_logits_kernel<kSpJob, false>), grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
                      si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
-                     block_size, block_stride_bytes, logits_bf16, ld);
+                     block_size, block_stride_bytes, logits_bf16, ld, (const unsigned long long*)nullptr, (int64_t)0);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
@@ -1069,8 +1117,101 @@ extern "C" int dsi_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, 
   const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
   const int64_t slots = 2 * (int64_t)cu_count();
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
-  hipLaunchKernelGGL(sparse_logits_mx_kernel<kMxJob>, grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
+  hipLaunchKernelGGL((sparse_logits_mx_kernel<kMxJob, false>), grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
                      si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
-                     block_size, block_stride_bytes, logits_bf16, ld);
+                     block_size, block_stride_bytes, logits_bf16, ld, (const unsigned long long*)nullptr, (int64_t)0);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+extern "C" size_t dsi_sparse_schedule_bytes(int32_t rows, int32_t num_sparse_blocks) {
+  return rows > 0 && num_sparse_blocks > 0 ? (size_t)rows * num_sparse_blocks * 8 : 0;
+}
+
+extern "C" int dsi_sparse_schedule(int32_t rows, const int32_t* row_ks, const int32_t* row_ke,
+                                   const int32_t* sparse_indices, int64_t si_ld, int32_t num_sparse_blocks,
+                                   const int32_t* end, int32_t sparse_block_kv, int32_t row_bytes, int64_t num_k,
+                                   const int32_t* block_table, int64_t bt_ld, int32_t bt_width, int32_t num_reqs,
+                                   const int32_t* row_to_req, int32_t block_size, int64_t block_stride_bytes,
+                                   uint64_t* schedule, hipStream_t stream) {
+  using namespace dsi;
+  const int sbk = sparse_block_kv;
+  if (sbk < 8 || sbk > 128 || (sbk & (sbk - 1))) return DSI_EUNSUPPORTED;
+  if (row_bytes != kRow && row_bytes != kMxRow) return DSI_EUNSUPPORTED;
+  if (rows < 0 || num_sparse_blocks < 1 || si_ld < num_sparse_blocks || num_k < 0) return DSI_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (bt_width < 0 || bt_ld < bt_width || num_reqs < 0) return DSI_EINVAL;
+    if (block_size < 8 || (block_size % sbk) != 0 || (block_size % 8) != 0) return DSI_EUNSUPPORTED;
+    if (block_stride_bytes < (int64_t)block_size * row_bytes) return DSI_EINVAL;
+    if (block_stride_bytes & 15) return DSI_EALIGN;
+  }
+  if (rows == 0) return DSI_OK;
+  if (!row_ks || !row_ke || !sparse_indices || !end || !schedule) return DSI_EINVAL;
+  if (reinterpret_cast<uintptr_t>(schedule) & 7) return DSI_EALIGN;
+  if (rows > 65535) return DSI_EUNSUPPORTED;
+  const int64_t src_bytes = paged ? num_k * block_stride_bytes : num_k * row_bytes;
+  if (src_bytes >= ((int64_t)1 << 34)) return DSI_EUNSUPPORTED;  // offsets are kept in 4-byte units in 32 bits
+  const dim3 grid((unsigned)((num_sparse_blocks + 255) / 256), (unsigned)rows);
+  hipLaunchKernelGGL(sparse_schedule_kernel, grid, dim3(256), 0, stream, rows, row_ks, row_ke, sparse_indices, si_ld,
+                     num_sparse_blocks, end, sbk, row_bytes, num_k, block_table, bt_ld, bt_width, num_reqs,
+                     row_to_req, block_size, block_stride_bytes, reinterpret_cast<unsigned long long*>(schedule));
+  return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+namespace dsi {
+namespace {
+
+template <bool MX>
+int sparse_scheduled(const uint8_t* q, const uint16_t* w, int32_t rows, const uint64_t* schedule,
+                     int32_t num_sparse_blocks, int32_t sparse_block_kv, const uint8_t* k_src, int64_t k_src_bytes,
+                     uint16_t* logits_bf16, int64_t ld, hipStream_t stream) {
+  const int sbk = sparse_block_kv;
+  if (sbk < 8 || sbk > 128 || (sbk & (sbk - 1))) return DSI_EUNSUPPORTED;
+  if (rows < 0 || num_sparse_blocks < 1 || k_src_bytes < 0) return DSI_EINVAL;
+  const int64_t width = (int64_t)num_sparse_blocks * sbk;
+  if (width > 0x7FFFFFFF || ld < width) return DSI_EINVAL;
+  if (rows == 0) return DSI_OK;
+  if (!q || !w || !schedule || !logits_bf16 || (!k_src && k_src_bytes > 0)) return DSI_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k_src) & 15) ||
+      (reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(logits_bf16) & 1) ||
+      (reinterpret_cast<uintptr_t>(schedule) & 7))
+    return DSI_EALIGN;
+  if (rows > 65535) return DSI_EUNSUPPORTED;
+  if (k_src_bytes >= ((int64_t)1 << 34)) return DSI_EUNSUPPORTED;
+  const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
+  const int64_t slots = 2 * (int64_t)cu_count();
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
+  const int64_t has_src = k_src_bytes > 0 ? 1 : 0;  // the kernels gather only when the source has rows
+  const unsigned long long* sched = reinterpret_cast<const unsigned long long*>(schedule);
+  if (MX)
+    hipLaunchKernelGGL((sparse_logits_mx_kernel<kMxJob, true>), grid, dim3(256), 0, stream, q, w, rows, (const int*)nullptr,
+                       (const int*)nullptr, (const int*)nullptr, (int64_t)0, (int)width, (const int*)nullptr, sbk,
+                       k_src, has_src, (const int*)nullptr, (int64_t)0, 0, 0, (const int*)nullptr, 0, (int64_t)0,
+                       logits_bf16, ld, sched, k_src_bytes);
+  else
+    hipLaunchKernelGGL((sparse_logits_kernel<kSpJob, true>), grid, dim3(256), 0, stream, q, w, rows, (const int*)nullptr,
+                       (const int*)nullptr, (const int*)nullptr, (int64_t)0, (int)width, (const int*)nullptr, sbk,
+                       k_src, has_src, (const int*)nullptr, (int64_t)0, 0, 0, (const int*)nullptr, 0, (int64_t)0,
+                       logits_bf16, ld, sched, k_src_bytes);
+  return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
+}
+
+}  // namespace
+}  // namespace dsi
+
+extern "C" int dsi_sparse_mqa_logits_scheduled(const uint8_t* q, const uint16_t* w, int32_t rows,
+                                               const uint64_t* schedule, int32_t num_sparse_blocks,
+                                               int32_t sparse_block_kv, const uint8_t* k_src, int64_t k_src_bytes,
+                                               uint16_t* logits_bf16, int64_t ld, hipStream_t stream) {
+  return dsi::sparse_scheduled<false>(q, w, rows, schedule, num_sparse_blocks, sparse_block_kv, k_src, k_src_bytes,
+                                      logits_bf16, ld, stream);
+}
+
+extern "C" int dsi_sparse_mqa_logits_scheduled_mxfp4(const uint8_t* q, const uint16_t* w, int32_t rows,
+                                                     const uint64_t* schedule, int32_t num_sparse_blocks,
+                                                     int32_t sparse_block_kv, const uint8_t* k_src,
+                                                     int64_t k_src_bytes, uint16_t* logits_bf16, int64_t ld,
+                                                     hipStream_t stream) {
+  return dsi::sparse_scheduled<true>(q, w, rows, schedule, num_sparse_blocks, sparse_block_kv, k_src, k_src_bytes,
+                                     logits_bf16, ld, stream);
 }

@@ -135,7 +135,8 @@ def test_fused_decode_call_graph_replays(mxfp4):
         assert np.array_equal(sl, want), rep
 
 
-def test_hierarchical_step_graph_replays():
+@pytest.mark.parametrize("scheduled", [False, True])
+def test_hierarchical_step_graph_replays(scheduled):
     rng = np.random.default_rng(91)
     T, S, sbk = 64, 6000, 64
     c = synth.prefill_case(92, T=T, S=S, first_pos=S - T)
@@ -151,9 +152,15 @@ def test_hierarchical_step_graph_replays():
     col = torch.empty((T, K), dtype=torch.int32, device="cuda")
     pos = torch.empty((T, K), dtype=torch.int32, device="cuda")
 
+    sched = torch.empty((T, 48), dtype=torch.int64, device="cuda")
+
     def step():
         dsi.expand_candidates(cand_t, ks_t, ke_t, sbk, sbk, out=(si, end))
-        dsi.sparse_mqa_logits(q, w, ks_t, ke_t, si, end, sbk, rows, out=out)
+        if scheduled:  # the per-step schedule, then the logits from it
+            dsi.sparse_schedule(ks_t, ke_t, si, end, sbk, rows, out=sched)
+            dsi.sparse_mqa_logits_scheduled(q, w, sched, sbk, rows, out=out)
+        else:
+            dsi.sparse_mqa_logits(q, w, ks_t, ke_t, si, end, sbk, rows, out=out)
         dsi.topk_select(out, end, k=K, out=col)
         dsi.topk_remap(col, si, ks_t, sbk, out=pos)
 
@@ -177,7 +184,7 @@ def test_hierarchical_step_graph_replays():
     with torch.cuda.graph(g):
         step()
     for rep in range(4):
-        for t in (si, end, out, col, pos):
+        for t in (si, end, out, col, pos, sched):
             t.fill_(-3)
         torch.cuda.synchronize()
         g.replay()

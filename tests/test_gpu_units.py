@@ -816,3 +816,89 @@ def test_decode_topk_call_ties_and_heavy_boundary():
         sel = idx[r][idx[r] >= 0]
         assert sel.size == min(K, L) and np.unique(sel).size == sel.size and sel.max() < L
         assert np.all(got[r][sel] == got[r][0]) and np.all(got[r][:L] == got[r][0])
+
+
+# ----------------------------------------------------------------------------- the per-step sparse schedule
+def _schedule_case(seed, paged, mxfp4, sbk=64, bs=128):
+    """Candidate blocks (duplicates, out-of-range ids, an unaligned start, an empty and a one-token row, a missing
+    page) over K quantized twice (two layers of one step: same layout, different values)."""
+    rng = np.random.default_rng(seed)
+    row = 68 if mxfp4 else ROW
+    quant_ref = oracle.k_quant_and_cache_mxfp4 if mxfp4 else oracle.k_quant_and_cache
+    lens = [3000, 1, 700, 129, 5000, 0, 2048, 4100]
+    R = len(lens)
+    ks = np.zeros(R, np.int32)
+    ks[2] = 3  # an unaligned start: columns before it score -inf
+    ke = np.array(lens, np.int32)
+    maxb = (np.maximum(ke - ks, 0) + sbk - 1) // sbk
+    cand = synth.draw_candidates(rng, np.maximum(maxb, 1), num=12, distinct=8, dup=2)
+    si, end = oracle.expand_candidates(cand, ks, ke, sbk, sbk)
+    if paged:
+        c = synth.decode_case(seed, B=R, next_n=1, lmin=0, lmax=0, block_size=bs, lens=lens)
+        stride, nb = bs * row, c["num_blocks"]
+        bt = c["block_table"].copy()
+        bt[4, 1] = nb + 3  # a page id outside the pool
+        pools = []
+        for layer in range(2):
+            k = synth.draw_k(np.random.default_rng(seed * 10 + layer), int(sum(lens)))
+            pool = np.zeros(nb * stride, np.uint8)
+            quant_ref(k, c["slot_mapping"], pool, bs, stride)
+            pools.append(pool)
+        kw = dict(block_table=bt, row_to_req=np.arange(R, dtype=np.int32), block_size=bs, block_stride=stride)
+        q, w = c["q"], c["w"]
+    else:
+        S = 6000
+        pc = synth.prefill_case(seed, T=R, S=S, first_pos=S - R)
+        pools = []
+        for layer in range(2):
+            k = synth.draw_k(np.random.default_rng(seed * 10 + layer), S)
+            pool = np.zeros(S * row, np.uint8)
+            quant_ref(k, np.arange(S, dtype=np.int64), pool, S, S * row)
+            pools.append(pool)
+        kw = {}
+        q, w = pc["q"], pc["w"]
+    return q, w, ks, ke, si, end, pools, kw, sbk
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("mxfp4", [False, True])
+def test_sparse_schedule_reused_over_two_layers(paged, mxfp4):
+    """One schedule per step, reused by two layers (different K of the same layout): every column of each layer's
+    scheduled logits equals the one-shot call's on that layer's K, bit for bit, and the oracle within tolerance."""
+    q, w, ks, ke, si, end, pools, kw, sbk = _schedule_case(57 + paged + 2 * mxfp4, paged, mxfp4)
+    once = dsi.sparse_mqa_logits_mxfp4 if mxfp4 else dsi.sparse_mqa_logits
+    ref_fn = oracle.sparse_mqa_logits_mxfp4 if mxfp4 else oracle.sparse_mqa_logits
+    args = dict(block_table=dev(kw["block_table"]), row_to_req=dev(kw["row_to_req"]), block_size=kw["block_size"],
+                block_stride_bytes=kw["block_stride"]) if paged else {}
+    ks_t, ke_t, si_t, end_t, q_t, w_t = dev(ks), dev(ke), dev(si), dev(end), dev(q), dev(w)
+    pool0 = dev(pools[0])
+    sched = dsi.sparse_schedule(ks_t, ke_t, si_t, end_t, sbk, pool0, mxfp4=mxfp4, **args)
+    for layer, pool in enumerate(pools):
+        p = dev(pool)
+        got = host(dsi.sparse_mqa_logits_scheduled(q_t, w_t, sched, sbk, p, mxfp4=mxfp4))
+        one = host(once(q_t, w_t, ks_t, ke_t, si_t, end_t, sbk, p, **args))
+        assert np.array_equal(got, one), f"layer {layer}"
+        okw = dict(kw)
+        if paged:
+            okw["block_table"] = np.where(kw["block_table"] < len(pool) // kw["block_stride"], kw["block_table"], 0)
+        ref = ref_fn(q, w, ks, ke, si, end, sbk, pool, out_f32=True, **okw)
+        if paged:  # the missing page's tokens (request 4, block 1) score -inf on the GPU
+            tok = (si[4][:, None] * sbk + np.arange(sbk)[None, :]).reshape(-1)
+            ref[4, (tok // kw["block_size"]) == 1] = -np.inf
+        valid = np.isfinite(ref)
+        assert np.all(got[~valid] == 0xFF80), f"layer {layer}"
+        assert_close(bf16_value(got[valid]), ref[valid], tol_fn=tol_bf16, what=f"layer {layer} scheduled logits")
+
+
+def test_sparse_schedule_bounds_the_source():
+    """A schedule built for a larger source than the one scored: columns whose rows lie past the given source's
+    size score -inf instead of reading outside it."""
+    q, w, ks, ke, si, end, pools, kw, sbk = _schedule_case(61, False, False)
+    sched = dsi.sparse_schedule(dev(ks), dev(ke), dev(si), dev(end), sbk, dev(pools[0]))
+    half = dev(pools[0][: (len(pools[0]) // 2 // ROW) * ROW])  # the first 3000 rows only
+    got = host(dsi.sparse_mqa_logits_scheduled(dev(q), dev(w), sched, sbk, half))
+    full = host(dsi.sparse_mqa_logits_scheduled(dev(q), dev(w), sched, sbk, dev(pools[0])))
+    tok = (si[:, :, None] * sbk + np.arange(sbk)[None, None, :]).reshape(si.shape[0], -1)
+    inside = tok < 3000
+    assert np.array_equal(got[inside], full[inside])
+    assert np.all(got[~inside] == 0xFF80)
