@@ -589,6 +589,16 @@ __device__ __forceinline__ void reserve2(int a, int b, int* ca, int* cb, int lan
   pb = bb + (excl & 0xFFFF);
 }
 
+// The boundary bin by passes over the row (heavy ties: more columns than the LDS list holds), out of line so that
+// its registers do not burden the common path.  s_hist: kHistBins ints.
+template <bool BF16, typename C>
+__device__ __forceinline__ void reg_resolve_by_row(const uint8_t* row, int st, int en, int k, uint32_t b1,
+                                                             int above1, int m, int* s_hist, int* s_wave, int* s_sel,
+                                                             int* s_cnt, int* s_out, int tid) {
+  resolve_boundary<BF16, C>(row, st, en, k, b1, above1, m, 0, nullptr, nullptr, s_hist, s_wave, s_sel, s_cnt, s_out,
+                            tid);
+}
+
 template <bool BF16, typename C>
 __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __restrict__ logits, int64_t row_bytes,
                                                               RowRange range, int k,
@@ -597,14 +607,21 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   constexpr int T = C::kThreads, E = K::kPerVec, V = C::kVpt, N = V * E;
   constexpr int kShift = K::kTopShift;
   constexpr int kCap = C::kCap;
-  constexpr uint32_t kLoBin = 4, kHiBin = kHistBins - 4;  // finite values have bins in [kLoBin, kHiBin)
+  constexpr uint32_t kLoBin = 8;  // finite values have bins in [kLoBin, kHistBins) in this kernel's key form
   static_assert((N + 2) * 64 < 65536, "packed per-wavefront counts must stay below 2^16");
   // Arrays carry 64 spare slots past their end: a lane with nothing to store (or add)
-  // writes its own spare slot instead of branching.
+  // writes its own spare slot instead of branching.  LDS is what bounds the rows resident
+  // per CU, so buffers are reused once dead: the first-digit histogram becomes the list of
+  // selected columns once the boundary bin is known, and the candidate list becomes the
+  // histogram of the passes over the row when the boundary bin outgrows it.
+  static_assert(DSI_MAX_TOPK == kHistBins, "the selected columns fill the first-digit histogram's storage");
+  static_assert(2 * (kCap + 64) >= kHistBins, "the candidate list holds an 11-bit histogram");
   __shared__ __attribute__((aligned(16))) int s_hist[kHistBins + 64];
-  __shared__ uint32_t s_ckey[kCap + 64];  // boundary-bin keys and columns
-  __shared__ int s_ccol[kCap + 64];
-  __shared__ int s_out[DSI_MAX_TOPK + 64];  // the selected columns
+  int* const s_out = s_hist;  // the selected columns, after the boundary bin is found
+  __shared__ __attribute__((aligned(16))) uint32_t s_cand[2 * (kCap + 64)];  // boundary-bin keys, then columns
+  uint32_t* const s_ckey = s_cand;
+  int* const s_ccol = reinterpret_cast<int*>(s_cand + kCap + 64);
+  __shared__ int s_dig[128];  // the boundary bin's further digits
   __shared__ int s_sel[4];
   __shared__ int s_wave[C::kWaves];
   __shared__ int s_cnt[4];  // 0: written, 3: boundary bin; 1/2: resolution
@@ -645,72 +662,105 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
       kk[j] = v;
     }
   };
+  // Keys: the order-preserving key plus four first-digit bins, modulo the key width.  Finite
+  // values keep their order and land in bins [8, 2048); +inf and +NaN wrap to bins 0..3 and
+  // -inf and -NaN stay in 4..7, below every finite value, as do the zero keys of slots outside
+  // the row.  Each later test is then one unsigned comparison.
+  auto reg_key = [](uint32_t raw) -> uint32_t {
+    if constexpr (BF16) {
+      const uint32_t t = (raw & 0x8000u) ? 0xFFFFu : 0x8000u;
+      return ((raw ^ t) + 0x80u) & 0xFFFFu;
+    } else {
+      const uint32_t t = (uint32_t)((int32_t)raw >> 31) | 0x80000000u;
+      return (raw ^ t) + 0x00800000u;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < V; i++) {
     const int vi = i * T + tid;
     uint4 x = uint4{0u, 0u, 0u, 0u};
     if (vi < nvec) x = vec[vi];
 #pragma unroll
-    for (int e = 0; e < E; e++) {
-      uint32_t key;
-      K::key(K::elem(x, e), key);
-      set_key(i * E + e, vi < nvec ? key : 0u);
-    }
+    for (int e = 0; e < E; e++) set_key(i * E + e, vi < nvec ? reg_key(K::elem(x, e)) : 0u);
   }
   const bool ha = tid < c0 - st, ta = tid < en - c1;
-  {
-    uint32_t key;
-    K::key(ha ? K::load1(row, st + tid) : 0u, key);
-    set_key(N, ha ? key : 0u);
-    K::key(ta ? K::load1(row, c1 + tid) : 0u, key);
-    set_key(N + 1, ta ? key : 0u);
-  }
+  set_key(N, ha ? reg_key(K::load1(row, st + tid)) : 0u);
+  set_key(N + 1, ta ? reg_key(K::load1(row, c1 + tid)) : 0u);
   // column of kk[j] relative to st
   const int col_base = c0 - st + tid * E;
   auto column = [&](int j) { return j < N ? col_base + (j / E) * T * E + (j % E) : (j == N ? tid : c1 - st + tid); };
 
   __syncthreads();
+  // First-digit histogram over the row's slots only (whole vectors past the row are skipped by
+  // the lanes holding them).
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    const bool in = i * T + tid < nvec;
+    if (i * T + tid < nvec) {
 #pragma unroll
-    for (int e = 0; e < E; e++) atomicAdd(&s_hist[in ? key_at(i * E + e) >> kShift : kHistBins + lane], 1);
+      for (int e = 0; e < E; e++) atomicAdd(&s_hist[key_at(i * E + e) >> kShift], 1);
+    }
   }
-  atomicAdd(&s_hist[ha ? key_at(N) >> kShift : kHistBins + lane], 1);
-  atomicAdd(&s_hist[ta ? key_at(N + 1) >> kShift : kHistBins + lane], 1);
+  if (ha) atomicAdd(&s_hist[key_at(N) >> kShift], 1);
+  if (ta) atomicAdd(&s_hist[key_at(N + 1) >> kShift], 1);
   launder(kk);  // the bins are recomputed where needed rather than kept, one register per key
   __syncthreads();
-  find_bin_all<C::kWaves>(s_hist, kLoBin, kHiBin, k, s_wave, s_sel, tid);
+  find_bin_all<C::kWaves>(s_hist, kLoBin, kHistBins, k, s_wave, s_sel, tid);  // its last read of s_hist precedes
+                                                                              // its closing barrier
   const int total = s_sel[2];
   const bool all = total <= k;  // every finite value is selected
   const uint32_t b1 = all ? 0xFFFFFFFFu : (uint32_t)s_sel[0];
   const int above1 = all ? total : s_sel[1];
-  // written: bins in (lo_w, kHiBin), i.e. (d - lo_w - 1) < (kHiBin - lo_w - 1) unsigned
-  const uint32_t lo_w = all ? kLoBin - 1 : b1;
-  const uint32_t span_w = kHiBin - lo_w - 1;
+  // Written: key > top (above the boundary bin; every finite value when all are taken).
+  // Candidates: key - t_eq < span (the boundary bin; none when all are taken).
+  const uint32_t top = all ? (kLoBin << kShift) - 1u : (b1 << kShift) | ((1u << kShift) - 1u);
+  const uint32_t t_eq = all ? 0u : b1 << kShift;
+  const uint32_t span = all ? 0u : 1u << kShift;
 
-  int ngt = 0, neq = 0;
+  // Each wavefront counts its columns of both kinds (ballots, scalar sums), reserves one range
+  // of each, then writes them in slot order: slot j of every lane, then slot j + 1.
+  int cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
-    const uint32_t d = key_at(j) >> kShift;
-    ngt += (d - lo_w - 1u) < span_w ? 1 : 0;
-    neq += d == b1 ? 1 : 0;
+    const uint32_t key = key_at(j);
+    cg += __popcll(__builtin_amdgcn_ballot_w64(key > top));
+    ce += __popcll(__builtin_amdgcn_ballot_w64(key - t_eq < span));
+    __builtin_amdgcn_sched_barrier(0);  // one slot at a time: each mask lives briefly
   }
-  int pg, pe;
-  reserve2(ngt, neq, &s_cnt[0], &s_cnt[3], lane, pg, pe);
+  asm volatile("" : "+s"(cg), "+s"(ce));  // the sums are complete here, not sunk into the branch below
+  int pg = 0, pe = 0;
+  if (lane == 0) {
+    pg = atomicAdd(&s_cnt[0], cg);
+    pe = atomicAdd(&s_cnt[3], ce);
+  }
   launder(kk);
+  // Byte offsets: each position is the wavefront's base plus the lane's rank among the set
+  // lanes of the slot's mask.  A candidate past the list (the boundary bin outgrew it, and the
+  // list will not be read) goes to the lane's spare entry instead.
+  uint32_t og = (uint32_t)__builtin_amdgcn_readfirstlane(pg) * 4u;
+  uint32_t oe = (uint32_t)__builtin_amdgcn_readfirstlane(pe);
+  char* const b_out = reinterpret_cast<char*>(s_out);
+  char* const b_key = reinterpret_cast<char*>(s_ckey);
+  char* const b_col = reinterpret_cast<char*>(s_ccol);
+  const uint32_t spare = kCap + lane;
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
-    const uint32_t d = key_at(j) >> kShift;
-    const bool gt = (d - lo_w - 1u) < span_w;
-    const bool eq = d == b1;
+    const uint32_t key = key_at(j);
+    const bool gt = key > top;
+    const bool eq = key - t_eq < span;
+    const uint64_t mg = __builtin_amdgcn_ballot_w64(gt);
+    const uint64_t me = __builtin_amdgcn_ballot_w64(eq);
     const int col = column(j);
-    s_out[gt ? pg : DSI_MAX_TOPK + lane] = col;
-    const int cs = (eq && pe < kCap) ? pe : kCap + lane;
-    s_ckey[cs] = key_at(j);
-    s_ccol[cs] = col;
-    pg += gt ? 1 : 0;
-    pe += eq ? 1 : 0;
+    const uint32_t rg = __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+    const uint32_t re = __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, oe));
+    if (gt) *reinterpret_cast<int*>(b_out + og + rg * 4u) = col;
+    if (eq) {
+      const uint32_t at = min(re, spare) * 4u;
+      *reinterpret_cast<uint32_t*>(b_key + at) = key;
+      *reinterpret_cast<int*>(b_col + at) = col;
+    }
+    og += (uint32_t)__popcll(mg) * 4u;
+    oe += (uint32_t)__popcll(me);
+    asm volatile("" : "+s"(og));  // kept as a byte offset: one shift-add per address
     __builtin_amdgcn_sched_barrier(0);  // one element at a time: keeps register pressure low
   }
   __syncthreads();
@@ -734,14 +784,14 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
       for (int p = 0; p < kDigits; p++) {
         if (whole) break;  // uniform: from LDS values read after a barrier
         const int sh = kSh[p], nb = 1 << kWd[p], hs = sh + kWd[p];
-        for (int i = tid; i < nb; i += T) s_hist[i] = 0;
+        for (int i = tid; i < nb; i += T) s_dig[i] = 0;
         __syncthreads();
         for (int i = tid; i < m; i += T) {
           const uint32_t key = s_ckey[i];
-          if ((key >> hs) == (prefix >> hs)) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1);
+          if ((key >> hs) == (prefix >> hs)) atomicAdd(&s_dig[(key >> sh) & (nb - 1)], 1);
         }
         __syncthreads();
-        find_bin_w0<(BF16 ? 32 : 128)>(s_hist, 0, nb, rem, s_sel, tid);
+        find_bin_w0<(BF16 ? 32 : 128)>(s_dig, 0, nb, rem, s_sel, tid);
         prefix |= (uint32_t)s_sel[0] << sh;
         rem -= s_sel[1];
         whole = !BF16 && s_sel[3] == rem;
@@ -768,8 +818,9 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
       __syncthreads();
       if (tid < 4) s_cnt[tid] = 0;
       __syncthreads();
-      resolve_boundary<BF16, C>(row, st, en, k, b1, above1, m, 0, s_ckey, s_ccol, s_hist, s_wave, s_sel, s_cnt, s_out,
-                                tid);
+      // (b1 - 4: the boundary bin in the plain key form that the passes over the row use)
+      reg_resolve_by_row<BF16, C>(row, st, en, k, b1 - 4, above1, m, reinterpret_cast<int*>(s_cand), s_wave, s_sel,
+                                  s_cnt, s_out, tid);
     }
     __syncthreads();
   }

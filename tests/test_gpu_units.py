@@ -902,3 +902,51 @@ def test_sparse_schedule_bounds_the_source():
     inside = tok < 3000
     assert np.array_equal(got[inside], full[inside])
     assert np.all(got[~inside] == 0xFF80)
+
+
+@pytest.mark.parametrize("width", [4096, 8192, 16384, 40000])
+def test_topk_extreme_values_and_non_finite(width):
+    """Boundaries at both ends of the finite range: values next to the largest float (the
+    top first-digit bin), next to minus the largest, and rows mixing them with +-inf and +-NaN
+    (never selected), in fp32 and bf16, for each row-length path."""
+    rng = np.random.default_rng(width)
+    fmax = np.finfo(np.float32).max
+    near_top = lambda n: (fmax * (1 - rng.uniform(0, 2 ** -10, n))).astype(np.float32)
+    rows = 6
+    x = rng.standard_normal((rows, width)).astype(np.float32)
+    x[0, :3000] = near_top(3000)                        # boundary in the top bin
+    x[1, :] = -fmax                                     # all equal, lowest finite bin
+    x[1, :2] = [np.inf, np.nan]
+    x[2, ::4] = np.inf
+    x[2, 1::4] = np.nan
+    x[2, 2::4] = -np.inf
+    x[2, 3::8] = near_top(len(x[2, 3::8]))
+    x[3] = rng.permutation(np.concatenate([near_top(width // 2), -near_top(width - width // 2)]))
+    x[4, :] = np.float32(-np.nan)                       # negative NaN everywhere: nothing valid
+    x[4, :5] = 1.0
+    x[5, : width // 2] = np.inf
+    for r in range(rows):
+        x[r] = rng.permutation(x[r])
+    ends = np.full(rows, width, np.int32)
+    ref = oracle.topk_select(x, ends, 2048)
+    got = host(dsi.topk_select(dev(x), dev(ends), k=2048))
+    for r in range(rows):
+        check_selection(got[r], ref[r], x[r], rule="exact", end=width)
+    if width > 16384:
+        return
+    bits = synth._bf16_bits(rng.standard_normal((rows, width)).astype(np.float32))
+    bits[0, :3000] = 0x7F7F - rng.integers(0, 2, 3000).astype(np.uint16)  # the two largest bf16 values
+    bits[1, :] = 0xFF7F                                                  # minus the largest, everywhere
+    bits[2, ::4] = 0x7F80
+    bits[2, 1::4] = 0x7FC0
+    bits[2, 2::4] = 0xFF80
+    bits[3, 3::2] = 0xFFC0                                               # negative NaN
+    bits[4, :] = 0xFFC1
+    bits[5, : width // 2] = 0x7F80
+    for r in range(rows):
+        bits[r] = rng.permutation(bits[r])
+    ref = oracle.topk_select(bits, ends, 2048, bf16=True)
+    got = host(dsi.topk_select(dev(bits), dev(ends), k=2048))
+    f = bf16_value(bits)
+    for r in range(rows):
+        check_selection(got[r], ref[r], f[r], rule="exact", end=width)
