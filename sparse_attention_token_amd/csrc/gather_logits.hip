@@ -455,8 +455,10 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_rsrc, (c * kDcChunk + key) * 4, 0, 0);
       if constexpr (HIST) {  // every column inside the row's range; non-finite values fall in bins the top-k ignores
         if (c * kDcChunk + key < ke) {
-          const uint32_t bin = f32_first_bin(out);
-          atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1u) << 4));
+          // word bin/2 of the packed histogram, half bin&1 (bin = f32_first_bin(out) = key >> 21)
+          const uint32_t u = __float_as_uint(out);
+          const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+          atomicAdd(&s_hist[k >> 22], 1u + ((k >> 21) & 1u) * 0xFFFFu);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -503,6 +505,9 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
       total += v;
     }
+    // Uniform in fact; said so, or the share's loop counts (and every value carried through the
+    // loop, the output row's buffer descriptor included) would be treated as per-lane values.
+    total = __builtin_amdgcn_readfirstlane(total);
     const int nwg = min((int)gridDim.x, total);
     if ((int)blockIdx.x >= nwg) return;  // uniform: no share
     g0 = (int)((int64_t)blockIdx.x * total / nwg);
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void paged_decode_kernel(
   }
   b = __builtin_amdgcn_readfirstlane(b);
   int lc = __builtin_amdgcn_readfirstlane(g0 - start);
-  int remaining = g1 - g0;
+  int remaining = __builtin_amdgcn_readfirstlane(g1 - g0);
   int counted = -1;  // HIST: the request whose counts s_hist holds
   // HIST: write request rb's counts to its slot and clear them (each word by the thread that owns it)
   auto flush = [&](int rb) {
