@@ -43,6 +43,7 @@ ROW_MXFP4 = 68  # MXFP4 cache row: 64 bytes of FP4 codes + 4 E8M0 block scales
 F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA (published)
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E (published)
+PAGED_CEILING = None      # the measured ceilings, once taken (the paged-read rates are read by the decode lines)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_logits_T2048_S8192_traffic.md")
 PREFILL_SOURCES = [os.path.join(ROOT, "sparse_attention_token_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
 FLOP_PER_PAIR = 2 * 64 * 128
@@ -131,6 +132,19 @@ def measure_ceilings():
         nb[0] = ceiling.copy(src, dst, 4096)
     out["copy_gbs"] = round(2 * (1 << 30) / (timed_ms(run) * 1e-3) / 1e9, 1)
     out["copy_bytes"] = 1 << 30
+    # The paged cache's read pattern alone: 64-token pages (132- or 68-byte rows) in a random order over 1 GiB.
+    rng = np.random.default_rng(11)
+    for name, page in (("paged_read_gbs_fp8_pages", 64 * ROW), ("paged_read_gbs_mxfp4_pages", 64 * ROW_MXFP4)):
+        n = (1 << 30) // page
+        pages = torch.from_numpy(rng.permutation(n).astype(np.int32)).cuda()
+        best = 0.0
+        for wg in (1024, 2048, 4096):
+            for ppr in (4, 8):
+                def run():
+                    nb[0] = ceiling.paged_read(big, page, pages, page, wg, isink, ppr)
+                run()
+                best = max(best, nb[0] / (timed_ms(run) * 1e-3) / 1e9)
+        out[name] = round(best, 1)
     del big
     torch.cuda.empty_cache()
     return out
@@ -423,12 +437,17 @@ def bench_decode(n, steps, warmup, copies=4, mxfp4=False):
     bytes_topk = 4 * V + rows * K * 4
     gbs = (bytes_logits + bytes_topk) / (ms_lt * 1e-3) / 1e9
     cache = ", MXFP4 cache (68 B per token)" if mxfp4 else ""
+    # the logits kernel against the measured rate of reading the same kind of pages with no scoring
+    key = "paged_read_gbs_mxfp4_pages" if mxfp4 else "paged_read_gbs_fp8_pages"
+    ceil_gbs = (PAGED_CEILING or {}).get(key)
+    vs_paged = (round(bytes_logits / (ms_l * 1e-3) / 1e9 / ceil_gbs, 4) if ceil_gbs else None)
     return dict(workload=f"paged decode {B} x next_n {nn}, lengths U{{{int(lens.min())}..{int(lens.max())}}}{cache}",
                 rows=rows, sum_tokens=sumL, ms_step=round(ms_step, 4), ms_logits_topk=round(ms_lt, 4),
                 ms_logits=round(ms_l, 4), ms_topk=round(ms_lt - ms_l, 4), ms_slot=round(ms_s, 4),
                 ms_separate_calls=round(ms_sep, 4),
                 logits_gbs=round(bytes_logits / (ms_l * 1e-3) / 1e9, 1),
                 logits_topk_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                logits_vs_paged_read_ceiling=vs_paged,
                 rows_per_s=round(rows / (ms_lt * 1e-3), 1),
                 algorithmic_bytes=bytes_logits + bytes_topk,
                 timing="ms_logits_topk: dsi_paged_mqa_topk_decode (one call); ms_logits: the logits call alone; "
@@ -621,11 +640,17 @@ def bars(achieved_tflops, extra):
                 "FP8-operand MFMAs truncate inside one instruction by more than the 1e-3 (1 + |ref|) logit "
                 "tolerance; the f16 peak is half the FP8 peak, so 0.5 of FP8 is 1.0 of f16, unreachable on this "
                 "path"}}
+    ceil = (PAGED_CEILING or {}).get("paged_read_gbs_fp8_pages")
     for n in (3, 4):
         w = extra.get(f"decode_w{n}")
         if w:
-            out[f"decode_w{n}_logits_topk_vs_hbm"] = {"target": 0.6, "achieved": w["hbm_frac"],
-                                                      "met": w["hbm_frac"] >= 0.6}
+            bar = {"target": 0.6, "achieved": w["hbm_frac"], "met": w["hbm_frac"] >= 0.6}
+            if ceil:
+                bar["note"] = (f"reading the cache's 8448-byte pages alone, in a random order and with no scoring, "
+                               f"measured {ceil:.0f} GB/s here ({ceil / HBM_PEAK_GBS:.3f} of the HBM peak), below "
+                               f"the target before any top-k time; the logits kernel reaches "
+                               f"{w['logits_vs_paged_read_ceiling']} of that rate")
+            out[f"decode_w{n}_logits_topk_vs_hbm"] = bar
     return out
 
 
@@ -658,6 +683,8 @@ def main():
         log("measured ceilings ...")
         ceil = measure_ceilings()
         log(ceil)
+    global PAGED_CEILING
+    PAGED_CEILING = ceil
     log("prefill chunk ...")
     pf = bench_prefill(args.steps, args.warmup)
     value = pf["pairs"] / (pf["ms_step"] * 1e-3)

@@ -10,6 +10,9 @@
  *     traffic, 16 independent accumulator chains per wavefront);
  *   - HBM streaming read bandwidth over a caller-sized buffer (sized well
  *     above the 256 MB Infinity Cache, so the bytes come from HBM);
+ *   - the paged cache's read pattern alone: whole pages (the decode
+ *     workloads' 64-token pages of 132- or 68-byte rows) read through a page
+ *     table that scatters them over a pool larger than the Infinity Cache;
  *   - a plain 16-byte-per-lane copy of a known number of bytes, whose
  *     FETCH_SIZE / WRITE_SIZE counter readings give the factor between those
  *     counters and real bytes.
@@ -55,6 +58,19 @@ DSIC_API int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups,
  * overlapping, bytes a multiple of 16) with 16-byte loads and stores,
  * grid-stride.  Errors as dsic_stream_read. */
 DSIC_API int dsic_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, hipStream_t stream);
+
+/* Read n_pages whole pages of page_bytes bytes, page i at pool +
+ * pages[i] * block_stride (pool 16-byte aligned; page_bytes a multiple of 16,
+ * at most 12288; block_stride a multiple of 16, at least page_bytes; every
+ * page id in [0, pool's blocks) — the caller's table), pages_per_round (4
+ * or 8) pages per workgroup round with all their loads in flight, and fold
+ * them into one word per thread written to `sink` (workgroups * 256 uint32).
+ * EINVAL: null pointer, n_pages < 1, pages_per_round not 4 or 8, workgroups
+ * not 1..4096, page_bytes or block_stride out of range; EALIGN: pool not
+ * 16-byte aligned. */
+DSIC_API int dsic_paged_read(const void* pool, int64_t block_stride, const int32_t* pages, int32_t n_pages,
+                             int32_t page_bytes, int32_t pages_per_round, int32_t workgroups, uint32_t* sink,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

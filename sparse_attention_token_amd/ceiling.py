@@ -16,6 +16,7 @@ _SIGNATURES = {
     "dsic_mfma_loop": (ctypes.c_int, [_i32, _i32, _i32, _p, _p]),
     "dsic_stream_read": (ctypes.c_int, [_p, _sz, _i32, _p, _p]),
     "dsic_copy": (ctypes.c_int, [_p, _p, _sz, _i32, _p]),
+    "dsic_paged_read": (ctypes.c_int, [_p, ctypes.c_int64, _p, _i32, _i32, _i32, _i32, _p, _p]),
 }
 ENTRY_POINTS = tuple(_SIGNATURES)
 _lib = None
@@ -65,3 +66,14 @@ def copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int) -> int:
     assert src.is_contiguous() and dst.is_contiguous() and dst.numel() * dst.element_size() >= nbytes
     _check(lib().dsic_copy(src.data_ptr(), dst.data_ptr(), nbytes, workgroups, _stream(src)), "dsic_copy")
     return nbytes
+
+
+def paged_read(pool: torch.Tensor, block_stride: int, pages: torch.Tensor, page_bytes: int, workgroups: int,
+               sink: torch.Tensor, pages_per_round: int = 4) -> int:
+    """Enqueue a read of the pages `pages` (int32 ids into `pool`); returns the byte count read."""
+    assert pool.is_contiguous() and pages.dtype == torch.int32 and pages.is_contiguous()
+    assert sink.dtype == torch.int32 and sink.numel() >= workgroups * THREADS
+    assert int(pages.max()) * block_stride + page_bytes <= pool.numel() * pool.element_size()
+    _check(lib().dsic_paged_read(pool.data_ptr(), block_stride, pages.data_ptr(), pages.numel(), page_bytes,
+                                 pages_per_round, workgroups, sink.data_ptr(), _stream(pool)), "dsic_paged_read")
+    return pages.numel() * page_bytes

@@ -92,6 +92,36 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict_
   for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Whole pages of page_bytes at pool + pages[i] * block_stride, P pages per workgroup round, each
+// page read by the workgroup's 256 threads in up to three 16-byte loads each (all 3P in flight).
+constexpr int kPageRounds = 3;  // pages of at most 3 * 256 * 16 = 12 KB
+template <int P>
+__global__ __launch_bounds__(kThreads) void paged_read_kernel(const uint8_t* __restrict__ pool, int64_t block_stride,
+                                                              const int* __restrict__ pages, int n_pages,
+                                                              int page_bytes, uint32_t* __restrict__ sink) {
+  const int n16 = page_bytes / 16, t = threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int p0 = blockIdx.x * P; p0 < n_pages; p0 += gridDim.x * P) {
+    u32x4 x[P][kPageRounds];
+#pragma unroll
+    for (int q = 0; q < P; q++) {
+      const int p = p0 + q;
+      const u32x4* base = reinterpret_cast<const u32x4*>(pool + (int64_t)pages[min(p, n_pages - 1)] * block_stride);
+#pragma unroll
+      for (int r = 0; r < kPageRounds; r++) {
+        const int j = r * kThreads + t;
+        x[q][r] = u32x4{0u, 0u, 0u, 0u};
+        if (p < n_pages && j < n16) x[q][r] = base[j];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < P; q++)
+#pragma unroll
+      for (int r = 0; r < kPageRounds; r++) acc ^= x[q][r];
+  }
+  sink[(size_t)blockIdx.x * kThreads + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 int launched() { return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH; }
 
 }  // namespace
@@ -121,5 +151,19 @@ extern "C" int dsic_copy(const void* src, void* dst, size_t bytes, int32_t workg
   if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return DSI_EALIGN;
   hipLaunchKernelGGL(copy_kernel, dim3(workgroups), dim3(kThreads), 0, stream, static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), bytes / 16);
+  return launched();
+}
+
+extern "C" int dsic_paged_read(const void* pool, int64_t block_stride, const int32_t* pages, int32_t n_pages,
+                               int32_t page_bytes, int32_t pages_per_round, int32_t workgroups, uint32_t* sink,
+                               hipStream_t stream) {
+  if (!pool || !pages || !sink || n_pages < 1 || workgroups < 1 || workgroups > 4096) return DSI_EINVAL;
+  if (pages_per_round != 4 && pages_per_round != 8) return DSI_EINVAL;
+  if (page_bytes < 16 || (page_bytes & 15) || page_bytes > kPageRounds * kThreads * 16) return DSI_EINVAL;
+  if (block_stride < page_bytes || (block_stride & 15)) return DSI_EINVAL;
+  if (reinterpret_cast<uintptr_t>(pool) & 15) return DSI_EALIGN;
+  auto k = pages_per_round == 8 ? paged_read_kernel<8> : paged_read_kernel<4>;
+  hipLaunchKernelGGL(k, dim3(workgroups), dim3(kThreads), 0, stream, static_cast<const uint8_t*>(pool), block_stride,
+                     pages, n_pages, page_bytes, sink);
   return launched();
 }
