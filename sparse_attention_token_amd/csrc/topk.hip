@@ -1036,9 +1036,6 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
   const int above1 = all ? total : s_sel[1];
   const int m = all ? 0 : s_sel[3];
   const bool collect = !all && m <= kSplitCap;
-  // written: bins in (lo_w, kHiBin)
-  const uint32_t lo_w = all ? kLoBin - 1 : b1;
-  const uint32_t span_w = kHiBin - lo_w - 1;
 
 #pragma unroll
   for (int i = 0; i < V; i++) {
@@ -1060,22 +1057,24 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
   // column of kk[j]
   auto column = [&](int j) { return j < N ? c0 + tid * E + (j / E) * T * E + (j % E) : (j == N ? a + tid : c1 + tid); };
 
-  int ngt = 0, neq = 0;
+  // Keys of non-finite values and empty slots are 0, below every finite value's key (bins >= kLoBin), so
+  // "above the boundary" is key > top and "in the boundary bin" is key - t_eq < span (span 0: none collected).
+  const uint32_t top = all ? (kLoBin << kShift) - 1u : (b1 << kShift) | ((1u << kShift) - 1u);
+  const uint32_t t_eq = all ? 0u : b1 << kShift;
+  const uint32_t span = collect ? 1u << kShift : 0u;
+  // Each wavefront counts both kinds with ballots; the workgroup's counts (packed gt << 16 | eq: a slice's stay
+  // below 2^16) are reserved with one device-scope atomic per kind; then each wavefront writes its columns in slot
+  // order (slot j of every lane, then slot j + 1) at mbcnt ranks, so that a store's lanes write consecutive words.
+  int cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
-    const uint32_t d = key_at(j) >> kShift;
-    ngt += (d - lo_w - 1u) < span_w ? 1 : 0;
-    neq += (collect && d == b1) ? 1 : 0;
+    const uint32_t key = key_at(j);
+    cg += __popcll(__builtin_amdgcn_ballot_w64(key > top));
+    ce += __popcll(__builtin_amdgcn_ballot_w64(key - t_eq < span));
+    __builtin_amdgcn_sched_barrier(0);  // one slot at a time: each mask lives briefly
   }
-  // workgroup exclusive prefix of both counts, packed (gt << 16 | eq)
-  const int packed = (ngt << 16) | neq;
-  int incl = packed;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
+  asm volatile("" : "+s"(cg), "+s"(ce));  // the sums are complete here
+  if (lane == 0) s_wsum[wave] = (cg << 16) | ce;
   __syncthreads();
   int before = 0, wg_total = 0;
 #pragma unroll
@@ -1089,25 +1088,28 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_select_kernel(
     s_base[1] = (wg_total & 0xFFFF) ? atomicAdd(&meta[kMetaCntEq], wg_total & 0xFFFF) : 0;
   }
   __syncthreads();
-  const int excl = before + incl - packed;
-  int pg = s_base[0] + (excl >> 16);
-  int pe = s_base[1] + (excl & 0xFFFF);
+  int pg = __builtin_amdgcn_readfirstlane(s_base[0] + (before >> 16));
+  int pe = __builtin_amdgcn_readfirstlane(s_base[1] + (before & 0xFFFF));
   unsigned long long* cand = w.cand + (int64_t)r * kSplitCap;
   // Candidates go to the row's list as device-scope atomic stores (written through to the point where every XCD
   // sees them); the wait below covers their completion before the slice counts itself done.
+  launder(kk);
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
     const uint32_t key = key_at(j);
-    const uint32_t d = key >> kShift;
-    const bool gt = (d - lo_w - 1u) < span_w;
-    const bool eq = collect && d == b1;
+    const bool gt = key > top;
+    const bool eq = key - t_eq < span;
+    const uint64_t mg = __builtin_amdgcn_ballot_w64(gt);
+    const uint64_t me = __builtin_amdgcn_ballot_w64(eq);
     const int col = column(j);
-    if (gt && pg < k) orow[pg] = col - st;
-    if (eq && pe < kSplitCap)
-      __hip_atomic_store(cand + pe, ((unsigned long long)(uint32_t)col << 32) | key, __ATOMIC_RELAXED,
+    const int ig = pg + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+    const int ie = pe + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+    if (gt && ig < k) orow[ig] = col - st;
+    if (eq && ie < kSplitCap)
+      __hip_atomic_store(cand + ie, ((unsigned long long)(uint32_t)col << 32) | key, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    pg += gt ? 1 : 0;
-    pe += eq ? 1 : 0;
+    pg += __popcll(mg);
+    pe += __popcll(me);
     __builtin_amdgcn_sched_barrier(0);  // one element at a time: no lane masks kept for later elements
   }
   if (all) {  // uniform: nothing to resolve; slice 0 pads the row
