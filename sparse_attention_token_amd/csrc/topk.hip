@@ -15,13 +15,13 @@
 //     those candidates, digit by digit (by passes over the row when the boundary bin
 //     outgrows LDS).  Output slots are reserved per wavefront (ballot + popcount, one LDS
 //     atomic);
-//   * few long rows are split between workgroups of 8192 columns, in three launches that
+//   * few long rows are split between workgroups of 8192 columns, in two launches that
 //     communicate through the caller's workspace: per-slice histograms; then every slice
 //     sums its row's histograms, finds the boundary bin, writes its columns above it at
 //     positions reserved by one atomic per workgroup and appends its boundary-bin columns to
-//     a per-row candidate list; one workgroup per row resolves the candidates as above.  The
-//     paged decode kernel can count the histograms while it writes the logits, which leaves
-//     two launches (topk_split.h).
+//     a per-row candidate list, and the row's last slice to finish resolves the candidates as
+//     above.  The paged decode kernel can count the histograms while it writes the logits,
+//     which leaves one launch (topk_split.h).
 #include <algorithm>
 #include <mutex>
 
@@ -830,7 +830,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
 
 // ---------------------------------------------------------------- long rows split between workgroups
 // Few long rows (decode): each row is cut into G slices of at most 8192 fp32 (16384 bf16)
-// columns, one 512-thread workgroup per slice, in up to three launches that communicate through
+// columns, one 512-thread workgroup per slice, in up to two launches that communicate through
 // the caller's workspace (layout in topk_split.h):
 //   1. topk_slice_hist_kernel: each slice's first-digit histogram into its slot — skipped when
 //      the paged decode kernel has counted the row's slots while writing its logits;
@@ -838,11 +838,11 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
 //      row's slots (the row's histogram, 4 bins per thread), finds the boundary bin b1, and
 //      writes its columns above b1 (every valid column when the row has at most k) at output
 //      positions reserved by one device-scope atomic per workgroup; its boundary-bin columns go
-//      to the row's candidate list the same way;
-//   3. topk_split_resolve_kernel: one workgroup per row resolves the boundary bin from the
-//      candidates (or from the row, when it holds more than the list) and pads with -1.
-// No workgroup waits for another within a launch: the output order is any order, so the only
-// shared state is two counters per row.
+//      to the row's candidate list the same way; the row's last slice to finish (a device-scope
+//      count of finished slices) resolves the boundary bin from the candidates (or from the
+//      row, when it holds more than the list) and pads with -1.
+// No workgroup waits for another: the output order is any order, so the shared state is the
+// row's counters and candidate list, all accessed with device-scope atomics.
 constexpr int kSplitThreads = 512;
 constexpr int kSplitVecs = 4;  // 16-byte vectors per thread: 16 fp32 or 32 bf16 columns
 using SliceCfg = Cfg<kSplitThreads, 0, 2>;  // two histogram copies in the slice step (measured 26.0 -> 25.6 us)
