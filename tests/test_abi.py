@@ -306,5 +306,7 @@ def test_decode_topk_call_validation():
     assert call(B=8, maxc=40000, ld=40000, ws_bytes=16) == EWS  # the split path needs a workspace
     assert call(B=0) == 0
     assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 1, 40000, 2048) > L.dsi_topk_workspace_bytes(8, 40000, 2048)
+    # two or more rows per request: the two steps as they are
     assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 2, 40000, 2048) == L.dsi_topk_workspace_bytes(16, 40000, 2048)
+    assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 3, 40000, 2048) == L.dsi_topk_workspace_bytes(24, 40000, 2048)
     assert L.dsi_paged_mqa_topk_decode_workspace_bytes(8, 1, 4000, 2048) == 0

@@ -76,32 +76,35 @@ def test_decode_step_graph_replays(mxfp4):
         assert np.array_equal(sl, want), rep
 
 
-@pytest.mark.parametrize("mxfp4", [False, True])
-def test_fused_decode_call_graph_replays(mxfp4):
+@pytest.mark.parametrize("mxfp4,next_n", [(False, 1), (True, 1), (False, 2)])
+def test_fused_decode_call_graph_replays(mxfp4, next_n):
     """The decode step through dsi_paged_mqa_topk_decode (logits with the top-k's histograms counted in the decode
-    kernel, the split top-k, slot conversion) captured once and replayed; the workspace is overwritten with other
-    bytes before every replay, since the call keeps no state in it."""
-    c = synth.decode_case(93, B=12, next_n=1, lmin=1000, lmax=50000, block_size=64)
+    kernel when there is one row per request, the split top-k, slot conversion) captured once and replayed; the
+    workspace is overwritten with other bytes before every replay, since the call keeps no state in it."""
+    c = synth.decode_case(93, B=12, next_n=next_n, lmin=1000, lmax=50000, block_size=64)
     bs, nb = c["block_size"], c["num_blocks"]
     stride = bs * 68 if mxfp4 else c["block_stride"]
     quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
     lens = c["context_lens"]
     maxc = int(lens.max())
-    B = 12
+    B, rows = 12, 12 * next_n
     pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
     quant(dev(c["k"]), dev(c["slot_mapping"]), pool, bs, stride, nb)
     q, w, cl, bt = dev(c["q"]), dev(c["w"]), dev(lens), dev(c["block_table"])
-    logits = torch.empty((B, maxc), dtype=torch.float32, device="cuda")
-    idx = torch.empty((B, K), dtype=torch.int32, device="cuda")
-    slots = torch.empty((B, K), dtype=torch.int32, device="cuda")
-    need = dsi.paged_mqa_topk_decode_workspace_bytes(B, 1, maxc)
-    assert need > dsi.topk_workspace_bytes(B, maxc, K) > 0  # the fused path (slots per workgroup and request)
+    logits = torch.empty((rows, maxc), dtype=torch.float32, device="cuda")
+    idx = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    slots = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    r2r = dev(np.repeat(np.arange(B, dtype=np.int32), next_n))
+    need = dsi.paged_mqa_topk_decode_workspace_bytes(B, next_n, maxc)
+    # one row per request: the fused path (slots per workgroup and request); two: the top-k's own split path
+    plain = dsi.topk_workspace_bytes(rows, maxc, K)
+    assert plain > 0 and (need > plain if next_n == 1 else need == plain)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
 
     def step():
-        dsi.paged_mqa_topk_decode(q, w, cl, pool, bs, bt, maxc, logits=logits, out=idx, workspace=ws,
+        dsi.paged_mqa_topk_decode(q, w, cl, pool, bs, bt, maxc, next_n=next_n, logits=logits, out=idx, workspace=ws,
                                   block_stride_bytes=stride, num_blocks=nb, mxfp4=mxfp4)
-        dsi.req_index_to_global_slot(idx, bt, bs, bs, out=slots)
+        dsi.req_index_to_global_slot(idx, bt, bs, bs, row_to_req=r2r, out=slots)
 
     step()
     torch.cuda.synchronize()
@@ -124,14 +127,15 @@ def test_fused_decode_call_graph_replays(mxfp4):
         g.replay()
         torch.cuda.synchronize()
         got, ix, sl = host(logits), host(idx), host(slots)
-        for r in range(B):
-            L = int(lens[r])
+        for r in range(rows):
+            L = int(lens[r // next_n]) - next_n + r % next_n + 1  # the row's visible tokens
             assert np.array_equal(got[r, :L], ref_logits[r, :L]), (rep, r)
             assert np.array_equal(np.sort(got[r][ix[r][ix[r] >= 0]]),
                                   np.sort(ref_logits[r][ref_idx[r][ref_idx[r] >= 0]])), (rep, r)
             assert np.all(ix[r][min(K, L):] == -1)
         p = np.maximum(ix, 0)
-        want = np.where(ix >= 0, np.take_along_axis(c["block_table"], p // bs, axis=1) * bs + p % bs, -1)
+        bt_rows = np.repeat(c["block_table"], next_n, axis=0)
+        want = np.where(ix >= 0, np.take_along_axis(bt_rows, p // bs, axis=1) * bs + p % bs, -1)
         assert np.array_equal(sl, want), rep
 
 

@@ -799,20 +799,23 @@ def test_decode_topk_call_short_and_long_rows(mxfp4, next_n, lens, maxc):
         assert np.array_equal(np.sort(got[r][a]), np.sort(got[r][b]))
 
 
-def test_decode_topk_call_ties_and_heavy_boundary():
+@pytest.mark.parametrize("next_n", [1, 2])
+def test_decode_topk_call_ties_and_heavy_boundary(next_n):
     """Every key of a long row equal (one logit value over 40000 columns): the boundary bin holds more columns
-    than the candidate list, so the split top-k resolves it by passes over the row; any 2048 of the tied
-    columns are correct."""
+    than the candidate list, so the split top-k resolves it by passes over the row (its histograms counted in the
+    decode kernel with one row per request, by the top-k itself with two); any 2048 of the tied columns are
+    correct."""
     lens = [40000, 30000, 3000]
-    c = synth.decode_case(44, B=3, next_n=1, lmin=0, lmax=0, block_size=64, lens=lens)
+    c = synth.decode_case(44, B=3, next_n=next_n, lmin=0, lmax=0, block_size=64, lens=lens)
     k = np.tile(c["k"][:1], (c["k"].shape[0], 1))  # one k row everywhere: every logit of a row is the same
     bs, nb, stride = 64, c["num_blocks"], 64 * ROW
     pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
     dsi.k_quant_and_cache(dev(k), dev(c["slot_mapping"]), pool, bs, stride, nb)
     logits, idx_t = dsi.paged_mqa_topk_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), pool, bs,
-                                              dev(c["block_table"]), 40000)
+                                              dev(c["block_table"]), 40000, next_n=next_n)
     idx, got = host(idx_t), host(logits)
-    for r, L in enumerate(lens):
+    for r in range(len(lens) * next_n):
+        L = lens[r // next_n] - next_n + r % next_n + 1  # the row's visible tokens
         sel = idx[r][idx[r] >= 0]
         assert sel.size == min(K, L) and np.unique(sel).size == sel.size and sel.max() < L
         assert np.all(got[r][sel] == got[r][0]) and np.all(got[r][:L] == got[r][0])
