@@ -285,18 +285,32 @@ struct Q32 {
   f16x8 a[2][8];
 };
 
-__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
+// The codes behind load_q32's fragments, as loaded (so that a caller can issue other loads
+// before decoding them).
+__device__ __forceinline__ void load_q32_codes(uint4 (&x)[2][4], const uint8_t* q_row, int lane) {
   const int m = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int hb = 0; hb < 2; hb++) {
     const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint4 x = p[j];
-      f.a[hb][2 * j] = e4m3x8_to_f16x8(x.x, x.y);
-      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x.z, x.w);
-    }
+    for (int j = 0; j < 4; j++) x[hb][j] = p[j];
   }
+}
+
+__device__ __forceinline__ void decode_q32(Q32& f, const uint4 (&x)[2][4]) {
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f.a[hb][2 * j] = e4m3x8_to_f16x8(x[hb][j].x, x[hb][j].y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x[hb][j].z, x[hb][j].w);
+    }
+}
+
+__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
+  uint4 x[2][4];
+  load_q32_codes(x, q_row, lane);
+  decode_q32(f, x);
 }
 
 // The weights of the 32 heads this lane holds in C: w[hb][i] is head hb*32 + 8*(i/4) + 4h + i%4.
@@ -304,18 +318,31 @@ struct W32 {
   float w[2][16];
 };
 
-__device__ __forceinline__ void load_w32(W32& f, const uint16_t* w_row, int lane) {
+// The bf16 weights behind load_w32's values, as loaded.
+__device__ __forceinline__ void load_w32_raw(uint2 (&x)[2][4], const uint16_t* w_row, int lane) {
   const int h = lane >> 5;
 #pragma unroll
   for (int hb = 0; hb < 2; hb++)
 #pragma unroll
+    for (int b = 0; b < 4; b++) x[hb][b] = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
+}
+
+__device__ __forceinline__ void decode_w32(W32& f, const uint2 (&x)[2][4]) {
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
     for (int b = 0; b < 4; b++) {
-      const uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
-      f.w[hb][4 * b + 0] = bf16_to_f32(x.x & 0xFFFFu);
-      f.w[hb][4 * b + 1] = bf16_to_f32(x.x >> 16);
-      f.w[hb][4 * b + 2] = bf16_to_f32(x.y & 0xFFFFu);
-      f.w[hb][4 * b + 3] = bf16_to_f32(x.y >> 16);
+      f.w[hb][4 * b + 0] = bf16_to_f32(x[hb][b].x & 0xFFFFu);
+      f.w[hb][4 * b + 1] = bf16_to_f32(x[hb][b].x >> 16);
+      f.w[hb][4 * b + 2] = bf16_to_f32(x[hb][b].y & 0xFFFFu);
+      f.w[hb][4 * b + 3] = bf16_to_f32(x[hb][b].y >> 16);
     }
+}
+
+__device__ __forceinline__ void load_w32(W32& f, const uint16_t* w_row, int lane) {
+  uint2 x[2][4];
+  load_w32_raw(x, w_row, lane);
+  decode_w32(f, x);
 }
 
 // B fragments of one 32-key group from the f16 tile: key l%32, dims [64h + 8s, +8).

@@ -102,17 +102,36 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
   const int t_first = rt * kPfRows;
 
   // Union of the workgroup's row ranges; this workgroup takes an equal share (part `part` of
-  // n_parts) of the tiles that cover it.
-  int lo = 0x7FFFFFFF, hi = 0;
+  // n_parts) of the tiles that cover it.  The range loads have uniform addresses and no
+  // branches between them, so they are issued together as scalar loads: two 8-word loads when
+  // all eight rows exist, else one load per row (rows past T repeat row T-1 and are ignored).
+  const int t = t_first + wave;  // this wavefront's row
+  int lo = 0x7FFFFFFF, hi = 0, rks = 0, rke = 0;
+  {
+    int a[kPfRows], b[kPfRows];
+    if (t_first + kPfRows <= T) {
 #pragma unroll
-  for (int i = 0; i < kPfRows; i++) {
-    const int t = t_first + i;
-    if (t < T) {
-      const int a = max(row_ks[t], 0), b = min(row_ke[t], S);
-      if (a < b) {
-        lo = min(lo, a);
-        hi = max(hi, b);
+      for (int i = 0; i < kPfRows; i++) {
+        a[i] = row_ks[t_first + i];
+        b[i] = row_ke[t_first + i];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPfRows; i++) {
+        const int ti = min(t_first + i, T - 1);
+        a[i] = row_ks[ti];
+        b[i] = row_ke[ti];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPfRows; i++) {
+      const int x = max(a[i], 0), y = min(b[i], S);
+      const bool real = t_first + i < T;
+      const bool use = real && x < y;
+      lo = use ? min(lo, x) : lo;
+      hi = use ? max(hi, y) : hi;
+      rks = i == wave ? (real ? x : 0) : rks;
+      rke = i == wave ? (real ? y : 0) : rke;
     }
   }
   if (lo >= hi) return;  // uniform across the workgroup
@@ -120,15 +139,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
   const int tile_first = t0 + part * nt / n_parts, tile_end = t0 + (part + 1) * nt / n_parts;
   if (tile_first >= tile_end) return;
 
-  // This wavefront's row.
-  const int t = t_first + wave;
+  // The row's q codes and weights are requested here and decoded only after the first tile's
+  // loads are issued (below), so the two round trips to memory overlap.
   const int tc = min(t, T - 1);
-  Q32 qf;
-  W32 wf;
-  load_q32(qf, q + (int64_t)tc * kHeads * kDim, lane);
-  load_w32(wf, w + (int64_t)tc * kHeads, lane);
-  const int rks = t < T ? max(row_ks[t], 0) : 0;
-  const int rke = t < T ? min(row_ke[t], S) : 0;
+  uint4 q_codes[2][4];
+  uint2 w_raw[2][4];
+  load_q32_codes(q_codes, q + (int64_t)tc * kHeads * kDim, lane);
+  load_w32_raw(w_raw, w + (int64_t)tc * kHeads, lane);
 
   // Output: a raw buffer over this row's logits whose record size ends at the row's range
   // end; a lane whose key is below the range start (or below this workgroup's first tile)
@@ -175,6 +192,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
 
 #pragma unroll
   for (int i = 0; i <= kRowsPerLane * kLoads; i++) load_piece(tile_first, i);
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first decode waits
+  Q32 qf;
+  W32 wf;
+  decode_q32(qf, q_codes);
+  decode_w32(wf, w_raw);
 #pragma unroll
   for (int i = 0; i <= kRowsPerLane * kVecs; i++) store_piece(s_tile[0], i);
   __syncthreads();
