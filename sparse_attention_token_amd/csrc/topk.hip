@@ -632,9 +632,6 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   const uint8_t* row = logits + (int64_t)r * row_bytes;
   int* orow = out + (int64_t)r * out_ld;
 
-  for (int i = tid; i < kHistBins; i += T) s_hist[i] = 0;
-  if (tid < 4) s_cnt[tid] = 0;
-
   // Head [st, c0) and tail [c1, en): fewer than E columns each, one element per thread;
   // nvec aligned vectors in between (the host guarantees nvec <= T * V).
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + (uintptr_t)st * K::kElemBytes;
@@ -675,31 +672,45 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
       return (raw ^ t) + 0x00800000u;
     }
   };
-#pragma unroll
-  for (int i = 0; i < V; i++) {
-    const int vi = i * T + tid;
-    uint4 x = uint4{0u, 0u, 0u, 0u};
-    if (vi < nvec) x = vec[vi];
-#pragma unroll
-    for (int e = 0; e < E; e++) set_key(i * E + e, vi < nvec ? reg_key(K::elem(x, e)) : 0u);
-  }
+  // The row's loads are all issued first; the histogram is cleared and the barrier passed while
+  // they are in flight (a barrier waits for LDS operations only), and each vector's keys are
+  // built and counted as soon as it arrives.  The vectors are read through a buffer record that
+  // ends at the row's last whole vector (reads past it return zeros), so the loads carry no
+  // branches and the compiler can wait for each one by its position.
+  // The head and tail elements go first: waiting for them then does not wait for the vectors.
   const bool ha = tid < c0 - st, ta = tid < en - c1;
-  set_key(N, ha ? reg_key(K::load1(row, st + tid)) : 0u);
-  set_key(N + 1, ta ? reg_key(K::load1(row, c1 + tid)) : 0u);
+  const uint32_t raw_h = ha ? K::load1(row, st + tid) : 0u;
+  const uint32_t raw_t = ta ? K::load1(row, c1 + tid) : 0u;
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(vec), (short)0, nvec * 16, 0x00020000);
+  uint4 xv[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) {  // in order: the keys are built in this order
+    xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (i * T + tid) * 16, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // column of kk[j] relative to st
   const int col_base = c0 - st + tid * E;
   auto column = [&](int j) { return j < N ? col_base + (j / E) * T * E + (j % E) : (j == N ? tid : c1 - st + tid); };
 
+  for (int i = tid; i < kHistBins; i += T) s_hist[i] = 0;
+  if (tid < 4) s_cnt[tid] = 0;
   __syncthreads();
-  // First-digit histogram over the row's slots only (whole vectors past the row are skipped by
-  // the lanes holding them).
+  __builtin_amdgcn_sched_barrier(0);  // no key is built before the barrier (it would wait for its load there)
+  // Keys and the first-digit histogram over the row's slots only (whole vectors past the row
+  // are skipped by the lanes holding them).
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    if (i * T + tid < nvec) {
+    const bool in = i * T + tid < nvec;
+#pragma unroll
+    for (int e = 0; e < E; e++) set_key(i * E + e, in ? reg_key(K::elem(xv[i], e)) : 0u);
+    if (in) {
 #pragma unroll
       for (int e = 0; e < E; e++) atomicAdd(&s_hist[key_at(i * E + e) >> kShift], 1);
     }
   }
+  set_key(N, ha ? reg_key(raw_h) : 0u);
+  set_key(N + 1, ta ? reg_key(raw_t) : 0u);
   if (ha) atomicAdd(&s_hist[key_at(N) >> kShift], 1);
   if (ta) atomicAdd(&s_hist[key_at(N + 1) >> kShift], 1);
   launder(kk);  // the bins are recomputed where needed rather than kept, one register per key
