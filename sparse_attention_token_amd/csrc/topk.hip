@@ -728,10 +728,16 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   const uint32_t span = all ? 0u : 1u << kShift;
 
   // Each wavefront counts its columns of both kinds (ballots, scalar sums), reserves one range
-  // of each, then writes them in slot order: slot j of every lane, then slot j + 1.
+  // of each, then writes them in slot order: slot j of every lane, then slot j + 1.  The head
+  // and tail slots are skipped by a wavefront none of whose lanes holds one (their keys are 0,
+  // neither written nor a candidate): rows that start aligned have no head, and only a few lanes
+  // of one wavefront hold a tail.
+  const bool any_h = __builtin_amdgcn_ballot_w64(ha) != 0, any_t = __builtin_amdgcn_ballot_w64(ta) != 0;
+  auto skip = [&](int j) { return (j == N && !any_h) || (j == N + 1 && !any_t); };
   int cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
+    if (skip(j)) continue;
     const uint32_t key = key_at(j);
     cg += __popcll(__builtin_amdgcn_ballot_w64(key > top));
     ce += __popcll(__builtin_amdgcn_ballot_w64(key - t_eq < span));
@@ -755,6 +761,7 @@ __global__ __launch_bounds__(C::kThreads) void topk_reg_kernel(const uint8_t* __
   const uint32_t spare = kCap + lane;
 #pragma unroll
   for (int j = 0; j < N + 2; j++) {
+    if (skip(j)) continue;
     const uint32_t key = key_at(j);
     const bool gt = key > top;
     const bool eq = key - t_eq < span;
