@@ -213,6 +213,37 @@ def _sparse_workload(mxfp4):
     parallel(check, range(0, rows, 16))
 
 
+@pytest.mark.parametrize("mxfp4", [False, True])
+def test_workload5_scheduled_equals_one_shot(mxfp4):
+    """Workload 5 at full size: the per-step schedule, then the scheduled logits of the decode rows (paged pool)
+    and the prefill rows (gathered chunk), equal the one-shot calls (checked against the oracle above) bit for
+    bit.  The prefill rows' 32 chunks each are cut into segments at workgroup-share boundaries inside rows."""
+    c = synth.workload(5)
+    sbk, cbs, nd, rows = c["sbk"], c["cbs"], c["n_decode"], c["rows"]
+    bs, nb = c["block_size"], c["num_blocks"]
+    row = 68 if mxfp4 else ROW
+    stride = bs * row
+    quant = dsi.k_quant_and_cache_mxfp4 if mxfp4 else dsi.k_quant_and_cache
+    once = dsi.sparse_mqa_logits_mxfp4 if mxfp4 else dsi.sparse_mqa_logits
+    ks_t, ke_t, cand_t = dev(c["ks"]), dev(c["ke"]), dev(c["cand"])
+    si, end = dsi.expand_candidates(cand_t, ks_t, ke_t, cbs, sbk)
+    pool = torch.zeros(nb * stride, dtype=torch.uint8, device="cuda")
+    quant(dev(c["k_dec"]), dev(c["dec_slot_mapping"]), pool, bs, stride, nb)
+    Lp = c["Lp"]
+    pre = torch.zeros(Lp * row, dtype=torch.uint8, device="cuda")
+    quant(dev(c["k_pre"]), dev(np.arange(Lp, dtype=np.int64)), pre, Lp, Lp * row, 1)
+    q, w, bt, r2r = dev(c["q"]), dev(c["w"]), dev(c["block_table"]), dev(c["row_to_req"])
+    paged = dict(block_table=bt, row_to_req=r2r, block_size=bs, block_stride_bytes=stride)
+    sched_d = dsi.sparse_schedule(ks_t[:nd], ke_t[:nd], si[:nd], end[:nd], sbk, pool, num_k=nb, mxfp4=mxfp4, **paged)
+    sched_p = dsi.sparse_schedule(ks_t[nd:], ke_t[nd:], si[nd:], end[nd:], sbk, pre, num_k=Lp, mxfp4=mxfp4)
+    got_d = host(dsi.sparse_mqa_logits_scheduled(q[:nd], w[:nd], sched_d, sbk, pool, mxfp4=mxfp4))
+    got_p = host(dsi.sparse_mqa_logits_scheduled(q[nd:], w[nd:], sched_p, sbk, pre, mxfp4=mxfp4))
+    one_d = host(once(q[:nd], w[:nd], ks_t[:nd], ke_t[:nd], si[:nd], end[:nd], sbk, pool, num_k=nb, **paged))
+    one_p = host(once(q[nd:], w[nd:], ks_t[nd:], ke_t[nd:], si[nd:], end[nd:], sbk, pre, num_k=Lp))
+    assert np.array_equal(got_d, one_d), "decode rows"
+    assert np.array_equal(got_p, one_p), "prefill rows"
+
+
 def test_workload5_hierarchical_sparse():
     _sparse_workload(False)
 

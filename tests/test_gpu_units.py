@@ -893,6 +893,40 @@ def test_sparse_schedule_reused_over_two_layers(paged, mxfp4):
         assert_close(bf16_value(got[valid]), ref[valid], tol_fn=tol_bf16, what=f"layer {layer} scheduled logits")
 
 
+@pytest.mark.parametrize("mxfp4", [False, True])
+@pytest.mark.parametrize("sbk", [8, 16, 128])
+def test_sparse_schedule_long_rows_small_blocks(sbk, mxfp4):
+    """Rows of 10240 candidate columns (40 chunks of 256) in blocks of 8, 16 and 128 tokens: the scheduled call
+    spans several segments per row (the FP8 kernel's segment is min(32, sbk) chunks, so at 8 tokens per block
+    its 256 staged entries are full) and segments that start inside a row; every column equals the one-shot
+    call's, bit for bit."""
+    rng = np.random.default_rng(71 + sbk + mxfp4)
+    R, S, width = 6, 12000, 10240
+    row = 68 if mxfp4 else ROW
+    quant_ref = oracle.k_quant_and_cache_mxfp4 if mxfp4 else oracle.k_quant_and_cache
+    once = dsi.sparse_mqa_logits_mxfp4 if mxfp4 else dsi.sparse_mqa_logits
+    pc = synth.prefill_case(80 + sbk, T=R, S=S, first_pos=S - R)
+    ks = np.zeros(R, np.int32)
+    ks[1] = 5 * sbk + 3  # an unaligned start
+    ke = (S - R + 1 + np.arange(R)).astype(np.int32)
+    maxb = (np.maximum(ke - ks, 0) + sbk - 1) // sbk
+    num = width // sbk
+    cand = synth.draw_candidates(rng, maxb, num=num, distinct=num - 4, dup=2)
+    # (the oracle's expansion: 1280 sparse blocks per row at 8 tokens exceed the expansion kernel's 1024)
+    si_np, end_np = oracle.expand_candidates(cand, ks, ke, sbk, sbk)
+    si, end = dev(si_np), dev(end_np)
+    k = synth.draw_k(np.random.default_rng(90 + sbk), S)
+    pool = np.zeros(S * row, np.uint8)
+    quant_ref(k, np.arange(S, dtype=np.int64), pool, S, S * row)
+    p, q_t, w_t, ks_t, ke_t = dev(pool), dev(pc["q"]), dev(pc["w"]), dev(ks), dev(ke)
+    sched = dsi.sparse_schedule(ks_t, ke_t, si, end, sbk, p, mxfp4=mxfp4)
+    got = host(dsi.sparse_mqa_logits_scheduled(q_t, w_t, sched, sbk, p, mxfp4=mxfp4))
+    one = host(once(q_t, w_t, ks_t, ke_t, si, end, sbk, p))
+    assert got.shape == (R, width)
+    assert np.array_equal(got, one)
+    assert (got != np.int16(-128)).sum() > R * width // 2  # most columns score (0xFF80 is -inf)
+
+
 def test_sparse_schedule_bounds_the_source():
     """A schedule built for a larger source than the one scored: columns whose rows lie past the given source's
     size score -inf instead of reading outside it."""
