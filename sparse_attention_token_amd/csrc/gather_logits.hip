@@ -12,6 +12,7 @@
 // pairs, decoding the FP8 codes from LDS per use.  Out-of-range table entries, page ids
 // or tokens never produce an access outside the source: those keys score -inf.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "topk_split.h"
@@ -601,35 +602,14 @@ __device__ __forceinline__ void sp_gather(uint8_t* buf, const uint32_t* key_off,
 }
 
 // Source offsets (4-byte units, kSpAbsent for columns that score -inf) of columns [c0, c0 + n) of row r into s_off,
-// for key rows of ROWB bytes.  With a schedule (one entry per sparse block: the block's base offset, and the first
-// and one-past-last valid column within it; dsi_sparse_schedule), one entry serves all the block's columns and every
-// offset is bounded by the source's size; without one, every column follows its token through sparse_indices and,
-// when paged, the block table.
-template <int ROWB, bool SCHED>
+// for key rows of ROWB bytes: every column follows its token through sparse_indices and, when paged, the block
+// table.
+template <int ROWB>
 __device__ __forceinline__ void fill_offsets(uint32_t* s_off, int r, int c0, int n, int tid, int width, int sbk,
-                                             int sbk_shift, const unsigned long long* sched, int nsb, int64_t src_bytes,
-                                             const int* row_ks, const int* row_ke, const int* end,
+                                             int sbk_shift, const int* row_ks, const int* row_ke, const int* end,
                                              const int* sparse_indices, int64_t si_ld, int64_t num_k,
                                              const int* block_table, int64_t bt_ld, int bt_width, int num_reqs,
                                              const int* row_to_req, int block_size, int64_t block_stride) {
-  if constexpr (SCHED) {
-    const unsigned long long* srow = sched + (int64_t)r * nsb;
-    for (int t = tid; t < n; t += 256) {
-      const int c = c0 + t;
-      uint32_t off = kSpAbsent;
-      if (c < width) {
-        const unsigned long long e = srow[c >> sbk_shift];
-        const uint32_t base = (uint32_t)e, lo = (uint32_t)(e >> 32) & 0xFFu, hi = (uint32_t)(e >> 40) & 0xFFu;
-        const uint32_t o = (uint32_t)(c & (sbk - 1));
-        if (base != kSpAbsent && o >= lo && o < hi) {
-          const uint32_t x = base + o * (ROWB / 4);
-          if ((uint64_t)x * 4 + ROWB <= (uint64_t)src_bytes) off = x;
-        }
-      }
-      s_off[t] = off;
-    }
-    return;
-  }
   const bool paged = block_table != nullptr;
   const int ks = row_ks[r], ke = row_ke[r], e = end[r];
   const int req = paged ? (row_to_req ? row_to_req[r] : r) : 0;
@@ -681,9 +661,9 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   // Score chunks [c_first, c_end) (at most JOB) of row r.
   auto run = [&](int r, int c_first, int c_end) {
     __syncthreads();  // the previous segment's buffers and offsets are no longer read
-    fill_offsets<kRow, false>(s_off, r, c_first * kDcChunk, (c_end - c_first) * kDcChunk, tid, width, sbk, sbk_shift,
-                              nullptr, 0, 0, row_ks, row_ke, end, sparse_indices, si_ld, num_k, block_table, bt_ld,
-                              bt_width, num_reqs, row_to_req, block_size, block_stride);
+    fill_offsets<kRow>(s_off, r, c_first * kDcChunk, (c_end - c_first) * kDcChunk, tid, width, sbk, sbk_shift, row_ks,
+                       row_ke, end, sparse_indices, si_ld, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
+                       block_size, block_stride);
     Q32 qf;
     W32p wf;
     load_q32(qf, q + (int64_t)r * kHeads * kDim, lane);
@@ -737,119 +717,6 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
   }
 }
 
-// The FP8 kernel with a per-step schedule: the columns' sources follow from one entry per
-// sparse block, so a segment stages its blocks' entries (at most kSgBlk) instead of a source
-// offset per column, and runs up to a whole 8192-column row (kSgJob chunks; min(kSgJob, sbk)
-// keeps the entries within kSgBlk).  The columns' offsets are derived one chunk at a time into
-// a ring of three chunks: chunk c is scored while chunk c+1's gather is in flight and chunk
-// c+2's offsets are written.  A segment's set-up (the entries, q and the first gather) is then
-// paid once per row share rather than once per eight chunks.
-constexpr int kSgJob = 32;
-constexpr int kSgBlk = 256;
-
-__global__ __launch_bounds__(256, 2) void sparse_logits_sched_kernel(
-    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, int width, int sbk,
-    const uint8_t* __restrict__ k_src, int64_t has_src_rows, uint16_t* __restrict__ out, int64_t ld,
-    const unsigned long long* __restrict__ sched, int64_t src_bytes) {
-  constexpr int NB = 2;
-  constexpr int kKeysPerWave = kDcChunk / 4;
-  constexpr int kGroups = kKeysPerWave / 32;
-  constexpr int kStores = kKeysPerWave / 64;
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][kDcBuf];
-  __shared__ uint32_t s_off[3][kDcChunk];       // source offsets (4-byte units) of chunks c % 3
-  __shared__ unsigned long long s_blk[kSgBlk];  // the segment's schedule entries
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool has_src = has_src_rows > 0;
-  const int sbk_shift = __builtin_ctz(sbk);
-  const int nch = (width + kDcChunk - 1) / kDcChunk;
-  const int nsb = width >> sbk_shift;  // entries per row (the width is a whole number of blocks)
-  const int job = min(kSgJob, sbk);    // chunks per segment: job * 256 / sbk <= kSgBlk entries
-  const int kbase = wave * kKeysPerWave;
-
-  // Offsets of chunk c's columns, one per thread, from the entries staged from block blk0 on.
-  auto fill = [&](int c, int blk0) {
-    const int col = c * kDcChunk + tid;
-    uint32_t off = kSpAbsent;
-    if (col < width) {
-      const unsigned long long e = s_blk[(col >> sbk_shift) - blk0];
-      const uint32_t base = (uint32_t)e, lo = (uint32_t)(e >> 32) & 0xFFu, hi = (uint32_t)(e >> 40) & 0xFFu;
-      const uint32_t o = (uint32_t)(col & (sbk - 1));
-      if (base != kSpAbsent && o >= lo && o < hi) {
-        const uint32_t x = base + o * (kRow / 4);
-        if ((uint64_t)x * 4 + kRow <= (uint64_t)src_bytes) off = x;
-      }
-    }
-    s_off[c % 3][tid] = off;
-  };
-
-  // Score chunks [c_first, c_end) (at most job) of row r.
-  auto run = [&](int r, int c_first, int c_end) {
-    __syncthreads();  // the previous segment's buffers, offsets and entries are no longer read
-    const int blk0 = (c_first * kDcChunk) >> sbk_shift;
-    const int nblk = min(nsb, (c_end * kDcChunk) >> sbk_shift) - blk0;
-    const unsigned long long* srow = sched + (int64_t)r * nsb + blk0;
-    for (int i = tid; i < nblk; i += 256) s_blk[i] = srow[i];
-    Q32 qf;
-    W32p wf;
-    load_q32(qf, q + (int64_t)r * kHeads * kDim, lane);
-    load_w32p(wf, w + (int64_t)r * kHeads, lane);
-    const __amdgpu_buffer_rsrc_t out_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)r * ld, (short)0, width * 2, 0x00020000);
-    __syncthreads();  // entries visible
-    fill(c_first, blk0);
-    if (c_first + 1 < c_end) fill(c_first + 1, blk0);
-    __syncthreads();  // the first two chunks' offsets visible
-
-    auto gather = [&](int c) {
-      if (has_src) sp_gather(s_buf[(c - c_first) % NB], s_off[c % 3], k_src, wave, lane);
-    };
-    auto score_chunk = [&](int c, const uint8_t* buf) {
-      const uint32_t* coff = s_off[c % 3];
-#pragma unroll
-      for (int h = 0; h < kGroups / 2; h++) {
-        const uint8_t* keys = buf + (kbase + 64 * h) * kDcRow;
-        if (h == 0) {
-          if (c + 1 < c_end) gather(c + 1);
-          if (c + 2 < c_end) fill(c + 2, blk0);  // chunk c-1's slot: read by nothing after the last barrier
-        }
-        K32 kb;
-        load_k32_raw(kb, keys, lane);
-        f32x16 a0, a1, b0 = {}, b1 = {};
-        float acc[4];
-        dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kDcRow, lane, wf, b0, b1, acc, [](int) {});
-        dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
-        const float v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
-        const int key = kbase + 64 * h + lane;  // key within the chunk
-        const float scale = *reinterpret_cast<const float*>(buf + key * kDcRow + 140);
-        const uint16_t o = coff[key] != kSpAbsent ? f32_to_bf16_rne(v * scale) : (uint16_t)0xFF80u;
-        __builtin_amdgcn_raw_buffer_store_b16(o, out_rsrc, (c * kDcChunk + key) * 2, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    gather(c_first);
-    for (int cc = c_first; cc < c_end; cc++) {
-      // as in the decode kernel: after chunk cc's gather this wavefront issued the stores of
-      // the chunk before it (when cc is not the segment's first)
-      if (has_src) wait_gather<NB, kStores>(min(cc - c_first, 1));
-      __syncthreads();
-      score_chunk(cc, s_buf[(cc - c_first) % NB]);
-    }
-  };
-
-  const int64_t total = (int64_t)rows * nch;
-  int64_t g = (int64_t)blockIdx.x * total / gridDim.x;
-  const int64_t g1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
-  while (g < g1) {  // uniform
-    const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
-    const int len = (int)min((int64_t)min(nch - lc, job), g1 - g);
-    run(r, lc, lc + len);
-    g += len;
-  }
-}
-
 // ------------------------------------------------------------------ sparse columns, MXFP4 cache
 // The same work split and DMA ring on 68-byte MXFP4 key rows (P1 motivation and
 // implementation: the V4.1 sparse indexer scores FP8 q against an MXFP4 k cache), with the
@@ -864,14 +731,14 @@ __device__ __forceinline__ void mx_gather(uint8_t* buf, const uint32_t* key_off,
   });
 }
 
-template <int JOB, bool SCHED>
+template <int JOB>
 __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, const int* __restrict__ row_ks,
     const int* __restrict__ row_ke, const int* __restrict__ sparse_indices, int64_t si_ld, int width,
     const int* __restrict__ end, int sbk, const uint8_t* __restrict__ k_src, int64_t num_k,
     const int* __restrict__ block_table, int64_t bt_ld, int bt_width, int num_reqs,
     const int* __restrict__ row_to_req, int block_size, int64_t block_stride, uint16_t* __restrict__ out,
-    int64_t ld, const unsigned long long* __restrict__ sched, int64_t src_bytes) {
+    int64_t ld) {
   constexpr int NB = 2;
   constexpr int kKeysPerWave = kDcChunk / 4;
   constexpr int kGroups = kKeysPerWave / 32;
@@ -888,9 +755,9 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
 
   auto run = [&](int r, int c_first, int c_end) {
     __syncthreads();  // the previous segment's buffers and offsets are no longer read
-    fill_offsets<kMxRow, SCHED>(s_off, r, c_first * kDcChunk, (c_end - c_first) * kDcChunk, tid, width, sbk, sbk_shift,
-                         sched, width >> sbk_shift, src_bytes, row_ks, row_ke, end, sparse_indices, si_ld, num_k,
-                         block_table, bt_ld, bt_width, num_reqs, row_to_req, block_size, block_stride);
+    fill_offsets<kMxRow>(s_off, r, c_first * kDcChunk, (c_end - c_first) * kDcChunk, tid, width, sbk, sbk_shift,
+                         row_ks, row_ke, end, sparse_indices, si_ld, num_k, block_table, bt_ld, bt_width, num_reqs,
+                         row_to_req, block_size, block_stride);
     Q32b qf;
     W32p wf;
     load_q32_bf16(qf, q + (int64_t)r * kHeads * kDim, lane);
@@ -938,6 +805,140 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_mx_kernel(
   while (g < g1) {  // uniform
     const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
     const int len = (int)min((int64_t)min(nch - lc, JOB), g1 - g);
+    run(r, lc, lc + len);
+    g += len;
+  }
+}
+
+// The sparse kernels with a per-step schedule (FP8 or MXFP4 key rows): the columns' sources
+// follow from one entry per sparse block, so a segment stages its blocks' entries (at most
+// kSgBlk) instead of a source offset per column, and runs up to a whole 8192-column row
+// (kSgJob chunks; min(kSgJob, sbk) keeps the entries within kSgBlk).  The columns' offsets are
+// derived one chunk at a time into a ring of three chunks: chunk c is scored while chunk c+1's
+// gather is in flight and chunk c+2's offsets are written.  A segment's set-up (the entries, q
+// and the first gather) is then paid once per row share rather than once per eight chunks.
+constexpr int kSgJob = 32;
+constexpr int kSgBlk = 256;
+
+template <bool MX>
+__global__ __launch_bounds__(256, 2) void sparse_logits_sched_kernel(
+    const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int rows, int width, int sbk,
+    const uint8_t* __restrict__ k_src, int64_t has_src_rows, uint16_t* __restrict__ out, int64_t ld,
+    const unsigned long long* __restrict__ sched, int64_t src_bytes) {
+  constexpr int NB = 2;
+  constexpr int kKeysPerWave = kDcChunk / 4;
+  constexpr int kGroups = kKeysPerWave / 32;
+  constexpr int kStores = kKeysPerWave / 64;
+  constexpr int kRowBytes = MX ? kMxRow : kRow;
+  constexpr int kLdsRowBytes = MX ? kMxLds : kDcRow;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[NB][MX ? kMxBuf : kDcBuf];
+  __shared__ uint32_t s_off[3][kDcChunk];       // source offsets (4-byte units) of chunks c % 3
+  __shared__ unsigned long long s_blk[kSgBlk];  // the segment's schedule entries
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_src = has_src_rows > 0;
+  const int sbk_shift = __builtin_ctz(sbk);
+  const int nch = (width + kDcChunk - 1) / kDcChunk;
+  const int nsb = width >> sbk_shift;  // entries per row (the width is a whole number of blocks)
+  const int job = min(kSgJob, sbk);    // chunks per segment: job * 256 / sbk <= kSgBlk entries
+  const int kbase = wave * kKeysPerWave;
+
+  // Offsets of chunk c's columns, one per thread, from the entries staged from block blk0 on.
+  auto fill = [&](int c, int blk0) {
+    const int col = c * kDcChunk + tid;
+    uint32_t off = kSpAbsent;
+    if (col < width) {
+      const unsigned long long e = s_blk[(col >> sbk_shift) - blk0];
+      const uint32_t base = (uint32_t)e, lo = (uint32_t)(e >> 32) & 0xFFu, hi = (uint32_t)(e >> 40) & 0xFFu;
+      const uint32_t o = (uint32_t)(col & (sbk - 1));
+      if (base != kSpAbsent && o >= lo && o < hi) {
+        const uint32_t x = base + o * (kRowBytes / 4);
+        if ((uint64_t)x * 4 + kRowBytes <= (uint64_t)src_bytes) off = x;
+      }
+    }
+    s_off[c % 3][tid] = off;
+  };
+
+  // Score chunks [c_first, c_end) (at most job) of row r.
+  auto run = [&](int r, int c_first, int c_end) {
+    __syncthreads();  // the previous segment's buffers, offsets and entries are no longer read
+    const int blk0 = (c_first * kDcChunk) >> sbk_shift;
+    const int nblk = min(nsb, (c_end * kDcChunk) >> sbk_shift) - blk0;
+    const unsigned long long* srow = sched + (int64_t)r * nsb + blk0;
+    for (int i = tid; i < nblk; i += 256) s_blk[i] = srow[i];
+    typename std::conditional<MX, Q32b, Q32>::type qf;
+    W32p wf;
+    if constexpr (MX)
+      load_q32_bf16(qf, q + (int64_t)r * kHeads * kDim, lane);
+    else
+      load_q32(qf, q + (int64_t)r * kHeads * kDim, lane);
+    load_w32p(wf, w + (int64_t)r * kHeads, lane);
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)r * ld, (short)0, width * 2, 0x00020000);
+    __syncthreads();  // entries visible
+    fill(c_first, blk0);
+    if (c_first + 1 < c_end) fill(c_first + 1, blk0);
+    __syncthreads();  // the first two chunks' offsets visible
+
+    auto gather = [&](int c) {
+      if (!has_src) return;
+      if constexpr (MX)
+        mx_gather(s_buf[(c - c_first) % NB], s_off[c % 3], k_src, wave, lane);
+      else
+        sp_gather(s_buf[(c - c_first) % NB], s_off[c % 3], k_src, wave, lane);
+    };
+    auto score_chunk = [&](int c, const uint8_t* buf) {
+      const uint32_t* coff = s_off[c % 3];
+#pragma unroll
+      for (int h = 0; h < kGroups / 2; h++) {
+        const uint8_t* keys = buf + (kbase + 64 * h) * kLdsRowBytes;
+        if (h == 0) {
+          if (c + 1 < c_end) gather(c + 1);
+          if (c + 2 < c_end) fill(c + 2, blk0);  // chunk c-1's slot: read by nothing after the last barrier
+        }
+        f32x16 a0, a1, b0 = {}, b1 = {};
+        float acc[4];
+        float v;
+        if constexpr (MX) {
+          K32b kb;
+          const MxRaw r0 = load_mx_raw(keys, lane);
+#pragma unroll
+          for (int j = 0; j < 4; j++) decode_mx_pair(kb, r0, j);
+          mx_phase<false, true>(a0, a1, qf, kb, keys + 32 * kLdsRowBytes, lane, wf, b0, b1, acc, [](int) {});
+          mx_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+          v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
+        } else {
+          K32 kb;
+          load_k32_raw(kb, keys, lane);
+          dc_phase<false, true>(a0, a1, qf, kb, keys + 32 * kLdsRowBytes, lane, wf, b0, b1, acc, [](int) {});
+          dc_phase<true, false>(b0, b1, qf, kb, keys, lane, wf, a0, a1, acc, [](int) {});
+          v = combine_halves(dc_acc_sum(acc), dc_head_sum(wf, b0, b1));
+        }
+        const int key = kbase + 64 * h + lane;  // key within the chunk
+        if constexpr (!MX) v *= *reinterpret_cast<const float*>(buf + key * kDcRow + 140);  // the row's scale
+        const uint16_t o = coff[key] != kSpAbsent ? f32_to_bf16_rne(v) : (uint16_t)0xFF80u;
+        __builtin_amdgcn_raw_buffer_store_b16(o, out_rsrc, (c * kDcChunk + key) * 2, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    gather(c_first);
+    for (int cc = c_first; cc < c_end; cc++) {
+      // as in the decode kernel: after chunk cc's gather this wavefront issued the stores of
+      // the chunk before it (when cc is not the segment's first)
+      if (has_src) wait_gather<NB, kStores>(min(cc - c_first, 1));
+      __syncthreads();
+      score_chunk(cc, s_buf[(cc - c_first) % NB]);
+    }
+  };
+
+  const int64_t total = (int64_t)rows * nch;
+  int64_t g = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t g1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
+  while (g < g1) {  // uniform
+    const int r = (int)(g / nch), lc = (int)(g - (int64_t)r * nch);
+    const int len = (int)min((int64_t)min(nch - lc, job), g1 - g);
     run(r, lc, lc + len);
     g += len;
   }
@@ -1235,9 +1236,9 @@ extern "C" int dsi_sparse_mqa_logits_mxfp4(const uint8_t* q, const uint16_t* w, 
   const int64_t nch = (width + kDcChunk - 1) / kDcChunk;
   const int64_t slots = 2 * (int64_t)cu_count();
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
-  hipLaunchKernelGGL((sparse_logits_mx_kernel<kMxJob, false>), grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke, sparse_indices,
-                     si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs, row_to_req,
-                     block_size, block_stride_bytes, logits_bf16, ld, (const unsigned long long*)nullptr, (int64_t)0);
+  hipLaunchKernelGGL((sparse_logits_mx_kernel<kMxJob>), grid, dim3(256), 0, stream, q, w, rows, row_ks, row_ke,
+                     sparse_indices, si_ld, (int)width, end, sbk, k_src, num_k, block_table, bt_ld, bt_width, num_reqs,
+                     row_to_req, block_size, block_stride_bytes, logits_bf16, ld);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
@@ -1301,14 +1302,8 @@ int sparse_scheduled(const uint8_t* q, const uint16_t* w, int32_t rows, const ui
   const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(slots, nch * rows)));
   const int64_t has_src = k_src_bytes > 0 ? 1 : 0;  // the kernels gather only when the source has rows
   const unsigned long long* sched = reinterpret_cast<const unsigned long long*>(schedule);
-  if (MX)
-    hipLaunchKernelGGL((sparse_logits_mx_kernel<kMxJob, true>), grid, dim3(256), 0, stream, q, w, rows, (const int*)nullptr,
-                       (const int*)nullptr, (const int*)nullptr, (int64_t)0, (int)width, (const int*)nullptr, sbk,
-                       k_src, has_src, (const int*)nullptr, (int64_t)0, 0, 0, (const int*)nullptr, 0, (int64_t)0,
-                       logits_bf16, ld, sched, k_src_bytes);
-  else
-    hipLaunchKernelGGL(sparse_logits_sched_kernel, grid, dim3(256), 0, stream, q, w, rows, (int)width, sbk, k_src,
-                       has_src, logits_bf16, ld, sched, k_src_bytes);
+  hipLaunchKernelGGL(sparse_logits_sched_kernel<MX>, grid, dim3(256), 0, stream, q, w, rows, (int)width, sbk, k_src,
+                     has_src, logits_bf16, ld, sched, k_src_bytes);
   return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH;
 }
 
