@@ -40,10 +40,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kRow = 132;              // bytes per cache row
-constexpr int kLdsKeyStride = 144;     // LDS bytes per FP8 key row: 128 codes + pad; 36 dwords = 4 mod 32
-                                       // banks, so 16-byte reads by 8 consecutive keys are conflict-free
 constexpr int kLdsKeyStrideF16 = 272;  // LDS bytes per f16 key row: 256 + pad, 68 dwords = 4 mod 32 banks
 
+// The 16x16x32 f16 matrix instruction (the dense prefill kernel's; its operand layout is described there).
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -138,132 +137,6 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t x0, uint32_t x1) {
 __device__ __forceinline__ uint32_t f32_key(uint32_t u) { return (u & 0x80000000u) ? ~u : (u | 0x80000000u); }
 __device__ __forceinline__ uint32_t bf16_key(uint32_t h) { return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u); }
 
-// 4x4 transpose-reduce across the lane groups g = lane/16.  v[j], j = 0..3, are
-// this lane's partial sums of four outputs; on return the lane holds the full
-// sum of output j = g (summed over the four lane groups of its column).
-__device__ __forceinline__ float transpose_reduce4(const float v[4], int lane) {
-  const bool hi = lane >= 32;        // g in {2,3}
-  const bool odd = (lane >> 4) & 1;  // g in {1,3}
-  float s0 = hi ? v[0] : v[2];
-  float s1 = hi ? v[1] : v[3];
-  float r0 = __shfl_xor(s0, 32);
-  float r1 = __shfl_xor(s1, 32);
-  float k0 = (hi ? v[2] : v[0]) + r0;  // output 2*hi + 0
-  float k1 = (hi ? v[3] : v[1]) + r1;  // output 2*hi + 1
-  float s = odd ? k0 : k1;
-  float r = __shfl_xor(s, 16);
-  return (odd ? k1 : k0) + r;
-}
-
-// A-operand fragments of one query row: four 16-head tiles x four 32-dim slices.
-struct QFrag {
-  f16x8 a[4][4];
-};
-
-// Load q[row] (64 x 128 codes, contiguous) and decode it into this lane's A fragments:
-// lane (head n, group g) reads the codes [32g, 32g+32) of head hb*16+n; slice s takes 8.
-__device__ __forceinline__ void load_q(QFrag& f, const uint8_t* q_row, int lane) {
-  const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int hb = 0; hb < 4; hb++) {
-    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 16 + n) * kDim + g * 32);
-    const uint4 x0 = p[0], x1 = p[1];
-    f.a[hb][0] = e4m3x8_to_f16x8(x0.x, x0.y);
-    f.a[hb][1] = e4m3x8_to_f16x8(x0.z, x0.w);
-    f.a[hb][2] = e4m3x8_to_f16x8(x1.x, x1.y);
-    f.a[hb][3] = e4m3x8_to_f16x8(x1.z, x1.w);
-  }
-}
-
-// This lane's 16 head weights of one row: heads hb*16 + 4*(lane/16) + i.
-struct WFrag {
-  float w[4][4];
-};
-
-__device__ __forceinline__ void load_w(WFrag& f, const uint16_t* w_row, int lane) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int hb = 0; hb < 4; hb++) {
-    uint2 x = *reinterpret_cast<const uint2*>(w_row + hb * 16 + g * 4);
-    f.w[hb][0] = bf16_to_f32(x.x & 0xFFFFu);
-    f.w[hb][1] = bf16_to_f32(x.x >> 16);
-    f.w[hb][2] = bf16_to_f32(x.y & 0xFFFFu);
-    f.w[hb][3] = bf16_to_f32(x.y >> 16);
-  }
-}
-
-// B-operand fragments for 16 keys: four 32-dim slices.
-struct KFrag {
-  f16x8 b[4];
-};
-
-// From FP8 key rows in LDS (kLdsKeyStride apart): read this lane's 32 codes and decode.
-__device__ __forceinline__ void load_kfrag_fp8(KFrag& f, const uint8_t* keys, int lane) {
-  const int n = lane & 15, g = lane >> 4;
-  const uint4* p = reinterpret_cast<const uint4*>(keys + n * kLdsKeyStride + g * 32);
-  const uint4 x0 = p[0], x1 = p[1];
-  f.b[0] = e4m3x8_to_f16x8(x0.x, x0.y);
-  f.b[1] = e4m3x8_to_f16x8(x0.z, x0.w);
-  f.b[2] = e4m3x8_to_f16x8(x1.x, x1.y);
-  f.b[3] = e4m3x8_to_f16x8(x1.z, x1.w);
-}
-
-// From key rows already decoded to f16 in LDS (kLdsKeyStrideF16 apart).
-__device__ __forceinline__ void load_kfrag_f16(KFrag& f, const uint8_t* keys, int lane) {
-  const int n = lane & 15, g = lane >> 4;
-  const f16x8* p = reinterpret_cast<const f16x8*>(keys + n * kLdsKeyStrideF16 + g * 64);
-#pragma unroll
-  for (int s = 0; s < 4; s++) f.b[s] = p[s];
-}
-
-// Head-weighted partials of four (row, 16-key group) outputs at once: out j uses
-// q[rows[j]] and kb[kgs[j]].  The 64 MFMAs run as 16 independent accumulator chains
-// (4 outputs x 4 head tiles) taken slice by slice, so consecutive MFMAs never wait on
-// each other; then each lane weights and sums its 16 heads per output.
-template <int NQ, int NK>
-__device__ __forceinline__ void score4(const QFrag (&q)[NQ], const WFrag (&w)[NQ], const KFrag (&kb)[NK],
-                                       const int (&rows)[4], const int (&kgs)[4], float (&part)[4]) {
-  f32x4 c[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-#pragma unroll
-    for (int hb = 0; hb < 4; hb++) c[j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; s++)
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int hb = 0; hb < 4; hb++) c[j][hb] = mfma_f16(q[rows[j]].a[hb][s], kb[kgs[j]].b[s], c[j][hb]);
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    float acc = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < 4; hb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) acc = fmaf(w[rows[j]].w[hb][i], c[j][hb][i], acc);
-    part[j] = acc;
-  }
-}
-
-// Copy one 16-byte chunk of a contiguous run of 132-byte cache rows into the FP8
-// LDS key layout: dword d of the run belongs to row d/33, word d%33 (word 32 is
-// the fp32 scale).  `chunk` is the chunk index within the run, `key0` the LDS key
-// slot of the run's first row.
-__device__ __forceinline__ void scatter_chunk(uint8_t* lds_codes, float* lds_scale, int key0, int chunk,
-                                              const uint4& v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    int d = chunk * 4 + j;
-    int row = d / 33, word = d - row * 33;
-    if (word < 32)
-      *reinterpret_cast<uint32_t*>(lds_codes + (key0 + row) * kLdsKeyStride + word * 4) = w[j];
-    else
-      lds_scale[key0 + row] = __uint_as_float(w[j]);
-  }
-}
-
-
 // ---------------------------------------------------------------------------
 // 32x32x16 layout (v_mfma_f32_32x32x16_f16), used where a wavefront scores one query row
 // against 32-key groups:
@@ -285,67 +158,21 @@ struct Q32 {
   f16x8 a[2][8];
 };
 
-// The codes behind load_q32's fragments, as loaded (so that a caller can issue other loads
-// before decoding them).
-__device__ __forceinline__ void load_q32_codes(uint4 (&x)[2][4], const uint8_t* q_row, int lane) {
+__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
   const int m = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int hb = 0; hb < 2; hb++) {
     const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 32 + m) * kDim + h * 64);
 #pragma unroll
-    for (int j = 0; j < 4; j++) x[hb][j] = p[j];
+    for (int j = 0; j < 4; j++) {
+      const uint4 x = p[j];
+      f.a[hb][2 * j] = e4m3x8_to_f16x8(x.x, x.y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x.z, x.w);
+    }
   }
 }
 
-__device__ __forceinline__ void decode_q32(Q32& f, const uint4 (&x)[2][4]) {
-#pragma unroll
-  for (int hb = 0; hb < 2; hb++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      f.a[hb][2 * j] = e4m3x8_to_f16x8(x[hb][j].x, x[hb][j].y);
-      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x[hb][j].z, x[hb][j].w);
-    }
-}
-
-__device__ __forceinline__ void load_q32(Q32& f, const uint8_t* q_row, int lane) {
-  uint4 x[2][4];
-  load_q32_codes(x, q_row, lane);
-  decode_q32(f, x);
-}
-
-// The weights of the 32 heads this lane holds in C: w[hb][i] is head hb*32 + 8*(i/4) + 4h + i%4.
-struct W32 {
-  float w[2][16];
-};
-
-// The bf16 weights behind load_w32's values, as loaded.
-__device__ __forceinline__ void load_w32_raw(uint2 (&x)[2][4], const uint16_t* w_row, int lane) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int hb = 0; hb < 2; hb++)
-#pragma unroll
-    for (int b = 0; b < 4; b++) x[hb][b] = *reinterpret_cast<const uint2*>(w_row + hb * 32 + 8 * b + 4 * h);
-}
-
-__device__ __forceinline__ void decode_w32(W32& f, const uint2 (&x)[2][4]) {
-#pragma unroll
-  for (int hb = 0; hb < 2; hb++)
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      f.w[hb][4 * b + 0] = bf16_to_f32(x[hb][b].x & 0xFFFFu);
-      f.w[hb][4 * b + 1] = bf16_to_f32(x[hb][b].x >> 16);
-      f.w[hb][4 * b + 2] = bf16_to_f32(x[hb][b].y & 0xFFFFu);
-      f.w[hb][4 * b + 3] = bf16_to_f32(x[hb][b].y >> 16);
-    }
-}
-
-__device__ __forceinline__ void load_w32(W32& f, const uint16_t* w_row, int lane) {
-  uint2 x[2][4];
-  load_w32_raw(x, w_row, lane);
-  decode_w32(f, x);
-}
-
-// B fragments of one 32-key group from the f16 tile: key l%32, dims [64h + 8s, +8).
+// B fragments of one 32-key group: key l%32, dims [64h + 8s, +8).
 struct K32 {
   f16x8 b[8];
 };

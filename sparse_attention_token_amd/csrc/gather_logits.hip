@@ -124,8 +124,9 @@ __device__ __forceinline__ void load_k32_raw(K32& f, const uint8_t* keys, int la
   }
 }
 
-// The 32 head weights of load_w32's layout kept as bf16 pairs (16 registers instead of 32):
-// w[hb][e / 2] holds weights e (low half) and e + 1 (high half) of head block hb.
+// The weights of the 32 heads this lane holds in C, kept as bf16 pairs (16 registers instead
+// of 32): weight e of head block hb is head hb*32 + 8*(e/4) + 4h + e%4, and w[hb][e / 2]
+// holds weights e (low half) and e + 1 (high half).
 struct W32p {
   uint32_t w[2][8];
   __device__ __forceinline__ float get(int hb, int e) const {

@@ -5,17 +5,19 @@
 // The contraction [T*64, 128] x [128, S] runs on the matrix cores with the FP8 codes
 // decoded exactly to f16 (common.h); the head-weighted sum is the epilogue.
 //
-// Matrix instruction: v_mfma_f32_32x32x16_f16 (measured on gfx950 to sustain a higher
-// rate than the 16x16x32 form, with only two independent accumulator chains).
-//   A = 32 heads x 16 dims of q   (lane l: head l%32, 8 dims of lane half h = l/32)
-//   B = 16 dims x 32 keys of K    (lane l: key  l%32, the same 8 dims)
-//   C = 32 heads x 32 keys, lane l holds heads 8*(i/4) + 4*h + i%4 (i < 16) of key l%32.
-// Lane half h owns dims [64h, 64h+64) of the 128 and feeds 8 of them to each of eight
-// slices; A and B use the same assignment, so the sum over dims is complete.  Two head
-// blocks cover the 64 heads, so after 16 MFMAs each lane holds 32 heads of one key and
-// the head-weighted sum is 32 FMAs.  The two lane halves hold the other 32 heads of the
-// same key: for a 64-key tile, one v_permlane32_swap exchanges the halves' partial sums
-// of the tile's two 32-key groups, and one add leaves lane l with key l of the tile.
+// Matrix instruction: v_mfma_f32_16x16x32_f16.  On random FP8 operands the chip is at its
+// power limit, and this form draws less energy per flop than the 32x32x16 one: its clock
+// stays higher by more than it loses in issue rate.
+//   A = 16 heads x 32 dims of q   (lane l: head l%16, 8 dims of lane group g = l/16)
+//   B = 32 dims x 16 keys of K    (lane l: key  l%16, the same 8 dims)
+//   C = 16 heads x 16 keys, lane l holds heads 4g + i (i < 4) of key l%16.
+// Lane group g owns dims [32g, 32g+32) of the 128 and feeds 8 of them to each of four
+// slices; A and B use the same assignment, so the sum over dims is complete.  Four head
+// blocks cover the 64 heads and a 32-key group is two 16-key blocks: after its 32 MFMAs each
+// lane holds 16 heads of each of two keys, and the head-weighted sums are 32 FMAs.  The other
+// three lane groups hold the other 48 heads of the same keys: for a 64-key half tile, two
+// v_permlane32_swap and one v_permlane16_swap exchange the four groups' partial sums of the
+// half's two 32-key groups, and three adds leave each lane with one key of the half.
 //
 // A workgroup of 8 wavefronts (one per CU) owns 8 query rows, one per wavefront, its q
 // decoded once into VGPRs, and a share of the keys streamed through LDS in double-buffered
@@ -41,48 +43,123 @@ constexpr int kRowsPerLane = kTileKeys / 64;  // staging: lane r of wave p takes
 constexpr int kStageDims = kDim / kPfRows;     // dims [kStageDims*p, kStageDims*(p+1))
 static_assert(kStageDims % 16 == 0, "staging moves whole 16-byte pieces");
 
-// One 32-key group on the matrix cores, with the previous group's head sum and other work
-// threaded between its 16 MFMAs in a fixed order (sched_barrier fences keep the compiler
-// from regrouping them).  Step i issues MFMA i (slice i/2, head block i%2) into x, then two
-// of the 32 FMAs of the head sum of y (the previous group's accumulators), then, after the
-// second MFMA of a slice has read it, the same slice of the next group's B fragments (when
-// kLoadNext), then extra(i).
+// This lane's A fragments of one query row: head block hb (heads 16hb + l%16), slice s
+// (dims 32g + 8s + [0, 8)), decoded from the codes as loaded.
+struct Q16 {
+  f16x8 a[4][4];
+};
+
+__device__ __forceinline__ void load_q16_codes(uint4 (&x)[4][2], const uint8_t* q_row, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) {
+    const uint4* p = reinterpret_cast<const uint4*>(q_row + (hb * 16 + n) * kDim + g * 32);
+    x[hb][0] = p[0];
+    x[hb][1] = p[1];
+  }
+}
+
+__device__ __forceinline__ void decode_q16(Q16& f, const uint4 (&x)[4][2]) {
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      f.a[hb][2 * j] = e4m3x8_to_f16x8(x[hb][j].x, x[hb][j].y);
+      f.a[hb][2 * j + 1] = e4m3x8_to_f16x8(x[hb][j].z, x[hb][j].w);
+    }
+}
+
+// The weights of the 16 heads this lane holds in C: w[hb][i] is head 16hb + 4g + i.
+struct W16 {
+  float w[4][4];
+};
+
+__device__ __forceinline__ void load_w16_raw(uint2 (&x)[4], const uint16_t* w_row, int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) x[hb] = *reinterpret_cast<const uint2*>(w_row + hb * 16 + g * 4);
+}
+
+__device__ __forceinline__ void decode_w16(W16& f, const uint2 (&x)[4]) {
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) {
+    f.w[hb][0] = bf16_to_f32(x[hb].x & 0xFFFFu);
+    f.w[hb][1] = bf16_to_f32(x[hb].x >> 16);
+    f.w[hb][2] = bf16_to_f32(x[hb].y & 0xFFFFu);
+    f.w[hb][3] = bf16_to_f32(x[hb].y >> 16);
+  }
+}
+
+// B fragments of one 32-key group from the f16 tile: key block kb (keys 16kb + l%16), slice s
+// (dims 32g + 8s + [0, 8)).
+struct K16 {
+  f16x8 b[2][4];
+};
+
+constexpr int kF16PerRow = kLdsKeyStrideF16 / 16;  // f16x8 units per LDS key row
+
+__device__ __forceinline__ const f16x8* k16_base(const uint8_t* keys, int lane) {
+  return reinterpret_cast<const f16x8*>(keys + (lane & 15) * kLdsKeyStrideF16 + (lane >> 4) * 64);
+}
+
+// All eight fragments of one group (after a barrier, when nothing else can run).
+__device__ __forceinline__ void load_k16(K16& f, const uint8_t* keys, int lane) {
+  const f16x8* p = k16_base(keys, lane);
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int s = 0; s < 4; s++) f.b[kb][s] = p[kb * 16 * kF16PerRow + s];
+}
+
+// Accumulators of one group: head block hb x key block kb.
+struct Acc16 {
+  f32x4 x[4][2];
+};
+
+// One 32-key group on the matrix cores, with the previous group's head sums and other work
+// threaded between its 32 MFMAs in a fixed order (sched_barrier fences keep the compiler from
+// regrouping them).  Step i issues MFMA i (slice i/8, key block (i/4)%2, head block i%4) into
+// x, then FMA i of the head sums of y (the previous group's accumulators: key block i/16, head
+// block (i/4)%4, head 4g + i%4), then, after the last MFMA of a slice and key block has read
+// it, that fragment of the next group (when kLoadNext), and on even steps extra(i/2).  acc[0]
+// + acc[1] is key block 0's sum, acc[2] + acc[3] key block 1's.
 template <bool kLoadNext, typename Extra>
-__device__ __forceinline__ void group_phase(f32x16& x0, f32x16& x1, const Q32& q, K32& kb, const uint8_t* next,
-                                            int lane, const W32& w, const f32x16& y0, const f32x16& y1,
-                                            float (&acc)[4], Extra&& extra) {
-  const f16x8* np = reinterpret_cast<const f16x8*>(next + (lane & 31) * kLdsKeyStrideF16 + (lane >> 5) * 128);
+__device__ __forceinline__ void group_phase(Acc16& x, const Q16& q, K16& kb, const uint8_t* next, int lane,
+                                            const W16& w, const Acc16& y, float (&acc)[4], Extra&& extra) {
+  const f16x8* np = k16_base(next, lane);
 #pragma unroll
   for (int j = 0; j < 4; j++) acc[j] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int sl = i >> 1;
-    if ((i & 1) == 0)
-      x0 = mfma32(q.a[0][sl], kb.b[sl], i == 0 ? f32x16{} : x0);
-    else
-      x1 = mfma32(q.a[1][sl], kb.b[sl], i == 1 ? f32x16{} : x1);
+  for (int i = 0; i < 32; i++) {
+    const int s = i >> 3, kk = (i >> 2) & 1, hb = i & 3;
+    x.x[hb][kk] = mfma_f16(q.a[hb][s], kb.b[kk][s], s == 0 ? f32x4{} : x.x[hb][kk]);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int e = 2 * i; e < 2 * i + 2; e++) {
-      if (e < 16)
-        acc[e & 3] = fmaf(w.w[0][e], y0[e], acc[e & 3]);
-      else
-        acc[e & 3] = fmaf(w.w[1][e - 16], y1[e - 16], acc[e & 3]);
+    {
+      const int k2 = i >> 4, h2 = (i >> 2) & 3, e = i & 3;
+      acc[2 * k2 + (i & 1)] = fmaf(w.w[h2][e], y.x[h2][k2][e], acc[2 * k2 + (i & 1)]);
     }
-    if (kLoadNext && (i & 1)) kb.b[sl] = np[sl];
-    extra(i);
+    if (kLoadNext && hb == 3) kb.b[kk][s] = np[kk * 16 * kF16PerRow + s];
+    if ((i & 1) == 0) extra(i >> 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__device__ __forceinline__ float acc_sum(const float (&acc)[4]) { return (acc[0] + acc[1]) + (acc[2] + acc[3]); }
-
-// All eight slices of one group's B fragments (after a barrier, when nothing else can run).
-__device__ __forceinline__ void load_k32(K32& f, const uint8_t* keys, int lane) {
-  const f16x8* p = reinterpret_cast<const f16x8*>(keys + (lane & 31) * kLdsKeyStrideF16 + (lane >> 5) * 128);
-#pragma unroll
-  for (int s = 0; s < 8; s++) f.b[s] = p[s];
+// The full sums of a 64-key half tile from its two groups' partial sums (gXkY: group X, key
+// block Y; each over the 16 heads of this lane's group).  The first swap pairs lane groups
+// {0, 2} and {1, 3} of each group; the second pairs the two results.  Lane l ends with key
+// half_key(l) of the half.
+__device__ __forceinline__ float combine_groups(float g0k0, float g0k1, float g1k0, float g1k1) {
+  const auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(g0k0), __float_as_uint(g0k1), false, false);
+  const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(g1k0), __float_as_uint(g1k1), false, false);
+  const float y0 = __uint_as_float(u[0]) + __uint_as_float(u[1]);
+  const float y1 = __uint_as_float(v[0]) + __uint_as_float(v[1]);
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(y0), __float_as_uint(y1), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
+
+// 16-lane row 0: group 0 keys 0..15; row 1: group 1 keys 0..15 (32..47 of the half); row 2:
+// group 0 keys 16..31; row 3: group 1 keys 16..31.
+__device__ __forceinline__ int half_key(int lane) { return (lane & 15) + 16 * ((lane >> 5) & 1) + 32 * ((lane >> 4) & 1); }
 
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ w, int T, const uint8_t* __restrict__ k_rows, int S,
@@ -142,10 +219,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
   // The row's q codes and weights are requested here and decoded only after the first tile's
   // loads are issued (below), so the two round trips to memory overlap.
   const int tc = min(t, T - 1);
-  uint4 q_codes[2][4];
-  uint2 w_raw[2][4];
-  load_q32_codes(q_codes, q + (int64_t)tc * kHeads * kDim, lane);
-  load_w32_raw(w_raw, w + (int64_t)tc * kHeads, lane);
+  uint4 q_codes[4][2];
+  uint2 w_raw[4];
+  load_q16_codes(q_codes, q + (int64_t)tc * kHeads * kDim, lane);
+  load_w16_raw(w_raw, w + (int64_t)tc * kHeads, lane);
 
   // Output: a raw buffer over this row's logits whose record size ends at the row's range
   // end; a lane whose key is below the range start (or below this workgroup's first tile)
@@ -193,10 +270,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
 #pragma unroll
   for (int i = 0; i <= kRowsPerLane * kLoads; i++) load_piece(tile_first, i);
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first decode waits
-  Q32 qf;
-  W32 wf;
-  decode_q32(qf, q_codes);
-  decode_w32(wf, w_raw);
+  Q16 qf;
+  W16 wf;
+  decode_q16(qf, q_codes);
+  decode_w16(wf, w_raw);
 #pragma unroll
   for (int i = 0; i <= kRowsPerLane * kVecs; i++) store_piece(s_tile[0], i);
   __syncthreads();
@@ -208,13 +285,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
   // group, whose fragments are already in registers, so the next tile's first fragments
   // load under that group's MFMAs.  The head sums of a tile's last group are taken during
   // the next tile's first group, so the matrix work never waits for an epilogue.
-  f32x16 a0 = {}, a1 = {}, b0 = {}, b1 = {};
+  Acc16 xa = {}, xb = {};
   float acc[4];
-  float p_even = 0.f;    // head sum of group 0 or 2, waiting for its partner
-  float scale_lo = 0.f;  // scale of key lane of the current tile
-  float scale_hi = 0.f;  // scale of key 64 + lane of the previous tile
-  K32 kb;
-  load_k32(kb, s_tile[0], lane);
+  float pe0 = 0.f, pe1 = 0.f;  // head sums of group 0 or 2 (key blocks 0 and 1), waiting for their partner
+  const int hk = half_key(lane);
+  float scale_lo = 0.f;  // scale of key hk of the current tile
+  float scale_hi = 0.f;  // scale of key 64 + hk of the previous tile
+  K16 kb;
+  load_k16(kb, s_tile[0], lane);
   for (int tile = tile_first; tile < tile_end; tile++) {
     const int buf = (tile - tile_first) & 1;
     const uint8_t* cur = s_tile[buf];
@@ -222,40 +300,44 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_logits_kernel(
     const float* scale = reinterpret_cast<const float*>(cur + kScaleOffset);
     const int next_tile = min(tile + 1, tile_end - 1);
 
-    // group 0 -> a; head sums of the previous tile's group 3; global loads of the next tile
-    group_phase<true>(a0, a1, qf, kb, cur + 32 * kLdsKeyStrideF16, lane, wf, b0, b1, acc, [&](int i) {
+    // group 0 -> xa; head sums of the previous tile's group 3; global loads of the next tile
+    group_phase<true>(xa, qf, kb, cur + 32 * kLdsKeyStrideF16, lane, wf, xb, acc, [&](int i) {
       if (i >= 2 && i <= 2 + kRowsPerLane * kLoads) load_piece(next_tile, i - 2);
-      if (i == 12) scale_lo = scale[lane];
+      if (i == 12) scale_lo = scale[hk];
     });
-    store_logit((tile - 1) * kTileKeys + 64 + lane, combine_halves(p_even, acc_sum(acc)) * scale_hi);
+    store_logit((tile - 1) * kTileKeys + 64 + hk, combine_groups(pe0, pe1, acc[0] + acc[1], acc[2] + acc[3]) * scale_hi);
 
-    // group 1 -> b; head sums of group 0
-    group_phase<true>(b0, b1, qf, kb, cur + 64 * kLdsKeyStrideF16, lane, wf, a0, a1, acc, [&](int) {});
-    p_even = acc_sum(acc);
+    // group 1 -> xb; head sums of group 0
+    group_phase<true>(xb, qf, kb, cur + 64 * kLdsKeyStrideF16, lane, wf, xa, acc, [&](int) {});
+    pe0 = acc[0] + acc[1];
+    pe1 = acc[2] + acc[3];
 
-    // group 2 -> a; head sums of group 1; decode the next tile into the other buffer
-    group_phase<true>(a0, a1, qf, kb, cur + 96 * kLdsKeyStrideF16, lane, wf, b0, b1, acc, [&](int i) {
+    // group 2 -> xa; head sums of group 1; decode the next tile into the other buffer
+    group_phase<true>(xa, qf, kb, cur + 96 * kLdsKeyStrideF16, lane, wf, xb, acc, [&](int i) {
       if (i >= 2 && i <= 2 + kRowsPerLane * kVecs) store_piece(nxt, i - 2);
-      if (i == 12) scale_hi = scale[64 + lane];
+      if (i == 12) scale_hi = scale[64 + hk];
     });
-    const float v_lo = combine_halves(p_even, acc_sum(acc)) * scale_lo;
+    const float v_lo = combine_groups(pe0, pe1, acc[0] + acc[1], acc[2] + acc[3]) * scale_lo;
     // Every wavefront is done with this tile's buffer (group 3's fragments and both scale
     // halves are in registers) and has written its part of the next tile.
     __syncthreads();
 
-    // group 3 -> b; head sums of group 2; fragments of the next tile's group 0
-    store_logit(tile * kTileKeys + lane, v_lo);
-    group_phase<true>(b0, b1, qf, kb, nxt, lane, wf, a0, a1, acc, [&](int) {});
-    p_even = acc_sum(acc);
+    // group 3 -> xb; head sums of group 2; fragments of the next tile's group 0
+    store_logit(tile * kTileKeys + hk, v_lo);
+    group_phase<true>(xb, qf, kb, nxt, lane, wf, xa, acc, [&](int) {});
+    pe0 = acc[0] + acc[1];
+    pe1 = acc[2] + acc[3];
   }
   // head sums of the last tile's group 3
 #pragma unroll
   for (int j = 0; j < 4; j++) acc[j] = 0.f;
 #pragma unroll
-  for (int e = 0; e < 16; e++) acc[e & 3] = fmaf(wf.w[0][e], b0[e], acc[e & 3]);
+  for (int kk = 0; kk < 2; kk++)
 #pragma unroll
-  for (int e = 0; e < 16; e++) acc[e & 3] = fmaf(wf.w[1][e], b1[e], acc[e & 3]);
-  store_logit((tile_end - 1) * kTileKeys + 64 + lane, combine_halves(p_even, acc_sum(acc)) * scale_hi);
+    for (int hb = 0; hb < 4; hb++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[2 * kk + (e & 1)] = fmaf(wf.w[hb][e], xb.x[hb][kk][e], acc[2 * kk + (e & 1)]);
+  store_logit((tile_end - 1) * kTileKeys + 64 + hk, combine_groups(pe0, pe1, acc[0] + acc[1], acc[2] + acc[3]) * scale_hi);
 }
 
 }  // namespace
