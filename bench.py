@@ -738,7 +738,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_logits_kernel", "achieved": round(achieved, 1),
                      "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / F16_PEAK_TFLOPS, 4),
                      "traffic": committed_traffic(), "algorithmic_flops_per_launch": flops,
-                     "mfma_dtype": "f16 (v_mfma_f32_32x32x16_f16)",
+                     "mfma_dtype": "f16 (v_mfma_f32_16x16x32_f16)",
                      "frac_of_fp8_peak": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "measured_ceiling": ceil},
         "cpu_baseline": cpu,
