@@ -48,11 +48,13 @@ DSIC_API int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, flo
 
 /* Stream-read `bytes` bytes from `src` (16-byte aligned, bytes a multiple of
  * 16) with 16-byte loads, grid-stride, and fold them into one word per thread
- * written to `sink` (workgroups * 256 uint32 = at most 4 MB).  EINVAL: null
- * pointer, bytes 0 or not a multiple of 16, workgroups < 1; EALIGN: src not
- * 16-byte aligned. */
-DSIC_API int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
-                              hipStream_t stream);
+ * written to `sink` (workgroups * 256 uint32 = at most 4 MB).  nontemporal 1
+ * sets the non-temporal hint on the loads (streaming data), 0 leaves the
+ * default cache policy.  EINVAL: null pointer, bytes 0 or not a multiple of
+ * 16, workgroups not 1..4096, nontemporal not 0 or 1; EALIGN: src not 16-byte
+ * aligned. */
+DSIC_API int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t nontemporal,
+                              uint32_t* sink, hipStream_t stream);
 
 /* Copy `bytes` bytes from `src` to `dst` (both 16-byte aligned, not
  * overlapping, bytes a multiple of 16) with 16-byte loads and stores,
@@ -60,17 +62,19 @@ DSIC_API int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups,
 DSIC_API int dsic_copy(const void* src, void* dst, size_t bytes, int32_t workgroups, hipStream_t stream);
 
 /* Read n_pages whole pages of page_bytes bytes, page i at pool +
- * pages[i] * block_stride (pool 16-byte aligned; page_bytes a multiple of 16,
- * at most 12288; block_stride a multiple of 16, at least page_bytes; every
- * page id in [0, pool's blocks) — the caller's table), pages_per_round (4
- * or 8) pages per workgroup round with all their loads in flight, and fold
- * them into one word per thread written to `sink` (workgroups * 256 uint32).
- * EINVAL: null pointer, n_pages < 1, pages_per_round not 4 or 8, workgroups
- * not 1..4096, page_bytes or block_stride out of range; EALIGN: pool not
- * 16-byte aligned. */
-DSIC_API int dsic_paged_read(const void* pool, int64_t block_stride, const int32_t* pages, int32_t n_pages,
-                             int32_t page_bytes, int32_t pages_per_round, int32_t workgroups, uint32_t* sink,
-                             hipStream_t stream);
+ * pages[i] * block_stride (pool 16-byte aligned, pool_bytes long; page_bytes
+ * a multiple of 16, at most 12288; block_stride a multiple of 16, at least
+ * page_bytes), pages_per_round (4 or 8) pages per workgroup round with all
+ * their loads in flight, and fold them into one word per thread written to
+ * `sink` (workgroups * 256 uint32).  A page id whose page does not lie wholly
+ * in the pool (negative, or past its last whole block) is read as nothing.
+ * nontemporal as for dsic_stream_read.  EINVAL: null pointer, n_pages < 1,
+ * pages_per_round not 4 or 8, nontemporal not 0 or 1, workgroups not
+ * 1..4096, page_bytes, block_stride or pool_bytes out of range; EALIGN: pool
+ * not 16-byte aligned. */
+DSIC_API int dsic_paged_read(const void* pool, int64_t pool_bytes, int64_t block_stride, const int32_t* pages,
+                             int32_t n_pages, int32_t page_bytes, int32_t pages_per_round, int32_t nontemporal,
+                             int32_t workgroups, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,9 +14,9 @@ CHAINS = {0: 16, 1: 16, 2: 8}                                                   
 _p, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGNATURES = {
     "dsic_mfma_loop": (ctypes.c_int, [_i32, _i32, _i32, _p, _p]),
-    "dsic_stream_read": (ctypes.c_int, [_p, _sz, _i32, _p, _p]),
+    "dsic_stream_read": (ctypes.c_int, [_p, _sz, _i32, _i32, _p, _p]),
     "dsic_copy": (ctypes.c_int, [_p, _p, _sz, _i32, _p]),
-    "dsic_paged_read": (ctypes.c_int, [_p, ctypes.c_int64, _p, _i32, _i32, _i32, _i32, _p, _p]),
+    "dsic_paged_read": (ctypes.c_int, [_p, ctypes.c_int64, ctypes.c_int64, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
 }
 ENTRY_POINTS = tuple(_SIGNATURES)
 _lib = None
@@ -51,12 +51,13 @@ def mfma_loop(kind: int, workgroups: int, iters: int, sink: torch.Tensor) -> int
     return workgroups * 4 * iters * CHAINS[kind] * FLOP_PER_INSTR[kind]
 
 
-def stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor) -> int:
-    """Enqueue a streaming read of all of `src`; returns the byte count."""
+def stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor, nontemporal: bool = False) -> int:
+    """Enqueue a streaming read of all of `src` (with the non-temporal load hint if asked); returns the byte
+    count."""
     assert src.is_contiguous() and sink.dtype == torch.int32 and sink.numel() >= workgroups * THREADS
     nbytes = src.numel() * src.element_size()
-    _check(lib().dsic_stream_read(src.data_ptr(), nbytes, workgroups, sink.data_ptr(), _stream(src)),
-           "dsic_stream_read")
+    _check(lib().dsic_stream_read(src.data_ptr(), nbytes, workgroups, int(nontemporal), sink.data_ptr(),
+                                  _stream(src)), "dsic_stream_read")
     return nbytes
 
 
@@ -69,11 +70,12 @@ def copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int) -> int:
 
 
 def paged_read(pool: torch.Tensor, block_stride: int, pages: torch.Tensor, page_bytes: int, workgroups: int,
-               sink: torch.Tensor, pages_per_round: int = 4) -> int:
-    """Enqueue a read of the pages `pages` (int32 ids into `pool`); returns the byte count read."""
+               sink: torch.Tensor, pages_per_round: int = 4, nontemporal: bool = False) -> int:
+    """Enqueue a read of the pages `pages` (int32 ids into `pool`; ids whose page is not in the pool are read as
+    nothing, on the device: no host synchronisation); returns the byte count of the pages' reads."""
     assert pool.is_contiguous() and pages.dtype == torch.int32 and pages.is_contiguous()
     assert sink.dtype == torch.int32 and sink.numel() >= workgroups * THREADS
-    assert int(pages.max()) * block_stride + page_bytes <= pool.numel() * pool.element_size()
-    _check(lib().dsic_paged_read(pool.data_ptr(), block_stride, pages.data_ptr(), pages.numel(), page_bytes,
-                                 pages_per_round, workgroups, sink.data_ptr(), _stream(pool)), "dsic_paged_read")
+    _check(lib().dsic_paged_read(pool.data_ptr(), pool.numel() * pool.element_size(), block_stride, pages.data_ptr(),
+                                 pages.numel(), page_bytes, pages_per_round, int(nontemporal), workgroups,
+                                 sink.data_ptr(), _stream(pool)), "dsic_paged_read")
     return pages.numel() * page_bytes

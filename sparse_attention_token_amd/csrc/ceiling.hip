@@ -17,6 +17,16 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChains = 16;
 
+// A 16-byte load, with the non-temporal hint (streaming data: the loads set the "nt" bit) or
+// without it.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float* __restrict__ sink, int iters) {
   f32x4 c[kChains];
@@ -72,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void mfma32_loop_kernel(float* __restrict
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
                                                                uint32_t* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * kThreads;
@@ -79,10 +90,11 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   u32x4 acc = {0u, 0u, 0u, 0u};
   // four independent loads in flight per thread
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
+    const u32x4 x0 = load16<NT>(src + i), x1 = load16<NT>(src + i + stride), x2 = load16<NT>(src + i + 2 * stride),
+                x3 = load16<NT>(src + i + 3 * stride);
     acc ^= x0 ^ x1 ^ x2 ^ x3;
   }
-  for (; i < n16; i += stride) acc ^= src[i];
+  for (; i < n16; i += stride) acc ^= load16<NT>(src + i);
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
@@ -94,11 +106,12 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict_
 
 // Whole pages of page_bytes at pool + pages[i] * block_stride, P pages per workgroup round, each
 // page read by the workgroup's 256 threads in up to three 16-byte loads each (all 3P in flight).
+// A page id outside [0, n_blocks) is read as nothing.
 constexpr int kPageRounds = 3;  // pages of at most 3 * 256 * 16 = 12 KB
-template <int P>
+template <int P, bool NT>
 __global__ __launch_bounds__(kThreads) void paged_read_kernel(const uint8_t* __restrict__ pool, int64_t block_stride,
-                                                              const int* __restrict__ pages, int n_pages,
-                                                              int page_bytes, uint32_t* __restrict__ sink) {
+                                                              int64_t n_blocks, const int* __restrict__ pages,
+                                                              int n_pages, int page_bytes, uint32_t* __restrict__ sink) {
   const int n16 = page_bytes / 16, t = threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (int p0 = blockIdx.x * P; p0 < n_pages; p0 += gridDim.x * P) {
@@ -106,12 +119,14 @@ __global__ __launch_bounds__(kThreads) void paged_read_kernel(const uint8_t* __r
 #pragma unroll
     for (int q = 0; q < P; q++) {
       const int p = p0 + q;
-      const u32x4* base = reinterpret_cast<const u32x4*>(pool + (int64_t)pages[min(p, n_pages - 1)] * block_stride);
+      const int id = pages[min(p, n_pages - 1)];
+      const bool ok = p < n_pages && id >= 0 && id < n_blocks;
+      const u32x4* base = reinterpret_cast<const u32x4*>(pool + (ok ? (int64_t)id * block_stride : 0));
 #pragma unroll
       for (int r = 0; r < kPageRounds; r++) {
         const int j = r * kThreads + t;
         x[q][r] = u32x4{0u, 0u, 0u, 0u};
-        if (p < n_pages && j < n16) x[q][r] = base[j];
+        if (ok && j < n16) x[q][r] = load16<NT>(base + j);
       }
     }
 #pragma unroll
@@ -137,12 +152,14 @@ extern "C" int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, f
   return launched();
 }
 
-extern "C" int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
-                                hipStream_t stream) {
+extern "C" int dsic_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t nontemporal,
+                                uint32_t* sink, hipStream_t stream) {
   if (!src || !sink || bytes == 0 || (bytes & 15) || workgroups < 1 || workgroups > 4096) return DSI_EINVAL;
+  if (nontemporal != 0 && nontemporal != 1) return DSI_EINVAL;
   if (reinterpret_cast<uintptr_t>(src) & 15) return DSI_EALIGN;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
-                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  auto k = nontemporal ? stream_read_kernel<true> : stream_read_kernel<false>;
+  hipLaunchKernelGGL(k, dim3(workgroups), dim3(kThreads), 0, stream, static_cast<const u32x4*>(src), bytes / 16,
+                     sink);
   return launched();
 }
 
@@ -154,16 +171,20 @@ extern "C" int dsic_copy(const void* src, void* dst, size_t bytes, int32_t workg
   return launched();
 }
 
-extern "C" int dsic_paged_read(const void* pool, int64_t block_stride, const int32_t* pages, int32_t n_pages,
-                               int32_t page_bytes, int32_t pages_per_round, int32_t workgroups, uint32_t* sink,
-                               hipStream_t stream) {
+extern "C" int dsic_paged_read(const void* pool, int64_t pool_bytes, int64_t block_stride, const int32_t* pages,
+                               int32_t n_pages, int32_t page_bytes, int32_t pages_per_round, int32_t nontemporal,
+                               int32_t workgroups, uint32_t* sink, hipStream_t stream) {
   if (!pool || !pages || !sink || n_pages < 1 || workgroups < 1 || workgroups > 4096) return DSI_EINVAL;
   if (pages_per_round != 4 && pages_per_round != 8) return DSI_EINVAL;
+  if (nontemporal != 0 && nontemporal != 1) return DSI_EINVAL;
   if (page_bytes < 16 || (page_bytes & 15) || page_bytes > kPageRounds * kThreads * 16) return DSI_EINVAL;
-  if (block_stride < page_bytes || (block_stride & 15)) return DSI_EINVAL;
+  if (block_stride < page_bytes || (block_stride & 15) || pool_bytes < page_bytes) return DSI_EINVAL;
   if (reinterpret_cast<uintptr_t>(pool) & 15) return DSI_EALIGN;
-  auto k = pages_per_round == 8 ? paged_read_kernel<8> : paged_read_kernel<4>;
+  // blocks whose whole page lies in the pool
+  const int64_t n_blocks = (pool_bytes - page_bytes) / block_stride + 1;
+  auto k = pages_per_round == 8 ? (nontemporal ? paged_read_kernel<8, true> : paged_read_kernel<8, false>)
+                                : (nontemporal ? paged_read_kernel<4, true> : paged_read_kernel<4, false>);
   hipLaunchKernelGGL(k, dim3(workgroups), dim3(kThreads), 0, stream, static_cast<const uint8_t*>(pool), block_stride,
-                     pages, n_pages, page_bytes, sink);
+                     n_blocks, pages, n_pages, page_bytes, sink);
   return launched();
 }

@@ -63,8 +63,11 @@ constexpr int kDcSegs = kDcJob * kDcChunk / 16;     // 16-token segments per job
 // reserved register, so naming it as a clobber would not protect a value the compiler keeps
 // there).  Every source address (each needs an LDS read of its key's offset) is computed
 // before the first load is issued: the assembly statements are ordered memory operations,
-// so interleaving them with those reads cost one LDS round trip per load.
-template <int NP, typename SrcOf>
+// so interleaving them with those reads cost one LDS round trip per load.  kStream sets the
+// loads' non-temporal hint ("nt"): the paged decode reads each page once per call, and the
+// hint made its reads of random 8448-byte pages faster; the sparse kernels re-read one
+// source from the caches and keep the default policy.
+template <bool kStream, int NP, typename SrcOf>
 __device__ __forceinline__ void dma_chunk(uint8_t* buf, int wave, int lane, SrcOf&& src_of) {
   const uint8_t* src[NP];
 #pragma unroll
@@ -73,7 +76,10 @@ __device__ __forceinline__ void dma_chunk(uint8_t* buf, int wave, int lane, SrcO
   for (int i = 0; i < NP; i++) {
     const uint32_t lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(buf + (wave + 4 * i) * 1024));
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[i]), "{m0}"(lds) : "memory");
+    if constexpr (kStream)
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src[i]), "{m0}"(lds) : "memory");
+    else
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[i]), "{m0}"(lds) : "memory");
   }
 }
 
@@ -82,7 +88,7 @@ __device__ __forceinline__ void dma_chunk(uint8_t* buf, int wave, int lane, SrcO
 // pool's first bytes (their keys score -inf).
 __device__ __forceinline__ void dc_gather(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
                                           int lane) {
-  dma_chunk<kDcSlabsPerWave>(buf, wave, lane, [&](int piece) {
+  dma_chunk<true, kDcSlabsPerWave>(buf, wave, lane, [&](int piece) {
     const int key = piece / 9, p = piece - key * 9;
     const int64_t base = seg_base[key >> 4];
     return base >= 0 ? pool + base + (key & 15) * kRow + (p < 8 ? 16 * p : 116) : pool;
@@ -311,7 +317,7 @@ __device__ __forceinline__ void mx_phase(f32x16& x0, f32x16& x1, const Q32b& q, 
 // s/5, piece s%5 of its 68-byte row (bytes 16p, or 52..67 for p = 4).
 __device__ __forceinline__ void dc_gather_mx(uint8_t* buf, const int64_t* seg_base, const uint8_t* pool, int wave,
                                              int lane) {
-  dma_chunk<kMxSlabsPerWave>(buf, wave, lane, [&](int piece) {
+  dma_chunk<true, kMxSlabsPerWave>(buf, wave, lane, [&](int piece) {
     const int key = piece / 5, p = piece - key * 5;
     const int64_t base = seg_base[key >> 4];
     return base >= 0 ? pool + base + (key & 15) * kMxRow + (p < 4 ? 16 * p : 52) : pool;
@@ -595,7 +601,7 @@ constexpr uint32_t kSpAbsent = 0xFFFFFFFFu;   // source offsets are in 4-byte un
 // This wavefront's share of one chunk's gather (as dc_gather, with one source offset per key).
 __device__ __forceinline__ void sp_gather(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
                                           int lane) {
-  dma_chunk<kDcSlabsPerWave>(buf, wave, lane, [&](int piece) {
+  dma_chunk<false, kDcSlabsPerWave>(buf, wave, lane, [&](int piece) {
     const int key = piece / 9, p = piece - key * 9;
     const uint32_t off = key_off[key];
     return off != kSpAbsent ? src + (int64_t)off * 4 + (p < 8 ? 16 * p : 116) : src;
@@ -725,7 +731,7 @@ __global__ __launch_bounds__(256, 2) void sparse_logits_kernel(
 // Five 16-byte pieces per 68-byte row: bytes 0..63 and 52..67.
 __device__ __forceinline__ void mx_gather(uint8_t* buf, const uint32_t* key_off, const uint8_t* src, int wave,
                                           int lane) {
-  dma_chunk<kMxSlabsPerWave>(buf, wave, lane, [&](int piece) {
+  dma_chunk<false, kMxSlabsPerWave>(buf, wave, lane, [&](int piece) {
     const int key = piece / 5, p = piece - key * 5;
     const uint32_t off = key_off[key];
     return off != kSpAbsent ? src + (int64_t)off * 4 + (p < 4 ? 16 * p : 52) : src;

@@ -260,16 +260,20 @@ def test_ceiling_library_exports_and_validation():
     assert L.dsic_mfma_loop(3, 1, 1, A16, None) == EINVAL
     assert L.dsic_mfma_loop(0, 0, 1, A16, None) == EINVAL
     assert L.dsic_mfma_loop(0, 1, 1, None, None) == EINVAL
-    assert L.dsic_stream_read(A16, 24, 1, A16, None) == EINVAL
-    assert L.dsic_stream_read(A16 + 4, 32, 1, A16, None) == EALIGN
+    assert L.dsic_stream_read(A16, 24, 1, 0, A16, None) == EINVAL
+    assert L.dsic_stream_read(A16, 32, 1, 2, A16, None) == EINVAL                     # nontemporal 0 or 1
+    assert L.dsic_stream_read(A16 + 4, 32, 1, 0, A16, None) == EALIGN
     assert L.dsic_copy(A16, A16 + 8, 32, 1, None) == EALIGN
     assert L.dsic_copy(None, A16, 32, 1, None) == EINVAL
-    assert L.dsic_paged_read(A16, 8448, A16, 1, 8448 + 8, 4, 1, A16, None) == EINVAL   # page not whole 16 B
-    assert L.dsic_paged_read(A16, 8448, A16, 1, 12304, 4, 1, A16, None) == EINVAL      # page over 12 KB
-    assert L.dsic_paged_read(A16, 4096, A16, 1, 8448, 4, 1, A16, None) == EINVAL       # stride below a page
-    assert L.dsic_paged_read(A16, 8448, A16, 0, 8448, 4, 1, A16, None) == EINVAL       # no pages
-    assert L.dsic_paged_read(A16, 8448, A16, 1, 8448, 6, 1, A16, None) == EINVAL       # 4 or 8 per round
-    assert L.dsic_paged_read(A16 + 4, 8448, A16, 1, 8448, 4, 1, A16, None) == EALIGN
+    P = 1 << 20
+    assert L.dsic_paged_read(A16, P, 8448, A16, 1, 8448 + 8, 4, 0, 1, A16, None) == EINVAL   # page not whole 16 B
+    assert L.dsic_paged_read(A16, P, 8448, A16, 1, 12304, 4, 0, 1, A16, None) == EINVAL      # page over 12 KB
+    assert L.dsic_paged_read(A16, P, 4096, A16, 1, 8448, 4, 0, 1, A16, None) == EINVAL       # stride below a page
+    assert L.dsic_paged_read(A16, P, 8448, A16, 0, 8448, 4, 0, 1, A16, None) == EINVAL       # no pages
+    assert L.dsic_paged_read(A16, P, 8448, A16, 1, 8448, 6, 0, 1, A16, None) == EINVAL       # 4 or 8 per round
+    assert L.dsic_paged_read(A16, P, 8448, A16, 1, 8448, 4, 3, 1, A16, None) == EINVAL       # nontemporal 0 or 1
+    assert L.dsic_paged_read(A16, 4096, 8448, A16, 1, 8448, 4, 0, 1, A16, None) == EINVAL    # pool below a page
+    assert L.dsic_paged_read(A16 + 4, P, 8448, A16, 1, 8448, 4, 0, 1, A16, None) == EALIGN
 
 
 def test_probe_library_exports_and_validation():
