@@ -1,29 +1,18 @@
 // Device helpers shared by the gfx950 indexer kernels.
 //
-// Scoring layout (used by every logits kernel).  The indexer score of P3 step ⑥
-// ("DeepSeek V3.2 稀疏注意力 DSA 推理流程图解") is a 64-head x 128-dim contraction of
-// FP8 values followed by a per-head weighted sum.
+// The indexer score of P3 step ⑥ ("DeepSeek V3.2 稀疏注意力 DSA 推理流程图解") is a 64-head x
+// 128-dim contraction of FP8 values followed by a per-head weighted sum.
 //
-// Matrix instruction.  The FP8 codes are decoded exactly to f16 and contracted with
-// v_mfma_f32_16x16x32_f16.  gfx950's FP8-operand MFMAs (16x16x128 f8f6f4 and
-// 16x16x32 fp8) were measured to drop product bits about 13 binades below the largest
-// product of their internal sum, with a one-sided (truncating) error that reaches
-// ~0.1 on indexer logits — beyond the path's 1e-3 (1 + |ref|) bar — while the f16
-// MFMA sums the same products exactly.  Every E4M3FN value is a normal f16 (2^-9 to
-// 448), so the decode (v_cvt_scalef32_pk_f16_fp8 with scale 1, two codes per
-// instruction) is exact.
+// Matrix instructions.  The FP8 codes are decoded exactly to f16 (or bf16) and contracted on
+// the f16 (bf16) matrix instructions.  gfx950's FP8-operand MFMAs (16x16x128 f8f6f4 and
+// 16x16x32 fp8) were measured to drop product bits about 13 binades below the largest product
+// of their internal sum, with a one-sided (truncating) error that reaches ~0.1 on indexer
+// logits — beyond the path's 1e-3 (1 + |ref|) bar — while the f16 MFMA sums the same products
+// exactly.  Every E4M3FN value is a normal f16 (2^-9 to 448), so the decode
+// (v_cvt_scalef32_pk_f16_fp8 with scale 1, two codes per instruction) is exact.
 //
-// Operands of one MFMA (k = 32 dims of a 128-dim slice):
-//   A = 16 heads x 32 dims of q   (lane l: head l%16, 8 dims of lane group g = l/16)
-//   B = 32 dims x 16 keys of K    (lane l: key  l%16, the same 8 dims)
-//   C = 16 heads x 16 keys, lane l holds heads 4*(l/16)+i, i<4, of key l%16.
-// Lane group g owns dims [32g, 32g+32) of the 128 and feeds 8 of them to each of the
-// four slices; A and B use the same assignment, so the sum over dims is complete.
-// Four head tiles cover the 64 heads, so after the MFMAs each lane holds 16 heads of
-// one key; the head-weighted sum is 16 FMAs per lane followed by a sum over the four
-// lane groups.  That cross-lane sum is done for four (row, key-group) outputs at once
-// as a 4x4 transpose-reduce: two exchange stages (lane^32, lane^16), after which each
-// lane group owns one output.
+// Two operand layouts: the dense prefill kernel's v_mfma_f32_16x16x32_f16 (described in
+// prefill.hip) and the one-row scoring kernels' v_mfma_f32_32x32x16_f16 (below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,6 +25,18 @@ namespace dsi {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Compute units of the current device (queried once per device), for sizing persistent grids.
+inline int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
 
 constexpr int kHeads = 64;
 constexpr int kDim = 128;

@@ -23,17 +23,6 @@ namespace {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glob_ptr_t;
 
-// Compute units of the current device (queried once per device).
-int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
-  }
-  return cached[dev];
-}
 // ------------------------------------------------------------------ paged decode
 // A workgroup (4 wavefronts) streams segments of up to 16 chunks of 256 keys of one request
 // through a ring of LDS buffers: the DMA gathers of the next chunks are in flight while
