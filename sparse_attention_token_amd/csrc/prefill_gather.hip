@@ -15,7 +15,9 @@
 // rows of one page at a 16-byte aligned address (every group of a request that starts on a
 // multiple of 4 rows when block_size is a multiple of 4) moves as one 16-byte load per
 // chunk; any other group assembles each chunk from four 4-byte loads of its rows.  Rows
-// without a source are written as zeros.
+// without a source are written as zeros.  The cache rows are read with the non-temporal hint
+// (each is read once; 131072 rows: 10.5 -> 9.9 us), the output with the default policy (the
+// logits kernel reads it next).
 #include "common.h"
 
 namespace dsi {
@@ -97,14 +99,18 @@ __global__ __launch_bounds__(kGThreads) void gather_prefill_k_kernel(
     if (c < kGChunks && c * 16 < nbytes) {
       const int g = c / 33, q = c - g * 33;
       if (s_fast[g]) {
-        v[it] = *reinterpret_cast<const uint4*>(pool + s_src[4 * g] + q * 16);
+        {
+          typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+          const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(pool + s_src[4 * g] + q * 16));
+          v[it] = make_uint4(x[0], x[1], x[2], x[3]);
+        }
       } else {
         uint32_t d[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
           const int b = q * 16 + 4 * k, rr = b / kRow, o = b - rr * kRow;
           const uint64_t a = s_src[4 * g + rr];
-          d[k] = a == kNoSrc ? 0u : *reinterpret_cast<const uint32_t*>(pool + a + o);
+          d[k] = a == kNoSrc ? 0u : __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(pool + a + o));
         }
         v[it] = make_uint4(d[0], d[1], d[2], d[3]);
       }
