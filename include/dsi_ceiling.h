@@ -39,11 +39,15 @@ extern "C" {
  * flop per instruction), kind 1 = v_mfma_scale_f32_16x16x128_f8f6f4 with FP8
  * E4M3 operands (65,536 flop per instruction), both with 16 chains per
  * wavefront; kind 2 = v_mfma_f32_32x32x16_f16 (32,768 flop per instruction)
- * with 8 chains.  `workgroups` workgroups of 256 threads each run `iters`
- * rounds of one instruction per chain per wavefront, so the total is
+ * with 8 chains.  Kinds 0..2 use small constant operands.  Kinds 3 and 4 are
+ * kinds 0 and 2 on pseudo-random E4M3 codes (magnitudes 2 to 448, random sign
+ * and mantissa) decoded to f16: the matrix cores' power depends on their
+ * operands' bits, and on such data the chip runs these loops at its power
+ * limit.  `workgroups` workgroups of 256 threads each run `iters` rounds of
+ * one instruction per chain per wavefront, so the total is
  * workgroups * 4 * iters * chains instructions.  `sink` receives one float
  * per thread (workgroups * 256 floats) so that nothing is optimised away.
- * EINVAL: kind not 0..2, workgroups < 1, iters < 1, sink NULL. */
+ * EINVAL: kind not 0..4, workgroups < 1, iters < 1, sink NULL. */
 DSIC_API int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, float* sink, hipStream_t stream);
 
 /* Stream-read `bytes` bytes from `src` (16-byte aligned, bytes a multiple of

@@ -8,8 +8,10 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsi_ceiling.so")
 THREADS = 256
-FLOP_PER_INSTR = {0: 16 * 16 * 32 * 2, 1: 16 * 16 * 128 * 2, 2: 32 * 32 * 16 * 2}  # f16 16x16x32, FP8 16x16x128,
-CHAINS = {0: 16, 1: 16, 2: 8}                                                      # f16 32x32x16
+# kinds: f16 16x16x32, FP8 16x16x128, f16 32x32x16 on constant operands; 3 and 4 = kinds 0 and 2 on random FP8 codes
+FLOP_PER_INSTR = {0: 16 * 16 * 32 * 2, 1: 16 * 16 * 128 * 2, 2: 32 * 32 * 16 * 2, 3: 16 * 16 * 32 * 2,
+                  4: 32 * 32 * 16 * 2}
+CHAINS = {0: 16, 1: 16, 2: 8, 3: 16, 4: 8}
 
 _p, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGNATURES = {

@@ -27,13 +27,36 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
     return *p;
 }
 
-template <int KIND>
+// Eight pseudo-random E4M3 codes with exponent field 8..15 (magnitudes 2 to 448, random sign and mantissa; the NaN
+// codes become the largest finite ones), decoded exactly to f16 by the hardware converter: operands whose bits switch
+// like the indexer's FP8 data, so that the loop runs at the clock the chip's power limit allows on such data.
+__device__ __forceinline__ f16x8 random_f16x8(uint32_t seed) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 h[4];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    uint32_t x = seed * 0x9E3779B1u + (uint32_t)i * 0x85EBCA77u;
+    x ^= x >> 15;
+    x *= 0x2C1B3C6Du;
+    x ^= x >> 12;
+    x *= 0x297A2D39u;
+    x ^= x >> 15;
+    x |= 0x40404040u;                                              // exponent field >= 8
+    x -= (((x & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) >> 7;  // 0x7F / 0xFF -> 0x7E / 0xFE
+    h[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+    h[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  }
+  return f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+}
+
+template <int KIND, bool RANDOM>
 __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float* __restrict__ sink, int iters) {
   f32x4 c[kChains];
 #pragma unroll
   for (int j = 0; j < kChains; j++) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Operands depend on the thread id so the compiler cannot fold the loop; their
-  // values are small and finite (f16 halves, FP8 codes 0x30..0x37 = 0.5..0.9375).
+  // values are small and finite (f16 halves, FP8 codes 0x30..0x37 = 0.5..0.9375), or
+  // random FP8 codes decoded to f16.
   f16x8 a16, b16;
   i32x8 a8, b8;
 #pragma unroll
@@ -42,6 +65,10 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float* __restrict__
     b16[j] = (_Float16)(0.5f + j * 0.03125f);
     a8[j] = 0x30303030 | ((threadIdx.x + j) & 7);
     b8[j] = 0x30303030 | (j & 7);
+  }
+  if constexpr (RANDOM) {
+    a16 = random_f16x8(blockIdx.x * kThreads + threadIdx.x);
+    b16 = random_f16x8(0x10000u + threadIdx.x);
   }
   for (int it = 0; it < iters; it++) {
 #pragma unroll
@@ -62,6 +89,7 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float* __restrict__
 // accumulators (128 registers) live in the accumulation registers.
 constexpr int kChains32 = 8;
 
+template <bool RANDOM>
 __global__ __launch_bounds__(kThreads) void mfma32_loop_kernel(float* __restrict__ sink, int iters) {
   f32x16 c[kChains32];
 #pragma unroll
@@ -71,6 +99,10 @@ __global__ __launch_bounds__(kThreads) void mfma32_loop_kernel(float* __restrict
   for (int j = 0; j < 8; j++) {
     a16[j] = (_Float16)((threadIdx.x & 7) * 0.125f + j * 0.0625f);
     b16[j] = (_Float16)(0.5f + j * 0.03125f);
+  }
+  if constexpr (RANDOM) {
+    a16 = random_f16x8(blockIdx.x * kThreads + threadIdx.x);
+    b16 = random_f16x8(0x10000u + threadIdx.x);
   }
   for (int it = 0; it < iters; it++) {
 #pragma unroll
@@ -142,13 +174,15 @@ int launched() { return hipGetLastError() == hipSuccess ? DSI_OK : DSI_ELAUNCH; 
 }  // namespace
 
 extern "C" int dsic_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, float* sink, hipStream_t stream) {
-  if (kind < 0 || kind > 2 || workgroups < 1 || iters < 1 || !sink) return DSI_EINVAL;
-  if (kind == 2)
-    hipLaunchKernelGGL(mfma32_loop_kernel, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
-  else if (kind == 0)
-    hipLaunchKernelGGL(mfma_loop_kernel<0>, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
-  else
-    hipLaunchKernelGGL(mfma_loop_kernel<1>, dim3(workgroups), dim3(kThreads), 0, stream, sink, iters);
+  if (kind < 0 || kind > 4 || workgroups < 1 || iters < 1 || !sink) return DSI_EINVAL;
+  const dim3 grid(workgroups), block(kThreads);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((mfma_loop_kernel<0, false>), grid, block, 0, stream, sink, iters); break;
+    case 1: hipLaunchKernelGGL((mfma_loop_kernel<1, false>), grid, block, 0, stream, sink, iters); break;
+    case 2: hipLaunchKernelGGL(mfma32_loop_kernel<false>, grid, block, 0, stream, sink, iters); break;
+    case 3: hipLaunchKernelGGL((mfma_loop_kernel<0, true>), grid, block, 0, stream, sink, iters); break;
+    default: hipLaunchKernelGGL(mfma32_loop_kernel<true>, grid, block, 0, stream, sink, iters); break;
+  }
   return launched();
 }
 

@@ -257,7 +257,8 @@ def test_ceiling_library_exports_and_validation():
     out = subprocess.run(["nm", "-D", "--defined-only", ceiling.LIB_PATH], capture_output=True, text=True).stdout
     assert sorted(set(re.findall(r" T (dsic_\w+)", out))) == names
     L = ceiling.lib()
-    assert L.dsic_mfma_loop(3, 1, 1, A16, None) == EINVAL
+    assert L.dsic_mfma_loop(5, 1, 1, A16, None) == EINVAL
+    assert L.dsic_mfma_loop(-1, 1, 1, A16, None) == EINVAL
     assert L.dsic_mfma_loop(0, 0, 1, A16, None) == EINVAL
     assert L.dsic_mfma_loop(0, 1, 1, None, None) == EINVAL
     assert L.dsic_stream_read(A16, 24, 1, 0, A16, None) == EINVAL
