@@ -689,7 +689,7 @@ def main():
                     help="comma-separated subset of the reported workloads (default: all): " + ",".join(ALL_WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the indexer path has no multi-GPU mode in this build "
+        print(f"bench.py measures one GPU: the indexer path runs on one GPU and has no multi-GPU mode "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
     chosen = ALL_WORKLOADS if args.workloads is None else [w for w in args.workloads.split(",") if w]
