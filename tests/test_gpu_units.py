@@ -799,6 +799,59 @@ def test_decode_topk_call_short_and_long_rows(mxfp4, next_n, lens, maxc):
         assert np.array_equal(np.sort(got[r][a]), np.sort(got[r][b]))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("k", [1, 64, 777, 2047])
+def test_topk_split_smaller_k(bf16, k):
+    """The split path (few long rows) with k below 2048: ordinary rows, many ties, a row with fewer than k finite
+    values, and one tie value everywhere; the selected values against the oracle's."""
+    rng = np.random.default_rng(71 + k + bf16)
+    rows, width = 6, 60000
+    x = (rng.standard_normal((rows, width)) * 30).astype(np.float32)
+    x[1] = np.round(x[1] / 4) * 4
+    x[2, k // 2:] = -np.inf
+    x[3, :] = 0.75
+    ends = np.array([width, 59999, width, 41000, 33333, width], np.int32)
+    starts = np.array([0, 5, 0, 0, 1000, 17], np.int32)
+    if bf16:
+        bits = synth._bf16_bits(x)
+        vals = bf16_value(bits)
+        ref = oracle.topk_select(bits, ends, k, starts=starts, bf16=True)
+        got = host(dsi.topk_select(dev(bits), dev(ends), k=k, row_starts=dev(starts)))
+    else:
+        vals = x
+        ref = oracle.topk_select(x, ends, k, starts=starts)
+        got = host(dsi.topk_select(dev(x), dev(ends), k=k, row_starts=dev(starts)))
+    assert got.shape == (rows, k)
+    for r in range(rows):
+        check_selection(got[r], ref[r], vals[r], rule="exact", start=starts[r], end=ends[r])
+        g = got[r][got[r] >= 0] + starts[r]
+        o = ref[r][ref[r] >= 0] + starts[r]
+        assert np.array_equal(np.sort(vals[r, g]), np.sort(vals[r, o]))
+        assert np.unique(g).size == g.size
+    assert np.sum(got[2] >= 0) == k // 2
+
+
+@pytest.mark.parametrize("next_n,k", [(1, 300), (2, 1), (4, 2048)])
+def test_decode_topk_call_other_k_and_next_n(next_n, k):
+    """dsi_paged_mqa_topk_decode with k below 2048 (histograms counted in the decode kernel for one row per
+    request) and with four rows per request (the plain top-k after the logits); selections against the oracle."""
+    lens, maxc = [30000, 20000, 1000, 2], 30000
+    c, pool_ref, bt, ref, ends, stride = _fused_decode_case(81 + next_n, lens, next_n, maxc, False)
+    bs, nb = 64, c["num_blocks"]
+    logits, idx_t = dsi.paged_mqa_topk_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(pool_ref), bs,
+                                              dev(bt), maxc, next_n=next_n, k=k, block_stride_bytes=stride,
+                                              num_blocks=nb)
+    got, idx = host(logits), host(idx_t)
+    assert idx.shape == (len(lens) * next_n, k)
+    for r in range(len(lens) * next_n):
+        e = int(ends[r])
+        assert_close(got[r][:e], ref[r][:e], what=f"row {r} logits")
+        ref_idx = oracle.topk_select(ref[r:r + 1], ends[r:r + 1], k)[0]
+        check_selection(idx[r], ref_idx, ref[r], end=e)
+        sel = idx[r][idx[r] >= 0]
+        assert sel.size == min(k, e) and np.unique(sel).size == sel.size
+
+
 @pytest.mark.parametrize("next_n", [1, 2])
 def test_decode_topk_call_ties_and_heavy_boundary(next_n):
     """Every key of a long row equal (one logit value over 40000 columns): the boundary bin holds more columns
