@@ -852,6 +852,28 @@ def test_decode_topk_call_other_k_and_next_n(next_n, k):
         assert sel.size == min(k, e) and np.unique(sel).size == sel.size
 
 
+def test_decode_topk_call_many_requests():
+    """More requests than the persistent decode grid takes (1100 > 1024): the per-request grid, and with 1100 rows
+    the top-k's one-workgroup-per-row path for long rows; short rows padded with -1, one long row, a request of
+    length 0.  Logits and selections of every row against the oracle."""
+    rng = np.random.default_rng(97)
+    B, maxc = 1100, 20000
+    lens = rng.integers(1, 600, B).astype(np.int32)
+    lens[5], lens[700], lens[1099] = 20000, 0, 2049
+    c, pool_ref, bt, ref, ends, stride = _fused_decode_case(97, list(lens), 1, maxc, False)
+    bs, nb = 64, c["num_blocks"]
+    logits, idx_t = dsi.paged_mqa_topk_decode(dev(c["q"]), dev(c["w"]), dev(c["context_lens"]), dev(pool_ref), bs,
+                                              dev(bt), maxc, block_stride_bytes=stride, num_blocks=nb)
+    got, idx = host(logits), host(idx_t)
+    ref_idx = oracle.topk_select(ref, ends, K)
+    for r in range(B):
+        e = int(ends[r])
+        assert_close(got[r][:e], ref[r][:e], what=f"row {r} logits")
+        check_selection(idx[r], ref_idx[r], ref[r], end=e)
+        assert np.sum(idx[r] >= 0) == min(K, e)
+    assert np.all(idx[700] == -1)
+
+
 @pytest.mark.parametrize("next_n", [1, 2])
 def test_decode_topk_call_ties_and_heavy_boundary(next_n):
     """Every key of a long row equal (one logit value over 40000 columns): the boundary bin holds more columns
