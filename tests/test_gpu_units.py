@@ -244,6 +244,38 @@ def test_topk_bf16_exact_values(width):
         assert np.array_equal(np.sort(f[r, got[r][got[r] >= 0]]), np.sort(f[r, ref[r][ref[r] >= 0]]))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_topk_many_long_rows(bf16):
+    """Enough long rows to fill the CUs (520 rows of 20000 columns): one 1024-thread workgroup per row, reading the
+    row twice; ordinary rows, heavy ties (the boundary bin larger than the candidate list, resolved by passes over
+    the row), rows with fewer than k finite values, ragged starts and ends; selected values against the oracle's."""
+    rng = np.random.default_rng(53 + bf16)
+    rows, width = 520, 20000
+    x = (rng.standard_normal((rows, width)) * 20).astype(np.float32)
+    x[1, :] = 3.0
+    x[2, 500:] = -np.inf
+    x[3] = np.round(x[3])
+    x[4, ::3] = 9.5
+    ends = rng.integers(15000, width + 1, rows).astype(np.int32)
+    starts = rng.integers(0, 3000, rows).astype(np.int32)
+    ends[:5], starts[:5] = width, 0
+    if bf16:
+        bits = synth._bf16_bits(x)
+        vals = bf16_value(bits)
+        ref = oracle.topk_select(bits, ends, 2048, starts=starts, bf16=True)
+        got = host(dsi.topk_select(dev(bits), dev(ends), k=2048, row_starts=dev(starts)))
+    else:
+        vals = x
+        ref = oracle.topk_select(x, ends, 2048, starts=starts)
+        got = host(dsi.topk_select(dev(x), dev(ends), k=2048, row_starts=dev(starts)))
+    for r in range(rows):
+        check_selection(got[r], ref[r], vals[r], rule="exact", start=starts[r], end=ends[r])
+        g = got[r][got[r] >= 0] + starts[r]
+        o = ref[r][ref[r] >= 0] + starts[r]
+        assert np.array_equal(np.sort(vals[r, g]), np.sort(vals[r, o]))
+    assert np.sum(got[2] >= 0) == 500
+
+
 @pytest.mark.parametrize("bf16,rows", [(False, 8), (True, 8), (False, 13)])
 def test_topk_split_long_rows(bf16, rows):
     """Few long rows are split between workgroups; cover the take-all, all-invalid, heavy-tie
